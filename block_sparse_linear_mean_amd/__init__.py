@@ -1,0 +1,111 @@
+"""Sparse-linear hybrid attention forward (SLA, SALAD, NSA-style selected blocks) on MI355X.
+
+The compute runs in libsla (HIP, gfx950); this package is its Python binding.
+Entry points keep the C names (see include/sla.h):
+
+    sla_pool_scores      block mean pooling of Q, K and pooled scores
+    sla_block_map        critical / marginal / negligible classification as CSR lists
+    sla_linear_kv_reduce per-key-block linear states H_j = phi(K_j)^T V_j, z_j
+    sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
+    sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
+
+`SlaForward` strings the four calls into one layer forward with every buffer
+allocated up front, so a step launches kernels only.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._lib import (  # noqa: F401
+    BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SlaError, alloc_block_map,
+    lib, sla_abi_version, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
+    sla_block_map_workspace_bytes, sla_counts, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
+    sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
+)
+
+
+class SlaForward:
+    """One attention-layer forward through libsla with preallocated buffers.
+
+    mode "sla":   top kh_bp critical, bottom kl_bp negligible, linear attention on marginal blocks.
+    mode "salad": top kh_bp sparse blocks plus the gated linear branch over all keys (w_gate [Hq, d]).
+    mode "nsa":   causal, GQA-shared selection of n_sel blocks plus a window of `window` tokens.
+    """
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_valid: int, mode: str,
+                 kh_bp: int = 0, kl_bp: int = 0, n_sel: int = 0, window: int = 0,
+                 w_gate: Optional[torch.Tensor] = None, scale: Optional[float] = None, out_dtype=None):
+        self.q, self.k, self.v = q, k, v
+        self.n_valid = n_valid
+        self.mode = mode
+        B, Hq, N, d = q.shape
+        Hkv = k.shape[1]
+        nb = N // BLOCK
+        self.scale = (1.0 / d ** 0.5) if scale is None else scale
+        self.window = 0
+        if mode == "sla":
+            self.n_crit, self.n_negl = sla_counts(nb, kh_bp, kl_bp)
+            self.causal, self.group = False, False
+            self.lin = SLA_LIN_MARGINAL
+        elif mode == "salad":
+            self.n_crit, _ = sla_counts(nb, kh_bp, 0)
+            self.n_negl = 0
+            self.causal, self.group = False, False
+            self.lin = SLA_LIN_GLOBAL_GATED
+            if w_gate is None:
+                raise ValueError("salad mode needs w_gate [Hq, d]")
+        elif mode == "nsa":
+            self.n_crit, self.n_negl = n_sel, 0
+            self.causal, self.group = True, True
+            self.window = window
+            self.lin = SLA_LIN_NONE
+        else:
+            raise ValueError(f"unknown mode {mode}")
+        self.w_gate = None if w_gate is None else w_gate.to(device=q.device, dtype=torch.float32).contiguous()
+        dev = q.device
+        f = dict(device=dev, dtype=torch.float32)
+        Hs = Hkv if self.group else Hq
+        self.pool = dict(q_pool=torch.empty((B, Hq, nb, d), **f), k_pool=torch.empty((B, Hkv, nb, d), **f),
+                         scores=torch.empty((B, Hs, nb, nb), **f))
+        self.maps = alloc_block_map(B, Hs, nb, nb, self.n_crit, self.n_negl, self.causal, self.window, dev,
+                                    want_marg=self.lin == SLA_LIN_MARGINAL)
+        self.kv = {}
+        if self.lin == SLA_LIN_MARGINAL:
+            self.kv = dict(H=torch.empty((B, Hkv, nb, d, d), **f), z=torch.empty((B, Hkv, nb, d), **f),
+                           workspace=None, workspace_bytes=0)
+        elif self.lin == SLA_LIN_GLOBAL_GATED:
+            ws = sla_kv_reduce_workspace_bytes(B, Hkv, N, d, False, True)
+            self.kv = dict(H_all=torch.empty((B, Hkv, d, d), **f), z_all=torch.empty((B, Hkv, d), **f),
+                           workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
+        ws = sla_attn_workspace_bytes(B, Hs, nb, d, self.lin)
+        self.attn_ws = torch.empty(ws, device=dev, dtype=torch.uint8) if ws else None
+        self.out = torch.empty(q.shape, device=dev, dtype=out_dtype or q.dtype)
+
+    def pool_scores(self):
+        return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
+                               scale=self.scale, out=self.pool)
+
+    def block_map(self):
+        return sla_block_map(self.pool["scores"], self.n_crit, self.n_negl, causal=self.causal,
+                             window=self.window, out=self.maps)
+
+    def kv_reduce(self):
+        if self.lin != SLA_LIN_NONE:
+            sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv)
+        return self.kv
+
+    def attention(self, maps=None):
+        kv = self.kv
+        return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
+                            scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
+                            H=kv.get("H"), z=kv.get("z"), H_all=kv.get("H_all"), z_all=kv.get("z_all"),
+                            w_gate=self.w_gate, out=self.out, workspace=self.attn_ws)
+
+    def run(self) -> torch.Tensor:
+        """One full forward: pool + scores, block map, linear states, attention."""
+        self.pool_scores()
+        self.block_map()
+        self.kv_reduce()
+        return self.attention()

@@ -1,0 +1,257 @@
+"""ctypes binding of libsla (include/sla.h): argument marshalling only.
+
+Every step of the forward runs in the HIP library; this module checks tensor
+placement, allocates outputs with torch on the tensors' device, passes raw device
+pointers, strides and torch's current HIP stream, and turns status codes into
+exceptions.  It fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint8, c_void_p
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsla.so")
+
+SLA_BF16, SLA_F32 = 0, 1
+SLA_LIN_NONE, SLA_LIN_MARGINAL, SLA_LIN_GLOBAL_GATED = 0, 1, 2
+BLOCK = 64
+
+
+class SlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class SlaTensor(ctypes.Structure):
+    _fields_ = [("ptr", c_void_p), ("dtype", c_int32), ("B", c_int32), ("H", c_int32), ("N", c_int32),
+                ("d", c_int32), ("sB", c_int64), ("sH", c_int64), ("sN", c_int64)]
+
+
+_lib = None
+_P = c_void_p
+_I32P = POINTER(c_int32)
+
+_SIGS = {
+    "sla_abi_version": (c_int32, []),
+    "sla_status_str": (c_char_p, [c_int32]),
+    "sla_counts": (c_int32, [c_int32, c_int32, c_int32, _I32P, _I32P]),
+    "sla_pool_scores": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_int32, c_int32, c_float,
+                                  _P, _P, _P, _P, _P]),
+    "sla_block_map_capacity": (c_int64, [c_int32] * 9),
+    "sla_block_map_workspace_bytes": (c_size_t, [c_int32] * 7),
+    "sla_block_map": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, c_size_t, _P]),
+    "sla_kv_reduce_workspace_bytes": (c_size_t, [c_int32] * 6),
+    "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P,
+                                       c_size_t, _P]),
+    "sla_marginal_states": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                      _P, _P, _P, _P, _P]),
+    "sla_attn_workspace_bytes": (c_size_t, [c_int32] * 5),
+    "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
+                               c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P, _P,
+                               c_int32, _P, c_size_t, _P]),
+}
+
+
+def lib():
+    """The loaded library (ctypes.CDLL).  Raises if libsla.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libsla.so not built at {LIB_PATH}: run `python -m block_sparse_linear_mean_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SlaError(fn, status, lib().sla_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libsla calls take GPU tensors")
+
+
+def tensor_desc(x: torch.Tensor) -> SlaTensor:
+    """Descriptor of a [B, H, N, d] bf16/fp32 tensor with unit d-stride."""
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("expected a [B, H, N, d] tensor with unit stride along d")
+    if x.dtype == torch.bfloat16:
+        dt = SLA_BF16
+    elif x.dtype == torch.float32:
+        dt = SLA_F32
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    B, H, N, d = x.shape
+    return SlaTensor(c_void_p(x.data_ptr()), dt, B, H, N, d, x.stride(0), x.stride(1), x.stride(2))
+
+
+# ----------------------------------------------------------------------------- host-only calls
+
+def sla_abi_version() -> int:
+    return lib().sla_abi_version()
+
+
+def sla_status_str(status: int) -> str:
+    return lib().sla_status_str(status).decode()
+
+
+def sla_counts(nb: int, kh_bp: int, kl_bp: int):
+    a, b = c_int32(), c_int32()
+    _check("sla_counts", lib().sla_counts(nb, kh_bp, kl_bp, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, which) -> int:
+    return lib().sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, int(causal), window, which)
+
+
+def sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, causal, window) -> int:
+    return lib().sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, int(causal), window)
+
+
+def sla_kv_reduce_workspace_bytes(B, Hkv, N, d, want_blocks, want_all) -> int:
+    return lib().sla_kv_reduce_workspace_bytes(B, Hkv, N, d, int(want_blocks), int(want_all))
+
+
+def sla_attn_workspace_bytes(B, Hs, nqb, d, lin_mode) -> int:
+    return lib().sla_attn_workspace_bytes(B, Hs, nqb, d, lin_mode)
+
+
+# ----------------------------------------------------------------------------- GPU calls
+
+def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, want_probs=False, out=None):
+    """Returns dict(q_pool, k_pool, scores[, probs]); `out` may hold preallocated tensors."""
+    _require_gpu(q, k)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nb = N // BLOCK
+    Hs = Hkv if group_sum else Hq
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    if out is None:
+        f = dict(device=q.device, dtype=torch.float32)
+        out = dict(q_pool=torch.empty((B, Hq, nb, d), **f), k_pool=torch.empty((B, Hkv, nb, d), **f),
+                   scores=torch.empty((B, Hs, nb, nb), **f))
+        if want_probs:
+            out["probs"] = torch.empty((B, Hs, nb, nb), **f)
+    qd, kd = tensor_desc(q), tensor_desc(k)
+    _check("sla_pool_scores", lib().sla_pool_scores(
+        ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale),
+        _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]), _ptr(out.get("probs")), _stream(q.device)))
+    return out
+
+
+def alloc_block_map(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, device, want_marg=True):
+    rows = B * Hs * nqb
+    cc = sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, 0)
+    mc = sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, 1) if want_marg else 0
+    if cc < 0 or mc < 0:
+        raise ValueError("invalid block-map sizes")
+    i32 = dict(device=device, dtype=torch.int32)
+    m = dict(crit_rowptr=torch.empty(rows + 1, **i32), crit_idx=torch.empty(max(cc, 1), **i32),
+             crit_flags=torch.empty(max(cc, 1), device=device, dtype=torch.uint8),
+             row_counts=torch.empty((rows, 3), **i32), crit_cap=cc, marg_cap=mc)
+    if want_marg and not causal:
+        m["marg_rowptr"] = torch.empty(rows + 1, **i32)
+        m["marg_idx"] = torch.empty(max(mc, 1), **i32)
+    ws = sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, causal, window)
+    m["workspace"] = torch.empty(max(ws, 16), device=device, dtype=torch.uint8) if ws else None
+    m["workspace_bytes"] = ws
+    return m
+
+
+def sla_block_map(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=True, out=None):
+    """Block map of scores [B, Hs, nqb, nkb]; returns the dict of CSR tensors."""
+    _require_gpu(scores)
+    B, Hs, nqb, nkb = scores.shape
+    if out is None:
+        out = alloc_block_map(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, scores.device, want_marg)
+    _check("sla_block_map", lib().sla_block_map(
+        _ptr(scores), B, Hs, nqb, nkb, n_crit, n_negl, int(causal), window,
+        _ptr(out["crit_rowptr"]), _ptr(out["crit_idx"]), _ptr(out["crit_flags"]), out["crit_cap"],
+        _ptr(out.get("marg_rowptr")), _ptr(out.get("marg_idx")), out["marg_cap"],
+        _ptr(out["row_counts"]), _ptr(out["workspace"]), out["workspace_bytes"], _stream(scores.device)))
+    return out
+
+
+def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None):
+    """Returns dict(H, z[, H_all, z_all])."""
+    _require_gpu(k, v)
+    B, Hkv, N, d = k.shape
+    nb = N // BLOCK
+    if out is None:
+        f = dict(device=k.device, dtype=torch.float32)
+        out = {}
+        if per_block:
+            out["H"] = torch.empty((B, Hkv, nb, d, d), **f)
+            out["z"] = torch.empty((B, Hkv, nb, d), **f)
+        if want_all:
+            out["H_all"] = torch.empty((B, Hkv, d, d), **f)
+            out["z_all"] = torch.empty((B, Hkv, d), **f)
+        ws = sla_kv_reduce_workspace_bytes(B, Hkv, N, d, per_block, want_all)
+        out["workspace"] = torch.empty(ws, device=k.device, dtype=torch.uint8) if ws else None
+        out["workspace_bytes"] = ws
+    kd, vd = tensor_desc(k), tensor_desc(v)
+    _check("sla_linear_kv_reduce", lib().sla_linear_kv_reduce(
+        ctypes.byref(kd), ctypes.byref(vd), n_valid, _ptr(out.get("H")), _ptr(out.get("z")),
+        _ptr(out.get("H_all")), _ptr(out.get("z_all")), _ptr(out.get("workspace")), out.get("workspace_bytes", 0),
+        _stream(k.device)))
+    return out
+
+
+def sla_marginal_states(H, z, Hq, group_map, marg_rowptr, marg_idx):
+    """S [rows, d, d], u [rows, d] for the map's rows (rows = B * Hs * nqb)."""
+    _require_gpu(H, z, marg_rowptr, marg_idx)
+    B, Hkv, nb, d, _ = H.shape
+    Hs = Hkv if group_map else Hq
+    rows = B * Hs * nb
+    S = torch.empty((rows, d, d), device=H.device, dtype=torch.float32)
+    u = torch.empty((rows, d), device=H.device, dtype=torch.float32)
+    _check("sla_marginal_states", lib().sla_marginal_states(
+        _ptr(H), _ptr(z), B, Hq, Hkv, nb, nb, d, int(group_map), _ptr(marg_rowptr), _ptr(marg_idx), _ptr(S),
+        _ptr(u), _stream(H.device)))
+    return S, u
+
+
+def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, causal=False, window=0,
+                 group_map=False, H=None, z=None, H_all=None, z_all=None, w_gate=None, out=None,
+                 out_dtype=None, workspace=None):
+    """Attention output [B, Hq, N, d]; `maps` is the dict returned by sla_block_map."""
+    _require_gpu(q, k, v)
+    B, Hq, N, d = q.shape
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    odt = SLA_F32 if out.dtype == torch.float32 else SLA_BF16
+    Hs = k.shape[1] if group_map else Hq
+    ws_bytes = sla_attn_workspace_bytes(B, Hs, N // BLOCK, d, lin_mode)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    qd, kd, vd = tensor_desc(q), tensor_desc(k), tensor_desc(v)
+    _check("sla_attn_fwd", lib().sla_attn_fwd(
+        ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), n_valid, float(scale), int(causal), window,
+        int(group_map), _ptr(maps["crit_rowptr"]), _ptr(maps["crit_idx"]), _ptr(maps.get("crit_flags")),
+        _ptr(maps.get("marg_rowptr")), _ptr(maps.get("marg_idx")), lin_mode, _ptr(H), _ptr(z), _ptr(H_all),
+        _ptr(z_all), _ptr(w_gate), _ptr(out), odt, _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out

@@ -1,0 +1,45 @@
+// Host-side helpers shared by the libsla entry points: argument validation and launch checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sla.h"
+
+namespace sla {
+
+inline int elem_bytes(int32_t dtype) { return dtype == SLA_BF16 ? 2 : 4; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates one [B, H, N, d] input descriptor (see the conventions in sla.h).
+inline sla_status check_tensor(const sla_tensor* t) {
+  if (t == nullptr || t->ptr == nullptr) return SLA_ERR_NULL;
+  if (t->dtype != SLA_BF16 && t->dtype != SLA_F32) return SLA_ERR_UNSUPPORTED;
+  if (t->B < 1 || t->H < 1 || t->N < SLA_BLOCK || t->N % SLA_BLOCK != 0) return SLA_ERR_SHAPE;
+  if (t->d != 64 && t->d != 128) return SLA_ERR_UNSUPPORTED;
+  if (t->N / SLA_BLOCK > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
+  if (t->sN < t->d || t->sH < 1 || t->sB < 1) return SLA_ERR_SHAPE;
+  const int64_t eb = elem_bytes(t->dtype);
+  if (!aligned16(t->ptr) || (t->sN * eb) % 16 || (t->sH * eb) % 16 || (t->sB * eb) % 16)
+    return SLA_ERR_ALIGN;
+  return SLA_OK;
+}
+
+inline bool same_geometry(const sla_tensor* a, const sla_tensor* b) {
+  return a->dtype == b->dtype && a->B == b->B && a->N == b->N && a->d == b->d;
+}
+
+inline sla_status check_valid_len(int32_t n_valid, int32_t N) {
+  if (n_valid <= N - SLA_BLOCK || n_valid > N) return SLA_ERR_RANGE;
+  return SLA_OK;
+}
+
+inline sla_status launch_status() {
+  return hipGetLastError() == hipSuccess ? SLA_OK : SLA_ERR_HIP;
+}
+
+// Key blocks touched by a sliding window of w tokens on either side of the diagonal block.
+inline int32_t window_reach(int32_t w) { return w > 0 ? (w + SLA_BLOCK - 2) / SLA_BLOCK : -1; }
+
+}  // namespace sla

@@ -1,0 +1,234 @@
+/*
+ * libsla — forward pass of sparse-linear hybrid attention on AMD MI355X (gfx950).
+ *
+ * The method (SLA analysis page for arXiv 2509.24006; "2025稀疏注意力架构综述",
+ * section 10 SLA and section 11 SpargeAttn prediction formulas):
+ *   1. predict:  mean-pool Q and K over 64-token blocks and score every
+ *                (query block, key block) pair with the pooled vectors;
+ *   2. classify: per query-block row the top share of key blocks is critical,
+ *                the bottom share negligible, the rest marginal;
+ *   3. execute:  critical pairs get exact softmax attention, marginal pairs
+ *                linear attention with phi = elu + 1 through per-key-block
+ *                states H_j = phi(K_j)^T V_j and z_j = sum phi(K_j),
+ *                negligible pairs are skipped;
+ *   4. combine:  O = O_sparse + O_linear (the learned projection on the linear
+ *                branch is the identity here).
+ * Variants: the SALAD gated linear branch over all keys (SALAD page, method
+ * framework) and an NSA-style selected-block + sliding-window causal branch
+ * whose block selection is shared by a GQA group ("Sparse Attention 方法综述",
+ * section 2 NSA and its key-parameter table).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named in an sla_tensor, and every float / int buffer argument, are
+ *   DEVICE pointers owned by the caller.  The library keeps no pointer after a
+ *   call returns and allocates no device memory: scratch space comes in through
+ *   `workspace` arguments sized by the matching *_workspace_bytes() query.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL = the null stream).  The caller keeps every buffer alive until the
+ *   stream has passed the work.  Calls never synchronise.
+ * - Arguments are validated on the host before anything is launched; an invalid
+ *   argument returns an error code and launches nothing.  A failed launch
+ *   returns SLA_ERR_HIP.  Device faults surface at the caller's next sync.
+ * - Q, K, V use layout [B, H, N, d] with element strides (sB, sH, sN) and unit
+ *   d-stride; rows are 16-byte aligned.  d is 64 or 128, the block size is 64,
+ *   N is a multiple of 64 and at most one block is partial:
+ *   N - 64 < n_valid <= N.  Positions >= n_valid are padding: they are excluded
+ *   from pooled means and from both attention branches, and the output rows of
+ *   padded queries are written as zeros.
+ * - All library outputs are dense row-major arrays with the shapes stated.
+ * - The calls are reentrant and keep no global mutable state.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLA_ABI_VERSION 1
+#define SLA_BLOCK 64
+#define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
+
+typedef int32_t sla_status;
+enum {
+  SLA_OK = 0,
+  SLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SLA_ERR_SHAPE = 2,       /* inconsistent or unsupported sizes */
+  SLA_ERR_ALIGN = 3,       /* a pointer or row stride is not 16-byte aligned */
+  SLA_ERR_RANGE = 4,       /* a count, share or length is out of range */
+  SLA_ERR_UNSUPPORTED = 5, /* valid but unsupported combination */
+  SLA_ERR_CAPACITY = 6,    /* an output capacity is too small */
+  SLA_ERR_HIP = 7,         /* a HIP launch failed */
+  SLA_ERR_WORKSPACE = 8    /* workspace missing or smaller than required */
+};
+
+enum { SLA_BF16 = 0, SLA_F32 = 1 };
+
+/* Linear-branch modes of sla_attn_fwd. */
+enum {
+  SLA_LIN_NONE = 0,         /* sparse branch only (NSA-style selected + window) */
+  SLA_LIN_MARGINAL = 1,     /* SLA: linear attention over each row's marginal blocks */
+  SLA_LIN_GLOBAL_GATED = 2  /* SALAD: gated linear attention over all valid keys */
+};
+
+typedef struct {
+  const void* ptr;       /* device pointer to element [0, 0, 0, 0] */
+  int32_t dtype;         /* SLA_BF16 or SLA_F32 */
+  int32_t B, H, N, d;
+  int64_t sB, sH, sN;    /* element strides; the d stride is 1 */
+} sla_tensor;
+
+/* ABI version of the loaded library (SLA_ABI_VERSION of its build). */
+int32_t sla_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sla_status_str(sla_status s);
+
+/*
+ * Critical and negligible block counts of a row of nb candidates, from shares in
+ * basis points (the pages give percentages per row; a fixed-budget top-k keeps the
+ * same number per row — subquadratic sparse attention probe, reading notes).
+ * n_crit = ceil(kh_bp * nb / 10000) (0 iff kh_bp == 0);
+ * n_negl = min(floor(kl_bp * nb / 10000), nb - n_crit).
+ * Host-only; returns SLA_ERR_RANGE unless 1 <= nb and 0 <= kh_bp, kl_bp <= 10000.
+ */
+sla_status sla_counts(int32_t nb, int32_t kh_bp, int32_t kl_bp, int32_t* n_crit, int32_t* n_negl);
+
+/*
+ * Prediction step (SpargeAttn prediction formulas in "2025稀疏注意力架构综述",
+ * section 11; mean-pooled compressed prediction on the SLA analysis page).
+ *
+ *   q_pool[b,h,i,:]  = mean of the valid rows of block i of Q[b,h]   (fp32, [B,Hq,nb,d])
+ *   k_pool[b,g,j,:]  = the same for K[b,g]                            (fp32, [B,Hkv,nb,d])
+ *   scores[b,s,i,j]  = fp32( scale * (qsum . k_pool[b,g,j]) )         (fp32, [B,Hs,nb,nb])
+ *     group_sum == 0: Hs = Hq, s = h, g = h / (Hq/Hkv), qsum = q_pool[b,h,i];
+ *     group_sum != 0: Hs = Hkv, s = g, qsum = sum of q_pool[b,h,i] over the group's heads.
+ *     Means and the dot product are taken in fp64; each stored value is rounded once.
+ *     causal != 0: entries j > i are -inf.
+ *   probs (nullable) = row softmax of scores over the row's finite candidates (fp32,
+ *     same shape as scores), for diagnostics; the classification ranks the scores.
+ * q and k share dtype and d; n_valid as in the conventions; scale > 0 (normally 1/sqrt(d)).
+ */
+sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
+                           int32_t group_sum, int32_t causal, float scale,
+                           float* q_pool, float* k_pool, float* scores, float* probs, void* stream);
+
+/*
+ * Number of block-map index entries to allocate for `rows` rows (rows = B * Hs * nqb).
+ * which = 0: critical (selected) list, which = 1: marginal list.  Non-causal maps are
+ * exact (rows * n_crit and rows * (nkb - n_crit - n_negl)); causal maps return an upper
+ * bound.  Returns -1 for invalid arguments.
+ */
+int64_t sla_block_map_capacity(int32_t B, int32_t Hs, int32_t nqb, int32_t nkb, int32_t n_crit,
+                               int32_t n_negl, int32_t causal, int32_t window_tokens, int32_t which);
+
+/* Workspace bytes sla_block_map needs (0 for non-causal maps). */
+size_t sla_block_map_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t nkb, int32_t n_crit,
+                                     int32_t causal, int32_t window_tokens);
+
+/*
+ * Classification step (three classes per Q-K block pair: SLA analysis page,
+ * comparison tables; NSA selection and window: "Sparse Attention 方法综述", section 2).
+ *
+ * Input scores [B, Hs, nqb, nkb] fp32 (as written by sla_pool_scores).  Rows are
+ * r = (b * Hs + s) * nqb + i.  Each row is ranked by one total order: score
+ * descending, then key-block index ascending; -0.0 equals +0.0 and NaN ranks last.
+ *
+ * Non-causal (nqb, nkb any; n_crit + n_negl <= nkb):
+ *   critical = first n_crit of the order, negligible = last n_negl, marginal = the rest.
+ *   crit_rowptr[r] = r * n_crit, marg_rowptr[r] = r * (nkb - n_crit - n_negl).
+ *   crit_flags (nullable) entries are 1.  marg_rowptr/marg_idx may both be NULL to skip
+ *   the marginal list.
+ * Causal (nqb == nkb, NSA-style): candidates are j <= i; the first min(n_crit, i + 1)
+ *   of the order are selected (flag bit 0) and united with the window blocks
+ *   max(0, i - floor((window_tokens + 62) / 64)) .. i (flag bit 1; none when
+ *   window_tokens == 0).  n_negl is ignored, the marginal list is empty and its
+ *   pointers may be NULL.  Needs the workspace.
+ *
+ * Outputs (int32 unless stated): crit_rowptr [rows + 1], crit_idx [crit_cap] ascending
+ * block indices per row, crit_flags [crit_cap] uint8, marg_rowptr [rows + 1],
+ * marg_idx [marg_cap], row_counts [rows][3] = (critical, marginal, negligible).
+ * crit_cap / marg_cap must be at least sla_block_map_capacity(...): SLA_ERR_CAPACITY.
+ */
+sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                         int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                         int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags, int64_t crit_cap,
+                         int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap,
+                         int32_t* row_counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sla_linear_kv_reduce needs (non-zero only when H is NULL and H_all is not). */
+size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, int32_t want_blocks,
+                                     int32_t want_all);
+
+/*
+ * Linear-attention key states (SLA analysis page: marginal pairs get linear attention,
+ * O(N d^2); phi = elu + 1).  Per KV head and key block j, over the valid rows s:
+ *   H[b,g,j,r,c] = sum_s phi(K[s,r]) * V[s,c]   (fp32, [B, Hkv, nb, d, d]; nullable)
+ *   z[b,g,j,r]   = sum_s phi(K[s,r])            (fp32, [B, Hkv, nb, d];     nullable with H)
+ *   H_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d, d];     nullable)
+ *   z_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d];        nullable with H_all)
+ * phi(K) is rounded to bf16 for the matrix-core contraction (fp32 accumulation); z sums
+ * the same rounded values.  At least one of H, H_all must be non-NULL.  When H is NULL
+ * and H_all is not, a workspace of sla_kv_reduce_workspace_bytes(..., 0, 1) is needed.
+ */
+sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
+                                float* H, float* z, float* H_all, float* z_all,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Marginal aggregation of one block map: for every map row r with KV head g,
+ *   S[r] = sum over marginal blocks j of H[b,g,j]  (fp32, [rows, d, d])
+ *   u[r] = sum over marginal blocks j of z[b,g,j]  (fp32, [rows, d])
+ * rows = B * Hs * nqb with Hs = Hkv if group_map else Hq; the KV head of map head s is
+ * s if group_map else s / (Hq / Hkv).  Sums run in ascending block order (deterministic).
+ * sla_attn_fwd performs this step itself; this entry exposes it on its own.
+ */
+sla_status sla_marginal_states(const float* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t nqb, int32_t nkb, int32_t d, int32_t group_map,
+                               const int32_t* marg_rowptr, const int32_t* marg_idx,
+                               float* S, float* u, void* stream);
+
+/* Workspace bytes sla_attn_fwd needs for (B, Hs map heads, nqb query blocks, d, lin mode). */
+size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, int32_t lin_mode);
+
+/*
+ * Attention step: exact block-sparse softmax attention over each query block's
+ * critical list (FlashAttention-style online softmax; SLA analysis page, the
+ * FlashAttn + linear attention pairing) plus the linear branch, summed
+ * (O = O_sparse + O_linear, projection = identity).
+ *
+ * For query row t of head h in block i, map row r = (b * Hs + s) * nqb + i with
+ * s = h / (Hq/Hkv) if group_map else h, KV head g = h / (Hq/Hkv):
+ *   O_sparse[t] = softmax over allowed keys of (scale * q_t . k_s) applied to v_s, or 0
+ *     when no key is allowed.  Allowed: s < n_valid in a listed block; causal != 0 adds
+ *     s <= t and (flag bit 0 of the block, or t - s < window_tokens).
+ *   lin_mode SLA_LIN_MARGINAL (needs marg_rowptr, marg_idx, H, z):
+ *     O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the sums of H_j and
+ *     z_j over row r's marginal blocks; 0 when the row has none.
+ *   lin_mode SLA_LIN_GLOBAL_GATED (needs H_all, z_all, w_gate [Hq][d] fp32):
+ *     O_linear[t] = sigmoid(q_t . w_gate[h]) * phi(q_t)^T H_all / (phi(q_t) . z_all).
+ *   Rows t >= n_valid are written as 0.
+ * q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; all the same dtype.  out: contiguous
+ * [B, Hq, N, d] in out_dtype (SLA_BF16 or SLA_F32).  The linear branch needs causal == 0.
+ * Arithmetic: bf16 matrix-core products (fp32 inputs are rounded to bf16), fp32
+ * softmax statistics and accumulators.
+ * workspace: sla_attn_workspace_bytes(B, Hs, nqb, d, lin_mode) bytes (0 unless MARGINAL).
+ */
+sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
+                        float scale, int32_t causal, int32_t window_tokens, int32_t group_map,
+                        const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
+                        const int32_t* marg_rowptr, const int32_t* marg_idx,
+                        int32_t lin_mode, const float* H, const float* z,
+                        const float* H_all, const float* z_all, const float* w_gate,
+                        void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

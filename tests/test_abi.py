@@ -1,0 +1,171 @@
+"""The C-ABI library loads, exports every symbol include/sla.h declares, and rejects invalid
+arguments on the host with the documented status codes.  CPU only: no call here reaches a
+kernel launch (every call either launches nothing or fails validation first)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+sla = pytest.importorskip("block_sparse_linear_mean_amd")
+from block_sparse_linear_mean_amd import _lib  # noqa: E402
+
+OK, ENULL, ESHAPE, EALIGN, ERANGE, EUNSUP, ECAP, EHIP, EWS = range(9)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsla.so is not built: run python -m block_sparse_linear_mean_amd.build")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), f"libsla.so does not export {n}"
+    assert set(names) == set(_lib._SIGS), "binding signatures and header declarations differ"
+
+
+def test_version_and_status_strings(L):
+    assert sla.sla_abi_version() == 1
+    for s in range(9):
+        assert len(sla.sla_status_str(s)) > 0
+    assert sla.sla_status_str(12345) == "unknown status"
+
+
+def test_counts_match_golden(L):
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "counts.json")))
+    for c in data["cases"]:
+        assert sla.sla_counts(c["nb"], c["kh_bp"], c["kl_bp"]) == (c["n_h"], c["n_l"]), c["what"]
+    with pytest.raises(sla.SlaError):
+        sla.sla_counts(0, 100, 100)
+    with pytest.raises(sla.SlaError):
+        sla.sla_counts(10, 10001, 0)
+
+
+def test_capacities_and_workspaces(L):
+    # non-causal maps are exact
+    assert sla.sla_block_map_capacity(1, 12, 512, 512, 26, 435, 0, 0, 0) == 12 * 512 * 26
+    assert sla.sla_block_map_capacity(1, 12, 512, 512, 26, 435, 0, 0, 1) == 12 * 512 * 51
+    assert sla.sla_block_map_capacity(1, 1, 16, 16, 10, 10, 0, 0, 0) == -1
+    # causal: row i holds at most min(i + 1, 16 + 9) blocks
+    nb = 1024
+    ub = sum(min(i + 1, 25) for i in range(nb))
+    assert sla.sla_block_map_capacity(1, 1, nb, nb, 16, 0, 1, 512, 0) == ub
+    assert sla.sla_block_map_capacity(1, 1, nb, nb, 16, 0, 1, 512, 1) == 0
+    assert sla.sla_block_map_workspace_bytes(1, 1, nb, nb, 16, 0, 512) == 0
+    assert sla.sla_block_map_workspace_bytes(1, 1, nb, nb, 16, 1, 512) >= nb * 25 * 5
+    assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 + 128) * 4
+    assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_NONE) == 0
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 0
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 16 * (128 * 128 + 128) * 4
+
+
+def desc(ptr=0x10000, dtype=0, B=1, H=2, N=256, d=128, sB=None, sH=None, sN=None):
+    sN = d if sN is None else sN
+    sH = N * sN if sH is None else sH
+    sB = H * sH if sB is None else sB
+    return _lib.SlaTensor(ctypes.c_void_p(ptr), dtype, B, H, N, d, sB, sH, sN)
+
+
+P = ctypes.c_void_p(0x20000)   # a fake, 16-byte aligned device address: never dereferenced
+
+
+def pool_call(L, q, k, n_valid=256, scale=0.1, qp=P, kp=P, sc=P):
+    return L.sla_pool_scores(ctypes.byref(q), ctypes.byref(k), n_valid, 0, 0, scale, qp, kp, sc, None, None)
+
+
+def test_pool_scores_validation(L):
+    good = desc()
+    assert pool_call(L, desc(ptr=0), good) == ENULL
+    assert pool_call(L, good, good, qp=None) == ENULL
+    assert pool_call(L, desc(d=96), desc(d=96)) == EUNSUP
+    assert pool_call(L, desc(dtype=7), good) == EUNSUP
+    assert pool_call(L, desc(N=200), desc(N=200)) == ESHAPE
+    assert pool_call(L, desc(ptr=0x10008), good) == EALIGN
+    assert pool_call(L, desc(sN=132), desc(sN=132)) == EALIGN
+    assert pool_call(L, good, desc(N=512)) == ESHAPE
+    assert pool_call(L, desc(H=3), desc(H=2)) == ESHAPE
+    assert pool_call(L, good, good, n_valid=192) == ERANGE      # more than one partial block
+    assert pool_call(L, good, good, n_valid=257) == ERANGE
+    assert pool_call(L, good, good, scale=0.0) == ERANGE
+    assert pool_call(L, good, good, scale=float("nan")) == ERANGE
+    assert pool_call(L, desc(N=64 * 4097), desc(N=64 * 4097)) == EUNSUP
+
+
+def test_block_map_validation(L):
+    def call(scores=P, B=1, Hs=1, nqb=16, nkb=16, nc=4, nn=8, causal=0, win=0, crp=P, ci=P, ccap=64,
+             mrp=P, mi=P, mcap=64, rc=P, ws=None, wsb=0):
+        return L.sla_block_map(scores, B, Hs, nqb, nkb, nc, nn, causal, win, crp, ci, None, ccap, mrp, mi, mcap,
+                               rc, ws, wsb, None)
+    assert call(scores=None) == ENULL
+    assert call(crp=None) == ENULL
+    assert call(rc=None) == ENULL
+    assert call(mrp=None) == ENULL            # marginal pointers must come together
+    assert call(nqb=0) == ESHAPE
+    assert call(nkb=5000) == EUNSUP
+    assert call(nc=-1) == ERANGE
+    assert call(nc=10, nn=10) == ERANGE
+    assert call(ccap=63) == ECAP
+    assert call(mcap=63) == ECAP
+    assert call(causal=1, nqb=16, nkb=15) == ESHAPE
+    assert call(causal=1, nc=4, win=128, ccap=10) == ECAP
+    assert call(causal=1, nc=4, win=128, ccap=1000) == EWS        # workspace missing
+    assert call(causal=1, nc=4, win=128, ccap=1000, ws=P, wsb=1) == EWS
+
+
+def test_kv_reduce_validation(L):
+    k = desc()
+    def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0):
+        return L.sla_linear_kv_reduce(ctypes.byref(kk), ctypes.byref(vv), nv, H, z, Ha, za, ws, wsb, None)
+    assert call(H=None, z=None) == ENULL
+    assert call(z=None) == ENULL
+    assert call(Ha=P, za=None) == ENULL
+    assert call(vv=desc(H=3)) == ESHAPE
+    assert call(vv=desc(dtype=1)) == ESHAPE
+    assert call(nv=0) == ERANGE
+    assert call(H=None, z=None, Ha=P, za=P) == EWS
+
+
+def test_marginal_states_validation(L):
+    def call(H=P, z=P, B=1, Hq=2, Hkv=1, nqb=4, nkb=4, d=128, rp=P, ix=P, S=P, u=P):
+        return L.sla_marginal_states(H, z, B, Hq, Hkv, nqb, nkb, d, 0, rp, ix, S, u, None)
+    assert call(H=None) == ENULL
+    assert call(rp=None) == ENULL
+    assert call(Hq=3, Hkv=2) == ESHAPE
+    assert call(d=96) == EUNSUP
+    assert call(S=ctypes.c_void_p(0x20004)) == EALIGN
+
+
+def test_attn_fwd_validation(L):
+    q = desc()
+    def call(qq=q, kk=q, vv=q, nv=256, scale=0.1, causal=0, win=0, group=0, crp=P, ci=P, cf=None, mrp=None,
+             mi=None, lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0):
+        return L.sla_attn_fwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), nv, scale, causal, win, group,
+                              crp, ci, cf, mrp, mi, lin, H, z, Ha, za, wg, out, odt, ws, wsb, None)
+    assert call(out=None) == ENULL
+    assert call(crp=None) == ENULL
+    assert call(causal=1) == ENULL                   # causal needs the flags
+    assert call(causal=1, cf=P, lin=1) == EUNSUP     # no linear branch under a causal mask
+    assert call(lin=1) == ENULL                      # marginal mode needs H, z and the marginal lists
+    assert call(lin=1, H=P, z=P, mrp=P, mi=P) == EWS
+    assert call(lin=2) == ENULL
+    assert call(lin=3) == EUNSUP
+    assert call(odt=5) == EUNSUP
+    assert call(out=ctypes.c_void_p(0x20002)) == EALIGN
+    assert call(kk=desc(H=3), vv=desc(H=3)) == ESHAPE
+    assert call(vv=desc(H=1)) == ESHAPE
+    assert call(win=-1) == ERANGE
+    assert call(nv=64) == ERANGE

@@ -1,0 +1,251 @@
+"""GPU parity of the HIP path (through the C-ABI) against the CPU oracle on seeded inputs.
+
+Bars: pooled vectors bit-exact, pooled scores within one fp32 ulp; block maps bit-exact given
+identical scores (the oracle's scores are uploaded); linear states within bf16-operand
+rounding; outputs within rel-L2 1e-2 and max-abs 3e-2 of the oracle, over every valid row.
+Sizes span several 64x64 score tiles and a ragged last block.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sla_oracle as orc
+from tests import refs
+from tests.gpu_helpers import (compare_outputs, gpu_map_rows, host, layer_for, oracle_csr, oracle_for, say,
+                               to_dev, ulp_distance)
+from workloads import WORKLOADS, make_inputs, scaled
+
+pytestmark = pytest.mark.gpu
+
+W = WORKLOADS
+MEDIUM = {
+    "tiny_sla": W["tiny_sla"],
+    "med_sla": scaled(W["wan13b_sla"], "med_sla", grid=(5, 18, 46), Hq=2, Hkv=2, kh_bp=2500, kl_bp=5000),
+    "med_sla_5pct": scaled(W["wan13b_sla"], "med_sla_5pct", grid=(5, 18, 46), Hq=2, Hkv=2),
+    "med_sla_d64": scaled(W["wan13b_sla"], "med_sla_d64", grid=(4, 9, 20), Hq=2, Hkv=2, d=64, kh_bp=1500,
+                          kl_bp=6000),
+    "med_salad": scaled(W["salad"], "med_salad", grid=(5, 18, 46), Hq=2, Hkv=2),
+    "med_nsa": scaled(W["nsa_prefill"], "med_nsa", N=4160, Nv=4150),
+    "med_nsa_full": scaled(W["nsa_prefill"], "med_nsa_full", N=2048, Nv=2048, Hq=4),
+    "med_gqa_sla": scaled(W["tiny_sla"], "med_gqa_sla", Hq=4, Hkv=2, N=1280, Nv=1250, d=128, dtype="bf16",
+                          kh_bp=3000, kl_bp=4000),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+_cache = {}
+
+
+def case(name):
+    """(workload, inputs, oracle Forward, layer) for a named medium case, built once."""
+    if name not in _cache:
+        w = MEDIUM[name]
+        q, k, v, wg = make_inputs(w)
+        _cache[name] = (w, (q, k, v, wg), oracle_for(w, q, k, v, wg), layer_for(w, q, k, v, wg))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_pool_scores(name):
+    say(f"[pool_scores] {name}")
+    w, (q, k, v, wg), f, layer = case(name)
+    out = layer.pool_scores()
+    torch.cuda.synchronize()
+    qp, kp = orc.pool(host(q), w.Nv), orc.pool(host(k), w.Nv)
+    assert np.array_equal(host(out["q_pool"]), qp)
+    assert np.array_equal(host(out["k_pool"]), kp)
+    S = orc.pooled_scores(qp, kp, orc.default_scale(w.d), group_sum=f.group_sum, causal=f.causal)
+    Sg = host(out["scores"])
+    assert np.array_equal(np.isneginf(Sg), np.isneginf(S))
+    fin = np.isfinite(S)
+    ulp = ulp_distance(Sg[fin], S[fin])
+    say(f"  scores: {np.count_nonzero(ulp)} of {ulp.size} differ, max {ulp.max()} ulp")
+    assert ulp.max() <= 1 and np.count_nonzero(ulp) <= max(2, ulp.size // 10000)
+    # diagnostic softmax of the rows
+    pr = torch.empty_like(out["scores"])
+    import block_sparse_linear_mean_amd as sla
+    sla.sla_pool_scores(layer.q, layer.k, w.Nv, group_sum=f.group_sum, causal=f.causal,
+                        out=dict(out, probs=pr))
+    torch.cuda.synchronize()
+    assert np.allclose(host(pr), orc.score_probs(S), rtol=1e-4, atol=1e-6)
+
+
+def _map_from_scores(S_np, n_crit, n_negl, causal, window):
+    import block_sparse_linear_mean_amd as sla
+    return sla.sla_block_map(to_dev(S_np, torch.float32), n_crit, n_negl, causal=causal, window=window)
+
+
+def _check_map(maps, S, n_crit, n_negl, causal, window, n_sel):
+    B, Hs, nqb, nkb = S.shape
+    rows = list(range(B * Hs * nqb))
+    got = gpu_map_rows(maps, rows)
+    ref = orc.block_map(S, n_h=n_crit, n_l=n_negl, causal=causal, n_sel=n_sel, window=window)
+    for r in rows:
+        b, rem = divmod(r, Hs * nqb)
+        h, i = divmod(rem, nqb)
+        m = ref[(b, h, i)]
+        crit, flags, marg, counts = got[r]
+        assert crit == m["crit"], (r, crit, m["crit"])
+        assert flags == m["flags"], (r, flags, m["flags"])
+        if not causal:
+            assert marg == m["marg"], (r, marg, m["marg"])
+        assert counts == (len(m["crit"]), len(m["marg"]), len(m["negl"])), r
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_block_map_identical_scores(name):
+    say(f"[block_map identical scores] {name}")
+    w, _, f, layer = case(name)
+    Hs = f.Hkv if f.group_sum else f.Hq
+    S = orc.pooled_scores(orc.pool(f.Q, w.Nv), orc.pool(f.K, w.Nv), f.scale, group_sum=f.group_sum,
+                          causal=f.causal)
+    maps = _map_from_scores(S, f.n_h if not f.causal else f.n_sel, f.n_l, f.causal, f.window)
+    torch.cuda.synchronize()
+    assert S.shape[1] == Hs
+    _check_map(maps, S, f.n_h, f.n_l, f.causal, f.window, f.n_sel)
+
+
+@pytest.mark.parametrize("nkb", [1, 7, 64, 65, 200, 700, 1300, 2100])
+def test_block_map_ties_nan_signed_zero(nkb):
+    say(f"[block_map ties] nkb={nkb}")
+    r = np.random.default_rng(nkb)
+    levels = np.array([-2.0, -0.5, -0.0, 0.0, 0.5, 0.5, 1.0, 7.0], np.float32)
+    rows = 40
+    S = r.choice(levels, size=(1, 2, rows, nkb)).astype(np.float32)
+    S[r.random(S.shape) < 0.02] = np.nan
+    S[r.random(S.shape) < 0.02] = -np.inf
+    S[r.random(S.shape) < 0.01] = np.inf
+    for kh, kl in [(0, 0), (2500, 5000), (500, 8500), (10000, 0), (9000, 1000)]:
+        nc, nn = orc.block_counts(nkb, kh, kl)
+        maps = _map_from_scores(S, nc, nn, False, 0)
+        torch.cuda.synchronize()
+        _check_map(maps, S, nc, nn, False, 0, 0)
+
+
+@pytest.mark.parametrize("nb,n_sel,window", [(40, 16, 512), (130, 16, 512), (130, 4, 0), (70, 0, 100),
+                                             (300, 16, 64)])
+def test_block_map_causal_ties(nb, n_sel, window):
+    say(f"[block_map causal] nb={nb} n_sel={n_sel} window={window}")
+    r = np.random.default_rng(nb + n_sel)
+    S = r.choice(np.array([-1.0, 0.0, 0.25, 0.25, 2.0], np.float32), size=(1, 2, nb, nb)).astype(np.float32)
+    S[:, :, np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]] = -np.inf
+    maps = _map_from_scores(S, n_sel, 0, True, window)
+    torch.cuda.synchronize()
+    _check_map(maps, S, 0, 0, True, window, n_sel)
+
+
+@pytest.mark.parametrize("name", ["tiny_sla", "med_sla", "med_sla_d64", "med_gqa_sla", "med_salad"])
+def test_linear_states(name):
+    say(f"[kv states] {name}")
+    w, _, f, layer = case(name)
+    import block_sparse_linear_mean_amd as sla
+    out = sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv, per_block=True, want_all=True)
+    alls = sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv, per_block=False, want_all=True)
+    torch.cuda.synchronize()
+    H, z = orc.kv_states(f.K, f.V, w.Nv)
+    for got, ref, what in [(out["H"], H, "H"), (out["z"], z, "z"), (out["H_all"], H.sum(2), "H_all"),
+                           (out["z_all"], z.sum(2), "z_all"), (alls["H_all"], H.sum(2), "H_all chunked"),
+                           (alls["z_all"], z.sum(2), "z_all chunked")]:
+        g = host(got).astype(np.float64)
+        rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
+        say(f"  {what}: rel-L2 {rel:.2e}")
+        assert rel < 3e-3, what     # phi(K) and fp32 V are rounded to bf16 matrix-core operands
+
+
+@pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla"])
+def test_marginal_states(name):
+    say(f"[marginal states] {name}")
+    w, _, f, layer = case(name)
+    import block_sparse_linear_mean_amd as sla
+    csr, maps = oracle_csr(f)
+    kv = sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv)
+    S, u = sla.sla_marginal_states(kv["H"], kv["z"], f.Hq, False, csr["marg_rowptr"], csr["marg_idx"])
+    torch.cuda.synchronize()
+    Sg, ug = host(S), host(u)
+    worst = 0.0
+    for (b, h, i), m in maps.items():
+        r = (b * f.Hq + h) * f.nb + i
+        refH = np.zeros((f.d, f.d))
+        refz = np.zeros(f.d)
+        for j in m["marg"]:
+            Hj, zj = f.state(b, h // f.G, j)
+            refH += Hj
+            refz += zj
+        if m["marg"]:
+            worst = max(worst, np.linalg.norm(Sg[r] - refH) / np.linalg.norm(refH),
+                        np.linalg.norm(ug[r] - refz) / np.linalg.norm(refz))
+        else:
+            assert not Sg[r].any() and not ug[r].any()
+    say(f"  worst row rel-L2 {worst:.2e}")
+    assert worst < 3e-3
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_attention_given_oracle_map(name):
+    say(f"[attention, oracle map] {name}")
+    w, _, f, layer = case(name)
+    csr, _ = oracle_csr(f)
+    layer.kv_reduce()
+    O = host(layer.attention(maps=csr))
+    torch.cuda.synchronize()
+    ref = f.output()
+    compare_outputs(O[:, :, :w.Nv], ref[:, :, :w.Nv], name)
+    assert not O[:, :, w.Nv:].any(), "padded query rows must be zero"
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_end_to_end_and_determinism(name):
+    say(f"[end to end] {name}")
+    w, _, f, layer = case(name)
+    O1 = host(layer.run()).copy()
+    maps1 = {k: v.clone() for k, v in layer.maps.items() if isinstance(v, torch.Tensor)}
+    O2 = host(layer.run())
+    torch.cuda.synchronize()
+    assert np.array_equal(O1, O2), "two runs differ"
+    for k_, v_ in maps1.items():
+        assert torch.equal(v_, layer.maps[k_]), f"map {k_} differs between runs"
+    Hs = f.Hkv if f.group_sum else f.Hq
+    got = gpu_map_rows(layer.maps, range(w.B * Hs * f.nb))
+    mism = 0
+    for r, (crit, flags, marg, counts) in got.items():
+        b, rem = divmod(r, Hs * f.nb)
+        h, i = divmod(rem, f.nb)
+        m = f.map_row(b, h, i)
+        if crit != m["crit"] or (marg is not None and marg != m["marg"]):
+            mism += 1
+    say(f"  map rows differing from the oracle's own map: {mism}")
+    assert mism == 0
+    compare_outputs(O1[:, :, :w.Nv], f.output()[:, :, :w.Nv], name)
+
+
+@pytest.mark.parametrize("name", ["med_sla", "tiny_sla"])
+def test_all_critical_is_dense(name):
+    say(f"[all critical] {name}")
+    w0, (q, k, v, wg), _, _ = case(name)
+    w = scaled(w0, name + "_dense", kh_bp=10000, kl_bp=0)
+    f = oracle_for(w, q, k, v, wg)
+    layer = layer_for(w, q, k, v, wg)
+    O = host(layer.run())
+    torch.cuda.synchronize()
+    ref = np.zeros_like(O, dtype=np.float64)
+    for h in range(w.Hq):
+        ref[0, h, :w.Nv] = refs.sdpa(f.Q[0, h, :w.Nv], f.K[0, h // f.G, :w.Nv], f.V[0, h // f.G, :w.Nv], f.scale)
+    compare_outputs(O[:, :, :w.Nv], ref[:, :, :w.Nv], name + " vs dense SDPA")
+
+
+def test_nothing_critical_is_linear_attention():
+    say("[nothing critical] med_sla")
+    w0, (q, k, v, wg), _, _ = case("med_sla")
+    w = scaled(w0, "med_sla_linear", kh_bp=0, kl_bp=0)
+    f = oracle_for(w, q, k, v, wg)
+    layer = layer_for(w, q, k, v, wg)
+    O = host(layer.run())
+    torch.cuda.synchronize()
+    ref = np.zeros_like(O, dtype=np.float64)
+    for h in range(w.Hq):
+        ref[0, h, :w.Nv] = refs.kernel_linear_attention(f.Q[0, h, :w.Nv], f.K[0, h, :w.Nv], f.V[0, h, :w.Nv])
+    compare_outputs(O[:, :, :w.Nv], ref[:, :, :w.Nv], "linear closed form")
