@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of one sparse-linear attention layer forward through libsla on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan13b_sla]
+
+A step is one pass of the whole hot path over one batch of synthetic input already
+resident in HBM: pooled scores, block map, linear key states, marginal sums and the
+attention kernel with its fused linear epilogue.  Prints one JSON line.
+
+value = effective TFLOP/s = dense-equivalent attention FLOPs (4 B Hq Nv^2 d, halved when
+causal) / measured time per layer; ms_per_step = milliseconds per layer forward.
+The roofline entry covers the pass that takes the most time, measured with HIP events
+recorded on the stream its kernels are launched on, over the timed steps.
+cpu_baseline times the CPU oracle on a bounded sample (whole heads) of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SLA fwd ms/layer + effective TFLOP/s, B1 H12 N32768 d128 bf16, 5% crit"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PASSES = ["pool_scores", "block_map", "kv_reduce", "marginal_states", "attention"]
+KERNEL_SOURCES = {
+    "pool_scores": "pool_scores.hip", "block_map": "block_map.hip", "kv_reduce": "kv_reduce.hip",
+    "marginal_states": "marginal.hip", "attention": "attn_fwd.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pass_work(w, layer):
+    """Algorithmic work of one launch of each pass: (bound, bytes or FLOPs)."""
+    B, Hq, Hkv, d, Nv, nb = w.B, w.Hq, w.Hkv, w.d, w.Nv, w.nb
+    eb = 2 if w.dtype == "bf16" else 4
+    Hs = Hkv if layer.group else Hq
+    rows = B * Hs * nb
+    n_crit_entries = int(layer.maps["crit_rowptr"][-1].item())
+    n_marg_entries = int(layer.maps["marg_rowptr"][-1].item()) if "marg_rowptr" in layer.maps else 0
+    G = Hq // Hkv
+    heads_per_row = G if layer.group else 1
+    pair_flops = 4.0 * 64 * 64 * d                 # QK^T and PV of one 64 x 64 block pair
+    work = {}
+    work["pool_scores"] = ("hbm", B * (Hq + Hkv) * Nv * d * eb + B * (Hq + Hkv) * nb * d * 4 + rows * nb * 4)
+    work["block_map"] = ("hbm", rows * nb * 4 + (n_crit_entries + n_marg_entries) * 4 + rows * 20)
+    if layer.lin == 1:
+        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d + d) * 4)
+        work["marginal_states"] = ("hbm", (n_marg_entries + rows) * (d * d + d) * 4)
+    elif layer.lin == 2:
+        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * (d * d + d) * 4)
+        work["marginal_states"] = ("hbm", 0)
+    else:
+        work["kv_reduce"] = ("hbm", 0)
+        work["marginal_states"] = ("hbm", 0)
+    attn = n_crit_entries * heads_per_row * pair_flops
+    if layer.lin != 0:
+        attn += B * Hq * nb * 64 * 2.0 * d * d    # linear epilogue phi(Q) S per query block
+    work["attention"] = ("mfma", attn)
+    return work, n_crit_entries * heads_per_row
+
+
+def kernel_source_digest(pass_name):
+    path = os.path.join(ROOT, "block_sparse_linear_mean_amd", "csrc", KERNEL_SOURCES[pass_name])
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(pass_name, workload):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel source.
+
+    The summary file profiles/<kernel>_<workload>_counters.txt holds a line
+      TRAFFIC bytes_per_launch=<int> kernel_source_sha=<hex16>
+    written from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), calibrated with a copy kernel.
+    """
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SOURCES[pass_name].split('.')[0]}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"TRAFFIC bytes_per_launch=(\d+) kernel_source_sha=([0-9a-f]+)", open(path).read())
+    if not m or m.group(2) != kernel_source_digest(pass_name):
+        return None
+    return int(m.group(1))
+
+
+def cpu_baseline(w, q, k, v, wg, heads):
+    """The CPU oracle as it stands, on whole heads of the same workload, extrapolated to all heads."""
+    import numpy as np
+    from oracle import sla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                           or [1])
+    except Exception:
+        blas_threads = 1
+    heads = max(1, min(heads, w.Hkv))
+    G = w.Hq // w.Hkv
+    Q = q[:, :heads * G].float().numpy()
+    K = k[:, :heads].float().numpy()
+    V = v[:, :heads].float().numpy()
+    wgn = None if wg is None else wg[:heads * G].numpy()
+    t0 = time.perf_counter()
+    f = orc.Forward(Q, K, V, n_valid=w.Nv, mode=w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
+                    window=w.window, w_gate=wgn)
+    f.output()
+    dt = time.perf_counter() - t0
+    full = dt * (w.Hkv / heads)
+    return {
+        "value": round(w.dense_flops() / full / 1e12, 6),
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{heads} of {w.Hkv} KV heads ({heads * G} query heads), every query block, full forward "
+                   f"in {dt:.1f} s, scaled x{w.Hkv / heads:g} to the whole layer ({full:.1f} s); "
+                   f"float64 numpy oracle, {blas_threads} BLAS thread(s)"),
+        "ms_per_layer": round(full * 1e3, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_sla")
+    ap.add_argument("--cpu-sample-heads", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: this build has no multi-GPU path "
+               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).")
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        log(msg)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_linear_mean_amd as sla
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    log(f"bench: generating {w.name} inputs")
+    q, k, v, wg = make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
+                           window=w.window, w_gate=wg)
+    log(f"bench: {args.warmup} warm-up steps")
+    for _ in range(args.warmup):
+        layer.run()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PASSES) + 1)] for _ in range(args.steps)]
+    log(f"bench: {args.steps} timed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        for i, name in enumerate(PASSES):
+            getattr(layer, name)()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    pass_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+               for i, name in enumerate(PASSES)}
+    gpu_ms = sum(pass_ms.values())
+    log("bench: per-pass ms " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in pass_ms.items()) +
+        f"; wall {ms_step:.4f} ms/step")
+
+    work, pairs = pass_work(w, layer)
+    dom = max(PASSES, key=lambda n: pass_ms[n])
+    bound, amount = work[dom]
+    t_dom = pass_ms[dom] / 1e3
+    if bound == "mfma":
+        achieved = amount / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = amount / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(achieved / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(dom, w.name)
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = amount
+    roof["avg_launch_ms"] = round(pass_ms[dom], 5)
+
+    passes = {}
+    for name in PASSES:
+        b_, a_ = work[name]
+        t_ = pass_ms[name] / 1e3
+        if a_ and t_ > 0:
+            frac = (a_ / t_ / 1e12 / PEAK_BF16_TFLOPS) if b_ == "mfma" else (a_ / t_ / 1e9 / PEAK_HBM_GBS)
+        else:
+            frac = None
+        passes[name] = {"ms": round(pass_ms[name], 5), "bound": b_,
+                        "roofline_frac": None if frac is None else round(frac, 4)}
+
+    value = w.dense_flops() / (ms_step / 1e3) / 1e12
+    cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "n_valid": w.Nv, "d": w.d,
+           "block": 64, "mode": w.mode, "causal": w.causal}
+    if w.mode == "sla":
+        cfg.update(kh_pct=w.kh_bp / 100, kl_pct=w.kl_bp / 100, n_crit=layer.n_crit, n_negl=layer.n_negl)
+    elif w.mode == "salad":
+        cfg.update(kh_pct=w.kh_bp / 100, n_crit=layer.n_crit, linear="all keys, gated")
+    else:
+        cfg.update(n_sel=w.n_sel, window=w.window)
+    cfg["critical_pairs"] = pairs
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Wan2.1-shaped Fourier-feature Q/K, Gaussian V)" if w.generator == "video"
+        else "synthetic (seeded)",
+        "config": cfg,
+        "roofline": roof,
+        "passes": passes,
+        "gpu_ms_per_step": round(gpu_ms, 5),
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (oracle) on {args.cpu_sample_heads} head(s)")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, wg, args.cpu_sample_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

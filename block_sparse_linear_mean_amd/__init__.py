@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 from ._lib import (  # noqa: F401
-    BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SlaError, alloc_block_map,
+    BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
     lib, sla_abi_version, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
     sla_block_map_workspace_bytes, sla_counts, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
@@ -79,8 +79,10 @@ class SlaForward:
             ws = sla_kv_reduce_workspace_bytes(B, Hkv, N, d, False, True)
             self.kv = dict(H_all=torch.empty((B, Hkv, d, d), **f), z_all=torch.empty((B, Hkv, d), **f),
                            workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
-        ws = sla_attn_workspace_bytes(B, Hs, nb, d, self.lin)
-        self.attn_ws = torch.empty(ws, device=dev, dtype=torch.uint8) if ws else None
+        self.row_states = None
+        if self.lin == SLA_LIN_MARGINAL:
+            # per-row marginal sums, filled by sla_marginal_states before the attention call
+            self.row_states = (torch.empty((B * Hs * nb, d, d), **f), torch.empty((B * Hs * nb, d), **f))
         self.out = torch.empty(q.shape, device=dev, dtype=out_dtype or q.dtype)
 
     def pool_scores(self):
@@ -96,16 +98,28 @@ class SlaForward:
             sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv)
         return self.kv
 
+    def marginal_states(self, maps=None):
+        """Per-row sums of the marginal key states (SLA mode only)."""
+        if self.lin == SLA_LIN_MARGINAL:
+            m = maps or self.maps
+            sla_marginal_states(self.kv["H"], self.kv["z"], self.q.shape[1], self.group, m["marg_rowptr"],
+                                m["marg_idx"], out=self.row_states)
+        return self.row_states
+
     def attention(self, maps=None):
         kv = self.kv
+        if self.lin == SLA_LIN_MARGINAL:
+            S, u = self.row_states
+            return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps,
+                                lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out)
         return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
                             scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
-                            H=kv.get("H"), z=kv.get("z"), H_all=kv.get("H_all"), z_all=kv.get("z_all"),
-                            w_gate=self.w_gate, out=self.out, workspace=self.attn_ws)
+                            H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out)
 
     def run(self) -> torch.Tensor:
-        """One full forward: pool + scores, block map, linear states, attention."""
+        """One full forward: pool + scores, block map, linear states, marginal sums, attention."""
         self.pool_scores()
         self.block_map()
         self.kv_reduce()
+        self.marginal_states()
         return self.attention()

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsla.so")
 
 SLA_BF16, SLA_F32 = 0, 1
-SLA_LIN_NONE, SLA_LIN_MARGINAL, SLA_LIN_GLOBAL_GATED = 0, 1, 2
+SLA_LIN_NONE, SLA_LIN_MARGINAL, SLA_LIN_GLOBAL_GATED, SLA_LIN_ROW_STATES = 0, 1, 2, 3
 BLOCK = 64
 
 
@@ -220,14 +220,17 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
     return out
 
 
-def sla_marginal_states(H, z, Hq, group_map, marg_rowptr, marg_idx):
+def sla_marginal_states(H, z, Hq, group_map, marg_rowptr, marg_idx, out=None):
     """S [rows, d, d], u [rows, d] for the map's rows (rows = B * Hs * nqb)."""
     _require_gpu(H, z, marg_rowptr, marg_idx)
     B, Hkv, nb, d, _ = H.shape
     Hs = Hkv if group_map else Hq
     rows = B * Hs * nb
-    S = torch.empty((rows, d, d), device=H.device, dtype=torch.float32)
-    u = torch.empty((rows, d), device=H.device, dtype=torch.float32)
+    if out is None:
+        S = torch.empty((rows, d, d), device=H.device, dtype=torch.float32)
+        u = torch.empty((rows, d), device=H.device, dtype=torch.float32)
+    else:
+        S, u = out
     _check("sla_marginal_states", lib().sla_marginal_states(
         _ptr(H), _ptr(z), B, Hq, Hkv, nb, nb, d, int(group_map), _ptr(marg_rowptr), _ptr(marg_idx), _ptr(S),
         _ptr(u), _stream(H.device)))

@@ -276,7 +276,7 @@ template <typename T, int D>
 static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hipStream_t st) {
   if (causal) {
     attn_fwd_kernel<T, D, true, SLA_LIN_NONE><<<grid, 256, 0, st>>>(p);
-  } else if (lin == SLA_LIN_MARGINAL) {
+  } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
     attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL><<<grid, 256, 0, st>>>(p);
   } else if (lin == SLA_LIN_GLOBAL_GATED) {
     attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED><<<grid, 256, 0, st>>>(p);
@@ -305,7 +305,7 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   if (out == nullptr || crit_rowptr == nullptr || crit_idx == nullptr) return SLA_ERR_NULL;
   if (!aligned16(out)) return SLA_ERR_ALIGN;
   if (out_dtype != SLA_BF16 && out_dtype != SLA_F32) return SLA_ERR_UNSUPPORTED;
-  if (lin_mode < SLA_LIN_NONE || lin_mode > SLA_LIN_GLOBAL_GATED) return SLA_ERR_UNSUPPORTED;
+  if (lin_mode < SLA_LIN_NONE || lin_mode > SLA_LIN_ROW_STATES) return SLA_ERR_UNSUPPORTED;
   if (causal && lin_mode != SLA_LIN_NONE) return SLA_ERR_UNSUPPORTED;
   if (causal && crit_flags == nullptr) return SLA_ERR_NULL;
   const int d = q->d, nqb = q->N / kBlock;
@@ -334,6 +334,11 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
       return st;
     p.S = S;
     p.u = u;
+  } else if (lin_mode == SLA_LIN_ROW_STATES) {
+    if (H == nullptr || z == nullptr) return SLA_ERR_NULL;
+    if (!aligned16(H) || !aligned16(z)) return SLA_ERR_ALIGN;
+    p.S = H;
+    p.u = z;
   } else if (lin_mode == SLA_LIN_GLOBAL_GATED) {
     if (H_all == nullptr || z_all == nullptr || w_gate == nullptr) return SLA_ERR_NULL;
     p.S = H_all;

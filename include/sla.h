@@ -72,7 +72,8 @@ enum { SLA_BF16 = 0, SLA_F32 = 1 };
 enum {
   SLA_LIN_NONE = 0,         /* sparse branch only (NSA-style selected + window) */
   SLA_LIN_MARGINAL = 1,     /* SLA: linear attention over each row's marginal blocks */
-  SLA_LIN_GLOBAL_GATED = 2  /* SALAD: gated linear attention over all valid keys */
+  SLA_LIN_GLOBAL_GATED = 2, /* SALAD: gated linear attention over all valid keys */
+  SLA_LIN_ROW_STATES = 3    /* SLA with the per-row sums precomputed by sla_marginal_states */
 };
 
 typedef struct {
@@ -209,6 +210,9 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  *   lin_mode SLA_LIN_MARGINAL (needs marg_rowptr, marg_idx, H, z):
  *     O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the sums of H_j and
  *     z_j over row r's marginal blocks; 0 when the row has none.
+ *   lin_mode SLA_LIN_ROW_STATES: as SLA_LIN_MARGINAL, but H and z already hold the per-row
+ *     sums S [rows, d, d] and u [rows, d] written by sla_marginal_states for this map; the
+ *     marginal lists are not read and no workspace is needed.
  *   lin_mode SLA_LIN_GLOBAL_GATED (needs H_all, z_all, w_gate [Hq][d] fp32):
  *     O_linear[t] = sigmoid(q_t . w_gate[h]) * phi(q_t)^T H_all / (phi(q_t) . z_all).
  *   Rows t >= n_valid are written as 0.

@@ -162,7 +162,9 @@ def test_attn_fwd_validation(L):
     assert call(lin=1) == ENULL                      # marginal mode needs H, z and the marginal lists
     assert call(lin=1, H=P, z=P, mrp=P, mi=P) == EWS
     assert call(lin=2) == ENULL
-    assert call(lin=3) == EUNSUP
+    assert call(lin=3) == ENULL                      # precomputed row states needed
+    assert call(lin=3, H=ctypes.c_void_p(0x20004), z=P) == EALIGN
+    assert call(lin=4) == EUNSUP
     assert call(odt=5) == EUNSUP
     assert call(out=ctypes.c_void_p(0x20002)) == EALIGN
     assert call(kk=desc(H=3), vv=desc(H=3)) == ESHAPE

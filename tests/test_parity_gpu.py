@@ -190,11 +190,26 @@ def test_attention_given_oracle_map(name):
     w, _, f, layer = case(name)
     csr, _ = oracle_csr(f)
     layer.kv_reduce()
+    layer.marginal_states(maps=csr)
     O = host(layer.attention(maps=csr))
     torch.cuda.synchronize()
     ref = f.output()
     compare_outputs(O[:, :, :w.Nv], ref[:, :, :w.Nv], name)
     assert not O[:, :, w.Nv:].any(), "padded query rows must be zero"
+
+
+@pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla", "tiny_sla"])
+def test_attention_one_call_marginal_mode(name):
+    """sla_attn_fwd in SLA_LIN_MARGINAL mode aggregates the marginal states itself."""
+    say(f"[attention, one-call marginal mode] {name}")
+    import block_sparse_linear_mean_amd as sla
+    w, _, f, layer = case(name)
+    csr, _ = oracle_csr(f)
+    kv = layer.kv_reduce()
+    O = sla.sla_attn_fwd(layer.q, layer.k, layer.v, w.Nv, csr, lin_mode=sla.SLA_LIN_MARGINAL, H=kv["H"],
+                         z=kv["z"])
+    torch.cuda.synchronize()
+    compare_outputs(host(O)[:, :, :w.Nv], f.output()[:, :, :w.Nv], name)
 
 
 @pytest.mark.parametrize("name", list(MEDIUM))
