@@ -132,7 +132,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b_sla")
-    ap.add_argument("--cpu-sample-heads", type=int, default=4)
+    ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 

@@ -27,8 +27,8 @@ def check_all_rows(w, f, layer):
     Hs = f.Hkv if f.group_sum else f.Hq
     rows = w.B * Hs * f.nb
     cr = layer.maps["crit_rowptr"].cpu().numpy().astype(np.int64)
-    ci = layer.maps["crit_idx"].cpu().numpy()
-    cf = layer.maps["crit_flags"].cpu().numpy()
+    ci = layer.maps["crit_idx"].cpu().numpy()[:cr[-1]]
+    cf = layer.maps["crit_flags"].cpu().numpy()[:cr[-1]]
     rc = layer.maps["row_counts"].cpu().numpy()
     assert cr[0] == 0 and np.all(np.diff(cr) == rc[:, 0])
     i_of_row = np.tile(np.arange(f.nb), w.B * Hs)
