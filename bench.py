@@ -56,7 +56,8 @@ def pass_work(w, layer):
     work["block_map"] = ("hbm", rows * nb * 4 + (n_crit_entries + n_marg_entries) * 4 + rows * 20)
     if layer.lin == 1:
         work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d + d) * 4)
-        work["marginal_states"] = ("hbm", (n_marg_entries + rows) * (d * d + d) * 4)
+        # mask product S = M H: reads every state once (fp32), writes bf16 row sums + fp32 u
+        work["marginal_states"] = ("hbm", B * Hkv * nb * (d * d + d) * 4 + rows * (d * d * 2 + d * 4))
     elif layer.lin == 2:
         work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * (d * d + d) * 4)
         work["marginal_states"] = ("hbm", 0)
@@ -134,6 +135,8 @@ def main():
     ap.add_argument("--workload", default="wan13b_sla")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -235,6 +238,14 @@ def main():
         "passes": passes,
         "gpu_ms_per_step": round(gpu_ms, 5),
     }
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 3 copies of {args.copy_calibration_mb} MiB")
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (oracle) on {args.cpu_sample_heads} head(s)")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, wg, args.cpu_sample_heads)

@@ -82,7 +82,8 @@ class SlaForward:
         self.row_states = None
         if self.lin == SLA_LIN_MARGINAL:
             # per-row marginal sums, filled by sla_marginal_states before the attention call
-            self.row_states = (torch.empty((B * Hs * nb, d, d), **f), torch.empty((B * Hs * nb, d), **f))
+            self.row_states = (torch.empty((B * Hs * nb, d, d), device=dev, dtype=torch.bfloat16),
+                               torch.empty((B * Hs * nb, d), **f))
         self.out = torch.empty(q.shape, device=dev, dtype=out_dtype or q.dtype)
 
     def pool_scores(self):
@@ -102,8 +103,8 @@ class SlaForward:
         """Per-row sums of the marginal key states (SLA mode only)."""
         if self.lin == SLA_LIN_MARGINAL:
             m = maps or self.maps
-            sla_marginal_states(self.kv["H"], self.kv["z"], self.q.shape[1], self.group, m["marg_rowptr"],
-                                m["marg_idx"], out=self.row_states)
+            sla_marginal_states(self.kv["H"], self.kv["z"], self.q.shape[1], self.group, m["marg_bits"],
+                                out=self.row_states)
         return self.row_states
 
     def attention(self, maps=None):

@@ -46,15 +46,15 @@ _SIGS = {
     "sla_block_map_capacity": (c_int64, [c_int32] * 9),
     "sla_block_map_workspace_bytes": (c_size_t, [c_int32] * 7),
     "sla_block_map": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
-                                _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, c_size_t, _P]),
+                                _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, _P, c_size_t, _P]),
     "sla_kv_reduce_workspace_bytes": (c_size_t, [c_int32] * 6),
     "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P,
                                        c_size_t, _P]),
     "sla_marginal_states": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
-                                      _P, _P, _P, _P, _P]),
+                                      _P, _P, _P, _P]),
     "sla_attn_workspace_bytes": (c_size_t, [c_int32] * 5),
     "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
-                               c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P, _P,
+                               c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P, _P,
                                c_int32, _P, c_size_t, _P]),
 }
 
@@ -175,6 +175,7 @@ def alloc_block_map(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, device, wan
     if want_marg and not causal:
         m["marg_rowptr"] = torch.empty(rows + 1, **i32)
         m["marg_idx"] = torch.empty(max(mc, 1), **i32)
+        m["marg_bits"] = torch.empty((rows, (nkb + 31) // 32), **i32)   # uint32 bit masks
     ws = sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, causal, window)
     m["workspace"] = torch.empty(max(ws, 16), device=device, dtype=torch.uint8) if ws else None
     m["workspace_bytes"] = ws
@@ -190,7 +191,7 @@ def sla_block_map(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=Tr
     _check("sla_block_map", lib().sla_block_map(
         _ptr(scores), B, Hs, nqb, nkb, n_crit, n_negl, int(causal), window,
         _ptr(out["crit_rowptr"]), _ptr(out["crit_idx"]), _ptr(out["crit_flags"]), out["crit_cap"],
-        _ptr(out.get("marg_rowptr")), _ptr(out.get("marg_idx")), out["marg_cap"],
+        _ptr(out.get("marg_rowptr")), _ptr(out.get("marg_idx")), out["marg_cap"], _ptr(out.get("marg_bits")),
         _ptr(out["row_counts"]), _ptr(out["workspace"]), out["workspace_bytes"], _stream(scores.device)))
     return out
 
@@ -220,20 +221,20 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
     return out
 
 
-def sla_marginal_states(H, z, Hq, group_map, marg_rowptr, marg_idx, out=None):
-    """S [rows, d, d], u [rows, d] for the map's rows (rows = B * Hs * nqb)."""
-    _require_gpu(H, z, marg_rowptr, marg_idx)
+def sla_marginal_states(H, z, Hq, group_map, marg_bits, out=None):
+    """Per-row marginal sums: S bf16 [rows, d, d] in H's [c][r] layout, u fp32 [rows, d]."""
+    _require_gpu(H, z, marg_bits)
     B, Hkv, nb, d, _ = H.shape
     Hs = Hkv if group_map else Hq
     rows = B * Hs * nb
     if out is None:
-        S = torch.empty((rows, d, d), device=H.device, dtype=torch.float32)
+        S = torch.empty((rows, d, d), device=H.device, dtype=torch.bfloat16)
         u = torch.empty((rows, d), device=H.device, dtype=torch.float32)
     else:
         S, u = out
     _check("sla_marginal_states", lib().sla_marginal_states(
-        _ptr(H), _ptr(z), B, Hq, Hkv, nb, nb, d, int(group_map), _ptr(marg_rowptr), _ptr(marg_idx), _ptr(S),
-        _ptr(u), _stream(H.device)))
+        _ptr(H), _ptr(z), B, Hq, Hkv, nb, nb, d, int(group_map), _ptr(marg_bits), _ptr(S), _ptr(u),
+        _stream(H.device)))
     return S, u
 
 
@@ -255,6 +256,6 @@ def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, caus
     _check("sla_attn_fwd", lib().sla_attn_fwd(
         ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), n_valid, float(scale), int(causal), window,
         int(group_map), _ptr(maps["crit_rowptr"]), _ptr(maps["crit_idx"]), _ptr(maps.get("crit_flags")),
-        _ptr(maps.get("marg_rowptr")), _ptr(maps.get("marg_idx")), lin_mode, _ptr(H), _ptr(z), _ptr(H_all),
+        _ptr(maps.get("marg_bits")), lin_mode, _ptr(H), _ptr(z), _ptr(H_all),
         _ptr(z_all), _ptr(w_gate), _ptr(out), odt, _ptr(workspace), ws_bytes, _stream(q.device)))
     return out

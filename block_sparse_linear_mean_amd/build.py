@@ -23,6 +23,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay off: ordinary float code is compiled to unpacked ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: no copies to and from AGPRs around the
+    # per-block online-softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

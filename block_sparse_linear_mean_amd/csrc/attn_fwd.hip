@@ -29,8 +29,7 @@
 namespace sla {
 
 sla_status launch_marginal_states(const float* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
-                                  int group_map, const int* rowptr, const int* idx, float* S, float* u,
-                                  hipStream_t st);
+                                  int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st);
 
 struct AttnParams {
   const void* q;
@@ -42,186 +41,327 @@ struct AttnParams {
   const int* crit_rowptr;
   const int* crit_idx;
   const uint8_t* crit_flags;
-  const float* S;       // SLA: per map row d x d ([r][c]); SALAD: per KV head H_all
-  const float* u;       // SLA: per map row d;         SALAD: per KV head z_all
+  const void* S;        // SLA: per map row d x d bf16 [c][r]; SALAD: per KV head H_all fp32 [c][r]
+  const float* u;       // SLA: per map row d;              SALAD: per KV head z_all
   const float* w_gate;  // SALAD: [Hq][d]
   void* out;
   int out_f32;
 };
 
+// Tile geometry of one 64-key block of K or V in LDS: row-major bf16, 16-byte chunks
+// permuted within each row so that both readers are free of bank conflicts:
+//  * K is read as the A operand of S^T = K Q^T (16 contiguous bytes per lane, 32 rows at a
+//    time): chunk c of row r sits at position c ^ (r % chunks);
+//  * V is read with the transposing LDS read (8 bytes per lane, 4 rows x 32 bytes per
+//    16-lane group): chunk c of row r sits at position c ^ 2 (r % 4).
+// The epilogue's S^T tile ([c][r], 128 x 128 bf16) reuses the K layout over both buffers.
 template <int D>
-struct AttnSmem {
-  static constexpr int kKs = kBlock * (D + 8);     // K block, row-major, padded rows
-  static constexpr int kVt = D * (kBlock + 8);     // V block, transposed, padded rows
-  static constexpr int kSt = D * (D + 8);          // epilogue: S^T (bf16)
-  static constexpr int kElems = (kKs + kVt) > kSt ? (kKs + kVt) : kSt;
+struct AttnTile {
+  static constexpr int kRowB = 2 * D;             // bytes per row
+  static constexpr int kChunks = D / 8;           // 16-byte chunks per row
+  static constexpr int kTileB = kBlock * kRowB;   // one 64-row tile
+  static constexpr int kInst = kTileB / 1024;     // 1 KB direct-load steps per tile
 };
 
-template <typename T, int D, bool CAUSAL, int LIN>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
-  constexpr int kQs = D / 32;      // 32-wide feature steps of the Q.K contraction
-  constexpr int kDt = D / 16;      // 16-wide feature tiles of the output
-  constexpr int kTpt = D / 32;     // tokens per thread in the V transpose
-  constexpr int kTg = kBlock / kTpt;
-  constexpr int kVs = kBlock + 8;  // Vt row stride
-  constexpr int kKsS = D + 8;      // Ks row stride
-  __shared__ __attribute__((aligned(16))) u16 smem[AttnSmem<D>::kElems];
-  __shared__ float lin_u[D];
-  u16* Ks = smem;
-  u16* Vt = smem + AttnSmem<D>::kKs;
+template <int D>
+__device__ __forceinline__ int k_pos(int r, int c) {
+  return r * AttnTile<D>::kRowB + 16 * (c ^ (r % AttnTile<D>::kChunks));
+}
+template <int D>
+__device__ __forceinline__ int v_pos(int r, int c) {
+  return r * AttnTile<D>::kRowB + 16 * (c ^ (2 * (r % 4)));
+}
 
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// Stage rows 64 j .. 64 j + 63 of X (row stride sN elements) into an LDS tile.  bf16 inputs go
+// straight from global memory to LDS (each lane picks the global chunk that belongs at its
+// LDS slot); fp32 inputs are converted through registers.  The two wavefronts split the tile.
+// For the direct path the per-lane element offsets (row * sN + 8 * chunk) are precomputed
+// once per kernel by stage_offsets; only the block's base address changes per call.
+template <int D, bool KLAYOUT>
+__device__ __forceinline__ void stage_offsets(int64_t sN, int (&off)[AttnTile<D>::kInst / 2]) {
+  using Tl = AttnTile<D>;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int n = 0; n < Tl::kInst / 2; ++n) {
+    const int q = w * (Tl::kInst / 2) + n;
+    const int o = q * 1024 + 16 * lane;
+    const int r = o / Tl::kRowB, pc = (o % Tl::kRowB) / 16;
+    const int c = KLAYOUT ? (pc ^ (r % Tl::kChunks)) : (pc ^ (2 * (r % 4)));
+    off[n] = int(r * sN) + 8 * c;
+  }
+}
+
+template <typename T, int D, bool KLAYOUT>
+__device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, int j, lds_u8* tile,
+                                           const int (&off)[AttnTile<D>::kInst / 2]) {
+  using Tl = AttnTile<D>;
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: the LDS base goes to M0
+  if constexpr (sizeof(T) == 2) {
+    const T* base = X + int64_t(kBlock * j) * sN;
+#pragma unroll
+    for (int n = 0; n < Tl::kInst / 2; ++n)
+      load_lds16(base + off[n], tile + (w * (Tl::kInst / 2) + n) * 1024);
+  } else {
+#pragma unroll
+    for (int n = 0; n < Tl::kChunks * kBlock / 128; ++n) {
+      const int e = t + 128 * n;
+      const int r = e / Tl::kChunks, c = e % Tl::kChunks;
+      const bf16x8 x = In<T>::load8(X + int64_t(kBlock * j + r) * sN + 8 * c);
+      lds_store16(tile + (KLAYOUT ? k_pos<D>(r, c) : v_pos<D>(r, c)), x);
+    }
+  }
+}
+
+// Workgroup order.  Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
+// the hardware index is remapped: the workgroups one XCD receives form one contiguous range
+// of the logical order, in which the query heads of a GQA group (same map row, same K/V
+// blocks) come first, then neighbouring query blocks (largely the same critical blocks).
+struct WgCoord {
+  int i, h, b;
+};
+__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv) {
+  const int n = gridDim.x;
+  const int L = blockIdx.x;
+  const int xcd = L % 8, slot = L / 8;
+  const int q = n / 8, r = n % 8;
+  const int logical = xcd * q + min(xcd, r) + slot;
+  const int G = Hq / Hkv;
+  const int hh = logical % G;
+  const int rest = logical / G;
+  const int i = rest % nqb;
+  const int bg = rest / nqb;
+  const int g = bg % Hkv, b = bg / Hkv;
+  return WgCoord{i, g * G + hh, b};
+}
+
+// One workgroup = one 64-row query block of one head: 2 wavefronts x 32 query rows, 32x32x16
+// bf16 matrix cores.  Per critical key block: S^T = K Q^T (lane = one query column, 32 keys),
+// online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
+// transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU): the next
+// K block streams into LDS during softmax and P.V, the next V block during the next S^T.
+template <typename T, int D, bool CAUSAL, int LIN>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
+  using Tl = AttnTile<D>;
+  constexpr int kQs = D / 16;      // 16-wide feature steps of the Q.K contraction
+  constexpr int kDt = D / 32;      // 32-wide feature tiles of the output
+  constexpr bool kDirect = sizeof(T) == 2;
+  constexpr int kWaitK = kDirect ? Tl::kInst / 2 : 0;   // loads of one tile per wavefront
+  __shared__ __attribute__((aligned(1024))) unsigned char ksm[Tl::kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char vsm[Tl::kTileB];
+  __shared__ float lin_u[D];
+  lds_u8* Kb = to_lds(ksm);
+  lds_u8* Vb = to_lds(vsm);
+
+  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv);
+  const int i = wc.i, h = wc.h, b = wc.b;
   const int G = p.Hq / p.Hkv;
   const int g = h / G;
   const int smap = p.group_map ? g : h;
   const int64_t mrow = (int64_t(b) * p.Hs + smap) * p.nqb + i;
-  const int t = threadIdx.x, w = t / kWave, lane = t % kWave, l16 = lane % 16, lg = lane / 16;
+  const int t = threadIdx.x, w = t / kWave, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
   const T* Q = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
   const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(g) * p.ksH;
   const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(g) * p.vsH;
 
-  const int tq = kBlock * i + 16 * w + l16;       // this lane's query row
+  const int tq = kBlock * i + 32 * w + l32;       // this lane's query row
   const bool qvalid = tq < p.n_valid;
   bf16x8 qf[kQs];
 #pragma unroll
   for (int ks = 0; ks < kQs; ++ks)
-    qf[ks] = qvalid ? In<T>::load8(Q + int64_t(tq) * p.qsN + 32 * ks + 8 * lg) : zero8();
+    qf[ks] = qvalid ? In<T>::load8(Q + int64_t(tq) * p.qsN + 16 * ks + 8 * lg) : zero8();
 
-  f32x4 oacc[kDt];
+  f32x16 oacc[kDt];
 #pragma unroll
-  for (int dt = 0; dt < kDt; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
+  const float c2 = p.scale_log2;
+
+  // per-lane offsets, computed once: direct-load sources, K operand reads, V transposed reads
+  int koff[Tl::kInst / 2], voff[Tl::kInst / 2];
+  stage_offsets<D, true>(p.ksN, koff);
+  stage_offsets<D, false>(p.vsN, voff);
+  int kread[kQs];                 // K row 32 kt + l32, chunk 2 ks + lg (+ 32 kt rows = kt * 8 KB)
+#pragma unroll
+  for (int ks = 0; ks < kQs; ++ks) kread[ks] = k_pos<D>(l32, 2 * ks + lg);
+  const int sg = (lane / 16) % 2, kk = lane % 16;
+  int vread[kDt];                 // V rows 16 u + 4 lg + kk / 4 (+ 8), 8-byte half kk % 2
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+    vread[dt] = v_pos<D>(4 * lg + kk / 4, 4 * dt + 2 * sg + (kk % 4) / 2) + 8 * (kk % 2);
 
   const int cbeg = p.crit_rowptr[mrow], cend = p.crit_rowptr[mrow + 1];
+  // the row's list, 128 entries at a time in two registers per lane, read back with readlane
+  int lj0 = 0, lj1 = 0, lf0 = 0, lf1 = 0;
+  auto load_list = [&](int base) {
+    const int e0 = base + lane, e1 = base + 64 + lane;
+    lj0 = e0 < cend ? p.crit_idx[e0] : 0;
+    lj1 = e1 < cend ? p.crit_idx[e1] : 0;
+    if constexpr (CAUSAL) {
+      lf0 = e0 < cend ? int(p.crit_flags[e0]) : 0;
+      lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
+    }
+  };
+  int lbase = cbeg;
+  load_list(lbase);
+  auto entry = [&](int n, int v0, int v1) {   // n = position relative to lbase, 0 <= n < 128
+    return n < 64 ? __builtin_amdgcn_readlane(v0, n) : __builtin_amdgcn_readlane(v1, n - 64);
+  };
+  auto safe_block = [&](int jraw) { return unsigned(jraw) < unsigned(p.nqb) ? jraw : 0; };
+  if (cbeg < cend) {
+    const int j0 = safe_block(entry(0, lj0, lj1));
+    stage_tile<T, D, true>(K, p.ksN, j0, Kb, koff);
+    stage_tile<T, D, false>(V, p.vsN, j0, Vb, voff);
+  }
   for (int pi = cbeg; pi < cend; ++pi) {
-    const int j = p.crit_idx[pi];
-    const int flag = CAUSAL ? int(p.crit_flags[pi]) : 1;
-    if (unsigned(j) >= unsigned(p.nqb)) continue;   // malformed list entry: never read outside K/V
-    __syncthreads();
-    // ---- stage K_j (row-major) and V_j (transposed) in LDS; padded keys are zero
-#pragma unroll
-    for (int u = 0; u < (kBlock * D / 8) / 256; ++u) {
-      const int e = t + 256 * u;
-      const int row = e / (D / 8), c8 = e % (D / 8);
-      const int s = kBlock * j + row;
-      const bf16x8 x = s < p.n_valid ? In<T>::load8(K + int64_t(s) * p.ksN + 8 * c8) : zero8();
-      *reinterpret_cast<bf16x8*>(Ks + row * kKsS + 8 * c8) = x;
+    if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
+      lbase += 64;
+      lj0 = lj1;
+      lf0 = lf1;
+      const int e1 = lbase + 64 + lane;
+      lj1 = e1 < cend ? p.crit_idx[e1] : 0;
+      if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
     }
-    {
-      const int tg = t % kTg, fg = t / kTg;
-      bf16x8 vv[kTpt];
-#pragma unroll
-      for (int uu = 0; uu < kTpt; ++uu) {
-        const int s = kBlock * j + kTpt * tg + uu;
-        vv[uu] = s < p.n_valid ? In<T>::load8(V + int64_t(s) * p.vsN + 8 * fg) : zero8();
-      }
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        u16* dst = Vt + (8 * fg + f) * kVs + kTpt * tg;
-        if constexpr (kTpt == 4) {
-          bf16x4 col = {vv[0][f], vv[1][f], vv[2][f], vv[3][f]};
-          *reinterpret_cast<bf16x4*>(dst) = col;
-        } else {
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          bf16x2 col = {vv[0][f], vv[1][f]};
-          *reinterpret_cast<bf16x2*>(dst) = col;
-        }
-      }
-    }
-    __syncthreads();
+    const int jraw = entry(pi - lbase, lj0, lj1);
+    const bool jok = unsigned(jraw) < unsigned(p.nqb);   // a malformed entry reads block 0, fully masked
+    const int j = jok ? jraw : 0;
+    const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
+    const bool more = pi + 1 < cend;
+    const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
+    const int rv = p.n_valid - kBlock * j;          // valid rows of this block (may exceed 64)
 
-    // ---- S^T = K Q^T: lane holds keys 16kt + 4lg + e (e < 4) for query column l16
-    f32x4 sacc[4];
+    // ---- K_j resident (V_j may still be in flight)
+    if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < kQs; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (16 * kt + l16) * kKsS + 32 * ks + 8 * lg);
-        sacc[kt] = mfma16(a, qf[ks], sacc[kt]);
+        const bf16x8 a = lds_load16(Kb + kread[ks] + kt * 32 * Tl::kRowB);
+        sacc[kt] = mfma32(a, qf[ks], sacc[kt]);
       }
     }
-    float x[4][4];
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                                   // every wavefront has read K_j
+    if (more) stage_tile<T, D, true>(K, p.ksN, jn, Kb, koff);
+
+    // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
+    const bool full = jok && rv >= kBlock && !CAUSAL;
+    if (!full) {                                     // padded, malformed or causal block
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int s = kBlock * j + 32 * kt + 8 * (e / 4) + 4 * lg + (e % 4);
+          bool ok = jok && s < p.n_valid;
+          if constexpr (CAUSAL) ok = ok && s <= tq && ((flag & 1) || tq - s < p.window);
+          sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
+        }
+    }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = kBlock * j + 16 * kt + 4 * lg + e;
-        bool ok = s < p.n_valid;
-        if constexpr (CAUSAL) ok = ok && s <= tq && ((flag & 1) || tq - s < p.window);
-        x[kt][e] = ok ? sacc[kt][e] * p.scale_log2 : -__builtin_inff();
-        mx = fmaxf(mx, x[kt][e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float base = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-    m_run = m_new;
-    l_run *= alpha;
+    // lazy rescale: keep the running max unless the block's max exceeds it by 2^8 in exp2 units
+    if (__any((mx - m_run) * c2 > 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
+    }
+    const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
+    bf16x8 pb[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int u = 0; u < 4; ++u) {
+      f32x8 pv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[kt][e] = __builtin_amdgcn_exp2f(x[kt][e] - base);
-        l_run += x[kt][e];
+      for (int m = 0; m < 8; ++m) {
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -mc));
+        l_run += x;
+        pv[m] = x;
       }
+      pb[u] = cvt8(pv);
+    }
 
-    // ---- O^T += V^T P^T over two 32-key steps; k-slot m of lane group lg holds key
-    //      32 ks + 16 (m / 4) + 4 lg + m % 4 in both operands
+    // ---- V_j resident
+    if constexpr (kDirect) {
+      if (more) SLA_WAIT_VMCNT(kWaitK);
+      else SLA_WAIT_VMCNT(0);
+    }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    if (!jok || rv < kBlock) {                       // padded keys: zero their V rows
+      const int r0 = jok ? max(rv, 0) : 0;
+      for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += 128) {
+        const int r = r0 + e / Tl::kChunks;
+        lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
+      }
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+    }
+    // O^T += V^T P^T: 16-key step u holds keys 16 u + 8 (m / 4) + 4 lg + m % 4 in slot m; each
+    // 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
+    // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const f32x8 pv = {x[2 * ks][0], x[2 * ks][1], x[2 * ks][2], x[2 * ks][3],
-                        x[2 * ks + 1][0], x[2 * ks + 1][1], x[2 * ks + 1][2], x[2 * ks + 1][3]};
-      const bf16x8 pb = cvt8(pv);
+    for (int dt = 0; dt < kDt; ++dt) {
 #pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) {
-        const u16* row = Vt + (16 * dt + l16) * kVs + 32 * ks + 4 * lg;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+      for (int u = 0; u < 4; ++u) {
+        const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
+        const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[dt] = mfma16(a, pb, oacc[dt]);
+        oacc[dt] = mfma32(a, pb[u], oacc[dt]);
       }
     }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                                   // every wavefront has read V_j
+    if (more) stage_tile<T, D, false>(V, p.vsN, jn, Vb, voff);
   }
 
   // ---- normalise the sparse branch
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= inv_l;
 
-  // ---- linear branch: phi(q)^T S / (phi(q) . u), S^T staged in LDS as bf16
+  // ---- linear branch: phi(q)^T S / (phi(q) . u) with S^T staged in LDS ([c][r], K layout)
   if constexpr (LIN != SLA_LIN_NONE) {
-    const float* Sg;
     const float* ug;
+    SLA_WAIT_VMCNT(0);
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    // S^T rows (c) 0..63 go to the K buffer, rows 64..D-1 to the V buffer, both in the K layout
+    auto st_tile = [&](int r) { return r < kBlock ? Kb : Vb; };
     if constexpr (LIN == SLA_LIN_MARGINAL) {
-      Sg = p.S + mrow * D * D;
+      const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
       ug = p.u + mrow * D;
+      int soff[Tl::kInst / 2];
+      stage_offsets<D, true>(D, soff);
+      stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
+      if constexpr (D == 128) stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
     } else {
-      Sg = p.S + (int64_t(b) * p.Hkv + g) * D * D;
+      const float* Sg = static_cast<const float*>(p.S) + (int64_t(b) * p.Hkv + g) * D * D;
       ug = p.u + (int64_t(b) * p.Hkv + g) * D;
-    }
-    __syncthreads();   // the last K/V tile is no longer read
-    u16* St = smem;    // [c][r], row stride D + 8
-    for (int blk = t; blk < (D / 4) * (D / 4); blk += 256) {
-      const int r0 = 4 * (blk / (D / 4)), c0 = 4 * (blk % (D / 4));
-      f32x4 rows4[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) rows4[rr] = *reinterpret_cast<const f32x4*>(Sg + (r0 + rr) * D + c0);
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const f32x4 col = {rows4[0][cc], rows4[1][cc], rows4[2][cc], rows4[3][cc]};
-        *reinterpret_cast<bf16x4*>(St + (c0 + cc) * (D + 8) + r0) = __builtin_convertvector(col, bf16x4);
+      for (int e = t; e < D * Tl::kChunks; e += 128) {
+        const int r = e / Tl::kChunks, c = e % Tl::kChunks;
+        const bf16x8 x = In<float>::load8(Sg + r * D + 8 * c);
+        lds_store16(st_tile(r) + k_pos<D>(r % kBlock, c), x);
       }
     }
     if (t < D) lin_u[t] = ug[t];
-    __syncthreads();
+    SLA_WAIT_VMCNT(0);
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
 
     bf16x8 pq[kQs];
     float den = 0.f, gdot = 0.f;
@@ -230,7 +370,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
       f32x8 ph;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const int r = 32 * ks + 8 * lg + m;
+        const int r = 16 * ks + 8 * lg + m;
         const float qv = float(qf[ks][m]);
         ph[m] = phi(qv);
         den += ph[m] * lin_u[r];
@@ -238,50 +378,54 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
       }
       pq[ks] = cvt8(ph);
     }
-    den += __shfl_xor(den, 16);
     den += __shfl_xor(den, 32);
     float scale_lin = den > 0.f ? 1.f / den : 0.f;
     if constexpr (LIN == SLA_LIN_GLOBAL_GATED) {
-      gdot += __shfl_xor(gdot, 16);
       gdot += __shfl_xor(gdot, 32);
       scale_lin *= 1.f / (1.f + __expf(-gdot));
     }
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt) {
-      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+      f32x16 num;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) num[e] = 0.f;
+      const int row = 32 * dt + l32;                 // c
 #pragma unroll
       for (int ks = 0; ks < kQs; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(St + (16 * dt + l16) * (D + 8) + 32 * ks + 8 * lg);
-        num = mfma16(a, pq[ks], num);
+        const bf16x8 a = lds_load16(st_tile(row) + k_pos<D>(row % kBlock, 2 * ks + lg));
+        num = mfma32(a, pq[ks], num);
       }
       oacc[dt] += num * scale_lin;
     }
   }
 
-  // ---- store: lane holds O[tq][16 dt + 4 lg + e]; padded query rows are zero
+  // ---- store: lane holds O[tq][32 dt + 8 (e / 4) + 4 lg + e % 4]; padded query rows are zero
   const int64_t obase = ((int64_t(b) * p.Hq + h) * p.N + tq) * D;
 #pragma unroll
-  for (int dt = 0; dt < kDt; ++dt) {
-    f32x4 o = qvalid ? oacc[dt] : f32x4{0.f, 0.f, 0.f, 0.f};
-    const int col = 16 * dt + 4 * lg;
-    if (p.out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + col) = o;
-    } else {
-      *reinterpret_cast<bf16x4*>(static_cast<u16*>(p.out) + obase + col) = __builtin_convertvector(o, bf16x4);
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      f32x4 o = {oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
+      if (!qvalid) o = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int col = 32 * dt + 8 * e4 + 4 * lg;
+      if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + col) = o;
+      } else {
+        *reinterpret_cast<bf16x4*>(static_cast<u16*>(p.out) + obase + col) = __builtin_convertvector(o, bf16x4);
+      }
     }
-  }
 }
 
 template <typename T, int D>
 static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hipStream_t st) {
   if (causal) {
-    attn_fwd_kernel<T, D, true, SLA_LIN_NONE><<<grid, 256, 0, st>>>(p);
+    attn_fwd_kernel<T, D, true, SLA_LIN_NONE><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
-    attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL><<<grid, 256, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_GLOBAL_GATED) {
-    attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED><<<grid, 256, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED><<<grid, 128, 0, st>>>(p);
   } else {
-    attn_fwd_kernel<T, D, false, SLA_LIN_NONE><<<grid, 256, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_NONE><<<grid, 128, 0, st>>>(p);
   }
 }
 
@@ -290,7 +434,7 @@ static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hip
 extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
                                    float scale, int32_t causal, int32_t window_tokens, int32_t group_map,
                                    const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
-                                   const int32_t* marg_rowptr, const int32_t* marg_idx, int32_t lin_mode,
+                                   const uint32_t* marg_bits, int32_t lin_mode,
                                    const float* H, const float* z, const float* H_all, const float* z_all,
                                    const float* w_gate, void* out, int32_t out_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream) {
@@ -324,13 +468,13 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   p.out = out; p.out_f32 = out_dtype == SLA_F32;
 
   if (lin_mode == SLA_LIN_MARGINAL) {
-    if (H == nullptr || z == nullptr || marg_rowptr == nullptr || marg_idx == nullptr) return SLA_ERR_NULL;
+    if (H == nullptr || z == nullptr || marg_bits == nullptr) return SLA_ERR_NULL;
     const size_t need = sla_attn_workspace_bytes(q->B, Hs, nqb, d, lin_mode);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
-    float* S = static_cast<float*>(workspace);
-    float* u = S + int64_t(q->B) * Hs * nqb * d * d;
-    if ((st = launch_marginal_states(H, z, q->B, q->H, k->H, nqb, nqb, d, p.group_map, marg_rowptr, marg_idx, S,
-                                     u, s)) != SLA_OK)
+    u16* S = static_cast<u16*>(workspace);
+    float* u = reinterpret_cast<float*>(S + int64_t(q->B) * Hs * nqb * d * d);
+    if ((st = launch_marginal_states(H, z, q->B, q->H, k->H, nqb, nqb, d, p.group_map, marg_bits, S, u, s)) !=
+        SLA_OK)
       return st;
     p.S = S;
     p.u = u;
@@ -345,7 +489,7 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
     p.u = z_all;
     p.w_gate = w_gate;
   }
-  dim3 grid(nqb, q->H, q->B);
+  dim3 grid(nqb * q->H * q->B);
   const bool bf = q->dtype == SLA_BF16;
   if (d == 128) {
     if (bf) launch_attn<bf16raw, 128>(p, causal, lin_mode, grid, s);

@@ -1,5 +1,6 @@
 // Classification step: per query-block row, label every key block critical, marginal
-// or negligible and emit CSR lists of the critical and marginal blocks.
+// or negligible and emit CSR lists of the critical and marginal blocks (and, optionally, the
+// marginal set as a bit mask per row, the form the marginal aggregation consumes).
 //
 // Method: each (query block, key block) pair falls in one of three classes — the top
 // share of a row is critical, the bottom share negligible, the rest marginal (SLA
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
                                                       int n_negl, int64_t rows, int* __restrict__ crit_rowptr,
                                                       int* __restrict__ crit_idx, uint8_t* __restrict__ crit_flags,
                                                       int* __restrict__ marg_rowptr, int* __restrict__ marg_idx,
-                                                      int* __restrict__ row_counts) {
+                                                      uint32_t* __restrict__ marg_bits, int* __restrict__ row_counts) {
   __shared__ uint32_t hist[256];
   const int64_t r = blockIdx.x;
   const int lane = threadIdx.x;
@@ -162,11 +163,21 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
 #pragma unroll
   for (int m = 0; m < M; ++m) one[m] = 1;
   compact_write<M>(crit, crit_idx + r * n_crit, crit_flags ? crit_flags + r * n_crit : nullptr, one, n_crit);
-  if (marg_idx != nullptr) {
+  if (marg_idx != nullptr || marg_bits != nullptr) {
     bool marg[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) marg[m] = keep[m] && !crit[m];
-    compact_write<M>(marg, marg_idx + r * n_marg, nullptr, one, n_marg);
+    if (marg_idx != nullptr) compact_write<M>(marg, marg_idx + r * n_marg, nullptr, one, n_marg);
+    if (marg_bits != nullptr) {
+      // block j = lane + 64 m is bit j % 32 of word j / 32: one ballot fills words 2m and 2m + 1
+      const int nw = (nkb + 31) / 32;
+      uint32_t* out = marg_bits + r * nw;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint64_t bm = __ballot(marg[m]);
+        if (lane < 2 && 2 * m + lane < nw) out[2 * m + lane] = uint32_t(bm >> (32 * lane));
+      }
+    }
   }
   if (lane == 0) {
     crit_rowptr[r] = int(r * n_crit);
@@ -279,6 +290,7 @@ extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, 
                                     int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
                                     int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags,
                                     int64_t crit_cap, int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap,
+                                    uint32_t* marg_bits,
                                     int32_t* row_counts, void* workspace, size_t workspace_bytes,
                                     void* stream) {
   using namespace sla;
@@ -308,10 +320,11 @@ extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, 
     if (crit_cap < rows * n_crit || (marg_idx != nullptr && marg_cap < rows * nm)) return SLA_ERR_CAPACITY;
     if (rows * n_crit > INT32_MAX || rows * nm > INT32_MAX) return SLA_ERR_CAPACITY;
     SLA_DISPATCH_M(classify_kernel, dim3(uint32_t(rows)), scores, nkb, n_crit, n_negl, rows, crit_rowptr,
-                   crit_idx, crit_flags, marg_rowptr, marg_idx, row_counts);
+                   crit_idx, crit_flags, marg_rowptr, marg_idx, marg_bits, row_counts);
     return launch_status();
   }
   if (nqb != nkb) return SLA_ERR_SHAPE;
+  if (marg_bits != nullptr) return SLA_ERR_UNSUPPORTED;   // causal maps have no marginal class
   const int64_t cap = sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, 1, window_tokens, 0);
   if (crit_cap < cap || cap > INT32_MAX) return SLA_ERR_CAPACITY;
   const size_t need = sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, 1, window_tokens);

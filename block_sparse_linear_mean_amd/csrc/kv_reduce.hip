@@ -7,6 +7,9 @@
 // keys.  SALAD's parallel linear branch covers all keys (SALAD page, method
 // framework), which needs only the sum over every block.
 //
+// Layout: states are stored feature-transposed, H[c][r] = sum_s phi(K[s,r]) V[s,c], which is
+// the operand layout the attention epilogue reads (16 contiguous bytes along r).
+//
 // Design (gfx950): one workgroup per (KV head, chunk of key blocks).  K and V blocks
 // are loaded with 16-byte reads and written to LDS transposed ([feature][token]), with
 // phi applied to K and rounded to bf16, so both matrix-core operands of the
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
       }
     }
   }
+  // store transposed, [c][r]: lane holds r = 16 rt + 4 lg + e (e < 4) for c = 16 ct + l16
   const int64_t sidx = int64_t(bg) * nch + c;
   float* Hs = Hout + sidx * D * D;
 #pragma unroll
@@ -134,8 +138,7 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
     const int rt = kRt * w + a;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Hs[(16 * rt + 4 * lg + e) * D + 16 * ct + l16] = acc[a][ct][e];
+      *reinterpret_cast<f32x4*>(Hs + (16 * ct + l16) * D + 16 * rt + 4 * lg) = acc[a][ct];
   }
   if (t < D) zout[sidx * D + t] = zacc;
 }

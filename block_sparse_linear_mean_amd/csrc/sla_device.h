@@ -29,6 +29,65 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ bf16x8 cvt8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 32x32x16 bf16 matrix-core product: D = A(32x16) * B(16x32) + C.
+// Lane l holds A[l % 32][8 * (l / 32) .. +8], B[8 * (l / 32) .. +8][l % 32],
+// and D[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32] for e = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ lds_u8* to_lds(void* p) { return (lds_u8*)p; }
+
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+__device__ __forceinline__ bf16x8 lds_load16(const lds_u8* p) { return *(const lds_bf16x8*)p; }
+__device__ __forceinline__ void lds_store16(lds_u8* p, bf16x8 v) { *(lds_bf16x8*)p = v; }
+
+// Transposing LDS read of 16-bit data (gfx950).  Within each group of 16 lanes, lane i
+// receives element (i % 4) of the 8 bytes addressed by lane 4 * e + i / 4, for e = 0..3.
+// So if lane k of a group addresses row r0 + k / 4, columns c0 + 4 (k % 4) .. +3 of a
+// row-major 16-bit matrix, lane i receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ bf16x4 lds_read_tr4(lds_u8* addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16 l
+// (lds must be the same for the whole wavefront).  Issued from a self-contained asm block
+// (M0 set inside it, no output registers), so the copy's completion is tracked only by the
+// caller's explicit SLA_WAIT_VMCNT: the compiler would otherwise drain every copy in flight
+// before any LDS read, which serialises the K/V pipeline.
+__device__ __forceinline__ void load_lds16(const void* gsrc, lds_u8* lds) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+// s_waitcnt encodings (gfx9 family): wait until at most N vector-memory operations of this
+// wavefront are outstanding; the other counters are left unconstrained.
+#define SLA_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+// wait until this wavefront's LDS operations have completed (lgkmcnt(0)), nothing else
+#define SLA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+// Workgroup barrier without a memory fence: the compiler may not move memory operations across
+// it, and the caller states with SLA_WAIT_* which of its own operations must have completed.
+// (A fenced barrier would also wait for every direct-to-LDS load still in flight.)
+#define SLA_BARRIER()                 \
+  do {                                \
+    asm volatile("" ::: "memory");    \
+    __builtin_amdgcn_s_barrier();     \
+    asm volatile("" ::: "memory");    \
+  } while (0)
+
 // Eight consecutive input elements as bf16 (bf16 inputs: one 16-byte load; fp32: two).
 template <typename T> struct In;
 template <> struct In<bf16raw> {

@@ -75,7 +75,7 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
 size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, int32_t lin_mode) {
   if (lin_mode != SLA_LIN_MARGINAL || B < 1 || Hs < 1 || nqb < 1) return 0;
   const int64_t rows = int64_t(B) * Hs * nqb;
-  return size_t(rows * (int64_t(d) * d + d) * 4);
+  return size_t(rows * (int64_t(d) * d * 2 + int64_t(d) * 4));   // bf16 row sums + fp32 u
 }
 
 }  // extern "C"

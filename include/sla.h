@@ -143,12 +143,14 @@ size_t sla_block_map_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t
  *   critical = first n_crit of the order, negligible = last n_negl, marginal = the rest.
  *   crit_rowptr[r] = r * n_crit, marg_rowptr[r] = r * (nkb - n_crit - n_negl).
  *   crit_flags (nullable) entries are 1.  marg_rowptr/marg_idx may both be NULL to skip
- *   the marginal list.
+ *   the marginal list.  marg_bits (nullable): the marginal set of each row as a bit mask,
+ *   [rows][ceil(nkb / 32)] uint32, block j = bit j % 32 of word j / 32 (the input of
+ *   sla_marginal_states).
  * Causal (nqb == nkb, NSA-style): candidates are j <= i; the first min(n_crit, i + 1)
  *   of the order are selected (flag bit 0) and united with the window blocks
  *   max(0, i - floor((window_tokens + 62) / 64)) .. i (flag bit 1; none when
  *   window_tokens == 0).  n_negl is ignored, the marginal list is empty and its
- *   pointers may be NULL.  Needs the workspace.
+ *   pointers may be NULL; marg_bits must be NULL.  Needs the workspace.
  *
  * Outputs (int32 unless stated): crit_rowptr [rows + 1], crit_idx [crit_cap] ascending
  * block indices per row, crit_flags [crit_cap] uint8, marg_rowptr [rows + 1],
@@ -158,7 +160,7 @@ size_t sla_block_map_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t
 sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
                          int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
                          int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags, int64_t crit_cap,
-                         int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap,
+                         int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
                          int32_t* row_counts, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes sla_linear_kv_reduce needs (non-zero only when H is NULL and H_all is not). */
@@ -168,9 +170,10 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
 /*
  * Linear-attention key states (SLA analysis page: marginal pairs get linear attention,
  * O(N d^2); phi = elu + 1).  Per KV head and key block j, over the valid rows s:
- *   H[b,g,j,r,c] = sum_s phi(K[s,r]) * V[s,c]   (fp32, [B, Hkv, nb, d, d]; nullable)
+ *   H[b,g,j,c,r] = sum_s phi(K[s,r]) * V[s,c]   (fp32, [B, Hkv, nb, d, d]; nullable)
+ *     i.e. each d x d state is stored transposed, V-feature major: (phi(K_j)^T V_j)^T.
  *   z[b,g,j,r]   = sum_s phi(K[s,r])            (fp32, [B, Hkv, nb, d];     nullable with H)
- *   H_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d, d];     nullable)
+ *   H_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d, d], same [c][r] layout; nullable)
  *   z_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d];        nullable with H_all)
  * phi(K) is rounded to bf16 for the matrix-core contraction (fp32 accumulation); z sums
  * the same rounded values.  At least one of H, H_all must be non-NULL.  When H is NULL
@@ -181,17 +184,20 @@ sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Marginal aggregation of one block map: for every map row r with KV head g,
- *   S[r] = sum over marginal blocks j of H[b,g,j]  (fp32, [rows, d, d])
+ * Marginal aggregation of one block map (marginal sets given as the bit masks sla_block_map
+ * writes, [rows][ceil(nkb / 32)]): for every map row r with KV head g,
+ *   S[r] = sum over marginal blocks j of H[b,g,j]  (bf16 bits, [rows, d, d], the [c][r] layout of H)
  *   u[r] = sum over marginal blocks j of z[b,g,j]  (fp32, [rows, d])
  * rows = B * Hs * nqb with Hs = Hkv if group_map else Hq; the KV head of map head s is
- * s if group_map else s / (Hq / Hkv).  Sums run in ascending block order (deterministic).
- * sla_attn_fwd performs this step itself; this entry exposes it on its own.
+ * s if group_map else s / (Hq / Hkv).
+ * Computed as a 0/1 mask matrix product on the matrix cores: the bit masks expand to 0/1
+ * operands, H and z are rounded to bf16 operands, sums accumulate in fp32 (deterministic) and S
+ * is rounded once to bf16, the operand precision of the attention epilogue that reads it.
+ * workspace: none.  sla_attn_fwd performs this step itself in SLA_LIN_MARGINAL mode.
  */
 sla_status sla_marginal_states(const float* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t nqb, int32_t nkb, int32_t d, int32_t group_map,
-                               const int32_t* marg_rowptr, const int32_t* marg_idx,
-                               float* S, float* u, void* stream);
+                               const uint32_t* marg_bits, void* S, float* u, void* stream);
 
 /* Workspace bytes sla_attn_fwd needs for (B, Hs map heads, nqb query blocks, d, lin mode). */
 size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, int32_t lin_mode);
@@ -207,12 +213,12 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  *   O_sparse[t] = softmax over allowed keys of (scale * q_t . k_s) applied to v_s, or 0
  *     when no key is allowed.  Allowed: s < n_valid in a listed block; causal != 0 adds
  *     s <= t and (flag bit 0 of the block, or t - s < window_tokens).
- *   lin_mode SLA_LIN_MARGINAL (needs marg_rowptr, marg_idx, H, z):
+ *   lin_mode SLA_LIN_MARGINAL (needs marg_bits, H, z):
  *     O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the sums of H_j and
  *     z_j over row r's marginal blocks; 0 when the row has none.
  *   lin_mode SLA_LIN_ROW_STATES: as SLA_LIN_MARGINAL, but H and z already hold the per-row
- *     sums S [rows, d, d] and u [rows, d] written by sla_marginal_states for this map; the
- *     marginal lists are not read and no workspace is needed.
+ *     sums S (bf16 bits, [rows, d, d]) and u (fp32, [rows, d]) written by sla_marginal_states
+ *     for this map; marg_bits is not read and no workspace is needed.
  *   lin_mode SLA_LIN_GLOBAL_GATED (needs H_all, z_all, w_gate [Hq][d] fp32):
  *     O_linear[t] = sigmoid(q_t . w_gate[h]) * phi(q_t)^T H_all / (phi(q_t) . z_all).
  *   Rows t >= n_valid are written as 0.
@@ -225,7 +231,7 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
 sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
                         float scale, int32_t causal, int32_t window_tokens, int32_t group_map,
                         const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
-                        const int32_t* marg_rowptr, const int32_t* marg_idx,
+                        const uint32_t* marg_bits,
                         int32_t lin_mode, const float* H, const float* z,
                         const float* H_all, const float* z_all, const float* w_gate,
                         void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,

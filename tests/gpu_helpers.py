@@ -76,8 +76,23 @@ def oracle_csr(f: orc.Forward):
             for i in range(f.nb):
                 maps[(b, h, i)] = f.map_row(b, h, i)
     csr = orc.to_csr(maps, f.B, Hs, f.nb)
+    csr["marg_bits"] = marg_bits_of(maps, f.B, Hs, f.nb, f.nb)
     dev = {k: to_dev(v, torch.uint8 if k == "crit_flags" else torch.int32) for k, v in csr.items()}
     return dev, maps
+
+
+def marg_bits_of(maps, B, Hs, nqb, nkb):
+    """Bit masks of the marginal lists: block j is bit j % 32 of word j / 32 (int32 view)."""
+    nw = (nkb + 31) // 32
+    bits = np.zeros((B * Hs * nqb, nw), dtype=np.uint32)
+    r = 0
+    for b in range(B):
+        for h in range(Hs):
+            for i in range(nqb):
+                for j in maps[(b, h, i)]["marg"]:
+                    bits[r, j // 32] |= np.uint32(1) << np.uint32(j % 32)
+                r += 1
+    return bits.view(np.int32)
 
 
 def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:

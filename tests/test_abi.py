@@ -67,7 +67,7 @@ def test_capacities_and_workspaces(L):
     assert sla.sla_block_map_capacity(1, 1, nb, nb, 16, 0, 1, 512, 1) == 0
     assert sla.sla_block_map_workspace_bytes(1, 1, nb, nb, 16, 0, 512) == 0
     assert sla.sla_block_map_workspace_bytes(1, 1, nb, nb, 16, 1, 512) >= nb * 25 * 5
-    assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 + 128) * 4
+    assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 * 2 + 128 * 4)
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_NONE) == 0
     assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 0
     assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 16 * (128 * 128 + 128) * 4
@@ -107,9 +107,9 @@ def test_pool_scores_validation(L):
 
 def test_block_map_validation(L):
     def call(scores=P, B=1, Hs=1, nqb=16, nkb=16, nc=4, nn=8, causal=0, win=0, crp=P, ci=P, ccap=64,
-             mrp=P, mi=P, mcap=64, rc=P, ws=None, wsb=0):
+             mrp=P, mi=P, mcap=64, rc=P, ws=None, wsb=0, bits=None):
         return L.sla_block_map(scores, B, Hs, nqb, nkb, nc, nn, causal, win, crp, ci, None, ccap, mrp, mi, mcap,
-                               rc, ws, wsb, None)
+                               bits, rc, ws, wsb, None)
     assert call(scores=None) == ENULL
     assert call(crp=None) == ENULL
     assert call(rc=None) == ENULL
@@ -124,6 +124,7 @@ def test_block_map_validation(L):
     assert call(causal=1, nc=4, win=128, ccap=10) == ECAP
     assert call(causal=1, nc=4, win=128, ccap=1000) == EWS        # workspace missing
     assert call(causal=1, nc=4, win=128, ccap=1000, ws=P, wsb=1) == EWS
+    assert call(causal=1, nc=4, win=128, ccap=1000, ws=P, wsb=1 << 20, bits=P) == EUNSUP
 
 
 def test_kv_reduce_validation(L):
@@ -140,10 +141,10 @@ def test_kv_reduce_validation(L):
 
 
 def test_marginal_states_validation(L):
-    def call(H=P, z=P, B=1, Hq=2, Hkv=1, nqb=4, nkb=4, d=128, rp=P, ix=P, S=P, u=P):
-        return L.sla_marginal_states(H, z, B, Hq, Hkv, nqb, nkb, d, 0, rp, ix, S, u, None)
+    def call(H=P, z=P, B=1, Hq=2, Hkv=1, nqb=4, nkb=4, d=128, bits=P, S=P, u=P):
+        return L.sla_marginal_states(H, z, B, Hq, Hkv, nqb, nkb, d, 0, bits, S, u, None)
     assert call(H=None) == ENULL
-    assert call(rp=None) == ENULL
+    assert call(bits=None) == ENULL
     assert call(Hq=3, Hkv=2) == ESHAPE
     assert call(d=96) == EUNSUP
     assert call(S=ctypes.c_void_p(0x20004)) == EALIGN
@@ -151,16 +152,16 @@ def test_marginal_states_validation(L):
 
 def test_attn_fwd_validation(L):
     q = desc()
-    def call(qq=q, kk=q, vv=q, nv=256, scale=0.1, causal=0, win=0, group=0, crp=P, ci=P, cf=None, mrp=None,
-             mi=None, lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0):
+    def call(qq=q, kk=q, vv=q, nv=256, scale=0.1, causal=0, win=0, group=0, crp=P, ci=P, cf=None, mb=None,
+             lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0):
         return L.sla_attn_fwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), nv, scale, causal, win, group,
-                              crp, ci, cf, mrp, mi, lin, H, z, Ha, za, wg, out, odt, ws, wsb, None)
+                              crp, ci, cf, mb, lin, H, z, Ha, za, wg, out, odt, ws, wsb, None)
     assert call(out=None) == ENULL
     assert call(crp=None) == ENULL
     assert call(causal=1) == ENULL                   # causal needs the flags
     assert call(causal=1, cf=P, lin=1) == EUNSUP     # no linear branch under a causal mask
-    assert call(lin=1) == ENULL                      # marginal mode needs H, z and the marginal lists
-    assert call(lin=1, H=P, z=P, mrp=P, mi=P) == EWS
+    assert call(lin=1) == ENULL                      # marginal mode needs H, z and the marginal bit masks
+    assert call(lin=1, H=P, z=P, mb=P) == EWS
     assert call(lin=2) == ENULL
     assert call(lin=3) == ENULL                      # precomputed row states needed
     assert call(lin=3, H=ctypes.c_void_p(0x20004), z=P) == EALIGN

@@ -11,8 +11,8 @@ import torch
 
 from oracle import sla_oracle as orc
 from tests import refs
-from tests.gpu_helpers import (compare_outputs, gpu_map_rows, host, layer_for, oracle_csr, oracle_for, say,
-                               to_dev, ulp_distance)
+from tests.gpu_helpers import (compare_outputs, gpu_map_rows, host, layer_for, marg_bits_of, oracle_csr, oracle_for,
+                               say, to_dev, ulp_distance)
 from workloads import WORKLOADS, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +84,8 @@ def _check_map(maps, S, n_crit, n_negl, causal, window, n_sel):
     rows = list(range(B * Hs * nqb))
     got = gpu_map_rows(maps, rows)
     ref = orc.block_map(S, n_h=n_crit, n_l=n_negl, causal=causal, n_sel=n_sel, window=window)
+    if "marg_bits" in maps:
+        assert np.array_equal(maps["marg_bits"].cpu().numpy(), marg_bits_of(ref, B, Hs, nqb, nkb))
     for r in rows:
         b, rem = divmod(r, Hs * nqb)
         h, i = divmod(rem, nqb)
@@ -147,6 +149,7 @@ def test_linear_states(name):
     alls = sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv, per_block=False, want_all=True)
     torch.cuda.synchronize()
     H, z = orc.kv_states(f.K, f.V, w.Nv)
+    H = np.swapaxes(H, -1, -2)      # the library stores each state V-feature major, [c][r]
     for got, ref, what in [(out["H"], H, "H"), (out["z"], z, "z"), (out["H_all"], H.sum(2), "H_all"),
                            (out["z_all"], z.sum(2), "z_all"), (alls["H_all"], H.sum(2), "H_all chunked"),
                            (alls["z_all"], z.sum(2), "z_all chunked")]:
@@ -163,7 +166,7 @@ def test_marginal_states(name):
     import block_sparse_linear_mean_amd as sla
     csr, maps = oracle_csr(f)
     kv = sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv)
-    S, u = sla.sla_marginal_states(kv["H"], kv["z"], f.Hq, False, csr["marg_rowptr"], csr["marg_idx"])
+    S, u = sla.sla_marginal_states(kv["H"], kv["z"], f.Hq, False, csr["marg_bits"])
     torch.cuda.synchronize()
     Sg, ug = host(S), host(u)
     worst = 0.0
@@ -176,12 +179,12 @@ def test_marginal_states(name):
             refH += Hj
             refz += zj
         if m["marg"]:
-            worst = max(worst, np.linalg.norm(Sg[r] - refH) / np.linalg.norm(refH),
+            worst = max(worst, np.linalg.norm(Sg[r] - refH.T) / np.linalg.norm(refH),
                         np.linalg.norm(ug[r] - refz) / np.linalg.norm(refz))
         else:
             assert not Sg[r].any() and not ug[r].any()
     say(f"  worst row rel-L2 {worst:.2e}")
-    assert worst < 3e-3
+    assert worst < 5e-3      # bf16 operands and a bf16 result
 
 
 @pytest.mark.parametrize("name", list(MEDIUM))
