@@ -73,35 +73,52 @@ __device__ __forceinline__ int v_pos(int r, int c) {
 }
 
 // Stage rows 64 j .. 64 j + 63 of X (row stride sN elements) into an LDS tile.  bf16 inputs go
-// straight from global memory to LDS (each lane picks the global chunk that belongs at its
-// LDS slot); fp32 inputs are converted through registers.  The two wavefronts split the tile.
-// For the direct path the per-lane element offsets (row * sN + 8 * chunk) are precomputed
-// once per kernel by stage_offsets; only the block's base address changes per call.
-template <int D, bool KLAYOUT>
-__device__ __forceinline__ void stage_offsets(int64_t sN, int (&off)[AttnTile<D>::kInst / 2]) {
+// straight from global memory to LDS: a 1 KB step q covers R = 1024 / rowbytes rows, and lane l
+// fetches the global chunk that belongs at LDS offset q * 1024 + 16 l.  With the swizzles above
+// that chunk's byte offset from the step's first row is a per-lane constant, except for the K
+// layout at d = 128 where it takes 4 values (q % 4); so each wavefront keeps at most four 32-bit
+// offsets and all other address arithmetic is wave-uniform.  fp32 inputs are converted through
+// registers.  The two wavefronts split the tile's steps.
+template <int D>
+struct StageOff {
+  uint32_t k[4];   // K layout, index q % 4 (d = 128) or 0
+  uint32_t v;      // V layout
+};
+
+template <int D>
+__device__ __forceinline__ StageOff<D> stage_offsets(int64_t sN) {
   using Tl = AttnTile<D>;
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  constexpr int R = 1024 / Tl::kRowB;             // rows per 1 KB step: 4 (d 128) or 8 (d 64)
+  const int lane = threadIdx.x % kWave;
+  const int r = (16 * lane) / Tl::kRowB;          // row within the step
+  const int pc = lane % Tl::kChunks;              // physical chunk
+  StageOff<D> o;
 #pragma unroll
-  for (int n = 0; n < Tl::kInst / 2; ++n) {
-    const int q = w * (Tl::kInst / 2) + n;
-    const int o = q * 1024 + 16 * lane;
-    const int r = o / Tl::kRowB, pc = (o % Tl::kRowB) / 16;
-    const int c = KLAYOUT ? (pc ^ (r % Tl::kChunks)) : (pc ^ (2 * (r % 4)));
-    off[n] = int(r * sN) + 8 * c;
+  for (int m = 0; m < 4; ++m) {
+    // K: logical chunk c = pc ^ (row % chunks), row = q R + r; q R % chunks = 4 m (d 128) or 0
+    const int rk = (D == 128 ? 4 * m : 0) + r;
+    const int c = pc ^ (rk % Tl::kChunks);
+    o.k[m] = uint32_t(2 * (r * sN + 8 * c));
   }
+  o.v = uint32_t(2 * (r * sN + 8 * (pc ^ (2 * (r % 4)))));
+  return o;
 }
 
 template <typename T, int D, bool KLAYOUT>
 __device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, int j, lds_u8* tile,
-                                           const int (&off)[AttnTile<D>::kInst / 2]) {
+                                           const StageOff<D>& off) {
   using Tl = AttnTile<D>;
+  constexpr int R = 1024 / Tl::kRowB;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: the LDS base goes to M0
   if constexpr (sizeof(T) == 2) {
-    const T* base = X + int64_t(kBlock * j) * sN;
 #pragma unroll
-    for (int n = 0; n < Tl::kInst / 2; ++n)
-      load_lds16(base + off[n], tile + (w * (Tl::kInst / 2) + n) * 1024);
+    for (int n = 0; n < Tl::kInst / 2; ++n) {
+      const int q = w * (Tl::kInst / 2) + n;
+      const T* sbase = X + int64_t(kBlock * j + q * R) * sN;
+      const uint32_t vo = KLAYOUT ? off.k[D == 128 ? n % 4 : 0] : off.v;   // q % 4 == n % 4
+      load_lds16_sbase(sbase, vo, tile + q * 1024);
+    }
   } else {
 #pragma unroll
     for (int n = 0; n < Tl::kChunks * kBlock / 128; ++n) {
@@ -181,9 +198,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float c2 = p.scale_log2;
 
   // per-lane offsets, computed once: direct-load sources, K operand reads, V transposed reads
-  int koff[Tl::kInst / 2], voff[Tl::kInst / 2];
-  stage_offsets<D, true>(p.ksN, koff);
-  stage_offsets<D, false>(p.vsN, voff);
+  const StageOff<D> koff = stage_offsets<D>(p.ksN);
+  const StageOff<D> voff = stage_offsets<D>(p.vsN);
   int kread[kQs];                 // K row 32 kt + l32, chunk 2 ks + lg (+ 32 kt rows = kt * 8 KB)
 #pragma unroll
   for (int ks = 0; ks < kQs; ++ks) kread[ks] = k_pos<D>(l32, 2 * ks + lg);
@@ -237,16 +253,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);
     SLA_WAIT_LGKM0();
     SLA_BARRIER();
+    // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
     f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+    bf16x8 ka[2][2];
+    ka[0][0] = lds_load16(Kb + kread[0]);
+    ka[0][1] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
 #pragma unroll
-      for (int ks = 0; ks < kQs; ++ks) {
-        const bf16x8 a = lds_load16(Kb + kread[ks] + kt * 32 * Tl::kRowB);
-        sacc[kt] = mfma32(a, qf[ks], sacc[kt]);
+    for (int ks = 0; ks < kQs; ++ks) {
+      if (ks + 1 < kQs) {
+        ka[(ks + 1) & 1][0] = lds_load16(Kb + kread[ks + 1]);
+        ka[(ks + 1) & 1][1] = lds_load16(Kb + kread[ks + 1] + 32 * Tl::kRowB);
       }
+      sacc[0] = mfma32(ka[ks & 1][0], qf[ks], sacc[0]);
+      sacc[1] = mfma32(ka[ks & 1][1], qf[ks], sacc[1]);
     }
     SLA_WAIT_LGKM0();
     SLA_BARRIER();                                   // every wavefront has read K_j
@@ -270,7 +293,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     // lazy rescale: keep the running max unless the block's max exceeds it by 2^8 in exp2 units
     if (__any((mx - m_run) * c2 > 8.f)) {
       const float m_new = fmaxf(m_run, mx);
@@ -313,15 +336,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // O^T += V^T P^T: 16-key step u holds keys 16 u + 8 (m / 4) + 4 lg + m % 4 in slot m; each
     // 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
     // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
+    // kDt independent accumulation chains; operands read one step ahead
+    auto vop = [&](int u, int dt) {
+      const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
+      const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 va[2];
+    va[0] = vop(0, 0);
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
-        const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[dt] = mfma32(a, pb[u], oacc[dt]);
-      }
+    for (int st = 0; st < 4 * kDt; ++st) {
+      const int u = st / kDt, dt = st % kDt;
+      if (st + 1 < 4 * kDt) va[(st + 1) & 1] = vop((st + 1) / kDt, (st + 1) % kDt);
+      oacc[dt] = mfma32(va[st & 1], pb[u], oacc[dt]);
     }
     SLA_WAIT_LGKM0();
     SLA_BARRIER();                                   // every wavefront has read V_j
@@ -329,7 +356,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- normalise the sparse branch
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= inv_l;
@@ -345,8 +372,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (LIN == SLA_LIN_MARGINAL) {
       const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
       ug = p.u + mrow * D;
-      int soff[Tl::kInst / 2];
-      stage_offsets<D, true>(D, soff);
+      const StageOff<D> soff = stage_offsets<D>(D);
       stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
       if constexpr (D == 128) stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
     } else {
@@ -378,10 +404,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       pq[ks] = cvt8(ph);
     }
-    den += __shfl_xor(den, 32);
+    den = xor32_sum(den);
     float scale_lin = den > 0.f ? 1.f / den : 0.f;
     if constexpr (LIN == SLA_LIN_GLOBAL_GATED) {
-      gdot += __shfl_xor(gdot, 32);
+      gdot = xor32_sum(gdot);
       scale_lin *= 1.f / (1.f + __expf(-gdot));
     }
 #pragma unroll

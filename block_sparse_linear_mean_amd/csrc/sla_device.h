@@ -70,7 +70,31 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, lds_u8* lds) {
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(gsrc), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");
+}
+
+// The same copy with a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte offset, which
+// keeps the per-lane address state to one 32-bit register per distinct offset.  (The kernels using
+// this issue nothing else that reads or writes M0.)
+__device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t voff_bytes, lds_u8* lds) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff_bytes), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
+// max / sum with the partner lane l ^ 32 (v_permlane32_swap, no LDS round trip).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // s_waitcnt encodings (gfx9 family): wait until at most N vector-memory operations of this

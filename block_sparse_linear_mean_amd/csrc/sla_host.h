@@ -20,6 +20,8 @@ inline sla_status check_tensor(const sla_tensor* t) {
   if (t->d != 64 && t->d != 128) return SLA_ERR_UNSUPPORTED;
   if (t->N / SLA_BLOCK > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
   if (t->sN < t->d || t->sH < 1 || t->sB < 1) return SLA_ERR_SHAPE;
+  // the attention kernel's tile copies address rows through 32-bit per-lane byte offsets
+  if (t->sN > SLA_MAX_ROW_STRIDE) return SLA_ERR_UNSUPPORTED;
   const int64_t eb = elem_bytes(t->dtype);
   if (!aligned16(t->ptr) || (t->sN * eb) % 16 || (t->sH * eb) % 16 || (t->sB * eb) % 16)
     return SLA_ERR_ALIGN;

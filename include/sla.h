@@ -31,7 +31,8 @@
  *   argument returns an error code and launches nothing.  A failed launch
  *   returns SLA_ERR_HIP.  Device faults surface at the caller's next sync.
  * - Q, K, V use layout [B, H, N, d] with element strides (sB, sH, sN) and unit
- *   d-stride; rows are 16-byte aligned.  d is 64 or 128, the block size is 64,
+ *   d-stride; rows are 16-byte aligned and sN <= SLA_MAX_ROW_STRIDE (larger row
+ *   strides return SLA_ERR_UNSUPPORTED).  d is 64 or 128, the block size is 64,
  *   N is a multiple of 64 and at most one block is partial:
  *   N - 64 < n_valid <= N.  Positions >= n_valid are padding: they are excluded
  *   from pooled means and from both attention branches, and the output rows of
@@ -52,6 +53,7 @@ extern "C" {
 #define SLA_ABI_VERSION 1
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
+#define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
 
 typedef int32_t sla_status;
 enum {
