@@ -127,6 +127,81 @@ def cpu_baseline(w, q, k, v, wg, heads):
     }
 
 
+# ----------------------------------------------------------------------------- profile summaries
+# Text summaries of rocprofv3 output (run on the host after a profiled run; no GPU needed).
+
+def _read_csv(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def _short(name, n=70):
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def summarize_trace(directory, command, note):
+    """Per-kernel call count and durations (us) from a --kernel-trace run's *kernel_trace.csv."""
+    rows = _read_csv(directory, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"# rocprofv3 kernel trace summary: {note}", f"# command: {command}",
+           "# durations in microseconds, one row per kernel, from the run's kernel_trace.csv",
+           f"{'kernel':72s} {'calls':>6s} {'total_us':>11s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{_short(name, 72):72s} {len(d):6d} {sum(d):11.1f} {sum(d) / len(d):9.2f} "
+                   f"{min(d):9.2f} {max(d):9.2f}")
+    return "\n".join(out) + "\n"
+
+
+def summarize_counters(fetch_dir, write_dir, kernel_pass, workload, copy_mib, commands):
+    """HBM traffic per launch of one pass's kernel from FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch),
+    each scaled by the ratio of known to counted bytes of an elementwise copy of copy_mib MiB."""
+    import statistics
+    key = {"attention": "attn_fwd_kernel", "marginal_states": "marginal_gemm_kernel",
+           "kv_reduce": "kv_state_kernel", "pool_scores": "scores_kernel", "block_map": "classify_kernel"}[kernel_pass]
+
+    def per_kernel(directory, counter):
+        vals = {}
+        for r in _read_csv(directory, "counter_collection.csv"):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * (1 << 20)
+
+    def pick(vals, match, counter):
+        names = [n for n in vals if match(n)]
+        if not names:
+            raise SystemExit(f"no {counter} rows for the kernel matching the {kernel_pass} pass")
+        return names[0], statistics.median(vals[names[0]])
+
+    is_copy = lambda n: "MulFunctor" in n or ("elementwise" in n and "mul" in n.lower())
+    ck_f, copy_f = pick(fetch, is_copy, "FETCH_SIZE")
+    ck_w, copy_w = pick(write, is_copy, "WRITE_SIZE")
+    fac_f, fac_w = copy_bytes / copy_f, copy_bytes / copy_w
+    kn, kf = pick(fetch, lambda n: key in n, "FETCH_SIZE")
+    _, kw = pick(write, lambda n: key in n, "WRITE_SIZE")
+    traffic = int(round(kf * fac_f + kw * fac_w))
+    out = [f"# HBM traffic per launch: {kernel_pass} pass ({_short(kn, 60)}), workload {workload}",
+           f"# fetch run: {commands[0]}", f"# write run: {commands[1]}",
+           f"# calibration kernel: {_short(ck_f, 60)}, {copy_mib} MiB read + {copy_mib} MiB written per launch",
+           f"copy   FETCH_SIZE {copy_f:.0f} B counted / {copy_bytes} B known -> factor {fac_f:.4f}",
+           f"copy   WRITE_SIZE {copy_w:.0f} B counted / {copy_bytes} B known -> factor {fac_w:.4f}",
+           f"kernel FETCH_SIZE median {kf:.0f} B/launch (scaled {kf * fac_f:.0f})",
+           f"kernel WRITE_SIZE median {kw:.0f} B/launch (scaled {kw * fac_w:.0f})",
+           f"TRAFFIC bytes_per_launch={traffic} kernel_source_sha={kernel_source_digest(kernel_pass)}"]
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,7 +212,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="print a kernel-trace summary of a rocprofv3 run")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM-traffic summary of the --pass kernel from two rocprofv3 --pmc runs")
+    ap.add_argument("--pass", dest="pass_name", default="attention", choices=PASSES)
+    ap.add_argument("--command", action="append", default=[], help="profiling command(s) to record")
+    ap.add_argument("--note", default="")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, (args.command or ["?"])[0], args.note), end="")
+        return
+    if args.summarize_counters:
+        cmds = (args.command + ["?", "?"])[:2]
+        print(summarize_counters(*args.summarize_counters, args.pass_name, args.workload,
+                                 args.copy_calibration_mb, cmds), end="")
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -239,13 +329,15 @@ def main():
         "gpu_ms_per_step": round(gpu_ms, 5),
     }
     if args.copy_calibration_mb:
+        # an elementwise kernel that reads and writes exactly n * 4 bytes each (a plain DtoD copy
+        # may go to a blit path that the counters do not see)
         n = args.copy_calibration_mb * (1 << 20) // 4
         src = torch.ones(n, device=dev, dtype=torch.float32)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log(f"bench: copy calibration, 3 copies of {args.copy_calibration_mb} MiB")
+        log(f"bench: copy calibration, 3 elementwise copies of {args.copy_calibration_mb} MiB")
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (oracle) on {args.cpu_sample_heads} head(s)")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, wg, args.cpu_sample_heads)
