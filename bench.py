@@ -55,9 +55,10 @@ def pass_work(w, layer):
     work["pool_scores"] = ("hbm", B * (Hq + Hkv) * Nv * d * eb + B * (Hq + Hkv) * nb * d * 4 + rows * nb * 4)
     work["block_map"] = ("hbm", rows * nb * 4 + (n_crit_entries + n_marg_entries) * 4 + rows * 20)
     if layer.lin == 1:
-        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d + d) * 4)
-        # mask product S = M H: reads every state once (fp32), writes bf16 row sums + fp32 u
-        work["marginal_states"] = ("hbm", B * Hkv * nb * (d * d + d) * 4 + rows * (d * d * 2 + d * 4))
+        # K, V in; one bf16 state + fp32 z per key block out
+        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d * 2 + d * 4))
+        # mask product S = M H: reads every bf16 state and z once, writes bf16 row sums + fp32 u
+        work["marginal_states"] = ("hbm", B * Hkv * nb * (d * d * 2 + d * 4) + rows * (d * d * 2 + d * 4))
     elif layer.lin == 2:
         work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * (d * d + d) * 4)
         work["marginal_states"] = ("hbm", 0)

@@ -73,7 +73,8 @@ class SlaForward:
                                     want_marg=self.lin == SLA_LIN_MARGINAL)
         self.kv = {}
         if self.lin == SLA_LIN_MARGINAL:
-            self.kv = dict(H=torch.empty((B, Hkv, nb, d, d), **f), z=torch.empty((B, Hkv, nb, d), **f),
+            self.kv = dict(H=torch.empty((B, Hkv, nb, d, d), device=dev, dtype=torch.bfloat16),
+                           z=torch.empty((B, Hkv, nb, d), **f),
                            workspace=None, workspace_bytes=0)
         elif self.lin == SLA_LIN_GLOBAL_GATED:
             ws = sla_kv_reduce_workspace_bytes(B, Hkv, N, d, False, True)

@@ -197,7 +197,7 @@ def sla_block_map(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=Tr
 
 
 def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None):
-    """Returns dict(H, z[, H_all, z_all])."""
+    """Returns dict(H, z[, H_all, z_all]): per-block states H in bf16, everything else fp32."""
     _require_gpu(k, v)
     B, Hkv, N, d = k.shape
     nb = N // BLOCK
@@ -205,7 +205,7 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
         f = dict(device=k.device, dtype=torch.float32)
         out = {}
         if per_block:
-            out["H"] = torch.empty((B, Hkv, nb, d, d), **f)
+            out["H"] = torch.empty((B, Hkv, nb, d, d), device=k.device, dtype=torch.bfloat16)
             out["z"] = torch.empty((B, Hkv, nb, d), **f)
         if want_all:
             out["H_all"] = torch.empty((B, Hkv, d, d), **f)
@@ -222,8 +222,10 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
 
 
 def sla_marginal_states(H, z, Hq, group_map, marg_bits, out=None):
-    """Per-row marginal sums: S bf16 [rows, d, d] in H's [c][r] layout, u fp32 [rows, d]."""
+    """Per-row marginal sums of the bf16 states H: S bf16 [rows, d, d] in H's [c][r] layout, u fp32 [rows, d]."""
     _require_gpu(H, z, marg_bits)
+    if H.dtype != torch.bfloat16:
+        raise ValueError("H must be the bf16 per-block states of sla_linear_kv_reduce")
     B, Hkv, nb, d, _ = H.shape
     Hs = Hkv if group_map else Hq
     rows = B * Hs * nb

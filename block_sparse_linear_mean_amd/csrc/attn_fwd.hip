@@ -28,7 +28,7 @@
 
 namespace sla {
 
-sla_status launch_marginal_states(const float* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
+sla_status launch_marginal_states(const u16* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
                                   int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st);
 
 struct AttnParams {
@@ -69,7 +69,7 @@ __device__ __forceinline__ int k_pos(int r, int c) {
 }
 template <int D>
 __device__ __forceinline__ int v_pos(int r, int c) {
-  return r * AttnTile<D>::kRowB + 16 * (c ^ (2 * (r % 4)));
+  return trs_pos<AttnTile<D>::kRowB>(r, c);
 }
 
 // Stage rows 64 j .. 64 j + 63 of X (row stride sN elements) into an LDS tile.  bf16 inputs go
@@ -138,11 +138,7 @@ struct WgCoord {
   int i, h, b;
 };
 __device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv) {
-  const int n = gridDim.x;
-  const int L = blockIdx.x;
-  const int xcd = L % 8, slot = L / 8;
-  const int q = n / 8, r = n % 8;
-  const int logical = xcd * q + min(xcd, r) + slot;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int G = Hq / Hkv;
   const int hh = logical % G;
   const int rest = logical / G;
@@ -461,7 +457,7 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
                                    float scale, int32_t causal, int32_t window_tokens, int32_t group_map,
                                    const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
                                    const uint32_t* marg_bits, int32_t lin_mode,
-                                   const float* H, const float* z, const float* H_all, const float* z_all,
+                                   const void* H, const float* z, const float* H_all, const float* z_all,
                                    const float* w_gate, void* out, int32_t out_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   using namespace sla;
@@ -499,7 +495,8 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
     u16* S = static_cast<u16*>(workspace);
     float* u = reinterpret_cast<float*>(S + int64_t(q->B) * Hs * nqb * d * d);
-    if ((st = launch_marginal_states(H, z, q->B, q->H, k->H, nqb, nqb, d, p.group_map, marg_bits, S, u, s)) !=
+    if (!aligned16(H) || !aligned16(z)) return SLA_ERR_ALIGN;
+    if ((st = launch_marginal_states(static_cast<const u16*>(H), z, q->B, q->H, k->H, nqb, nqb, d, p.group_map, marg_bits, S, u, s)) !=
         SLA_OK)
       return st;
     p.S = S;

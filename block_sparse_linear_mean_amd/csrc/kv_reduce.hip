@@ -8,139 +8,215 @@
 // framework), which needs only the sum over every block.
 //
 // Layout: states are stored feature-transposed, H[c][r] = sum_s phi(K[s,r]) V[s,c], which is
-// the operand layout the attention epilogue reads (16 contiguous bytes along r).
+// the operand layout the attention epilogue reads (16 contiguous bytes along r).  Per-block
+// states are written in bf16 (rounded once from the fp32 sums): they are summed again in fp32
+// by the marginal aggregation, whose matrix-core operands are bf16 anyway, and bf16 halves the
+// pass's dominant cost, the state writes.  Sums over chunks of blocks stay fp32.
 //
-// Design (gfx950): one workgroup per (KV head, chunk of key blocks).  K and V blocks
-// are loaded with 16-byte reads and written to LDS transposed ([feature][token]), with
-// phi applied to K and rounded to bf16, so both matrix-core operands of the
-// token contraction read 16 contiguous bytes per lane.  Each of the 4 wavefronts
-// owns a quarter of the d x d output in fp32 accumulators; a chunk of several blocks
-// accumulates in registers before one store.  The pass is HBM-bound and
-// write-dominated (a fp32 state per block is twice the bytes of the block's K and V).
+// Design (gfx950): one workgroup of 4 wavefronts per (KV head, run of cb key blocks).  Each
+// thread loads its 16-byte pieces of K and V of the next block into registers while the current
+// block is contracted (one block of prefetch), applies phi to K in fp32 and writes both tiles to
+// LDS row-major in the layout of the transposing read; the 32x32x16 matrix-core operands
+// phi(K)^T (A) and V (B) are both read with it.  Wavefront w owns H rows r = 32 w .. 32 w + 31
+// (d = 128; at d = 64 a quarter of the 64 x 64 state) and gets z from one more product against
+// a B operand of ones, so z sums exactly the rounded phi(K) values H uses.  A lane's accumulator
+// holds 4 consecutive r for one c; bf16 states are re-staged through LDS and written with
+// 1 KB-contiguous wavefront stores, fp32 run sums with 16-byte stores.  The pass is HBM-bound:
+// K and V in, one state per block out.
 #include "sla_device.h"
 #include "sla_host.h"
 
+#include <algorithm>
+
 namespace sla {
 
+// The 16-byte pieces one thread moves per tile: element chunk e = t + 256 n of the 64 x D tile.
+// load() only issues the global loads (raw input elements stay in registers, so the loads of
+// the next block are in flight while the current one is contracted); store() converts, applies
+// phi to K in fp32 and writes both tiles to LDS.
 template <typename T, int D>
-struct KvTile {
-  static constexpr int kTpt = D / 32;            // tokens per thread in the transposing load
-  static constexpr int kTg = kBlock / kTpt;      // token groups
-  static constexpr int kStride = kBlock + 8;     // LDS row stride (bf16 elements)
+struct KvPiece {
+  static constexpr int kChunks = D / 8;                  // 16-byte bf16 chunks per row
+  static constexpr int kPer = kBlock * kChunks / 256;    // per thread: 4 (d 128) or 2 (d 64)
+  static constexpr int kVec = sizeof(T) == 2 ? 1 : 2;    // 16-byte loads per 8 elements
+  f32x4 k[kPer][kVec], v[kPer][kVec];                    // raw bits (bf16 inputs use [n][0] only)
+  uint32_t valid;                                        // bit n: piece n is a valid token row
+
+  __device__ __forceinline__ void load(const T* __restrict__ K, int64_t ksN, const T* __restrict__ V, int64_t vsN,
+                                       int j, int n_valid) {
+    valid = 0;
+#pragma unroll
+    for (int n = 0; n < kPer; ++n) {
+      const int e = threadIdx.x + 256 * n;
+      const int r = e / kChunks, c = e % kChunks;
+      int s = kBlock * j + r;
+      if (s < n_valid) valid |= 1u << n;
+      else s = n_valid - 1;                              // in-bounds stand-in; zeroed in store()
+      const f32x4* kp = reinterpret_cast<const f32x4*>(K + int64_t(s) * ksN + 8 * c);
+      const f32x4* vp = reinterpret_cast<const f32x4*>(V + int64_t(s) * vsN + 8 * c);
+#pragma unroll
+      for (int h = 0; h < kVec; ++h) {
+        k[n][h] = kp[h];
+        v[n][h] = vp[h];
+      }
+    }
+  }
+  __device__ __forceinline__ void unpack(const f32x4* x, float* out) const {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t a[4] = {__float_as_uint(x[0][0]), __float_as_uint(x[0][1]), __float_as_uint(x[0][2]),
+                             __float_as_uint(x[0][3])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(a[i] << 16);
+        out[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { out[i] = x[0][i]; out[4 + i] = x[1][i]; }
+    }
+  }
+  // phi(K) rounded to bf16 and V (zero for padded rows), into trs-layout tiles
+  __device__ __forceinline__ void store(lds_u8* kt, lds_u8* vt) const {
+#pragma unroll
+    for (int n = 0; n < kPer; ++n) {
+      const int e = threadIdx.x + 256 * n;
+      const int r = e / kChunks, c = e % kChunks;
+      float kf[8];
+      unpack(k[n], kf);
+      f32x8 f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) f[m] = phi(kf[m]);
+      bf16x8 vb;
+      if constexpr (sizeof(T) == 2) {
+        vb = __builtin_bit_cast(bf16x8, v[n][0]);
+      } else {
+        const f32x8 vf = {v[n][0][0], v[n][0][1], v[n][0][2], v[n][0][3],
+                          v[n][1][0], v[n][1][1], v[n][1][2], v[n][1][3]};
+        vb = cvt8(vf);
+      }
+      const bool ok = (valid >> n) & 1u;
+      lds_store16(kt + trs_pos<2 * D>(r, c), ok ? cvt8(f) : zero8());
+      lds_store16(vt + trs_pos<2 * D>(r, c), ok ? vb : zero8());
+    }
+  }
 };
 
-// Loads key block j (rows >= n_valid as zero) into Kt = bf16(phi(K))^T and Vt = bf16(V)^T.
-template <typename T, int D>
-__device__ __forceinline__ void load_kv_transposed(const T* __restrict__ K, int64_t ksN, const T* __restrict__ V,
-                                                   int64_t vsN, int j, int n_valid, u16* Kt, u16* Vt) {
-  using Tile = KvTile<T, D>;
-  const int t = threadIdx.x;
-  const int tg = t % Tile::kTg, fg = t / Tile::kTg;    // tokens kTpt*tg.., features 8*fg..
-  float kv[Tile::kTpt][8], vv[Tile::kTpt][8];
-#pragma unroll
-  for (int u = 0; u < Tile::kTpt; ++u) {
-    const int tok = Tile::kTpt * tg + u;
-    const int s = kBlock * j + tok;
-    if (s < n_valid) {
-      In<T>::load8_f32(K + int64_t(s) * ksN + 8 * fg, kv[u]);
-      In<T>::load8_f32(V + int64_t(s) * vsN + 8 * fg, vv[u]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kv[u][e] = phi(kv[u][e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kv[u][e] = vv[u][e] = 0.f;   // padding contributes nothing
-    }
-  }
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int row = 8 * fg + f;
-    const int col = Tile::kTpt * tg;
-    if constexpr (Tile::kTpt == 4) {
-      typedef float f32x4_t __attribute__((ext_vector_type(4)));
-      f32x4_t a = {kv[0][f], kv[1][f], kv[2][f], kv[3][f]};
-      f32x4_t b = {vv[0][f], vv[1][f], vv[2][f], vv[3][f]};
-      *reinterpret_cast<bf16x4*>(Kt + row * Tile::kStride + col) = __builtin_convertvector(a, bf16x4);
-      *reinterpret_cast<bf16x4*>(Vt + row * Tile::kStride + col) = __builtin_convertvector(b, bf16x4);
-    } else {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      typedef float f32x2_t __attribute__((ext_vector_type(2)));
-      f32x2_t a = {kv[0][f], kv[1][f]};
-      f32x2_t b = {vv[0][f], vv[1][f]};
-      *reinterpret_cast<bf16x2*>(Kt + row * Tile::kStride + col) = __builtin_convertvector(a, bf16x2);
-      *reinterpret_cast<bf16x2*>(Vt + row * Tile::kStride + col) = __builtin_convertvector(b, bf16x2);
-    }
-  }
-}
-
-// grid: x = chunk of `cb` key blocks, y = b * Hkv + g.  Output state index = y * nch + x,
-// so with cb == 1 the output is laid out [B, Hkv, nb, d, d] / [B, Hkv, nb, d].
-template <typename T, int D>
+// grid: x = run of cb key blocks, y = b * Hkv + g.  PER_BLOCK: every block's state goes to
+// Hb (bf16) and z; otherwise the run's sum goes to Hf (fp32) and z at index y * gridDim.x + x.
+template <typename T, int D, bool PER_BLOCK>
 __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, int64_t ksB, int64_t ksH,
                                                        int64_t ksN, const T* __restrict__ v, int64_t vsB,
                                                        int64_t vsH, int64_t vsN, int Hkv, int nb, int n_valid,
-                                                       int cb, float* __restrict__ Hout,
+                                                       int cb, u16* __restrict__ Hb, float* __restrict__ Hf,
                                                        float* __restrict__ zout) {
-  using Tile = KvTile<T, D>;
-  constexpr int kRt = D / 16 / 4;   // row tiles per wavefront
-  constexpr int kCt = D / 16;       // column tiles
-  __shared__ __attribute__((aligned(16))) u16 Kt[D * Tile::kStride];
-  __shared__ __attribute__((aligned(16))) u16 Vt[D * Tile::kStride];
-  const int c = blockIdx.x, bg = blockIdx.y;
-  const int nch = gridDim.x;
+  constexpr int RB = 2 * D;
+  constexpr int kCt = D == 128 ? 4 : 1;          // 32-column tiles of c per wavefront
+  constexpr int kChunks = D / 8;                 // 16-byte chunks per 2D-byte row
+  // phi(K) and V tiles; after a block's products the same 2 x 64 x 2D bytes stage its D x D bf16 state
+  __shared__ __attribute__((aligned(1024))) unsigned char tsm[2 * kBlock * RB];
+  lds_u8* Kt = to_lds(tsm);
+  lds_u8* Vt = Kt + kBlock * RB;
+  const int x = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const T* K = k + int64_t(b) * ksB + int64_t(g) * ksH;
   const T* V = v + int64_t(b) * vsB + int64_t(g) * vsH;
-  const int t = threadIdx.x, w = t / kWave, lane = t % kWave, l16 = lane % 16, lg = lane / 16;
+  const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
+  const int rt = D == 128 ? w : w % 2;           // r rows 32 rt .. 32 rt + 31
+  const int ct0 = D == 128 ? 0 : w / 2;          // first c tile
+  const bool z_owner = D == 128 || w < 2;
 
-  f32x4 acc[kRt][kCt];
+  int aoff, boff[kCt];
+  aoff = tr_operand_off<RB>(32 * rt, lane);
 #pragma unroll
-  for (int a = 0; a < kRt; ++a)
+  for (int ct = 0; ct < kCt; ++ct) boff[ct] = tr_operand_off<RB>(32 * (ct0 + ct), lane);
+  bf16x8 ones;
 #pragma unroll
-    for (int e = 0; e < kCt; ++e) acc[a][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f;
+  for (int m = 0; m < 8; ++m) ones[m] = (__bf16)1.0f;
 
-  const int j0 = c * cb, j1 = min(nb, j0 + cb);
-  for (int j = j0; j < j1; ++j) {
-    if (kBlock * j >= n_valid) break;
-    __syncthreads();
-    load_kv_transposed<T, D>(K, ksN, V, vsN, j, n_valid, Kt, Vt);
-    __syncthreads();
-    if (t < D) {   // z: sum of the rounded phi(K) of this block, fixed order
-      const u16* row = Kt + t * Tile::kStride;
-#pragma unroll
-      for (int s8 = 0; s8 < kBlock; s8 += 8) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + s8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zacc += float(x[e]);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < kBlock / 32; ++ks) {
-      bf16x8 bv[kCt];
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct)
-        bv[ct] = *reinterpret_cast<const bf16x8*>(Vt + (16 * ct + l16) * Tile::kStride + 32 * ks + 8 * lg);
-#pragma unroll
-      for (int a = 0; a < kRt; ++a) {
-        const int rt = kRt * w + a;
-        const bf16x8 av =
-            *reinterpret_cast<const bf16x8*>(Kt + (16 * rt + l16) * Tile::kStride + 32 * ks + 8 * lg);
-#pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) acc[a][ct] = mfma16(av, bv[ct], acc[a][ct]);
-      }
-    }
-  }
-  // store transposed, [c][r]: lane holds r = 16 rt + 4 lg + e (e < 4) for c = 16 ct + l16
-  const int64_t sidx = int64_t(bg) * nch + c;
-  float* Hs = Hout + sidx * D * D;
-#pragma unroll
-  for (int a = 0; a < kRt; ++a) {
-    const int rt = kRt * w + a;
+  f32x16 acc[kCt], zacc;
+  auto clear = [&]() {
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
-      *reinterpret_cast<f32x4*>(Hs + (16 * ct + l16) * D + 16 * rt + 4 * lg) = acc[a][ct];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) zacc[e] = 0.f;
+  };
+  // lane holds D[r = 32 rt + 8 q + 4 (lane / 32) + e % 4][c = 32 ct + lane % 32] in acc[ct][4 q + e % 4]
+  // bf16 states go through LDS ([c][r], chunk c8 of row c at c8 ^ (c % kChunks)) so that every
+  // wavefront store writes 1 KB of consecutive bytes; fp32 run sums are stored directly.
+  auto store = [&](int64_t sidx) {
+    const int c_l = lane % 32, r_l = 32 * rt + 4 * (lane / 32);
+    if constexpr (PER_BLOCK) {
+      __syncthreads();                  // every wavefront has read this block's operands
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) {
+        const int c = 32 * (ct0 + ct) + c_l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x4 = {acc[ct][4 * q], acc[ct][4 * q + 1], acc[ct][4 * q + 2], acc[ct][4 * q + 3]};
+          const int ch = (r_l + 8 * q) / 8;
+          lds_u8* pos = Kt + c * RB + 16 * (ch ^ (c % kChunks)) + 8 * (lane / 32);
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(pos) = __builtin_convertvector(x4, bf16x4);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < D * RB / (256 * 16); ++p) {
+        const int e = t + 256 * p;
+        const int row = e / kChunks, ch = e % kChunks;
+        const bf16x8 x = lds_load16(Kt + row * RB + 16 * (ch ^ (row % kChunks)));
+        *reinterpret_cast<bf16x8*>(Hb + sidx * D * D + row * D + 8 * ch) = x;
+      }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) {
+        const int c = 32 * (ct0 + ct) + c_l;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x4 = {acc[ct][4 * q], acc[ct][4 * q + 1], acc[ct][4 * q + 2], acc[ct][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(Hf + sidx * D * D + int64_t(c) * D + r_l + 8 * q) = x4;
+        }
+      }
+    }
+    if (z_owner && c_l == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(zout + sidx * D + r_l + 8 * q) =
+            f32x4{zacc[4 * q], zacc[4 * q + 1], zacc[4 * q + 2], zacc[4 * q + 3]};
+    }
+  };
+
+  const int j0 = x * cb;
+  const int j1 = min(min(nb, j0 + cb), (n_valid + kBlock - 1) / kBlock);   // blocks with valid rows
+  clear();
+  KvPiece<T, D> pc;
+  if (j0 < j1) pc.load(K, ksN, V, vsN, j0, n_valid);
+  for (int j = j0; j < j1; ++j) {
+    __syncthreads();                    // the previous block's operands (and staged state) have been read
+    pc.store(Kt, Vt);
+    __syncthreads();
+    if (j + 1 < j1) pc.load(K, ksN, V, vsN, j + 1, n_valid);
+#pragma unroll
+    for (int ks = 0; ks < kBlock / 16; ++ks) {
+      lds_u8* kk0 = Kt + 16 * ks * RB;
+      lds_u8* vk0 = Vt + 16 * ks * RB;
+      const bf16x8 a = tr_operand(kk0, aoff, 4 * RB);
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] = mfma32(a, tr_operand(vk0, boff[ct], 4 * RB), acc[ct]);
+      if (z_owner) zacc = mfma32(a, ones, zacc);
+    }
+    if constexpr (PER_BLOCK) {
+      store(int64_t(bg) * nb + j);
+      clear();
+    }
   }
-  if (t < D) zout[sidx * D + t] = zacc;
+  if constexpr (PER_BLOCK) {
+    // blocks with no valid rows (only possible past n_valid): zero states
+    for (int j = max(j0, j1); j < min(nb, j0 + cb); ++j) store(int64_t(bg) * nb + j);
+  } else {
+    store(int64_t(bg) * gridDim.x + x);
+  }
 }
 
 // out[bg] = sum over p of in[bg * parts + p] (fixed order), for states of `len` floats.
@@ -155,18 +231,23 @@ __global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict
 }
 
 template <typename T>
-static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int cb, int nch, float* H, float* z,
-                      hipStream_t st) {
+static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int cb, int nch, u16* Hb, float* Hf,
+                      float* z, hipStream_t st) {
   const int nb = k->N / kBlock;
   dim3 grid(nch, k->B * k->H);
   const T* kp = static_cast<const T*>(k->ptr);
   const T* vp = static_cast<const T*>(v->ptr);
-  if (k->d == 128)
-    kv_state_kernel<T, 128><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, nb,
-                                                  n_valid, cb, H, z);
-  else
-    kv_state_kernel<T, 64><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, nb,
-                                                 n_valid, cb, H, z);
+#define SLA_KV_LAUNCH(DD, PB)                                                                                    \
+  kv_state_kernel<T, DD, PB><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, nb, \
+                                                   n_valid, cb, Hb, Hf, z)
+  if (k->d == 128) {
+    if (Hb != nullptr) SLA_KV_LAUNCH(128, true);
+    else SLA_KV_LAUNCH(128, false);
+  } else {
+    if (Hb != nullptr) SLA_KV_LAUNCH(64, true);
+    else SLA_KV_LAUNCH(64, false);
+  }
+#undef SLA_KV_LAUNCH
 }
 
 static void launch_sum(const float* in, int parts, int64_t len, int bgs, float* out, hipStream_t st) {
@@ -176,7 +257,7 @@ static void launch_sum(const float* in, int parts, int64_t len, int bgs, float* 
 
 }  // namespace sla
 
-extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid, float* H,
+extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid, void* H,
                                            float* z, float* H_all, float* z_all, void* workspace,
                                            size_t workspace_bytes, void* stream) {
   using namespace sla;
@@ -187,29 +268,32 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
   if ((st = check_valid_len(n_valid, k->N)) != SLA_OK) return st;
   if (H == nullptr && H_all == nullptr) return SLA_ERR_NULL;
   if ((H == nullptr) != (z == nullptr) || (H_all == nullptr) != (z_all == nullptr)) return SLA_ERR_NULL;
+  if ((H != nullptr && (!aligned16(H) || !aligned16(z))) || (H_all != nullptr && (!aligned16(H_all) || !aligned16(z_all))))
+    return SLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = k->N / kBlock;
   const int d = k->d;
   const int bgs = k->B * k->H;
   const bool bf = k->dtype == SLA_BF16;
-  if (H != nullptr) {
-    if (bf) launch_kv<bf16raw>(k, v, n_valid, 1, nb, H, z, s);
-    else launch_kv<float>(k, v, n_valid, 1, nb, H, z, s);
-    if (H_all != nullptr) {
-      launch_sum(H, nb, int64_t(d) * d, bgs, H_all, s);
-      launch_sum(z, nb, d, bgs, z_all, s);
-    }
-    return launch_status();
+  if (H_all != nullptr) {
+    // fp32 sums over runs of key blocks into the workspace, then over the runs
+    const size_t need = sla_kv_reduce_workspace_bytes(k->B, k->H, k->N, d, H != nullptr, 1);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
+    const int cb = kKvSumRun;
+    const int nch = (nb + cb - 1) / cb;
+    float* Hp = static_cast<float*>(workspace);
+    float* zp = Hp + int64_t(bgs) * nch * d * d;
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, nullptr, Hp, zp, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, nullptr, Hp, zp, s);
+    launch_sum(Hp, nch, int64_t(d) * d, bgs, H_all, s);
+    launch_sum(zp, nch, d, bgs, z_all, s);
   }
-  const size_t need = sla_kv_reduce_workspace_bytes(k->B, k->H, k->N, d, 0, 1);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
-  const int cb = 32;
-  const int nch = (nb + cb - 1) / cb;
-  float* Hp = static_cast<float*>(workspace);
-  float* zp = Hp + int64_t(bgs) * nch * d * d;
-  if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, Hp, zp, s);
-  else launch_kv<float>(k, v, n_valid, cb, nch, Hp, zp, s);
-  launch_sum(Hp, nch, int64_t(d) * d, bgs, H_all, s);
-  launch_sum(zp, nch, d, bgs, z_all, s);
+  if (H != nullptr) {
+    // runs of a few blocks per workgroup (one block of prefetch), at least ~2048 workgroups
+    const int cb = std::max(1, std::min(4, nb * bgs / 2048));
+    const int nch = (nb + cb - 1) / cb;
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, static_cast<u16*>(H), nullptr, z, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, static_cast<u16*>(H), nullptr, z, s);
+  }
   return launch_status();
 }

@@ -7,18 +7,20 @@
 // at O(N d^2)).
 //
 // Design: gathering each row's states reads n_m whole d x d states per query block (about
-// 20 GB of cache traffic for the 12-head 32K-token layer), so the sums are instead one
-// product per head, S = M H, of the 0/1 marginal mask M [nqb x nkb] with the states
-// H [nkb x d*d] (and z), on the bf16 matrix cores: H is read about once.  The mask comes in
-// as one bit per (row, key block), as the classification writes it; each workgroup stages its
-// rows' words in LDS and every lane expands its 8 mask bits into the 8 bf16 ones/zeros of its
-// A operand.  B tiles
-// (32 key blocks x 128 state columns) are converted to bf16 and staged row-major in LDS with
-// 16-byte stores, and read back k-packed with the transposing LDS read (rows padded to 288 bytes,
-// so every 16-lane group's four rows x 32 bytes hit all banks once); double buffered behind a
-// register prefetch.  Each wavefront owns 64 rows x 128 columns,
-// so one mask expansion feeds 8 matrix-core products.  Sums accumulate in fp32 in a fixed order
-// (deterministic); S is written once in bf16, the precision the epilogue consumes.
+// 10 GB of cache traffic for the 12-head 32K-token layer), so the sums are instead one
+// product per head, S = M H, of the 0/1 marginal mask M [nqb x nkb] with the bf16 states
+// H [nkb x d*d] (and z), on the bf16 matrix cores, computed transposed (S^T = H^T M^T) so that a
+// lane's accumulators hold 4 consecutive state columns of one row.
+// A workgroup owns 256 map rows x 128 state columns; each of its 4 wavefronts takes 64 rows and
+// all 128 columns, so each expanded mask operand feeds 4 products.  H tiles (32 key
+// blocks x 128 columns, 8 KB) go straight from global memory to LDS in a 4-stage ring, in the
+// layout of the transposing LDS read that feeds the A operand; the mask comes in as one bit per
+// (row, key block), staged in LDS 512 key blocks at a time, and each lane expands 8 bits into
+// its B operand.  A wavefront skips a step whose 64 x 32 mask block is all zero.  Sums
+// accumulate in fp32 in a fixed order (deterministic); S is written once in bf16, the
+// precision the epilogue consumes, re-staged through LDS for 1 KB-contiguous stores.  The z columns (u) take the same
+// path from fp32 z converted to bf16 operands.  Workgroups are numbered so that the row tiles of
+// one column slice run on one XCD and share its L2.
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -26,10 +28,12 @@ namespace sla {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMgRows = 256;     // map rows per workgroup: 4 wavefronts x 64
-constexpr int kMgCols = 128;     // state columns per workgroup
-constexpr int kMgChunkW = 16;    // mask words per row held at once (512 key blocks)
-constexpr int kMgBs = 128 + 16;  // LDS row stride of the row-major B tile (bf16): 288 bytes
+constexpr int kMgRows = 256;    // map rows per workgroup
+constexpr int kMgCols = 128;    // state columns per workgroup (256-byte tile rows)
+constexpr int kMgK = 32;        // key blocks per step (one mask word)
+constexpr int kMgStages = 4;    // H tiles in flight
+constexpr int kMgWords = 16;    // mask words per row held in LDS (512 key blocks)
+constexpr int kMgTileB = kMgK * kMgCols * 2;
 
 // 8 mask bits -> 8 bf16 values 1.0 / 0.0 (bit m -> element m).
 __device__ __forceinline__ bf16x8 expand_bits(uint32_t byte) {
@@ -42,131 +46,210 @@ __device__ __forceinline__ bf16x8 expand_bits(uint32_t byte) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// grid: x = tile of 256 map rows, y = 128-column slice (state columns, then z columns),
-// z = b * Hs + s.
+// 1-D grid of B * Hs * n_slices * n_row_tiles workgroups; slices: D * D / 128 state slices, then
+// ceil(D / 128) z slices.
 template <int D>
-__global__ __launch_bounds__(256) void marginal_gemm_kernel(const float* __restrict__ H, const float* __restrict__ z,
+__global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restrict__ H, const float* __restrict__ z,
                                                             int Hq, int Hkv, int Hs, int nqb, int nkb, int group_map,
-                                                            const uint32_t* __restrict__ bits,
-                                                            u16* __restrict__ S, float* __restrict__ u) {
-  __shared__ uint32_t mask[kMgRows][kMgChunkW + 1];
-  __shared__ __attribute__((aligned(16))) u16 Bt[2][32 * kMgBs];
+                                                            const uint32_t* __restrict__ bits, u16* __restrict__ S,
+                                                            float* __restrict__ u, int n_row_tiles, int n_slices) {
+  __shared__ __attribute__((aligned(1024))) unsigned char bsm[kMgStages][kMgTileB];
+  __shared__ uint32_t mask[kMgRows][kMgWords + 1];
 
-  const int it = blockIdx.x, slice = blockIdx.y, bs = blockIdx.z;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int it = logical % n_row_tiles;
+  const int rest = logical / n_row_tiles;
+  const int slice = rest % n_slices, bs = rest / n_slices;
   const int b = bs / Hs, s = bs % Hs;
   const int g = group_map ? s : s / (Hq / Hkv);
   constexpr int kStateSlices = D * D / kMgCols;
   const bool is_z = slice >= kStateSlices;
-  const int width = is_z ? D : D * D;
   const int c0 = is_z ? (slice - kStateSlices) * kMgCols : slice * kMgCols;
-  const float* src = (is_z ? z + (int64_t(b) * Hkv + g) * nkb * D : H + (int64_t(b) * Hkv + g) * nkb * D * D) + c0;
-  const int64_t row0 = int64_t(bs) * nqb + int64_t(it) * kMgRows;
-  const int t = threadIdx.x, w = t / kWave, lane = t % kWave, l16 = lane % 16, lg = lane / 16;
-
+  const int64_t head = int64_t(b) * Hkv + g;
+  const int t = threadIdx.x, lane = t % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform (feeds M0 and SGPR bases)
+  const int row0 = it * kMgRows;
   const int nw = (nkb + 31) / 32;
-  const bool my_row = it * kMgRows + t < nqb;     // this thread stages the mask words of row0 + t
-  const uint32_t* my_bits = bits + (row0 + t) * nw;
+  const int nsteps = nw;
 
-  constexpr int kCt = kMgCols / 16;
-  f32x4 acc[4][kCt];
+  // ---- H tile staging: step ks holds key blocks 32 ks .. 32 ks + 31 (rows past nkb repeat row
+  // nkb - 1; their mask bits are zero), columns c0 .. c0 + 127
+  const u16* hsrc = H + head * nkb * D * D + c0;
+  const int lrow = lane / 16, lchunk = (lane % 16) ^ (2 * lrow);   // trs layout: row % 4 == lrow
+  auto issue = [&](int ks) {
+    lds_u8* dst = to_lds(bsm[ks % kMgStages]);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < kCt; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // B-tile load mapping: rows (key blocks) t / 16 and t / 16 + 16, columns cc .. cc + 7
-  const int jr = t / 16, cc = 8 * (t % 16);
-  const int nks_total = (nkb + 31) / 32;
-  f32x4 pre[2][2];
-  const bool col_ok = c0 + cc < width;   // z of d = 64 fills half a slice
-  auto load_b = [&](int ksg) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int j = 32 * ksg + jr + 16 * q;
-      const float* rp = src + int64_t(j) * width + cc;
-      const bool ok = j < nkb && col_ok;
-      pre[q][0] = ok ? *reinterpret_cast<const f32x4*>(rp) : f32x4{0.f, 0.f, 0.f, 0.f};
-      pre[q][1] = ok ? *reinterpret_cast<const f32x4*>(rp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 2; ++n) {
+      const int qi = 2 * w + n;                    // 1 KB step: rows 4 qi .. 4 qi + 3
+      const int j = min(kMgK * ks + 4 * qi + lrow, nkb - 1);
+      const uint32_t voff = uint32_t(j) * uint32_t(D * D * 2) + 16u * uint32_t(lchunk);
+      load_lds16_sbase(hsrc, voff, dst + qi * 1024);
     }
   };
-  // transposing-read address of this lane: row 8 (lane / 16) + (lane % 16) / 4, column 4 (lane % 4)
-  const int tr_off = (8 * lg + (lane % 16) / 4) * kMgBs + 4 * (lane % 4);
-  load_b(0);
-  int buf = 0;
-  for (int jc = 0; jc < nkb; jc += 32 * kMgChunkW) {
-    __syncthreads();   // the previous chunk's masks are no longer read
+  // z slice: fp32 z rows converted to bf16 through registers (columns past D are zero)
+  auto fill_z = [&](int ks) {
+    lds_u8* dst = to_lds(bsm[ks % kMgStages]);
 #pragma unroll
-    for (int q = 0; q < kMgChunkW; ++q) {
-      const int wq = jc / 32 + q;
-      mask[t][q] = (my_row && wq < nw) ? my_bits[wq] : 0u;
+    for (int n = 0; n < 2; ++n) {
+      const int e = t + 256 * n;                   // 512 chunks of 8 columns
+      const int r = e / 16, c = e % 16;
+      const int j = kMgK * ks + r, col = c0 + 8 * c;
+      f32x8 x;
+      if (j < nkb && col < D) {
+        const float* zp = z + (head * nkb + j) * D + col;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(zp), hi = *reinterpret_cast<const f32x4*>(zp + 4);
+        x = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) x[m] = 0.f;
+      }
+      lds_store16(dst + trs_pos<256>(r, c), cvt8(x));
     }
-    const int nks = min(kMgChunkW, (nkb - jc + 31) / 32);
-    for (int ks = 0; ks < nks; ++ks) {
-      const int ksg = jc / 32 + ks;
-      u16* bt = Bt[buf];
+  };
+
+  // wavefront w: rows 64 w .. 64 w + 63 (two 32-row tiles) x all 128 columns (four 32-column tiles);
+  // each expanded mask operand feeds 4 products
+  f32x16 acc[2][4];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f32x8 x = {pre[q][0][0], pre[q][0][1], pre[q][0][2], pre[q][0][3],
-                         pre[q][1][0], pre[q][1][1], pre[q][1][2], pre[q][1][3]};
-        *reinterpret_cast<bf16x8*>(bt + (jr + 16 * q) * kMgBs + cc) = cvt8(x);
-      }
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rr][ct][e] = 0.f;
+  int aoff[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) aoff[ct] = tr_operand_off<256>(32 * ct, lane);
+  const bool my_row = row0 + t < nqb;
+  const uint32_t* my_bits = bits + (int64_t(bs) * nqb + min(row0 + t, nqb - 1)) * nw;
+
+  auto load_mask = [&](int wc) {                   // words wc .. wc + 15 of this thread's row
+    uint32_t wv[kMgWords];
+#pragma unroll
+    for (int q = 0; q < kMgWords; ++q) wv[q] = my_bits[min(wc + q, nw - 1)];   // all loads in flight at once
+#pragma unroll
+    for (int q = 0; q < kMgWords; ++q) mask[t][q] = (my_row && wc + q < nw) ? wv[q] : 0u;
+  };
+
+  if (!is_z) {
+    for (int ks = 0; ks < min(kMgStages - 1, nsteps); ++ks) issue(ks);
+    load_mask(0);                                  // overlaps the first copies' latency
+  }
+  for (int ks = 0; ks < nsteps; ++ks) {
+    if (is_z) {
       __syncthreads();
-      if (ksg + 1 < nks_total) load_b(ksg + 1);
-      // B[k = 8 lg + m][col 16 ct + l16]: rows 8 lg .. 8 lg + 3 and 8 lg + 4 .. 8 lg + 7
-      lds_u8* bl = to_lds(bt);
-      bf16x8 bop[kCt];
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) {
-        const bf16x4 lo = lds_read_tr4(bl + 2 * (tr_off + 16 * ct));
-        const bf16x4 hi = lds_read_tr4(bl + 2 * (tr_off + 4 * kMgBs + 16 * ct));
-        bop[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (ks % kMgWords == 0) load_mask(ks);
+      fill_z(ks);
+      __syncthreads();
+    } else {
+      // this wavefront's copies of step ks are done once at most those of the later steps in flight are
+      const int later = min(kMgStages - 2, nsteps - 1 - ks);
+      if (later >= 2) SLA_WAIT_VMCNT(4);
+      else if (later == 1) SLA_WAIT_VMCNT(2);
+      else SLA_WAIT_VMCNT(0);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                               // step ks landed for every wavefront; step ks - 1 is consumed
+      if (ks % kMgWords == 0 && ks > 0) {          // next 512 key blocks of mask words
+        load_mask(ks);
+        SLA_WAIT_LGKM0();
+        SLA_BARRIER();
       }
+      if (ks + kMgStages - 1 < nsteps) issue(ks + kMgStages - 1);
+    }
+    lds_u8* tile = to_lds(bsm[ks % kMgStages]);
+    const int wq = ks % kMgWords;
+    const uint32_t w0 = mask[64 * w + lane % 32][wq];
+    const uint32_t w1 = mask[64 * w + 32 + lane % 32][wq];
+    if (__ballot((w0 | w1) != 0u) == 0) continue;  // no marginal block of this wavefront's rows here
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const uint32_t word = mask[64 * w + 16 * rt + l16][ks];
-        const bf16x8 aop = expand_bits((word >> (8 * lg)) & 0xffu);
+    for (int h = 0; h < 2; ++h) {                  // 16 key blocks 16 h .. 16 h + 15
+      bf16x8 a[4];
 #pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) acc[rt][ct] = mfma16(aop, bop[ct], acc[rt][ct]);
+      for (int ct = 0; ct < 4; ++ct) a[ct] = tr_operand(tile + 16 * h * 256, aoff[ct], 4 * 256);
+      const int sh = 8 * (2 * h + lane / 32);
+      const bf16x8 b0 = expand_bits((w0 >> sh) & 0xffu);
+      const bf16x8 b1 = expand_bits((w1 >> sh) & 0xffu);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        acc[0][ct] = mfma32(a[ct], b0, acc[0][ct]);
+        acc[1][ct] = mfma32(a[ct], b1, acc[1][ct]);
       }
-      buf ^= 1;
     }
   }
 
-  // lane holds rows 64 w + 16 rt + 4 lg + e, column c0 + 16 ct + l16
+  // lane holds S[row0 + 64 w + 32 rr + lane % 32][c0 + 32 ct + 8 q + 4 (lane / 32) + 0..3] in acc[rr][ct][4 q ..]
+  if (is_z) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = it * kMgRows + 64 * w + 16 * rt + 4 * lg + e;
+    for (int rr = 0; rr < 2; ++rr) {
+      const int i = row0 + 64 * w + 32 * rr + lane % 32;
       if (i >= nqb) continue;
       const int64_t r = int64_t(bs) * nqb + i;
 #pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) {
-        const int col = c0 + 16 * ct + l16;
-        if (is_z) {
-          if (col < D) u[r * D + col] = acc[rt][ct][e];
-        } else {
-          const __bf16 v = (__bf16)acc[rt][ct][e];
-          S[r * D * D + col] = __builtin_bit_cast(u16, v);
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c0 + 32 * ct + 8 * q + 4 * (lane / 32);
+          if (col < D)
+            *reinterpret_cast<f32x4*>(u + r * D + col) =
+                f32x4{acc[rr][ct][4 * q], acc[rr][ct][4 * q + 1], acc[rr][ct][4 * q + 2], acc[rr][ct][4 * q + 3]};
         }
+    }
+    return;
+  }
+  // S in bf16 through LDS (128 rows x 256 bytes at a time in the H ring, chunk c16 of row r at
+  // c16 ^ (r % 16)), so that every wavefront store writes 1 KB of consecutive bytes
+  lds_u8* stg = to_lds(bsm[0]);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    if (w / 2 == half) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = 64 * (w % 2) + 32 * rr + lane % 32;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 x4 = {acc[rr][ct][4 * q], acc[rr][ct][4 * q + 1], acc[rr][ct][4 * q + 2], acc[rr][ct][4 * q + 3]};
+            lds_u8* pos = stg + row * 256 + 16 * ((4 * ct + q) ^ (row % 16)) + 8 * (lane / 32);
+            *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(pos) = __builtin_convertvector(x4, bf16x4);
+          }
       }
     }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int e = t + 256 * p;
+      const int row = e / 16, ch = e % 16;
+      const int i = row0 + 128 * half + row;
+      if (i < nqb) {
+        const bf16x8 x = lds_load16(stg + row * 256 + 16 * (ch ^ (row % 16)));
+        *reinterpret_cast<bf16x8*>(S + (int64_t(bs) * nqb + i) * D * D + c0 + 8 * ch) = x;
+      }
+    }
+  }
 }
 
-sla_status launch_marginal_states(const float* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
+sla_status launch_marginal_states(const u16* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
                                   int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st) {
   const int Hs = group_map ? Hkv : Hq;
-  dim3 grid((nqb + kMgRows - 1) / kMgRows, d * d / kMgCols + (d + kMgCols - 1) / kMgCols, B * Hs);
+  const int n_row_tiles = (nqb + kMgRows - 1) / kMgRows;
+  const int n_slices = d * d / kMgCols + (d + kMgCols - 1) / kMgCols;
+  const int64_t n = int64_t(B) * Hs * n_slices * n_row_tiles;
+  if (n > (int64_t(1) << 31) - 1) return SLA_ERR_UNSUPPORTED;
   if (d == 128)
-    marginal_gemm_kernel<128><<<grid, 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u);
+    marginal_gemm_kernel<128><<<dim3(uint32_t(n)), 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u,
+                                                                 n_row_tiles, n_slices);
   else
-    marginal_gemm_kernel<64><<<grid, 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u);
+    marginal_gemm_kernel<64><<<dim3(uint32_t(n)), 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u,
+                                                                n_row_tiles, n_slices);
   return launch_status();
 }
 
 }  // namespace sla
 
-extern "C" sla_status sla_marginal_states(const float* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
+extern "C" sla_status sla_marginal_states(const void* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
                                           int32_t nqb, int32_t nkb, int32_t d, int32_t group_map,
                                           const uint32_t* marg_bits, void* S, float* u, void* stream) {
   using namespace sla;
@@ -175,6 +258,6 @@ extern "C" sla_status sla_marginal_states(const float* H, const float* z, int32_
   if (nkb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return SLA_ERR_UNSUPPORTED;
   if (!aligned16(H) || !aligned16(z) || !aligned16(S) || !aligned16(u)) return SLA_ERR_ALIGN;
-  return launch_marginal_states(H, z, B, Hq, Hkv, nqb, nkb, d, group_map ? 1 : 0, marg_bits, static_cast<u16*>(S), u,
-                                static_cast<hipStream_t>(stream));
+  return launch_marginal_states(static_cast<const u16*>(H), z, B, Hq, Hkv, nqb, nkb, d, group_map ? 1 : 0, marg_bits,
+                                static_cast<u16*>(S), u, static_cast<hipStream_t>(stream));
 }

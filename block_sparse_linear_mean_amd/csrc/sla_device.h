@@ -57,6 +57,28 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(lds_u8* addr) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Row-major LDS tile of 16-bit elements with RB-byte rows, laid out for the transposing read:
+// 16-byte chunk c of row r sits at r * RB + 16 * (c ^ 2 (r % 4)).  A 16-lane group of the
+// transposing read touches 4 consecutive rows in one 32-byte column window; the XOR moves the
+// four rows' windows onto different banks.
+template <int RB>
+__device__ __forceinline__ int trs_pos(int r, int c) { return r * RB + 16 * (c ^ (2 * (r % 4))); }
+
+// Per-lane byte offset of a 32x32x16 matrix-core operand read with two transposing reads from a
+// trs-layout tile T[k][m]: lane l receives T[k0 + 8 (l / 32) + 0..7][m0 + l % 32], which is the A
+// operand of A[m][k] = T[k][m] and the B operand of B[k][n] = T[k][n].  Read it as
+// tr_operand(tile + k0 * RB, off, 4 * RB) for any k0 that is a multiple of 4.
+template <int RB>
+__device__ __forceinline__ int tr_operand_off(int m0, int lane) {
+  const int sg = (lane / 16) % 2, kk = lane % 16, lg = lane / 32;
+  return trs_pos<RB>(8 * lg + kk / 4, m0 / 8 + 2 * sg + (kk % 4) / 2) + 8 * (kk % 2);
+}
+__device__ __forceinline__ bf16x8 tr_operand(lds_u8* tile_k0, int off, int hi_step) {
+  const bf16x4 lo = lds_read_tr4(tile_k0 + off);
+  const bf16x4 hi = lds_read_tr4(tile_k0 + off + hi_step);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds + 16 l
 // (lds must be the same for the whole wavefront).  Issued from a self-contained asm block
 // (M0 set inside it, no output registers), so the copy's completion is tracked only by the
@@ -95,6 +117,15 @@ __device__ __forceinline__ float xor32_max(float x) {
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs of the chip, each with its own L2.  This maps a
+// hardware workgroup index of a 1-D grid of n to a logical index such that the workgroups one XCD
+// receives form one contiguous range of the logical order (in dispatch order within the range).
+__device__ __forceinline__ int xcd_logical(int bid, int n) {
+  const int xcd = bid % 8, slot = bid / 8;
+  const int q = n / 8, r = n % 8;
+  return xcd * q + min(xcd, r) + slot;
 }
 
 // s_waitcnt encodings (gfx9 family): wait until at most N vector-memory operations of this

@@ -8,6 +8,9 @@
 
 namespace sla {
 
+// key blocks per fp32 partial state when summing the linear states over all keys
+constexpr int kKvSumRun = 32;
+
 inline int elem_bytes(int32_t dtype) { return dtype == SLA_BF16 ? 2 : 4; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

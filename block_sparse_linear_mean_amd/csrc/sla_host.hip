@@ -66,9 +66,10 @@ size_t sla_block_map_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t
 
 size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, int32_t want_blocks,
                                      int32_t want_all) {
-  if (want_blocks || !want_all || B < 1 || Hkv < 1 || N < SLA_BLOCK) return 0;
+  (void)want_blocks;   // per-block states need no workspace; the sum over all keys does
+  if (!want_all || B < 1 || Hkv < 1 || N < SLA_BLOCK) return 0;
   const int64_t nb = N / SLA_BLOCK;
-  const int64_t chunks = (nb + 31) / 32;     // 32 key blocks (2048 tokens) per partial state
+  const int64_t chunks = (nb + sla::kKvSumRun - 1) / sla::kKvSumRun;   // fp32 partial state per run
   return size_t(int64_t(B) * Hkv * chunks * (int64_t(d) * d + d) * 4);
 }
 

@@ -165,24 +165,26 @@ sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb
                          int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
                          int32_t* row_counts, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sla_linear_kv_reduce needs (non-zero only when H is NULL and H_all is not). */
+/* Workspace bytes sla_linear_kv_reduce needs (non-zero only when the sums over all keys are wanted). */
 size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, int32_t want_blocks,
                                      int32_t want_all);
 
 /*
  * Linear-attention key states (SLA analysis page: marginal pairs get linear attention,
  * O(N d^2); phi = elu + 1).  Per KV head and key block j, over the valid rows s:
- *   H[b,g,j,c,r] = sum_s phi(K[s,r]) * V[s,c]   (fp32, [B, Hkv, nb, d, d]; nullable)
- *     i.e. each d x d state is stored transposed, V-feature major: (phi(K_j)^T V_j)^T.
+ *   H[b,g,j,c,r] = sum_s phi(K[s,r]) * V[s,c]   (bf16 bits, [B, Hkv, nb, d, d]; nullable)
+ *     i.e. each d x d state is stored transposed, V-feature major: (phi(K_j)^T V_j)^T,
+ *     summed in fp32 and rounded once to bf16.
  *   z[b,g,j,r]   = sum_s phi(K[s,r])            (fp32, [B, Hkv, nb, d];     nullable with H)
  *   H_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d, d], same [c][r] layout; nullable)
  *   z_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d];        nullable with H_all)
  * phi(K) is rounded to bf16 for the matrix-core contraction (fp32 accumulation); z sums
- * the same rounded values.  At least one of H, H_all must be non-NULL.  When H is NULL
- * and H_all is not, a workspace of sla_kv_reduce_workspace_bytes(..., 0, 1) is needed.
+ * the same rounded values.  At least one of H, H_all must be non-NULL; outputs are 16-byte
+ * aligned.  H_all needs a workspace of sla_kv_reduce_workspace_bytes(..., 1) bytes (fp32
+ * partial sums over runs of 32 key blocks, then summed in a fixed order).
  */
 sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
-                                float* H, float* z, float* H_all, float* z_all,
+                                void* H, float* z, float* H_all, float* z_all,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -192,12 +194,13 @@ sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_
  *   u[r] = sum over marginal blocks j of z[b,g,j]  (fp32, [rows, d])
  * rows = B * Hs * nqb with Hs = Hkv if group_map else Hq; the KV head of map head s is
  * s if group_map else s / (Hq / Hkv).
+ * H is the bf16 output of sla_linear_kv_reduce, z its fp32 z.
  * Computed as a 0/1 mask matrix product on the matrix cores: the bit masks expand to 0/1
- * operands, H and z are rounded to bf16 operands, sums accumulate in fp32 (deterministic) and S
+ * operands, z is rounded to bf16 operands, sums accumulate in fp32 (deterministic) and S
  * is rounded once to bf16, the operand precision of the attention epilogue that reads it.
  * workspace: none.  sla_attn_fwd performs this step itself in SLA_LIN_MARGINAL mode.
  */
-sla_status sla_marginal_states(const float* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
+sla_status sla_marginal_states(const void* H, const float* z, int32_t B, int32_t Hq, int32_t Hkv,
                                int32_t nqb, int32_t nkb, int32_t d, int32_t group_map,
                                const uint32_t* marg_bits, void* S, float* u, void* stream);
 
@@ -215,9 +218,10 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  *   O_sparse[t] = softmax over allowed keys of (scale * q_t . k_s) applied to v_s, or 0
  *     when no key is allowed.  Allowed: s < n_valid in a listed block; causal != 0 adds
  *     s <= t and (flag bit 0 of the block, or t - s < window_tokens).
- *   lin_mode SLA_LIN_MARGINAL (needs marg_bits, H, z):
+ *   lin_mode SLA_LIN_MARGINAL (needs marg_bits, H (bf16) and z from sla_linear_kv_reduce):
  *     O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the sums of H_j and
- *     z_j over row r's marginal blocks; 0 when the row has none.
+ *     z_j over row r's marginal blocks (computed as by sla_marginal_states); 0 when the
+ *     row has none.
  *   lin_mode SLA_LIN_ROW_STATES: as SLA_LIN_MARGINAL, but H and z already hold the per-row
  *     sums S (bf16 bits, [rows, d, d]) and u (fp32, [rows, d]) written by sla_marginal_states
  *     for this map; marg_bits is not read and no workspace is needed.
@@ -234,7 +238,7 @@ sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         float scale, int32_t causal, int32_t window_tokens, int32_t group_map,
                         const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
                         const uint32_t* marg_bits,
-                        int32_t lin_mode, const float* H, const float* z,
+                        int32_t lin_mode, const void* H, const float* z,
                         const float* H_all, const float* z_all, const float* w_gate,
                         void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                         void* stream);

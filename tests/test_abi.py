@@ -69,7 +69,8 @@ def test_capacities_and_workspaces(L):
     assert sla.sla_block_map_workspace_bytes(1, 1, nb, nb, 16, 1, 512) >= nb * 25 * 5
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 * 2 + 128 * 4)
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_NONE) == 0
-    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 0
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 0) == 0
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 12 * 16 * (128 * 128 + 128) * 4
     assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 16 * (128 * 128 + 128) * 4
 
 
