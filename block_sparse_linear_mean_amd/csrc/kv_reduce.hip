@@ -136,11 +136,8 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   f32x16 acc[kCt], zacc;
   auto clear = [&]() {
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) zacc[e] = 0.f;
+    for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x16{};
+    zacc = f32x16{};
   };
   // lane holds D[r = 32 rt + 8 q + 4 (lane / 32) + e % 4][c = 32 ct + lane % 32] in acc[ct][4 q + e % 4]
   // bf16 states go through LDS ([c][r], chunk c8 of row c at c8 ^ (c % kChunks)) so that every

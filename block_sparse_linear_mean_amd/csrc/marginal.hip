@@ -19,8 +19,8 @@
 // its B operand.  A wavefront skips a step whose 64 x 32 mask block is all zero.  Sums
 // accumulate in fp32 in a fixed order (deterministic); S is written once in bf16, the
 // precision the epilogue consumes, re-staged through LDS for 1 KB-contiguous stores.  The z columns (u) take the same
-// path from fp32 z converted to bf16 operands.  Workgroups are numbered so that the row tiles of
-// one column slice run on one XCD and share its L2.
+// path from fp32 z converted to bf16 operands, in workgroups dispatched first.  State workgroups
+// are numbered so that the row tiles of one column slice run on one XCD and share its L2.
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -46,25 +46,39 @@ __device__ __forceinline__ bf16x8 expand_bits(uint32_t byte) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// 1-D grid of B * Hs * n_slices * n_row_tiles workgroups; slices: D * D / 128 state slices, then
-// ceil(D / 128) z slices.
+// 1-D grid: z workgroups (B * Hs * ceil(D / 128) * n_row_tiles, padded to a multiple of 8), then
+// B * Hs * (D * D / 128) * n_row_tiles state workgroups.
 template <int D>
 __global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restrict__ H, const float* __restrict__ z,
                                                             int Hq, int Hkv, int Hs, int nqb, int nkb, int group_map,
                                                             const uint32_t* __restrict__ bits, u16* __restrict__ S,
-                                                            float* __restrict__ u, int n_row_tiles, int n_slices) {
+                                                            float* __restrict__ u, int n_row_tiles, int n_z,
+                                                            int n_zwg) {
   __shared__ __attribute__((aligned(1024))) unsigned char bsm[kMgStages][kMgTileB];
   __shared__ uint32_t mask[kMgRows][kMgWords + 1];
 
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int it = logical % n_row_tiles;
-  const int rest = logical / n_row_tiles;
-  const int slice = rest % n_slices, bs = rest / n_slices;
+  // The first n_zwg workgroups (a multiple of 8) take the z columns, which go through registers
+  // and take longer, so they start first; the state slices follow in XCD-contiguous order.
+  constexpr int kStateSlices = D * D / kMgCols;
+  constexpr int kZSlices = (D + kMgCols - 1) / kMgCols;
+  const bool is_z = int(blockIdx.x) < n_zwg;
+  int it, slice, bs;
+  if (is_z) {
+    const int zi = blockIdx.x;
+    if (zi >= n_z) return;
+    it = zi % n_row_tiles;
+    slice = (zi / n_row_tiles) % kZSlices;
+    bs = zi / n_row_tiles / kZSlices;
+  } else {
+    const int logical = xcd_logical(blockIdx.x - n_zwg, gridDim.x - n_zwg);
+    it = logical % n_row_tiles;
+    const int rest = logical / n_row_tiles;
+    slice = rest % kStateSlices;
+    bs = rest / kStateSlices;
+  }
   const int b = bs / Hs, s = bs % Hs;
   const int g = group_map ? s : s / (Hq / Hkv);
-  constexpr int kStateSlices = D * D / kMgCols;
-  const bool is_z = slice >= kStateSlices;
-  const int c0 = is_z ? (slice - kStateSlices) * kMgCols : slice * kMgCols;
+  const int c0 = slice * kMgCols;
   const int64_t head = int64_t(b) * Hkv + g;
   const int t = threadIdx.x, lane = t % kWave;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform (feeds M0 and SGPR bases)
@@ -235,15 +249,17 @@ sla_status launch_marginal_states(const u16* H, const float* z, int B, int Hq, i
                                   int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st) {
   const int Hs = group_map ? Hkv : Hq;
   const int n_row_tiles = (nqb + kMgRows - 1) / kMgRows;
-  const int n_slices = d * d / kMgCols + (d + kMgCols - 1) / kMgCols;
-  const int64_t n = int64_t(B) * Hs * n_slices * n_row_tiles;
+  const int64_t n_state = int64_t(B) * Hs * (d * d / kMgCols) * n_row_tiles;
+  const int64_t n_z = int64_t(B) * Hs * ((d + kMgCols - 1) / kMgCols) * n_row_tiles;
+  const int64_t n_zwg = (n_z + 7) / 8 * 8;
+  const int64_t n = n_zwg + n_state;
   if (n > (int64_t(1) << 31) - 1) return SLA_ERR_UNSUPPORTED;
   if (d == 128)
     marginal_gemm_kernel<128><<<dim3(uint32_t(n)), 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u,
-                                                                 n_row_tiles, n_slices);
+                                                                 n_row_tiles, int(n_z), int(n_zwg));
   else
     marginal_gemm_kernel<64><<<dim3(uint32_t(n)), 256, 0, st>>>(H, z, Hq, Hkv, Hs, nqb, nkb, group_map, bits, S, u,
-                                                                n_row_tiles, n_slices);
+                                                                n_row_tiles, int(n_z), int(n_zwg));
   return launch_status();
 }
 

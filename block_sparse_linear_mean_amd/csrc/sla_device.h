@@ -109,6 +109,18 @@ __device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t vof
       : "memory");
 }
 
+// The 4-byte form: lane l's dword lands at lds + 4 l.
+__device__ __forceinline__ void load_lds4_sbase(const void* sbase, uint32_t voff_bytes, lds_u8* lds) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff_bytes), "s"(sbase), "s"(lds_addr)
+      : "memory");
+}
+
 // max / sum with the partner lane l ^ 32 (v_permlane32_swap, no LDS round trip).
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
