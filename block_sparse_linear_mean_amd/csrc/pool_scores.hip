@@ -14,52 +14,72 @@
 
 namespace sla {
 
-// One workgroup pools one (b, h, block i): 256 threads, each loads 8 consecutive
-// features of a row per pass and sums in fp64 (exact for bf16 inputs); partial sums
-// are combined in a fixed order, so the result does not depend on scheduling.
+// One workgroup pools kPoolBlocks consecutive blocks of one (b, h) of Q or K (grid y runs over
+// the Q heads, then the K heads): 256 threads; each thread owns 8 consecutive features of one
+// row group, issues all of its 16-byte loads before summing, and sums in fp64 (exact for bf16
+// inputs); partial sums are combined in a fixed order, so the result does not depend on
+// scheduling.
+constexpr int kPoolBlocks = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, int64_t sB, int64_t sH,
-                                                   int64_t sN, int H, int nb, int n_valid,
-                                                   float* __restrict__ out) {
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t qsB, int64_t qsH, int64_t qsN,
+                                                   int Hq, const T* __restrict__ k, int64_t ksB, int64_t ksH,
+                                                   int64_t ksN, int Hkv, int nb, int n_valid,
+                                                   float* __restrict__ qout, float* __restrict__ kout) {
   constexpr int kTpr = D / 8;          // threads per row
   constexpr int kRpp = 256 / kTpr;     // rows per pass
   constexpr int kPasses = kBlock / kRpp;
-  const int i = blockIdx.x;
-  const int bh = blockIdx.y;
+  const int y = blockIdx.y;
+  const int B = gridDim.y / (Hq + Hkv);
+  const bool is_q = y < B * Hq;
+  const int bh = is_q ? y : y - B * Hq;            // (b, h) index within its tensor
+  const int H = is_q ? Hq : Hkv;
   const int h = bh % H, b = bh / H;
+  const T* x = is_q ? q : k;
+  const int64_t sB = is_q ? qsB : ksB, sH = is_q ? qsH : ksH, sN = is_q ? qsN : ksN;
+  float* out = is_q ? qout : kout;
   const int t = threadIdx.x;
   const int cg = t % kTpr, rg = t / kTpr;
-  const int rows = min(kBlock, n_valid - kBlock * i);
-  const T* base = x + int64_t(b) * sB + int64_t(h) * sH + int64_t(kBlock * i) * sN + cg * 8;
-
-  double acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int r = rg + p * kRpp;
-    if (r < rows) {
-      float v[8];
-      In<T>::load8_f32(base + int64_t(r) * sN, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += double(v[e]);
-    }
-  }
   __shared__ double part[kRpp][D + 1];
+  for (int ib = 0; ib < kPoolBlocks; ++ib) {
+    const int i = blockIdx.x * kPoolBlocks + ib;
+    if (i >= nb) break;
+    const int rows = min(kBlock, n_valid - kBlock * i);
+    const T* base = x + int64_t(b) * sB + int64_t(h) * sH + int64_t(kBlock * i) * sN + cg * 8;
+    float v[kPasses][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][cg * 8 + e] = acc[e];
-  __syncthreads();
-  if (t < D) {
-    double s = 0.0;
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = rg + p * kRpp;
+      In<T>::load8_f32(base + int64_t(min(r, rows - 1)) * sN, v[p]);   // in-bounds stand-in for padding
+    }
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+      if (rg + p * kRpp < rows)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += double(v[p][e]);
+    __syncthreads();                     // the previous block's partial sums have been read
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][cg * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+      double s = 0.0;
 #pragma unroll 4
-    for (int r = 0; r < kRpp; ++r) s += part[r][t];
-    out[(int64_t(bh) * nb + i) * D + t] = float(s / double(rows));
+      for (int r = 0; r < kRpp; ++r) s += part[r][t];
+      out[(int64_t(bh) * nb + i) * D + t] = float(s / double(rows));
+    }
   }
 }
 
-// Pooled scores, one 64 x 64 tile of one score matrix per workgroup.
-// scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a sequential fp64
-// FMA chain over r; qsum sums the group's pooled queries in fp64 when group_sum is set.
+// Pooled scores, one 64 (i) x 128 (j) tile of one score matrix per workgroup; each thread owns
+// 4 x 8 outputs.  scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a sequential
+// fp64 FMA chain over r; qsum sums the group's pooled queries in fp64 when group_sum is set.
+// The pooled vectors stream through LDS 32 features at a time, the next chunk's loads in flight
+// in registers while the current chunk is multiplied.
+constexpr int kScI = 64, kScJ = 128, kScR = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qpool,
                                                      const float* __restrict__ kpool, int Hq, int Hkv,
@@ -69,61 +89,78 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
   const int b = bs / Hs, s = bs % Hs;
   const int G = Hq / Hkv;
   const int g = group_sum ? s : s / G;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int i0 = blockIdx.y * kScI, j0 = blockIdx.x * kScJ;
   const int t = threadIdx.x;
   const int tx = t % 16, ty = t / 16;
   float* out = scores + int64_t(bs) * nb * nb;
 
-  if (causal && j0 > i0 + 63) {   // the whole tile lies above the diagonal
-    for (int e = t; e < 64 * 64; e += 256) {
-      const int ii = i0 + e / 64, jj = j0 + e % 64;
+  if (causal && j0 > i0 + kScI - 1) {   // the whole tile lies above the diagonal
+    for (int e = t; e < kScI * kScJ; e += 256) {
+      const int ii = i0 + e / kScJ, jj = j0 + e % kScJ;
       if (ii < nb && jj < nb) out[int64_t(ii) * nb + jj] = -__builtin_inff();
     }
     return;
   }
 
-  __shared__ double qs[64][33];
-  __shared__ float ks[64][33];
-  double acc[4][4];
+  __shared__ double qs[kScI][kScR + 1];
+  __shared__ float ks[kScJ][kScR + 1];
+  double acc[4][8];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0;
 
   const int gh0 = group_sum ? g * G : s;
   const int ngh = group_sum ? G : 1;
-  for (int r0 = 0; r0 < D; r0 += 32) {
-    for (int e = t; e < 64 * 32; e += 256) {
-      const int row = e / 32, col = e % 32;
-      const int ii = i0 + row, jj = j0 + row;
+  // staging map: q chunk 64 x 32 -> 8 elements per thread, k chunk 128 x 32 -> 16 per thread
+  double qreg[8];
+  float kreg[16];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int e = t + 256 * n;
+      const int row = e / kScR, col = e % kScR;
+      const int ii = i0 + row;
       double qv = 0.0;
-      if (ii < nb) {
-        for (int hh = 0; hh < ngh; ++hh)
-          qv += double(qpool[((int64_t(b) * Hq + gh0 + hh) * nb + ii) * D + r0 + col]);
-      }
-      qs[row][col] = qv;
-      ks[row][col] = jj < nb ? kpool[((int64_t(b) * Hkv + g) * nb + jj) * D + r0 + col] : 0.f;
+      if (ii < nb)
+        for (int hh = 0; hh < ngh; ++hh) qv += double(qpool[((int64_t(b) * Hq + gh0 + hh) * nb + ii) * D + r0 + col]);
+      qreg[n] = qv;
     }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int e = t + 256 * n;
+      const int row = e / kScR, col = e % kScR;
+      const int jj = j0 + row;
+      kreg[n] = jj < nb ? kpool[((int64_t(b) * Hkv + g) * nb + jj) * D + r0 + col] : 0.f;
+    }
+  };
+  load(0);
+  for (int r0 = 0; r0 < D; r0 += kScR) {
+    __syncthreads();                      // the previous chunk has been read
+#pragma unroll
+    for (int n = 0; n < 8; ++n) { const int e = t + 256 * n; qs[e / kScR][e % kScR] = qreg[n]; }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = kreg[n]; }
     __syncthreads();
+    if (r0 + kScR < D) load(r0 + kScR);
 #pragma unroll 8
-    for (int r = 0; r < 32; ++r) {
-      double qa[4], kb[4];
+    for (int r = 0; r < kScR; ++r) {
+      double qa[4], kb[8];
 #pragma unroll
       for (int a = 0; a < 4; ++a) qa[a] = qs[ty + 16 * a][r];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kb[c] = double(ks[tx + 16 * c][r]);
+      for (int c = 0; c < 8; ++c) kb[c] = double(ks[tx + 16 * c][r]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = __fma_rn(qa[a], kb[c], acc[a][c]);
+        for (int c = 0; c < 8; ++c) acc[a][c] = __fma_rn(qa[a], kb[c], acc[a][c]);
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int ii = i0 + ty + 16 * a;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 8; ++c) {
       const int jj = j0 + tx + 16 * c;
       if (ii < nb && jj < nb) {
         const float v = (causal && jj > ii) ? -__builtin_inff() : float(acc[a][c] * scale);
@@ -151,14 +188,18 @@ __global__ __launch_bounds__(64) void probs_kernel(const float* __restrict__ sco
 }
 
 template <typename T>
-static void launch_pool(const sla_tensor* x, int n_valid, float* out, hipStream_t st) {
-  const int nb = x->N / kBlock;
-  dim3 grid(nb, x->B * x->H);
-  const T* p = static_cast<const T*>(x->ptr);
-  if (x->d == 128)
-    pool_kernel<T, 128><<<grid, 256, 0, st>>>(p, x->sB, x->sH, x->sN, x->H, nb, n_valid, out);
+static void launch_pool(const sla_tensor* q, const sla_tensor* k, int n_valid, float* qout, float* kout,
+                        hipStream_t st) {
+  const int nb = q->N / kBlock;
+  dim3 grid((nb + kPoolBlocks - 1) / kPoolBlocks, q->B * (q->H + k->H));
+  const T* qp = static_cast<const T*>(q->ptr);
+  const T* kp = static_cast<const T*>(k->ptr);
+  if (q->d == 128)
+    pool_kernel<T, 128><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nb,
+                                              n_valid, qout, kout);
   else
-    pool_kernel<T, 64><<<grid, 256, 0, st>>>(p, x->sB, x->sH, x->sN, x->H, nb, n_valid, out);
+    pool_kernel<T, 64><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nb,
+                                             n_valid, qout, kout);
 }
 
 }  // namespace sla
@@ -176,16 +217,10 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = q->N / kBlock;
-  if (q->dtype == SLA_BF16) {
-    launch_pool<bf16raw>(q, n_valid, q_pool, s);
-    launch_pool<bf16raw>(k, n_valid, k_pool, s);
-  } else {
-    launch_pool<float>(q, n_valid, q_pool, s);
-    launch_pool<float>(k, n_valid, k_pool, s);
-  }
+  if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, q_pool, k_pool, s);
+  else launch_pool<float>(q, k, n_valid, q_pool, k_pool, s);
   const int Hs = group_sum ? k->H : q->H;
-  const int tiles = (nb + 63) / 64;
-  dim3 grid(tiles, tiles, q->B * Hs);
+  dim3 grid((nb + kScJ - 1) / kScJ, (nb + kScI - 1) / kScI, q->B * Hs);
   if (q->d == 128)
     scores_kernel<128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
                                             causal ? 1 : 0, double(scale), scores);
