@@ -156,7 +156,11 @@ def test_linear_states(name):
         g = host(got).astype(np.float64)
         rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
         say(f"  {what}: rel-L2 {rel:.2e}")
-        assert rel < 3e-3, what     # phi(K) and fp32 V are rounded to bf16 matrix-core operands
+        # phi(K) and V are rounded to bf16 matrix-core operands (rms relative error 2^-9/sqrt(3)
+        # each, about 1.6e-3 per product term), and per-block H is stored in bf16 (one more
+        # rounding, rms 1.1e-3): about 2e-3 rms expected; the sums over all keys stay fp32.
+        bound = 5e-3 if what == "H" else 3e-3
+        assert rel < bound, what
 
 
 @pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla"])
