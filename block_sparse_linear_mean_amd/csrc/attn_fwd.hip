@@ -81,15 +81,16 @@ __device__ __forceinline__ int v_pos(int r, int c) {
 // registers.  The two wavefronts split the tile's steps.
 template <int D>
 struct StageOff {
-  uint32_t k[4];   // K layout, index q % 4 (d = 128) or 0
-  uint32_t v;      // V layout
+  uint32_t lane[4];                         // per-lane part: K layout index q % 4 (d = 128), V layout [0]
+  uint32_t step[AttnTile<D>::kInst / 2];    // this wavefront's steps: byte offset of the step's first row
 };
 
-template <int D>
+template <int D, bool KLAYOUT>
 __device__ __forceinline__ StageOff<D> stage_offsets(int64_t sN) {
   using Tl = AttnTile<D>;
   constexpr int R = 1024 / Tl::kRowB;             // rows per 1 KB step: 4 (d 128) or 8 (d 64)
   const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = (16 * lane) / Tl::kRowB;          // row within the step
   const int pc = lane % Tl::kChunks;              // physical chunk
   StageOff<D> o;
@@ -97,10 +98,12 @@ __device__ __forceinline__ StageOff<D> stage_offsets(int64_t sN) {
   for (int m = 0; m < 4; ++m) {
     // K: logical chunk c = pc ^ (row % chunks), row = q R + r; q R % chunks = 4 m (d 128) or 0
     const int rk = (D == 128 ? 4 * m : 0) + r;
-    const int c = pc ^ (rk % Tl::kChunks);
-    o.k[m] = uint32_t(2 * (r * sN + 8 * c));
+    const int c = KLAYOUT ? pc ^ (rk % Tl::kChunks) : pc ^ (2 * (r % 4));
+    o.lane[m] = uint32_t(2 * (r * sN + 8 * c));
   }
-  o.v = uint32_t(2 * (r * sN + 8 * (pc ^ (2 * (r % 4)))));
+#pragma unroll
+  for (int n = 0; n < Tl::kInst / 2; ++n)
+    o.step[n] = uint32_t(int64_t(w * (Tl::kInst / 2) + n) * R * sN * 2);
   return o;
 }
 
@@ -108,16 +111,16 @@ template <typename T, int D, bool KLAYOUT>
 __device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, int j, lds_u8* tile,
                                            const StageOff<D>& off) {
   using Tl = AttnTile<D>;
-  constexpr int R = 1024 / Tl::kRowB;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: the LDS base goes to M0
   if constexpr (sizeof(T) == 2) {
+    // one 64-bit tile base per tile; each copy adds a wave-uniform step offset to a per-lane offset
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(X) + int64_t(kBlock * j) * sN * 2;
 #pragma unroll
     for (int n = 0; n < Tl::kInst / 2; ++n) {
       const int q = w * (Tl::kInst / 2) + n;
-      const T* sbase = X + int64_t(kBlock * j + q * R) * sN;
-      const uint32_t vo = KLAYOUT ? off.k[D == 128 ? n % 4 : 0] : off.v;   // q % 4 == n % 4
-      load_lds16_sbase(sbase, vo, tile + q * 1024);
+      const uint32_t vo = off.lane[KLAYOUT && D == 128 ? n % 4 : 0] + off.step[n];   // q % 4 == n % 4
+      load_lds16_sbase(tb, vo, tile + q * 1024);
     }
   } else {
 #pragma unroll
@@ -194,8 +197,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float c2 = p.scale_log2;
 
   // per-lane offsets, computed once: direct-load sources, K operand reads, V transposed reads
-  const StageOff<D> koff = stage_offsets<D>(p.ksN);
-  const StageOff<D> voff = stage_offsets<D>(p.vsN);
+  const StageOff<D> koff = stage_offsets<D, true>(p.ksN);
+  const StageOff<D> voff = stage_offsets<D, false>(p.vsN);
   int kread[kQs];                 // K row 32 kt + l32, chunk 2 ks + lg (+ 32 kt rows = kt * 8 KB)
 #pragma unroll
   for (int ks = 0; ks < kQs; ++ks) kread[ks] = k_pos<D>(l32, 2 * ks + lg);
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (LIN == SLA_LIN_MARGINAL) {
       const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
       ug = p.u + mrow * D;
-      const StageOff<D> soff = stage_offsets<D>(D);
+      const StageOff<D> soff = stage_offsets<D, true>(D);
       stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
       if constexpr (D == 128) stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
     } else {
