@@ -277,13 +277,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
     const bool full = jok && rv >= kBlock && !CAUSAL;
     if (!full) {                                     // padded, malformed or causal block
+      // key s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot: every test compares
+      // C with a per-lane bound, so no per-slot key index has to live in registers
+      const int rel = kBlock * j + 4 * lg;
+      const int lim_valid = jok ? p.n_valid - rel : 0;   // s < n_valid      <=> C < lim_valid
+      const int lim_causal = tq - rel;                    // s <= tq          <=> C <= lim_causal
+      const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
+      const bool sel = flag & 1;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int s = kBlock * j + 32 * kt + 8 * (e / 4) + 4 * lg + (e % 4);
-          bool ok = jok && s < p.n_valid;
-          if constexpr (CAUSAL) ok = ok && s <= tq && ((flag & 1) || tq - s < p.window);
+          const int C = 32 * kt + 8 * (e / 4) + (e % 4);
+          bool ok = C < lim_valid;
+          if constexpr (CAUSAL) ok = ok && C <= lim_causal && (sel || C > lim_win);
           sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
         }
     }
