@@ -230,6 +230,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j0 = safe_block(entry(0, lj0, lj1));
     stage_tile<T, D, true>(K, p.ksN, j0, Kb, koff);
     stage_tile<T, D, false>(V, p.vsN, j0, Vb, voff);
+    if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);   // K_0 resident (V_0 may still be in flight)
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
   }
   for (int pi = cbeg; pi < cend; ++pi) {
     if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
@@ -248,10 +251,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
     const int rv = p.n_valid - kBlock * j;          // valid rows of this block (may exceed 64)
 
-    // ---- K_j resident (V_j may still be in flight)
-    if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);
-    SLA_WAIT_LGKM0();
-    SLA_BARRIER();
+    // ---- K_j resident (V_j may still be in flight): the previous block's last barrier
     // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
     f32x16 sacc[2];
 #pragma unroll
@@ -356,9 +356,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (st + 1 < 4 * kDt) va[(st + 1) & 1] = vop((st + 1) / kDt, (st + 1) % kDt);
       oacc[dt] = mfma32(va[st & 1], pb[u], oacc[dt]);
     }
-    SLA_WAIT_LGKM0();
-    SLA_BARRIER();                                   // every wavefront has read V_j
-    if (more) stage_tile<T, D, false>(V, p.vsN, jn, Vb, voff);
+    if (more) {
+      // one barrier for both: every wavefront has read V_j, and K_{j+1} (the only copy in flight)
+      // has landed
+      if constexpr (kDirect) SLA_WAIT_VMCNT(0);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      stage_tile<T, D, false>(V, p.vsN, jn, Vb, voff);
+    }
   }
 
   // ---- normalise the sparse branch
