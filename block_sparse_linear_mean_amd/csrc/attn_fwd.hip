@@ -31,6 +31,8 @@ namespace sla {
 sla_status launch_marginal_states(const u16* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
                                   int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st);
 
+constexpr int kGroupHeads = 4;   // heads per workgroup when a GQA group shares the block map
+
 struct AttnParams {
   const void* q;
   const void* k;
@@ -78,54 +80,57 @@ __device__ __forceinline__ int v_pos(int r, int c) {
 // that chunk's byte offset from the step's first row is a per-lane constant, except for the K
 // layout at d = 128 where it takes 4 values (q % 4); so each wavefront keeps at most four 32-bit
 // offsets and all other address arithmetic is wave-uniform.  fp32 inputs are converted through
-// registers.  The two wavefronts split the tile's steps.
-template <int D>
+// registers.  The NW wavefronts of a workgroup split the tile's steps.
+template <int D, int NW>
 struct StageOff {
-  uint32_t lane[4];                         // per-lane part: K layout index q % 4 (d = 128), V layout [0]
-  uint32_t step[AttnTile<D>::kInst / 2];    // this wavefront's steps: byte offset of the step's first row
+  static constexpr int kSteps = AttnTile<D>::kInst / NW;   // steps per wavefront
+  static constexpr int kLanes = kSteps < 4 ? kSteps : 4;
+  uint32_t lane[kLanes];          // per-lane part of this wavefront's step n, index n % kLanes
+  uint32_t step[kSteps];          // this wavefront's steps: byte offset of the step's first row
 };
 
-template <int D, bool KLAYOUT>
-__device__ __forceinline__ StageOff<D> stage_offsets(int64_t sN) {
+template <int D, bool KLAYOUT, int NW>
+__device__ __forceinline__ StageOff<D, NW> stage_offsets(int64_t sN) {
   using Tl = AttnTile<D>;
+  using SO = StageOff<D, NW>;
   constexpr int R = 1024 / Tl::kRowB;             // rows per 1 KB step: 4 (d 128) or 8 (d 64)
   const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r = (16 * lane) / Tl::kRowB;          // row within the step
   const int pc = lane % Tl::kChunks;              // physical chunk
-  StageOff<D> o;
+  SO o;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    // K: logical chunk c = pc ^ (row % chunks), row = q R + r; q R % chunks = 4 m (d 128) or 0
-    const int rk = (D == 128 ? 4 * m : 0) + r;
-    const int c = KLAYOUT ? pc ^ (rk % Tl::kChunks) : pc ^ (2 * (r % 4));
+  for (int m = 0; m < SO::kLanes; ++m) {
+    const int q = w * SO::kSteps + m;             // q % 4 repeats with period 4 in m
+    const int c = KLAYOUT ? pc ^ ((q * R + r) % Tl::kChunks) : pc ^ (2 * (r % 4));
     o.lane[m] = uint32_t(2 * (r * sN + 8 * c));
   }
 #pragma unroll
-  for (int n = 0; n < Tl::kInst / 2; ++n)
-    o.step[n] = uint32_t(int64_t(w * (Tl::kInst / 2) + n) * R * sN * 2);
+  for (int n = 0; n < SO::kSteps; ++n)
+    o.step[n] = uint32_t(int64_t(w * SO::kSteps + n) * R * sN * 2);
   return o;
 }
 
-template <typename T, int D, bool KLAYOUT>
+template <typename T, int D, bool KLAYOUT, int NW>
 __device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, int j, lds_u8* tile,
-                                           const StageOff<D>& off) {
+                                           const StageOff<D, NW>& off) {
   using Tl = AttnTile<D>;
+  using SO = StageOff<D, NW>;
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: the LDS base goes to M0
   if constexpr (sizeof(T) == 2) {
     // one 64-bit tile base per tile; each copy adds a wave-uniform step offset to a per-lane offset
     const unsigned char* tb = reinterpret_cast<const unsigned char*>(X) + int64_t(kBlock * j) * sN * 2;
 #pragma unroll
-    for (int n = 0; n < Tl::kInst / 2; ++n) {
-      const int q = w * (Tl::kInst / 2) + n;
-      const uint32_t vo = off.lane[KLAYOUT && D == 128 ? n % 4 : 0] + off.step[n];   // q % 4 == n % 4
+    for (int n = 0; n < SO::kSteps; ++n) {
+      const int q = w * SO::kSteps + n;
+      const uint32_t vo = off.lane[KLAYOUT ? n % SO::kLanes : 0] + off.step[n];
       load_lds16_sbase(tb, vo, tile + q * 1024);
     }
   } else {
 #pragma unroll
-    for (int n = 0; n < Tl::kChunks * kBlock / 128; ++n) {
-      const int e = t + 128 * n;
+    for (int n = 0; n < Tl::kChunks * kBlock / (kWave * NW); ++n) {
+      const int e = t + kWave * NW * n;
       const int r = e / Tl::kChunks, c = e % Tl::kChunks;
       const bf16x8 x = In<T>::load8(X + int64_t(kBlock * j + r) * sN + 8 * c);
       lds_store16(tile + (KLAYOUT ? k_pos<D>(r, c) : v_pos<D>(r, c)), x);
@@ -140,47 +145,51 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, 
 struct WgCoord {
   int i, h, b;
 };
-__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv) {
+// hg heads per workgroup (hg divides the group size G): h is the workgroup's first head
+__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg) {
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int G = Hq / Hkv;
-  const int hh = logical % G;
-  const int rest = logical / G;
+  const int G = Hq / Hkv, ng = G / hg;
+  const int hh = logical % ng;
+  const int rest = logical / ng;
   const int i = rest % nqb;
   const int bg = rest / nqb;
   const int g = bg % Hkv, b = bg / Hkv;
-  return WgCoord{i, g * G + hh, b};
+  return WgCoord{i, g * G + hh * hg, b};
 }
 
-// One workgroup = one 64-row query block of one head: 2 wavefronts x 32 query rows, 32x32x16
+// One workgroup = one 64-row query block of NW / 2 heads (heads of one GQA group sharing the
+// block map, so they share every staged K/V tile): 2 wavefronts x 32 query rows per head, 32x32x16
 // bf16 matrix cores.  Per critical key block: S^T = K Q^T (lane = one query column, 32 keys),
 // online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
 // transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU): the next
 // K block streams into LDS during softmax and P.V, the next V block during the next S^T.
-template <typename T, int D, bool CAUSAL, int LIN>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
+template <typename T, int D, bool CAUSAL, int LIN, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
   using Tl = AttnTile<D>;
   constexpr int kQs = D / 16;      // 16-wide feature steps of the Q.K contraction
   constexpr int kDt = D / 32;      // 32-wide feature tiles of the output
   constexpr bool kDirect = sizeof(T) == 2;
-  constexpr int kWaitK = kDirect ? Tl::kInst / 2 : 0;   // loads of one tile per wavefront
+  constexpr int kWaitK = kDirect ? Tl::kInst / NW : 0;  // loads of one tile per wavefront
+  constexpr int kThreads = kWave * NW;
   __shared__ __attribute__((aligned(1024))) unsigned char ksm[Tl::kTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char vsm[Tl::kTileB];
   __shared__ float lin_u[D];
   lds_u8* Kb = to_lds(ksm);
   lds_u8* Vb = to_lds(vsm);
 
-  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv);
-  const int i = wc.i, h = wc.h, b = wc.b;
+  const int t = threadIdx.x, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: head and K/V bases in SGPRs
+  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, NW / 2);
+  const int i = wc.i, h = wc.h + w / 2, b = wc.b;  // this wavefront's head
   const int G = p.Hq / p.Hkv;
   const int g = h / G;
   const int smap = p.group_map ? g : h;
   const int64_t mrow = (int64_t(b) * p.Hs + smap) * p.nqb + i;
-  const int t = threadIdx.x, w = t / kWave, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
   const T* Q = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
   const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(g) * p.ksH;
   const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(g) * p.vsH;
 
-  const int tq = kBlock * i + 32 * w + l32;       // this lane's query row
+  const int tq = kBlock * i + 32 * (w % 2) + l32; // this lane's query row
   const bool qvalid = tq < p.n_valid;
   bf16x8 qf[kQs];
 #pragma unroll
@@ -197,8 +206,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float c2 = p.scale_log2;
 
   // per-lane offsets, computed once: direct-load sources, K operand reads, V transposed reads
-  const StageOff<D> koff = stage_offsets<D, true>(p.ksN);
-  const StageOff<D> voff = stage_offsets<D, false>(p.vsN);
+  const StageOff<D, NW> koff = stage_offsets<D, true, NW>(p.ksN);
+  const StageOff<D, NW> voff = stage_offsets<D, false, NW>(p.vsN);
   int kread[kQs];                 // K row 32 kt + l32, chunk 2 ks + lg (+ 32 kt rows = kt * 8 KB)
 #pragma unroll
   for (int ks = 0; ks < kQs; ++ks) kread[ks] = k_pos<D>(l32, 2 * ks + lg);
@@ -228,8 +237,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto safe_block = [&](int jraw) { return unsigned(jraw) < unsigned(p.nqb) ? jraw : 0; };
   if (cbeg < cend) {
     const int j0 = safe_block(entry(0, lj0, lj1));
-    stage_tile<T, D, true>(K, p.ksN, j0, Kb, koff);
-    stage_tile<T, D, false>(V, p.vsN, j0, Vb, voff);
+    stage_tile<T, D, true, NW>(K, p.ksN, j0, Kb, koff);
+    stage_tile<T, D, false, NW>(V, p.vsN, j0, Vb, voff);
     if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);   // K_0 resident (V_0 may still be in flight)
     SLA_WAIT_LGKM0();
     SLA_BARRIER();
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     SLA_WAIT_LGKM0();
     SLA_BARRIER();                                   // every wavefront has read K_j
-    if (more) stage_tile<T, D, true>(K, p.ksN, jn, Kb, koff);
+    if (more) stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
 
     // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
     const bool full = jok && rv >= kBlock && !CAUSAL;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     SLA_BARRIER();
     if (!jok || rv < kBlock) {                       // padded keys: zero their V rows
       const int r0 = jok ? max(rv, 0) : 0;
-      for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += 128) {
+      for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += kThreads) {
         const int r = r0 + e / Tl::kChunks;
         lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
       }
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (kDirect) SLA_WAIT_VMCNT(0);
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
-      stage_tile<T, D, false>(V, p.vsN, jn, Vb, voff);
+      stage_tile<T, D, false, NW>(V, p.vsN, jn, Vb, voff);
     }
   }
 
@@ -383,13 +392,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (LIN == SLA_LIN_MARGINAL) {
       const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
       ug = p.u + mrow * D;
-      const StageOff<D> soff = stage_offsets<D, true>(D);
-      stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
-      if constexpr (D == 128) stage_tile<bf16raw, D, true>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
+      const StageOff<D, NW> soff = stage_offsets<D, true, NW>(D);
+      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
+      if constexpr (D == 128) stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
     } else {
       const float* Sg = static_cast<const float*>(p.S) + (int64_t(b) * p.Hkv + g) * D * D;
       ug = p.u + (int64_t(b) * p.Hkv + g) * D;
-      for (int e = t; e < D * Tl::kChunks; e += 128) {
+      for (int e = t; e < D * Tl::kChunks; e += kThreads) {
         const int r = e / Tl::kChunks, c = e % Tl::kChunks;
         const bf16x8 x = In<float>::load8(Sg + r * D + 8 * c);
         lds_store16(st_tile(r) + k_pos<D>(r % kBlock, c), x);
@@ -454,15 +463,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <typename T, int D>
-static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hipStream_t st) {
-  if (causal) {
-    attn_fwd_kernel<T, D, true, SLA_LIN_NONE><<<grid, 128, 0, st>>>(p);
+static void launch_attn(const AttnParams& p, int causal, int lin, int hg, dim3 grid, hipStream_t st) {
+  if (hg == kGroupHeads) {   // GQA heads sharing one map: NW = 2 * kGroupHeads wavefronts
+    if (causal) attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2 * kGroupHeads><<<grid, 128 * kGroupHeads, 0, st>>>(p);
+    else attn_fwd_kernel<T, D, false, SLA_LIN_NONE, 2 * kGroupHeads><<<grid, 128 * kGroupHeads, 0, st>>>(p);
+  } else if (causal) {
+    attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
-    attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL><<<grid, 128, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_GLOBAL_GATED) {
-    attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED><<<grid, 128, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED, 2><<<grid, 128, 0, st>>>(p);
   } else {
-    attn_fwd_kernel<T, D, false, SLA_LIN_NONE><<<grid, 128, 0, st>>>(p);
+    attn_fwd_kernel<T, D, false, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
   }
 }
 
@@ -527,14 +539,16 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
     p.u = z_all;
     p.w_gate = w_gate;
   }
-  dim3 grid(nqb * q->H * q->B);
+  // heads of a GQA group that share the map (and so every K/V tile) run in one workgroup
+  const int hg = (p.group_map && lin_mode == SLA_LIN_NONE && (q->H / k->H) % kGroupHeads == 0) ? kGroupHeads : 1;
+  dim3 grid(nqb * (q->H / hg) * q->B);
   const bool bf = q->dtype == SLA_BF16;
   if (d == 128) {
-    if (bf) launch_attn<bf16raw, 128>(p, causal, lin_mode, grid, s);
-    else launch_attn<float, 128>(p, causal, lin_mode, grid, s);
+    if (bf) launch_attn<bf16raw, 128>(p, causal, lin_mode, hg, grid, s);
+    else launch_attn<float, 128>(p, causal, lin_mode, hg, grid, s);
   } else {
-    if (bf) launch_attn<bf16raw, 64>(p, causal, lin_mode, grid, s);
-    else launch_attn<float, 64>(p, causal, lin_mode, grid, s);
+    if (bf) launch_attn<bf16raw, 64>(p, causal, lin_mode, hg, grid, s);
+    else launch_attn<float, 64>(p, causal, lin_mode, hg, grid, s);
   }
   return launch_status();
 }
