@@ -22,8 +22,13 @@ computes, in the order the pages describe it:
      H_j = phi(K_j)^T V_j and z_j = sum phi(K_j), negligible pairs are skipped
      (SLA analysis page: FlashAttn + linear attention per block pair, the
      marginal cost is O(N d^2));
-  4. combine:  O = O^s + Proj(O^l) with Proj the identity (SLA analysis page,
-     the zero-initialised Proj remark; no trained weights exist here).
+  4. combine:  O = O^s + Proj(O^l) (SLA analysis page, the zero-initialised Proj
+     remark).  Proj is the identity unless a weight is given; a given Proj is a
+     linear layer on each output row, x W^T + b.
+
+Smooth-K (SLA analysis page, the remark that the open-source code zero-means K,
+a step the paper does not mention): optionally the keys of the linear branch are
+replaced by K - mean(K), the mean over the valid tokens of each (batch, KV head).
 
 Variants: SALAD adds a linear branch over all keys in parallel with the sparse
 branch and mixes it with an input-dependent gate (SALAD page, method
@@ -56,6 +61,13 @@ Readings where the pages are silent (each also listed in the design notes):
   * NSA: group score = scale * (sum over the group's heads of q_pool) . k_pool,
     candidates j <= i, selected = top min(n_sel, i+1), window = key s with
     0 <= t - s < window, one softmax over (selected or window) and causal keys.
+  * Proj: weight W [d, d] (one for all heads) or [Hq, d, d] (one per head), bias
+    b [d] or [Hq, d] or none; applied to O^l of every valid row of an SLA output,
+    also where the row has no marginal block (O^l = 0 there, so the row gets b);
+  * smooth-K shifts the keys of the linear branch only (the key states H_j, z_j).
+    The softmax branch and the pooled ranking are unchanged by it in exact
+    arithmetic: subtracting one vector from every key adds the same amount to
+    every logit of a query row (and to every pooled score of a row).
 """
 from __future__ import annotations
 
@@ -245,14 +257,25 @@ def to_csr(maps: Dict, B: int, Hs: int, nqb: int):
 
 # ----------------------------------------------------------------------------- step 3: execute
 
-def kv_state(K_head: np.ndarray, V_head: np.ndarray, j: int, n_valid: int):
-    """H_j = phi(K_j)^T V_j (d x d) and z_j = sum_s phi(K_j[s]) over the valid rows of key block j."""
+def key_mean(K_head: np.ndarray, n_valid: int) -> np.ndarray:
+    """Smooth-K shift of one head: the mean over its valid key rows (float64, [d])."""
+    return K_head[:n_valid].astype(F64).mean(axis=0)
+
+
+def kv_state(K_head: np.ndarray, V_head: np.ndarray, j: int, n_valid: int, shift=None):
+    """H_j = phi(K_j)^T V_j (d x d) and z_j = sum_s phi(K_j[s]) over the valid rows of key block j.
+
+    With `shift` (smooth-K) the keys are K_j - shift before phi.
+    """
     lo, hi = BLOCK * j, min(BLOCK * (j + 1), n_valid)
-    pk = phi(K_head[lo:hi])
+    Kj = K_head[lo:hi].astype(F64)
+    if shift is not None:
+        Kj = Kj - shift
+    pk = phi(Kj)
     return pk.T @ V_head[lo:hi].astype(F64), pk.sum(axis=0)
 
 
-def kv_states(K: np.ndarray, V: np.ndarray, n_valid: int):
+def kv_states(K: np.ndarray, V: np.ndarray, n_valid: int, smooth_k: bool = False):
     """All per-block states: H [B, Hkv, nb, d, d], z [B, Hkv, nb, d], float64."""
     B, Hkv, N, d = K.shape
     nb = N // BLOCK
@@ -260,9 +283,10 @@ def kv_states(K: np.ndarray, V: np.ndarray, n_valid: int):
     z = np.zeros((B, Hkv, nb, d), dtype=F64)
     for b in range(B):
         for h in range(Hkv):
+            shift = key_mean(K[b, h], n_valid) if smooth_k else None
             for j in range(nb):
                 if BLOCK * j < n_valid:
-                    H[b, h, j], z[b, h, j] = kv_state(K[b, h], V[b, h], j, n_valid)
+                    H[b, h, j], z[b, h, j] = kv_state(K[b, h], V[b, h], j, n_valid, shift)
     return H, z
 
 
@@ -299,6 +323,12 @@ def linear_block(Qi: np.ndarray, Hsum: np.ndarray, zsum: np.ndarray) -> np.ndarr
     return (pq @ Hsum) / (pq @ zsum)[:, None]
 
 
+def project(O_lin: np.ndarray, W: np.ndarray, bias=None) -> np.ndarray:
+    """The learned projection of the linear branch on each row: O_lin W^T (+ bias)."""
+    out = O_lin @ np.asarray(W, dtype=F64).T
+    return out if bias is None else out + np.asarray(bias, dtype=F64)
+
+
 def sigmoid(x):
     """1 / (1 + exp(-x)); exp overflow for very negative x correctly gives 0."""
     with np.errstate(over="ignore"):
@@ -315,7 +345,8 @@ class Forward:
     """
 
     def __init__(self, Q, K, V, *, n_valid: int, mode: str, kh_bp: int = 0, kl_bp: int = 0,
-                 n_sel: int = 0, window: int = 0, w_gate=None, scale: Optional[float] = None):
+                 n_sel: int = 0, window: int = 0, w_gate=None, scale: Optional[float] = None,
+                 proj_w=None, proj_b=None, smooth_k: bool = False):
         self.Q, self.K, self.V = Q, K, V
         self.B, self.Hq, self.N, self.d = Q.shape
         self.Hkv = K.shape[1]
@@ -328,6 +359,13 @@ class Forward:
         self.n_sel, self.window = n_sel, window
         self.scale = default_scale(self.d) if scale is None else float(scale)
         self.w_gate = None if w_gate is None else np.asarray(w_gate, dtype=F64)
+        self.proj_w = None if proj_w is None else np.asarray(proj_w, dtype=F64)
+        self.proj_b = None if proj_b is None else np.asarray(proj_b, dtype=F64)
+        if self.proj_w is None and self.proj_b is not None:
+            raise ValueError("a Proj bias needs a Proj weight")
+        if self.proj_w is not None and mode != "sla":
+            raise ValueError("Proj applies to the SLA linear branch")
+        self.smooth_k = smooth_k
         if mode == "sla":
             self.n_h, self.n_l = block_counts(self.nb, kh_bp, kl_bp)
         elif mode == "salad":
@@ -349,8 +387,19 @@ class Forward:
     def state(self, b, hk, j):
         key = (b, hk, j)
         if key not in self._H:
-            self._H[key] = kv_state(self.K[b, hk], self.V[b, hk], j, self.n_valid)
+            shift = key_mean(self.K[b, hk], self.n_valid) if self.smooth_k else None
+            self._H[key] = kv_state(self.K[b, hk], self.V[b, hk], j, self.n_valid, shift)
         return self._H[key]
+
+    def proj_head(self, h):
+        """(W, b) of head h's projection; W None = identity."""
+        if self.proj_w is None:
+            return None, None
+        W = self.proj_w[h] if self.proj_w.ndim == 3 else self.proj_w
+        bias = None
+        if self.proj_b is not None:
+            bias = self.proj_b[h] if self.proj_b.ndim == 2 else self.proj_b
+        return W, bias
 
     def global_state(self, b, hk):
         key = (b, hk)
@@ -401,14 +450,20 @@ class Forward:
         Qi = self.Q[b, h, t0:t0 + BLOCK].astype(F64)
         O = sparse_block(Qi, t0, self.K[b, hk], self.V[b, hk], m["crit"], m["flags"], self.n_valid,
                          self.scale, self.causal, self.window)
-        if self.mode == "sla" and m["marg"]:
-            Hs = np.zeros((self.d, self.d))
-            zs = np.zeros(self.d)
-            for j in m["marg"]:
-                H, z = self.state(b, hk, j)
-                Hs += H
-                zs += z
-            O = O + linear_block(Qi, Hs, zs)
+        if self.mode == "sla":
+            O_lin = np.zeros_like(O)
+            if m["marg"]:
+                Hs = np.zeros((self.d, self.d))
+                zs = np.zeros(self.d)
+                for j in m["marg"]:
+                    H, z = self.state(b, hk, j)
+                    Hs += H
+                    zs += z
+                O_lin = linear_block(Qi, Hs, zs)
+            W, bias = self.proj_head(h)
+            if W is not None:
+                O_lin = project(O_lin, W, bias)
+            O = O + O_lin
         elif self.mode == "salad":
             Hs, zs = self.global_state(b, hk)
             gate = sigmoid(Qi @ self.w_gate[h])

@@ -198,6 +198,80 @@ def test_nothing_critical_equals_closed_form_linear_attention(N, nv):
     assert np.all(O[0, 0, nv:] == 0.0)
 
 
+# ----------------------------------------------------------------------------- Proj and smooth-K
+
+def _linear_layer(x, W, b):
+    """torch's Linear convention (x W^T + b), as a library routine."""
+    import torch
+    return torch.nn.functional.linear(torch.as_tensor(x), torch.as_tensor(np.asarray(W, np.float64)),
+                                      None if b is None else torch.as_tensor(np.asarray(b, np.float64))).numpy()
+
+
+def test_proj_all_marginal_is_projected_closed_form_linear_attention():
+    N, nv, d, H = 256, 230, 16, 2
+    Q, K, V = rand_qkv(1, H, H, N, d, seed=21, n_valid=nv, garbage=True)
+    r = np.random.default_rng(22)
+    W, b = r.standard_normal((H, d, d)) / 4.0, r.standard_normal((H, d))
+    O = orc.forward(Q, K, V, n_valid=nv, mode="sla", kh_bp=0, kl_bp=0, proj_w=W, proj_b=b)
+    for h in range(H):
+        la = refs.kernel_linear_attention(Q[0, h, :nv], K[0, h, :nv], V[0, h, :nv])
+        assert np.allclose(O[0, h, :nv], _linear_layer(la, W[h], b[h]), rtol=1e-10, atol=1e-12)
+        assert np.all(O[0, h, nv:] == 0.0)
+    # one weight shared by all heads, no bias
+    O1 = orc.forward(Q, K, V, n_valid=nv, mode="sla", kh_bp=0, kl_bp=0, proj_w=W[1])
+    la = refs.kernel_linear_attention(Q[0, 0, :nv], K[0, 0, :nv], V[0, 0, :nv])
+    assert np.allclose(O1[0, 0, :nv], _linear_layer(la, W[1], None), rtol=1e-10, atol=1e-12)
+
+
+def test_zero_proj_weight_leaves_sparse_branch_plus_bias():
+    N, nv, d = 384, 350, 16
+    Q, K, V = rand_qkv(1, 2, 1, N, d, seed=23, n_valid=nv, garbage=True)
+    b = np.random.default_rng(24).standard_normal(d)
+    kw = dict(n_valid=nv, mode="sla", kh_bp=2500)
+    O = orc.forward(Q, K, V, kl_bp=3000, proj_w=np.zeros((d, d)), proj_b=b, **kw)
+    O_sparse = orc.forward(Q, K, V, kl_bp=10000, **kw)     # every non-critical block negligible
+    assert np.allclose(O[:, :, :nv], O_sparse[:, :, :nv] + b, rtol=1e-12, atol=1e-12)
+    assert np.all(O[:, :, nv:] == 0.0)
+
+
+def test_identity_proj_equals_no_proj():
+    N, nv, d = 320, 320, 16
+    Q, K, V = rand_qkv(1, 1, 1, N, d, seed=25)
+    kw = dict(n_valid=nv, mode="sla", kh_bp=2500, kl_bp=2500)
+    assert np.allclose(orc.forward(Q, K, V, proj_w=np.eye(d), **kw), orc.forward(Q, K, V, **kw),
+                       rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("N,nv", [(256, 256), (320, 300)])
+def test_smooth_k_all_marginal_is_linear_attention_of_centred_keys(N, nv):
+    d = 16
+    Q, K, V = rand_qkv(1, 1, 1, N, d, seed=26, n_valid=nv, garbage=True)
+    K = K + 0.7      # a non-zero key mean
+    O = orc.forward(Q, K, V, n_valid=nv, mode="sla", kh_bp=0, kl_bp=0, smooth_k=True)
+    Kc = K[0, 0, :nv] - np.mean(K[0, 0, :nv], axis=0, dtype=np.float64)     # padding excluded
+    ref = refs.kernel_linear_attention(Q[0, 0, :nv], Kc, V[0, 0, :nv])
+    assert np.allclose(O[0, 0, :nv], ref, rtol=1e-10, atol=1e-12)
+    assert not np.allclose(ref, refs.kernel_linear_attention(Q[0, 0, :nv], K[0, 0, :nv], V[0, 0, :nv]),
+                           rtol=1e-3, atol=1e-3)
+    assert np.all(O[0, 0, nv:] == 0.0)
+
+
+def test_smooth_k_leaves_softmax_branch_and_salad_gates_centred_linear_branch():
+    N, nv, d = 256, 250, 16
+    Q, K, V = rand_qkv(1, 1, 1, N, d, seed=27, n_valid=nv, garbage=True)
+    K = K - 0.5
+    sc = orc.default_scale(d)
+    dense = _valid_sdpa(Q[0, 0], K[0, 0], V[0, 0], nv, sc)
+    Kc = K[0, 0, :nv] - np.mean(K[0, 0, :nv], axis=0, dtype=np.float64)
+    # premise of the reading: one shift of every key leaves softmax attention unchanged
+    assert np.allclose(refs.sdpa(Q[0, 0, :nv], Kc, V[0, 0, :nv], sc), dense, rtol=1e-10, atol=1e-12)
+    O = orc.forward(Q, K, V, n_valid=nv, mode="sla", kh_bp=10000, kl_bp=0, smooth_k=True)
+    assert np.allclose(O[0, 0, :nv], dense, rtol=1e-10, atol=1e-12)
+    Os = orc.forward(Q, K, V, n_valid=nv, mode="salad", kh_bp=10000, w_gate=np.zeros((1, d)), smooth_k=True)
+    ref = dense + 0.5 * refs.kernel_linear_attention(Q[0, 0, :nv], Kc, V[0, 0, :nv])
+    assert np.allclose(Os[0, 0, :nv], ref, rtol=1e-10, atol=1e-12)
+
+
 def test_everything_negligible_gives_zero():
     Q, K, V = rand_qkv(1, 1, 1, 192, 8, seed=8)
     O = orc.forward(Q, K, V, n_valid=192, mode="sla", kh_bp=0, kl_bp=10000)
