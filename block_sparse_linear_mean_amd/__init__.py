@@ -4,6 +4,7 @@ The compute runs in libsla (HIP, gfx950); this package is its Python binding.
 Entry points keep the C names (see include/sla.h):
 
     sla_pool_scores      block mean pooling of Q, K and pooled scores
+    sla_key_mean         smooth-K shift (mean key of each head) from the pooled key blocks
     sla_block_map        critical / marginal / negligible classification as CSR lists
     sla_linear_kv_reduce per-key-block linear states H_j = phi(K_j)^T V_j, z_j
     sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
@@ -21,7 +22,7 @@ import torch
 from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
     lib, sla_abi_version, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
-    sla_block_map_workspace_bytes, sla_counts, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
+    sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
 )
 
@@ -32,11 +33,16 @@ class SlaForward:
     mode "sla":   top kh_bp critical, bottom kl_bp negligible, linear attention on marginal blocks.
     mode "salad": top kh_bp sparse blocks plus the gated linear branch over all keys (w_gate [Hq, d]).
     mode "nsa":   causal, GQA-shared selection of n_sel blocks plus a window of `window` tokens.
+    proj_w / proj_b (sla mode): the learned projection of the linear branch, [d, d] or [Hq, d, d]
+    (out x in) and [d] or [Hq, d]; None = identity.  smooth_k (sla and salad modes): the linear
+    branch uses the keys minus their mean over the valid tokens of each head.
     """
 
     def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_valid: int, mode: str,
                  kh_bp: int = 0, kl_bp: int = 0, n_sel: int = 0, window: int = 0,
-                 w_gate: Optional[torch.Tensor] = None, scale: Optional[float] = None, out_dtype=None):
+                 w_gate: Optional[torch.Tensor] = None, scale: Optional[float] = None, out_dtype=None,
+                 proj_w: Optional[torch.Tensor] = None, proj_b: Optional[torch.Tensor] = None,
+                 smooth_k: bool = False):
         self.q, self.k, self.v = q, k, v
         self.n_valid = n_valid
         self.mode = mode
@@ -64,6 +70,15 @@ class SlaForward:
         else:
             raise ValueError(f"unknown mode {mode}")
         self.w_gate = None if w_gate is None else w_gate.to(device=q.device, dtype=torch.float32).contiguous()
+        if (proj_w is not None or proj_b is not None) and mode != "sla":
+            raise ValueError("proj_w / proj_b apply to the sla mode's linear branch")
+        if proj_w is None and proj_b is not None:
+            raise ValueError("proj_b needs proj_w")
+        as32 = lambda x: None if x is None else x.to(device=q.device, dtype=torch.float32).contiguous()
+        self.proj_w, self.proj_b = as32(proj_w), as32(proj_b)
+        if smooth_k and mode == "nsa":
+            raise ValueError("smooth_k applies to a linear branch (sla or salad mode)")
+        self.smooth_k = smooth_k
         dev = q.device
         f = dict(device=dev, dtype=torch.float32)
         Hs = Hkv if self.group else Hq
@@ -80,6 +95,7 @@ class SlaForward:
             ws = sla_kv_reduce_workspace_bytes(B, Hkv, N, d, False, True)
             self.kv = dict(H_all=torch.empty((B, Hkv, d, d), **f), z_all=torch.empty((B, Hkv, d), **f),
                            workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
+        self.k_mean = torch.empty((B, Hkv, d), **f) if smooth_k else None
         self.row_states = None
         if self.lin == SLA_LIN_MARGINAL:
             # per-row marginal sums, filled by sla_marginal_states before the attention call
@@ -96,8 +112,11 @@ class SlaForward:
                              window=self.window, out=self.maps)
 
     def kv_reduce(self):
+        """Linear-branch key states (after pool_scores when smooth_k: the shift comes from k_pool)."""
         if self.lin != SLA_LIN_NONE:
-            sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv)
+            if self.smooth_k:
+                sla_key_mean(self.pool["k_pool"], self.n_valid, out=self.k_mean)
+            sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv, k_shift=self.k_mean)
         return self.kv
 
     def marginal_states(self, maps=None):
@@ -113,7 +132,8 @@ class SlaForward:
         if self.lin == SLA_LIN_MARGINAL:
             S, u = self.row_states
             return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps,
-                                lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out)
+                                lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out,
+                                proj_w=self.proj_w, proj_b=self.proj_b)
         return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
                             scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
                             H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out)

@@ -48,14 +48,15 @@ _SIGS = {
     "sla_block_map": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                 _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, _P, c_size_t, _P]),
     "sla_kv_reduce_workspace_bytes": (c_size_t, [c_int32] * 6),
-    "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P,
+    "sla_key_mean": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, _P, _P]),
+    "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P, _P,
                                        c_size_t, _P]),
     "sla_marginal_states": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                       _P, _P, _P, _P]),
     "sla_attn_workspace_bytes": (c_size_t, [c_int32] * 5),
     "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
-                               c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P, _P,
-                               c_int32, _P, c_size_t, _P]),
+                               c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P,
+                               _P, _P, c_int32, _P, c_int32, _P, c_size_t, _P]),
 }
 
 
@@ -196,9 +197,25 @@ def sla_block_map(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=Tr
     return out
 
 
-def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None):
-    """Returns dict(H, z[, H_all, z_all]): per-block states H in bf16, everything else fp32."""
+def sla_key_mean(k_pool, n_valid, out=None):
+    """Smooth-K shift [B, Hkv, d] fp32: the mean of the valid key rows, from the block means k_pool."""
+    _require_gpu(k_pool)
+    B, Hkv, nb, d = k_pool.shape
+    if out is None:
+        out = torch.empty((B, Hkv, d), device=k_pool.device, dtype=torch.float32)
+    _check("sla_key_mean", lib().sla_key_mean(_ptr(k_pool), B, Hkv, nb, d, n_valid, _ptr(out),
+                                              _stream(k_pool.device)))
+    return out
+
+
+def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None, k_shift=None):
+    """Returns dict(H, z[, H_all, z_all]): per-block states H in bf16, everything else fp32.
+
+    k_shift [B, Hkv, d] fp32 (smooth-K, e.g. from sla_key_mean): states of phi(K - k_shift).
+    """
     _require_gpu(k, v)
+    if k_shift is not None and (k_shift.dtype != torch.float32 or not k_shift.is_contiguous()):
+        raise ValueError("k_shift must be a contiguous float32 [B, Hkv, d] tensor")
     B, Hkv, N, d = k.shape
     nb = N // BLOCK
     if out is None:
@@ -215,7 +232,7 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
         out["workspace_bytes"] = ws
     kd, vd = tensor_desc(k), tensor_desc(v)
     _check("sla_linear_kv_reduce", lib().sla_linear_kv_reduce(
-        ctypes.byref(kd), ctypes.byref(vd), n_valid, _ptr(out.get("H")), _ptr(out.get("z")),
+        ctypes.byref(kd), ctypes.byref(vd), n_valid, _ptr(k_shift), _ptr(out.get("H")), _ptr(out.get("z")),
         _ptr(out.get("H_all")), _ptr(out.get("z_all")), _ptr(out.get("workspace")), out.get("workspace_bytes", 0),
         _stream(k.device)))
     return out
@@ -242,10 +259,22 @@ def sla_marginal_states(H, z, Hq, group_map, marg_bits, out=None):
 
 def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, causal=False, window=0,
                  group_map=False, H=None, z=None, H_all=None, z_all=None, w_gate=None, out=None,
-                 out_dtype=None, workspace=None):
-    """Attention output [B, Hq, N, d]; `maps` is the dict returned by sla_block_map."""
+                 out_dtype=None, workspace=None, proj_w=None, proj_b=None):
+    """Attention output [B, Hq, N, d]; `maps` is the dict returned by sla_block_map.
+
+    proj_w [d, d] or [Hq, d, d] fp32 (out x in) and proj_b [d] or [Hq, d]: the learned
+    projection of the SLA linear branch (None = identity).
+    """
     _require_gpu(q, k, v)
     B, Hq, N, d = q.shape
+    proj_heads = 0
+    if proj_w is not None:
+        if proj_w.dtype != torch.float32 or not proj_w.is_contiguous() or proj_w.shape[-2:] != (d, d):
+            raise ValueError("proj_w must be a contiguous float32 [d, d] or [Hq, d, d] tensor")
+        proj_heads = 1 if proj_w.dim() == 2 else proj_w.shape[0]
+        if proj_b is not None and (proj_b.dtype != torch.float32 or not proj_b.is_contiguous()
+                                   or proj_b.numel() != proj_heads * d):
+            raise ValueError("proj_b must be a contiguous float32 tensor with one d-vector per weight")
     scale = (1.0 / d ** 0.5) if scale is None else scale
     if out is None:
         out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
@@ -259,5 +288,6 @@ def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, caus
         ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), n_valid, float(scale), int(causal), window,
         int(group_map), _ptr(maps["crit_rowptr"]), _ptr(maps["crit_idx"]), _ptr(maps.get("crit_flags")),
         _ptr(maps.get("marg_bits")), lin_mode, _ptr(H), _ptr(z), _ptr(H_all),
-        _ptr(z_all), _ptr(w_gate), _ptr(out), odt, _ptr(workspace), ws_bytes, _stream(q.device)))
+        _ptr(z_all), _ptr(w_gate), _ptr(proj_w), _ptr(proj_b), proj_heads, _ptr(out), odt, _ptr(workspace),
+        ws_bytes, _stream(q.device)))
     return out

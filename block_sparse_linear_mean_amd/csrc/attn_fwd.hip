@@ -4,25 +4,26 @@
 // Method: critical (query block, key block) pairs get exact softmax attention, i.e.
 // FlashAttention restricted to the listed blocks, and marginal pairs linear attention;
 // the outputs are summed (SLA analysis page for arXiv 2509.24006: FlashAttn + linear
-// attention per block pair, O = O_s + Proj(O_l) with Proj zero-initialised and here
-// the identity).  SALAD gates a linear branch over all keys by an input-dependent
-// gate (SALAD page, method framework).  The NSA-style variant attends to selected
-// blocks plus a sliding window under a causal mask, and the query heads of a GQA
-// group share the selection ("Sparse Attention 方法综述", section 2 NSA).
+// attention per block pair, O = O_s + Proj(O_l) with Proj a learned, zero-initialised
+// layer: the identity unless a weight is passed).  SALAD gates a linear branch over all
+// keys by an input-dependent gate (SALAD page, method framework).  The NSA-style variant
+// attends to selected blocks plus a sliding window under a causal mask, and the query
+// heads of a GQA group share the selection ("Sparse Attention 方法综述", section 2 NSA).
 //
-// Design (gfx950, wave64, 16x16x32 bf16 matrix cores):
-//  * one workgroup = one 64-row query block of one head, 4 wavefronts x 16 query rows;
+// Design (gfx950, wave64, 32x32x16 bf16 matrix cores):
+//  * one workgroup = one 64-row query block of one head (2 wavefronts x 32 query rows),
+//    or of four heads of a GQA group that share the block map (8 wavefronts);
 //  * the query fragment stays in registers for the whole block list;
-//  * per critical key block, K is staged in LDS row-major and V transposed
-//    ([feature][token]); scores are computed transposed (S^T = K Q^T), so each lane
-//    owns one query column and 16 keys: the row max needs two cross-lane steps and
-//    the online-softmax rescale of the (transposed) output accumulators is per lane;
-//  * P^T feeds the P.V product directly from registers: the 32-key contraction uses a
-//    fixed permutation of keys that matches how the S^T tiles sit in the lanes, and
-//    V^T is read from LDS in the same permuted order (two 8-byte reads per operand);
+//  * per critical key block, K and V tiles are copied global -> LDS by the direct-to-LDS
+//    loads; scores are computed transposed (S^T = K Q^T), so each lane owns one query
+//    column: the row max and sum need one half-wave swap, and the online-softmax
+//    rescale of the (transposed) output accumulators is per lane;
+//  * P^T feeds the P.V product directly from registers, V^T comes from the transposing
+//    LDS read;
 //  * exp2 with scale*log2(e) folded in; fp32 running max / sum / accumulators;
 //  * epilogue: 1/l normalisation, then the linear term phi(q)^T S / (phi(q) . u)
-//    as one more matrix-core product against S^T staged in LDS as bf16.
+//    as one more matrix-core product against S^T staged in LDS as bf16, and, with a
+//    projection, one more product against the staged weight.
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -46,6 +47,9 @@ struct AttnParams {
   const void* S;        // SLA: per map row d x d bf16 [c][r]; SALAD: per KV head H_all fp32 [c][r]
   const float* u;       // SLA: per map row d;              SALAD: per KV head z_all
   const float* w_gate;  // SALAD: [Hq][d]
+  const float* proj_w;  // SLA: Proj weight [heads][d (out)][d (in)] fp32, or null (identity)
+  const float* proj_b;  // SLA: Proj bias [heads][d] fp32, or null
+  int64_t proj_sH;      // elements between the weights of consecutive heads (0: one shared weight)
   void* out;
   int out_f32;
 };
@@ -163,7 +167,7 @@ __device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg) {
 // online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
 // transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU): the next
 // K block streams into LDS during softmax and P.V, the next V block during the next S^T.
-template <typename T, int D, bool CAUSAL, int LIN, int NW>
+template <typename T, int D, bool CAUSAL, int LIN, int NW, bool PROJ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
   using Tl = AttnTile<D>;
   constexpr int kQs = D / 16;      // 16-wide feature steps of the Q.K contraction
@@ -430,18 +434,70 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       gdot = xor32_sum(gdot);
       scale_lin *= 1.f / (1.f + __expf(-gdot));
     }
+    bf16x8 lb[PROJ ? kQs : 1];    // Proj: O_l^T as B operands
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt) {
-      f32x16 num;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) num[e] = 0.f;
+      f32x16 num = f32x16{};
       const int row = 32 * dt + l32;                 // c
 #pragma unroll
       for (int ks = 0; ks < kQs; ++ks) {
         const bf16x8 a = lds_load16(st_tile(row) + k_pos<D>(row % kBlock, 2 * ks + lg));
         num = mfma32(a, pq[ks], num);
       }
-      oacc[dt] += num * scale_lin;
+      if constexpr (!PROJ) {
+        oacc[dt] += num * scale_lin;
+      } else {
+        // Proj(O_l)^T = W O_l^T + b with O_l^T as the B operand.  For k-step ks the lane needs
+        // O_l[tq][16 ks + 8 lg .. + 7]; it holds features 16 ks + 4 lg + {0..3} and
+        // 16 ks + 8 + 4 lg + {0..3} (elements 8 (ks % 2) + {0..3, 4..7} of this dt's tile, dt =
+        // ks / 2), so one half-wave swap per register pair trades the lower half-wave's second
+        // group for the upper half-wave's first.
+        num *= scale_lin;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 x;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(num[8 * h2 + m]),
+                                                            __float_as_uint(num[8 * h2 + 4 + m]), false, false);
+            x[m] = __uint_as_float(r[0]);
+            x[4 + m] = __uint_as_float(r[1]);
+          }
+          lb[2 * dt + h2] = cvt8(x);
+        }
+      }
+    }
+    if constexpr (PROJ) {
+      // every wavefront has read S^T; stage W [o][c] (bf16, K layout) over the same buffers
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      const float* Wg = p.proj_w + int64_t(h) * p.proj_sH;
+      for (int e = t; e < D * Tl::kChunks; e += kThreads) {
+        const int r = e / Tl::kChunks, c = e % Tl::kChunks;
+        lds_store16(st_tile(r) + k_pos<D>(r % kBlock, c), In<float>::load8(Wg + r * D + 8 * c));
+      }
+      if (p.proj_b != nullptr) {
+        // lane holds output features 32 dt + 8 q4 + 4 lg + {0..3} in oacc[dt][4 q4 .. 4 q4 + 3]
+        const float* bias = p.proj_b + int64_t(h) * (p.proj_sH != 0 ? D : 0);
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(bias + 32 * dt + 8 * q4 + 4 * lg);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) oacc[dt][4 * q4 + m] += bb[m];
+          }
+      }
+      SLA_WAIT_VMCNT(0);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        const int row = 32 * dt + l32;               // output feature o
+#pragma unroll
+        for (int ks = 0; ks < kQs; ++ks)
+          oacc[dt] = mfma32(lds_load16(st_tile(row) + k_pos<D>(row % kBlock, 2 * ks + lg)), lb[ks], oacc[dt]);
+      }
     }
   }
 
@@ -470,7 +526,8 @@ static void launch_attn(const AttnParams& p, int causal, int lin, int hg, dim3 g
   } else if (causal) {
     attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
-    attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2><<<grid, 128, 0, st>>>(p);
+    if (p.proj_w != nullptr) attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2, true><<<grid, 128, 0, st>>>(p);
+    else attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_GLOBAL_GATED) {
     attn_fwd_kernel<T, D, false, SLA_LIN_GLOBAL_GATED, 2><<<grid, 128, 0, st>>>(p);
   } else {
@@ -485,7 +542,8 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
                                    const int32_t* crit_rowptr, const int32_t* crit_idx, const uint8_t* crit_flags,
                                    const uint32_t* marg_bits, int32_t lin_mode,
                                    const void* H, const float* z, const float* H_all, const float* z_all,
-                                   const float* w_gate, void* out, int32_t out_dtype, void* workspace,
+                                   const float* w_gate, const float* proj_w, const float* proj_b,
+                                   int32_t proj_heads, void* out, int32_t out_dtype, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(q);
@@ -501,6 +559,12 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   if (lin_mode < SLA_LIN_NONE || lin_mode > SLA_LIN_ROW_STATES) return SLA_ERR_UNSUPPORTED;
   if (causal && lin_mode != SLA_LIN_NONE) return SLA_ERR_UNSUPPORTED;
   if (causal && crit_flags == nullptr) return SLA_ERR_NULL;
+  if (proj_w == nullptr && proj_b != nullptr) return SLA_ERR_NULL;
+  if (proj_w != nullptr) {
+    if (lin_mode != SLA_LIN_MARGINAL && lin_mode != SLA_LIN_ROW_STATES) return SLA_ERR_UNSUPPORTED;
+    if (proj_heads != 1 && proj_heads != q->H) return SLA_ERR_SHAPE;
+    if (!aligned16(proj_w) || (proj_b != nullptr && !aligned16(proj_b))) return SLA_ERR_ALIGN;
+  }
   const int d = q->d, nqb = q->N / kBlock;
   const int Hs = group_map ? k->H : q->H;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -515,6 +579,8 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   p.scale_log2 = scale * 1.4426950408889634f;
   p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx; p.crit_flags = crit_flags;
   p.out = out; p.out_f32 = out_dtype == SLA_F32;
+  p.proj_w = proj_w; p.proj_b = proj_b;
+  p.proj_sH = (proj_w != nullptr && proj_heads != 1) ? int64_t(q->d) * q->d : 0;
 
   if (lin_mode == SLA_LIN_MARGINAL) {
     if (H == nullptr || z == nullptr || marg_bits == nullptr) return SLA_ERR_NULL;

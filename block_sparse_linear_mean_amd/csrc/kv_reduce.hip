@@ -75,8 +75,9 @@ struct KvPiece {
       for (int i = 0; i < 4; ++i) { out[i] = x[0][i]; out[4 + i] = x[1][i]; }
     }
   }
-  // phi(K) rounded to bf16 and V (zero for padded rows), into trs-layout tiles
-  __device__ __forceinline__ void store(lds_u8* kt, lds_u8* vt) const {
+  // phi(K - shift) rounded to bf16 and V (zero for padded rows), into trs-layout tiles.  A
+  // thread's pieces all cover features 8 (t % kChunks) .. + 7, the 8 entries of `shift`.
+  __device__ __forceinline__ void store(lds_u8* kt, lds_u8* vt, const float* shift) const {
 #pragma unroll
     for (int n = 0; n < kPer; ++n) {
       const int e = threadIdx.x + 256 * n;
@@ -85,7 +86,7 @@ struct KvPiece {
       unpack(k[n], kf);
       f32x8 f;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) f[m] = phi(kf[m]);
+      for (int m = 0; m < 8; ++m) f[m] = phi(kf[m] - shift[m]);
       bf16x8 vb;
       if constexpr (sizeof(T) == 2) {
         vb = __builtin_bit_cast(bf16x8, v[n][0]);
@@ -107,7 +108,8 @@ template <typename T, int D, bool PER_BLOCK>
 __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, int64_t ksB, int64_t ksH,
                                                        int64_t ksN, const T* __restrict__ v, int64_t vsB,
                                                        int64_t vsH, int64_t vsN, int Hkv, int nb, int n_valid,
-                                                       int cb, u16* __restrict__ Hb, float* __restrict__ Hf,
+                                                       int cb, const float* __restrict__ kshift,
+                                                       u16* __restrict__ Hb, float* __restrict__ Hf,
                                                        float* __restrict__ zout) {
   constexpr int RB = 2 * D;
   constexpr int kCt = D == 128 ? 4 : 1;          // 32-column tiles of c per wavefront
@@ -121,6 +123,10 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   const T* K = k + int64_t(b) * ksB + int64_t(g) * ksH;
   const T* V = v + int64_t(b) * vsB + int64_t(g) * vsH;
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
+  static_assert(256 % kChunks == 0, "a thread's K pieces share one 8-feature chunk");
+  float shift[8];                                // smooth-K: this thread's 8 features of the key mean
+#pragma unroll
+  for (int m = 0; m < 8; ++m) shift[m] = kshift != nullptr ? kshift[int64_t(bg) * D + 8 * (t % kChunks) + m] : 0.f;
   const int rt = D == 128 ? w : w % 2;           // r rows 32 rt .. 32 rt + 31
   const int ct0 = D == 128 ? 0 : w / 2;          // first c tile
   const bool z_owner = D == 128 || w < 2;
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   if (j0 < j1) pc.load(K, ksN, V, vsN, j0, n_valid);
   for (int j = j0; j < j1; ++j) {
     __syncthreads();                    // the previous block's operands (and staged state) have been read
-    pc.store(Kt, Vt);
+    pc.store(Kt, Vt, shift);
     __syncthreads();
     if (j + 1 < j1) pc.load(K, ksN, V, vsN, j + 1, n_valid);
 #pragma unroll
@@ -228,15 +234,15 @@ __global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict
 }
 
 template <typename T>
-static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int cb, int nch, u16* Hb, float* Hf,
-                      float* z, hipStream_t st) {
+static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int cb, int nch, const float* kshift,
+                      u16* Hb, float* Hf, float* z, hipStream_t st) {
   const int nb = k->N / kBlock;
   dim3 grid(nch, k->B * k->H);
   const T* kp = static_cast<const T*>(k->ptr);
   const T* vp = static_cast<const T*>(v->ptr);
 #define SLA_KV_LAUNCH(DD, PB)                                                                                    \
   kv_state_kernel<T, DD, PB><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, nb, \
-                                                   n_valid, cb, Hb, Hf, z)
+                                                   n_valid, cb, kshift, Hb, Hf, z)
   if (k->d == 128) {
     if (Hb != nullptr) SLA_KV_LAUNCH(128, true);
     else SLA_KV_LAUNCH(128, false);
@@ -254,9 +260,9 @@ static void launch_sum(const float* in, int parts, int64_t len, int bgs, float* 
 
 }  // namespace sla
 
-extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid, void* H,
-                                           float* z, float* H_all, float* z_all, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
+extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
+                                           const float* k_shift, void* H, float* z, float* H_all, float* z_all,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(k);
   if (st != SLA_OK) return st;
@@ -267,6 +273,7 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
   if ((H == nullptr) != (z == nullptr) || (H_all == nullptr) != (z_all == nullptr)) return SLA_ERR_NULL;
   if ((H != nullptr && (!aligned16(H) || !aligned16(z))) || (H_all != nullptr && (!aligned16(H_all) || !aligned16(z_all))))
     return SLA_ERR_ALIGN;
+  if (k_shift != nullptr && !aligned16(k_shift)) return SLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = k->N / kBlock;
   const int d = k->d;
@@ -280,8 +287,8 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     const int nch = (nb + cb - 1) / cb;
     float* Hp = static_cast<float*>(workspace);
     float* zp = Hp + int64_t(bgs) * nch * d * d;
-    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, nullptr, Hp, zp, s);
-    else launch_kv<float>(k, v, n_valid, cb, nch, nullptr, Hp, zp, s);
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, s);
     launch_sum(Hp, nch, int64_t(d) * d, bgs, H_all, s);
     launch_sum(zp, nch, d, bgs, z_all, s);
   }
@@ -289,8 +296,8 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     // runs of a few blocks per workgroup (one block of prefetch), at least ~2048 workgroups
     const int cb = std::max(1, std::min(4, nb * bgs / 2048));
     const int nch = (nb + cb - 1) / cb;
-    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, static_cast<u16*>(H), nullptr, z, s);
-    else launch_kv<float>(k, v, n_valid, cb, nch, static_cast<u16*>(H), nullptr, z, s);
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, s);
   }
   return launch_status();
 }

@@ -230,3 +230,54 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if (probs != nullptr) probs_kernel<<<dim3(q->B * Hs * nb), 64, 0, s>>>(scores, nb, probs);
   return launch_status();
 }
+
+namespace sla {
+
+// Smooth-K shift of one (batch, KV head): the mean of its valid key rows, taken from the block
+// means, mu[r] = sum_j c_j kpool[j][r] / n_valid with c_j the valid rows of block j (SLA analysis
+// page: the open-source code zero-means K).  One workgroup per (8 features, head); each thread
+// sums a strided set of blocks in fp64, then a fixed-order LDS tree; one rounding to fp32.
+__global__ __launch_bounds__(256) void key_mean_kernel(const float* __restrict__ kpool, int nb, int d,
+                                                       int n_valid, float* __restrict__ mu) {
+  const int bg = blockIdx.y, r0 = 8 * blockIdx.x, t = threadIdx.x;
+  double s[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) s[m] = 0.0;
+  for (int j = t; j < nb; j += 256) {
+    const double c = double(min(kBlock, n_valid - kBlock * j));    // >= 1: at most one partial block
+    const float* p = kpool + (int64_t(bg) * nb + j) * d + r0;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s[m] += c * double(a[m]);
+      s[4 + m] += c * double(b[m]);
+    }
+  }
+  __shared__ double red[256][9];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) red[t][m] = s[m];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) red[t][m] += red[t + w][m];
+    }
+    __syncthreads();
+  }
+  if (t < 8) mu[int64_t(bg) * d + r0 + t] = float(red[0][t] / double(n_valid));
+}
+
+}  // namespace sla
+
+extern "C" sla_status sla_key_mean(const float* k_pool, int32_t B, int32_t Hkv, int32_t nkb, int32_t d,
+                                   int32_t n_valid, float* k_mean, void* stream) {
+  using namespace sla;
+  if (k_pool == nullptr || k_mean == nullptr) return SLA_ERR_NULL;
+  if (B < 1 || Hkv < 1 || nkb < 1 || nkb > (1 << 24) || (d != 64 && d != 128)) return SLA_ERR_SHAPE;
+  sla_status st = check_valid_len(n_valid, nkb * kBlock);
+  if (st != SLA_OK) return st;
+  if (!aligned16(k_pool) || !aligned16(k_mean)) return SLA_ERR_ALIGN;
+  key_mean_kernel<<<dim3(d / 8, B * Hkv), 256, 0, static_cast<hipStream_t>(stream)>>>(k_pool, nkb, d, n_valid,
+                                                                                       k_mean);
+  return launch_status();
+}

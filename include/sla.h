@@ -11,8 +11,10 @@
  *                linear attention with phi = elu + 1 through per-key-block
  *                states H_j = phi(K_j)^T V_j and z_j = sum phi(K_j),
  *                negligible pairs are skipped;
- *   4. combine:  O = O_sparse + O_linear (the learned projection on the linear
- *                branch is the identity here).
+ *   4. combine:  O = O_sparse + Proj(O_linear), Proj a learned linear layer on
+ *                the linear branch (the identity unless a weight is passed).
+ * Smooth-K (the open-source code's zero-mean K, SLA analysis page) is available
+ * for the linear branch: sla_key_mean, then sla_linear_kv_reduce with k_shift.
  * Variants: the SALAD gated linear branch over all keys (SALAD page, method
  * framework) and an NSA-style selected-block + sliding-window causal branch
  * whose block selection is shared by a GQA group ("Sparse Attention 方法综述",
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SLA_ABI_VERSION 1
+#define SLA_ABI_VERSION 2
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
 #define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
@@ -121,6 +123,18 @@ sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_v
                            float* q_pool, float* k_pool, float* scores, float* probs, void* stream);
 
 /*
+ * Smooth-K shift (SLA analysis page: the open-source code zero-means K, which the paper
+ * does not mention): the mean of the valid key rows of each (batch, KV head),
+ *   k_mean[b,g,r] = sum_j c_j * k_pool[b,g,j,r] / n_valid      (fp32, [B, Hkv, d])
+ * with c_j = min(64, n_valid - 64 j) the valid rows of key block j, from the block means
+ * k_pool [B, Hkv, nkb, d] that sla_pool_scores writes; summed in fp64, rounded once.
+ * nkb * 64 - 64 < n_valid <= nkb * 64; d is 64 or 128; both pointers 16-byte aligned.
+ * workspace: none.
+ */
+sla_status sla_key_mean(const float* k_pool, int32_t B, int32_t Hkv, int32_t nkb, int32_t d,
+                        int32_t n_valid, float* k_mean, void* stream);
+
+/*
  * Number of block-map index entries to allocate for `rows` rows (rows = B * Hs * nqb).
  * which = 0: critical (selected) list, which = 1: marginal list.  Non-causal maps are
  * exact (rows * n_crit and rows * (nkb - n_crit - n_negl)); causal maps return an upper
@@ -178,13 +192,15 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
  *   z[b,g,j,r]   = sum_s phi(K[s,r])            (fp32, [B, Hkv, nb, d];     nullable with H)
  *   H_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d, d], same [c][r] layout; nullable)
  *   z_all[b,g]   = sum over all valid s          (fp32, [B, Hkv, d];        nullable with H_all)
+ * k_shift (nullable, fp32 [B, Hkv, d], 16-byte aligned; smooth-K, normally from
+ * sla_key_mean): when given, every phi(K[s,r]) above is phi(K[s,r] - k_shift[b,g,r]).
  * phi(K) is rounded to bf16 for the matrix-core contraction (fp32 accumulation); z sums
  * the same rounded values.  At least one of H, H_all must be non-NULL; outputs are 16-byte
  * aligned.  H_all needs a workspace of sla_kv_reduce_workspace_bytes(..., 1) bytes (fp32
  * partial sums over runs of 32 key blocks, then summed in a fixed order).
  */
 sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
-                                void* H, float* z, float* H_all, float* z_all,
+                                const float* k_shift, void* H, float* z, float* H_all, float* z_all,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -211,7 +227,7 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  * Attention step: exact block-sparse softmax attention over each query block's
  * critical list (FlashAttention-style online softmax; SLA analysis page, the
  * FlashAttn + linear attention pairing) plus the linear branch, summed
- * (O = O_sparse + O_linear, projection = identity).
+ * (O = O_sparse + Proj(O_linear); SLA analysis page, the zero-initialised Proj).
  *
  * For query row t of head h in block i, map row r = (b * Hs + s) * nqb + i with
  * s = h / (Hq/Hkv) if group_map else h, KV head g = h / (Hq/Hkv):
@@ -227,6 +243,12 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  *     for this map; marg_bits is not read and no workspace is needed.
  *   lin_mode SLA_LIN_GLOBAL_GATED (needs H_all, z_all, w_gate [Hq][d] fp32):
  *     O_linear[t] = sigmoid(q_t . w_gate[h]) * phi(q_t)^T H_all / (phi(q_t) . z_all).
+ *   Proj (MARGINAL and ROW_STATES only; proj_w NULL = identity, then proj_b must be NULL):
+ *     Proj(x) = W_h x + b_h on each valid row, W_h = proj_w[h'] a fp32 [d (out)][d (in)]
+ *     row-major matrix and b_h = proj_b[h'] (nullable) fp32 [d], h' = 0 when
+ *     proj_heads == 1 (one weight for all heads) and h' = h when proj_heads == Hq.  It
+ *     applies to rows with no marginal block too (O_linear = 0 there, so they get b_h).
+ *     O_linear and W are rounded to bf16 for the matrix-core product (fp32 accumulation).
  *   Rows t >= n_valid are written as 0.
  * q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; all the same dtype.  out: contiguous
  * [B, Hq, N, d] in out_dtype (SLA_BF16 or SLA_F32).  The linear branch needs causal == 0.
@@ -240,6 +262,7 @@ sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         const uint32_t* marg_bits,
                         int32_t lin_mode, const void* H, const float* z,
                         const float* H_all, const float* z_all, const float* w_gate,
+                        const float* proj_w, const float* proj_b, int32_t proj_heads,
                         void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
 

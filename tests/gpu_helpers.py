@@ -11,7 +11,7 @@ import torch
 
 import block_sparse_linear_mean_amd as sla
 from oracle import sla_oracle as orc
-from workloads import BLOCK
+from workloads import BLOCK, make_inputs
 
 REL_L2 = 1e-2      # output tolerance, bf16 I/O with fp32 accumulation
 MAX_ABS = 3e-2
@@ -37,6 +37,20 @@ def oracle_for(w, q, k, v, wg):
 def layer_for(w, q, k, v, wg):
     return sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp,
                           n_sel=w.n_sel, window=w.window, w_gate=wg)
+
+
+def make_case(w, proj_w=None, proj_b=None, smooth_k=False):
+    """Seeded inputs of workload w, the oracle Forward and the library layer, both with the given
+    Proj weights (float32 numpy) and smooth-K setting."""
+    q, k, v, wg = make_inputs(w)
+    f = orc.Forward(host(q), host(k), host(v), n_valid=w.Nv, mode=w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp,
+                    n_sel=w.n_sel, window=w.window, w_gate=None if wg is None else wg.numpy(),
+                    proj_w=proj_w, proj_b=proj_b, smooth_k=smooth_k)
+    t = lambda x: None if x is None else torch.as_tensor(x)
+    layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp,
+                           n_sel=w.n_sel, window=w.window, w_gate=wg, proj_w=t(proj_w), proj_b=t(proj_b),
+                           smooth_k=smooth_k)
+    return q, k, v, wg, f, layer
 
 
 def gpu_map_rows(maps, rows_idx):

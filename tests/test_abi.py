@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert sla.sla_abi_version() == 1
+    assert sla.sla_abi_version() == 2
     for s in range(9):
         assert len(sla.sla_status_str(s)) > 0
     assert sla.sla_status_str(12345) == "unknown status"
@@ -130,8 +130,8 @@ def test_block_map_validation(L):
 
 def test_kv_reduce_validation(L):
     k = desc()
-    def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0):
-        return L.sla_linear_kv_reduce(ctypes.byref(kk), ctypes.byref(vv), nv, H, z, Ha, za, ws, wsb, None)
+    def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0, shift=None):
+        return L.sla_linear_kv_reduce(ctypes.byref(kk), ctypes.byref(vv), nv, shift, H, z, Ha, za, ws, wsb, None)
     assert call(H=None, z=None) == ENULL
     assert call(z=None) == ENULL
     assert call(Ha=P, za=None) == ENULL
@@ -139,6 +139,19 @@ def test_kv_reduce_validation(L):
     assert call(vv=desc(dtype=1)) == ESHAPE
     assert call(nv=0) == ERANGE
     assert call(H=None, z=None, Ha=P, za=P) == EWS
+    assert call(shift=ctypes.c_void_p(0x20004)) == EALIGN
+
+
+def test_key_mean_validation(L):
+    def call(kp=P, B=1, Hkv=2, nkb=4, d=128, nv=256, out=P):
+        return L.sla_key_mean(kp, B, Hkv, nkb, d, nv, out, None)
+    assert call(kp=None) == ENULL
+    assert call(out=None) == ENULL
+    assert call(d=96) == ESHAPE
+    assert call(nkb=0) == ESHAPE
+    assert call(nv=192) == ERANGE
+    assert call(nv=257) == ERANGE
+    assert call(out=ctypes.c_void_p(0x20004)) == EALIGN
 
 
 def test_marginal_states_validation(L):
@@ -154,9 +167,10 @@ def test_marginal_states_validation(L):
 def test_attn_fwd_validation(L):
     q = desc()
     def call(qq=q, kk=q, vv=q, nv=256, scale=0.1, causal=0, win=0, group=0, crp=P, ci=P, cf=None, mb=None,
-             lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0):
+             lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0, pw=None, pb=None,
+             ph=0):
         return L.sla_attn_fwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), nv, scale, causal, win, group,
-                              crp, ci, cf, mb, lin, H, z, Ha, za, wg, out, odt, ws, wsb, None)
+                              crp, ci, cf, mb, lin, H, z, Ha, za, wg, pw, pb, ph, out, odt, ws, wsb, None)
     assert call(out=None) == ENULL
     assert call(crp=None) == ENULL
     assert call(causal=1) == ENULL                   # causal needs the flags
@@ -173,3 +187,7 @@ def test_attn_fwd_validation(L):
     assert call(vv=desc(H=1)) == ESHAPE
     assert call(win=-1) == ERANGE
     assert call(nv=64) == ERANGE
+    assert call(pb=P) == ENULL                       # a Proj bias needs the weight
+    assert call(pw=P, ph=1) == EUNSUP                # Proj is for the SLA linear branch only
+    assert call(lin=3, H=P, z=P, pw=P, ph=3) == ESHAPE
+    assert call(lin=3, H=P, z=P, pw=ctypes.c_void_p(0x20004), ph=1) == EALIGN
