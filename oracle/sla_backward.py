@@ -1,0 +1,108 @@
+"""CPU oracle for the gradients of the SLA forward (dQ, dK, dV).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call this module.  The product path never calls it.
+
+The pages train SLA by fine-tuning (SLA analysis page for arXiv 2509.24006: the
+Proj layer and the linear path need fine-tuning), so the layer needs its
+backward; the pages print no backward, so this oracle takes the plainest one:
+the exact gradient of the forward the pages define, through both branches,
+obtained by automatic differentiation of that forward written out in float64
+torch operations.
+
+Readings (also listed in the design notes):
+  * the block map is a piecewise-constant function of Q and K (it changes only
+    where two pooled scores swap order), so it is held fixed: the gradient flows
+    through the critical softmax branch and the marginal linear branch only,
+    never through pooling, scores or classification;
+  * Proj (when given) is part of the forward, so dQ, dK, dV see it; the
+    gradients of the Proj weight itself are not part of this oracle;
+  * padded positions (>= n_valid) get zero gradient;
+  * smooth-K is off.
+
+The forward here restates the numpy oracle's steps with masks: a query row
+attends with one softmax to the keys of its critical blocks (s < n_valid), and
+gets the linear term phi(q)^T (sum of H_j) / (phi(q) . sum of z_j) over its
+marginal blocks j, with H_j = phi(K_j)^T V_j and z_j = sum phi(K_j) over the
+valid rows of block j.  Its output is checked against the numpy oracle, and its
+gradients against central finite differences of the numpy oracle.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+BLOCK = 64
+
+
+def _phi(x: torch.Tensor) -> torch.Tensor:
+    """elu + 1, written by cases (x + 1 above zero, exp(x) otherwise)."""
+    return torch.where(x > 0, x + 1.0, torch.exp(torch.clamp(x, max=0.0)))
+
+
+def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, proj_b=None) -> torch.Tensor:
+    """SLA output [B, H, N, d] for a fixed block map, in float64 torch ops (differentiable).
+
+    Q, K, V: float64 tensors [B, H, N, d] (one KV head per query head).
+    maps[(b, h, i)]: dict with the ascending lists "crit" and "marg" of query block i of head h.
+    """
+    B, H, N, d = Q.shape
+    nb = N // BLOCK
+    tok = torch.arange(N)
+    valid_k = tok < n_valid
+    rows = []
+    for b in range(B):
+        heads = []
+        for h in range(H):
+            q, k, v = Q[b, h], K[b, h], V[b, h]
+            pk = _phi(k) * valid_k[:, None]                       # padded keys contribute nothing
+            blocks_out = []
+            for i in range(nb):
+                m = maps[(b, h, i)]
+                qi = q[BLOCK * i:BLOCK * (i + 1)]
+                # sparse branch: one softmax over the keys of the critical blocks
+                allowed = torch.zeros(N, dtype=torch.bool)
+                for j in m["crit"]:
+                    allowed[BLOCK * j:BLOCK * (j + 1)] = True
+                allowed &= valid_k
+                if allowed.any():
+                    x = (qi @ k[allowed].T) * scale
+                    p = torch.softmax(x, dim=1)
+                    o = p @ v[allowed]
+                else:
+                    o = torch.zeros_like(qi)
+                # linear branch over the marginal blocks
+                if m["marg"]:
+                    sel = torch.zeros(N, dtype=torch.bool)
+                    for j in m["marg"]:
+                        sel[BLOCK * j:BLOCK * (j + 1)] = True
+                    Hs = pk[sel].T @ v[sel]                           # sum of H_j, [d, d]
+                    zs = pk[sel].sum(dim=0)                           # sum of z_j, [d]
+                    pq = _phi(qi)
+                    ol = (pq @ Hs) / (pq @ zs)[:, None]
+                else:
+                    ol = torch.zeros_like(qi)
+                if proj_w is not None:
+                    W = proj_w[h] if proj_w.dim() == 3 else proj_w
+                    ol = ol @ W.T
+                    if proj_b is not None:
+                        ol = ol + (proj_b[h] if proj_b.dim() == 2 else proj_b)
+                blocks_out.append(o + ol)
+            out = torch.cat(blocks_out, dim=0)
+            heads.append(out * (tok < n_valid)[:, None])              # padded query rows are 0
+        rows.append(torch.stack(heads))
+    return torch.stack(rows)
+
+
+def gradients(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, maps: Dict, n_valid: int,
+              scale: float, proj_w=None, proj_b=None):
+    """(O, dQ, dK, dV) as float64 numpy arrays: the output and the gradient of sum(dO * O)."""
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    q, k, v = t(Q), t(K), t(V)
+    pw = None if proj_w is None else torch.tensor(np.asarray(proj_w, np.float64))
+    pb = None if proj_b is None else torch.tensor(np.asarray(proj_b, np.float64))
+    O = forward_torch(q, k, v, maps, n_valid, scale, pw, pb)
+    O.backward(torch.tensor(np.asarray(dO, dtype=np.float64)))
+    return O.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()

@@ -1,0 +1,86 @@
+"""Pins of the gradient oracle (CPU only): its forward against the numpy oracle, its gradients
+against central finite differences of the numpy oracle, and the all-critical special case
+against torch SDPA's own autograd."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import sla_backward as bwd
+from oracle import sla_oracle as orc
+from tests.test_oracle import rand_qkv
+
+
+def _setup(seed, N=256, nv=240, d=8, H=2, kh=2500, kl=2500, proj=False):
+    Q, K, V = rand_qkv(1, H, H, N, d, seed=seed, n_valid=nv, garbage=True)
+    r = np.random.default_rng(seed + 100)
+    dO = r.standard_normal(Q.shape)
+    pw = pb = None
+    if proj:
+        pw, pb = r.standard_normal((H, d, d)) / np.sqrt(d), r.standard_normal((H, d))
+    f = orc.Forward(Q, K, V, n_valid=nv, mode="sla", kh_bp=kh, kl_bp=kl, proj_w=pw, proj_b=pb)
+    return Q, K, V, dO, f, f.maps(), pw, pb
+
+
+def _numpy_loss(f, maps, dO, Q, K, V):
+    """sum(dO * O) of the numpy oracle with the block map held fixed."""
+    g = orc.Forward(Q, K, V, n_valid=f.n_valid, mode="sla", kh_bp=0, kl_bp=0, proj_w=f.proj_w, proj_b=f.proj_b)
+    tot = 0.0
+    for (b, h, i), m in maps.items():
+        tot += float(np.sum(dO[b, h, 64 * i:64 * (i + 1)] * g.output_block(b, h, i, m)))
+    return tot
+
+
+@pytest.mark.parametrize("proj", [False, True])
+def test_forward_matches_numpy_oracle(proj):
+    Q, K, V, dO, f, maps, pw, pb = _setup(31, proj=proj)
+    O, *_ = bwd.gradients(Q, K, V, dO, maps, f.n_valid, f.scale, pw, pb)
+    assert np.allclose(O, f.output(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed,proj", [(32, False), (33, True)])
+def test_gradients_match_finite_differences(seed, proj):
+    Q, K, V, dO, f, maps, pw, pb = _setup(seed, proj=proj)
+    n_crit = sum(len(m["crit"]) for m in maps.values())
+    n_marg = sum(len(m["marg"]) for m in maps.values())
+    assert n_crit and n_marg            # both branches carry gradient
+    _, dQ, dK, dV = bwd.gradients(Q, K, V, dO, maps, f.n_valid, f.scale, pw, pb)
+    r = np.random.default_rng(seed)
+    eps = 1e-6
+    for X, G, name in [(Q, dQ, "Q"), (K, dK, "K"), (V, dV, "V")]:
+        for _ in range(12):
+            idx = (0, r.integers(2), r.integers(f.n_valid), r.integers(X.shape[-1]))
+            Xp, Xm = X.astype(np.float64).copy(), X.astype(np.float64).copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args_p = {"Q": Q, "K": K, "V": V}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = Xp, Xm
+            fd = (_numpy_loss(f, maps, dO, **args_p) - _numpy_loss(f, maps, dO, **args_m)) / (2 * eps)
+            assert abs(fd - G[idx]) <= 1e-6 * (1.0 + abs(fd)), (name, idx, fd, G[idx])
+        assert np.all(G[:, :, f.n_valid:] == 0.0), f"padded rows of d{name} must be zero"
+
+
+def test_all_critical_gradients_equal_sdpa_autograd():
+    N, nv, d, H = 256, 230, 16, 2
+    Q, K, V, dO, f, maps, _, _ = _setup(34, N=N, nv=nv, d=d, H=H, kh=10000, kl=0)
+    _, dQ, dK, dV = bwd.gradients(Q, K, V, dO, maps, nv, f.scale)
+    for h in range(H):
+        q, k, v = (torch.tensor(np.asarray(X[0, h, :nv], np.float64), requires_grad=True) for X in (Q, K, V))
+        o = F.scaled_dot_product_attention(q, k, v, scale=f.scale)
+        o.backward(torch.tensor(dO[0, h, :nv]))
+        for G, ref in [(dQ, q.grad), (dK, k.grad), (dV, v.grad)]:
+            assert np.allclose(G[0, h, :nv], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_nothing_critical_gradients_equal_closed_form_linear_autograd():
+    N, nv, d = 192, 180, 8
+    Q, K, V, dO, f, maps, _, _ = _setup(35, N=N, nv=nv, d=d, H=1, kh=0, kl=0)
+    _, dQ, dK, dV = bwd.gradients(Q, K, V, dO, maps, nv, f.scale)
+    q, k, v = (torch.tensor(np.asarray(X[0, 0, :nv], np.float64), requires_grad=True) for X in (Q, K, V))
+    pq, pk = F.elu(q) + 1.0, F.elu(k) + 1.0
+    A = pq @ pk.T
+    o = (A @ v) / A.sum(dim=1, keepdim=True)
+    o.backward(torch.tensor(dO[0, 0, :nv]))
+    for G, ref in [(dQ, q.grad), (dK, k.grad), (dV, v.grad)]:
+        assert np.allclose(G[0, 0, :nv], ref.numpy(), rtol=1e-10, atol=1e-12)
