@@ -9,6 +9,7 @@ Entry points keep the C names (see include/sla.h):
     sla_linear_kv_reduce per-key-block linear states H_j = phi(K_j)^T V_j, z_j
     sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
     sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
+    sla_attn_bwd         dQ, dK, dV of the SLA layer for a fixed block map
 
 `SlaForward` strings the four calls into one layer forward with every buffer
 allocated up front, so a step launches kernels only.
@@ -21,7 +22,7 @@ import torch
 
 from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
-    lib, sla_abi_version, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
+    lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
     sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
 )
@@ -42,7 +43,7 @@ class SlaForward:
                  kh_bp: int = 0, kl_bp: int = 0, n_sel: int = 0, window: int = 0,
                  w_gate: Optional[torch.Tensor] = None, scale: Optional[float] = None, out_dtype=None,
                  proj_w: Optional[torch.Tensor] = None, proj_b: Optional[torch.Tensor] = None,
-                 smooth_k: bool = False):
+                 smooth_k: bool = False, training: bool = False):
         self.q, self.k, self.v = q, k, v
         self.n_valid = n_valid
         self.mode = mode
@@ -96,6 +97,11 @@ class SlaForward:
             self.kv = dict(H_all=torch.empty((B, Hkv, d, d), **f), z_all=torch.empty((B, Hkv, d), **f),
                            workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
         self.k_mean = torch.empty((B, Hkv, d), **f) if smooth_k else None
+        # training: the forward also writes each row's log-sum-exp, which backward() reads
+        if training and (mode != "sla" or Hq != Hkv or proj_w is not None or smooth_k):
+            raise ValueError("backward is provided for the sla mode with Hq == Hkv, no Proj and no smooth-K")
+        self.lse = torch.empty((B, Hq, N), **f) if training else None
+        self.bwd_ws = None
         self.row_states = None
         if self.lin == SLA_LIN_MARGINAL:
             # per-row marginal sums, filled by sla_marginal_states before the attention call
@@ -133,10 +139,22 @@ class SlaForward:
             S, u = self.row_states
             return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps,
                                 lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out,
-                                proj_w=self.proj_w, proj_b=self.proj_b)
+                                proj_w=self.proj_w, proj_b=self.proj_b, lse=self.lse)
         return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
                             scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
                             H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out)
+
+    def backward(self, dout: torch.Tensor, maps=None, grads=None):
+        """(dq, dk, dv) fp32 of sum(dout * out) after run() (or attention()) with training=True."""
+        if self.lse is None:
+            raise ValueError("construct the layer with training=True to keep what the backward needs")
+        if self.bwd_ws is None:
+            B, H, N, d = self.q.shape
+            self.bwd_ws = torch.empty(sla_attn_bwd_workspace_bytes(B, H, N, d), device=self.q.device,
+                                      dtype=torch.uint8)
+        S, u = self.row_states
+        return sla_attn_bwd(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid, maps or self.maps, S, u,
+                            scale=self.scale, grads=grads, workspace=self.bwd_ws)
 
     def run(self) -> torch.Tensor:
         """One full forward: pool + scores, block map, linear states, marginal sums, attention."""

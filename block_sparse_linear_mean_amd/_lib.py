@@ -56,7 +56,10 @@ _SIGS = {
     "sla_attn_workspace_bytes": (c_size_t, [c_int32] * 5),
     "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
                                c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P,
-                               _P, _P, c_int32, _P, c_int32, _P, c_size_t, _P]),
+                               _P, _P, c_int32, _P, c_int32, _P, _P, c_size_t, _P]),
+    "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 4),
+    "sla_attn_bwd": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                          c_size_t, _P]),
 }
 
 
@@ -259,8 +262,10 @@ def sla_marginal_states(H, z, Hq, group_map, marg_bits, out=None):
 
 def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, causal=False, window=0,
                  group_map=False, H=None, z=None, H_all=None, z_all=None, w_gate=None, out=None,
-                 out_dtype=None, workspace=None, proj_w=None, proj_b=None):
+                 out_dtype=None, workspace=None, proj_w=None, proj_b=None, lse=None):
     """Attention output [B, Hq, N, d]; `maps` is the dict returned by sla_block_map.
+
+    lse: optional float32 [B, Hq, N] output, the log-sum-exp of each row's sparse logits (for sla_attn_bwd).
 
     proj_w [d, d] or [Hq, d, d] fp32 (out x in) and proj_b [d] or [Hq, d]: the learned
     projection of the SLA linear branch (None = identity).
@@ -288,6 +293,32 @@ def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, caus
         ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), n_valid, float(scale), int(causal), window,
         int(group_map), _ptr(maps["crit_rowptr"]), _ptr(maps["crit_idx"]), _ptr(maps.get("crit_flags")),
         _ptr(maps.get("marg_bits")), lin_mode, _ptr(H), _ptr(z), _ptr(H_all),
-        _ptr(z_all), _ptr(w_gate), _ptr(proj_w), _ptr(proj_b), proj_heads, _ptr(out), odt, _ptr(workspace),
-        ws_bytes, _stream(q.device)))
+        _ptr(z_all), _ptr(w_gate), _ptr(proj_w), _ptr(proj_b), proj_heads, _ptr(out), odt, _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(q.device)))
     return out
+
+
+def sla_attn_bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(lib().sla_attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def sla_attn_bwd(q, k, v, o, dout, lse, n_valid, maps, S, u, scale=None, grads=None, workspace=None):
+    """(dq, dk, dv) fp32 [B, H, N, d]: gradients of sum(dout * o) for the SLA forward with the same map.
+
+    o and lse come from sla_attn_fwd; S, u are that map's per-row marginal sums (sla_marginal_states).
+    """
+    _require_gpu(q, k, v, o, dout, lse)
+    B, H, N, d = q.shape
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), device=q.device, dtype=torch.float32) for _ in range(3))
+    ws_bytes = sla_attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+    descs = [tensor_desc(x) for x in (q, k, v, o, dout)]
+    dq, dk, dv = grads
+    _check("sla_attn_bwd", lib().sla_attn_bwd(
+        *[ctypes.byref(x) for x in descs], _ptr(lse), n_valid, float(scale), _ptr(maps["crit_rowptr"]),
+        _ptr(maps["crit_idx"]), _ptr(maps["marg_bits"]), _ptr(S), _ptr(u), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), ws_bytes, _stream(q.device)))
+    return dq, dk, dv

@@ -50,6 +50,7 @@ struct AttnParams {
   const float* proj_w;  // SLA: Proj weight [heads][d (out)][d (in)] fp32, or null (identity)
   const float* proj_b;  // SLA: Proj bias [heads][d] fp32, or null
   int64_t proj_sH;      // elements between the weights of consecutive heads (0: one shared weight)
+  float* lse;           // optional [B][Hq][N]: natural log-sum-exp of each row's sparse-branch logits
   void* out;
   int out_f32;
 };
@@ -382,6 +383,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ---- normalise the sparse branch
   const float l_tot = xor32_sum(l_run);
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (p.lse != nullptr && lg == 0)   // ln sum_s exp(scale q.k_s) = (m c2 + log2 l) ln 2; -inf without keys
+    p.lse[(int64_t(b) * p.Hq + h) * p.N + tq] =
+        (qvalid && l_tot > 0.f) ? (m_run * c2 + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= inv_l;
 
@@ -543,8 +547,8 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
                                    const uint32_t* marg_bits, int32_t lin_mode,
                                    const void* H, const float* z, const float* H_all, const float* z_all,
                                    const float* w_gate, const float* proj_w, const float* proj_b,
-                                   int32_t proj_heads, void* out, int32_t out_dtype, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+                                   int32_t proj_heads, void* out, int32_t out_dtype, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(q);
   if (st != SLA_OK) return st;
@@ -580,6 +584,7 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx; p.crit_flags = crit_flags;
   p.out = out; p.out_f32 = out_dtype == SLA_F32;
   p.proj_w = proj_w; p.proj_b = proj_b;
+  p.lse = lse;
   p.proj_sH = (proj_w != nullptr && proj_heads != 1) ? int64_t(q->d) * q->d : 0;
 
   if (lin_mode == SLA_LIN_MARGINAL) {

@@ -250,6 +250,9 @@ size_t sla_attn_workspace_bytes(int32_t B, int32_t Hs, int32_t nqb, int32_t d, i
  *     applies to rows with no marginal block too (O_linear = 0 there, so they get b_h).
  *     O_linear and W are rounded to bf16 for the matrix-core product (fp32 accumulation).
  *   Rows t >= n_valid are written as 0.
+ * lse (nullable, fp32 [B, Hq, N]): for training, the natural log-sum-exp of each row's
+ *   sparse-branch logits, ln sum_s exp(scale q_t . k_s) over the allowed keys (-inf for a row
+ *   with none and for rows t >= n_valid); sla_attn_bwd reads it.
  * q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; all the same dtype.  out: contiguous
  * [B, Hq, N, d] in out_dtype (SLA_BF16 or SLA_F32).  The linear branch needs causal == 0.
  * Arithmetic: bf16 matrix-core products (fp32 inputs are rounded to bf16), fp32
@@ -263,7 +266,36 @@ sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         int32_t lin_mode, const void* H, const float* z,
                         const float* H_all, const float* z_all, const float* w_gate,
                         const float* proj_w, const float* proj_b, int32_t proj_heads,
-                        void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                        void* out, int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes sla_attn_bwd needs (0 for unsupported sizes). */
+size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
+
+/*
+ * Backward of the SLA layer (the method is fine-tuned: SLA analysis page for arXiv
+ * 2509.24006, the learned Proj and linear path).  Gradients of sum(dout * O) with respect to
+ * Q, K and V, where O is the sla_attn_fwd output in SLA mode with Proj the identity, for the
+ * SAME block map (held fixed: it is piecewise constant in Q and K):
+ *   critical branch:  P = exp(scale q.k - lse), dP = dO V^T, D_t = dO_t . O_sparse_t,
+ *                     dS = P (dP - D); dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO;
+ *   marginal branch:  through O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the
+ *                     sums of H_j = phi(K_j)^T V_j and z_j over row r's marginal blocks.
+ * Inputs: q, k, v and o (the forward output), dout: [B, H, N, d], one dtype (bf16 or fp32),
+ * one KV head per query head (Hq == Hkv, else SLA_ERR_UNSUPPORTED); lse [B, H, N] from
+ * sla_attn_fwd; the block map's critical CSR lists and marginal bit masks; S (bf16 bits
+ * [rows, d, d]) and u (fp32 [rows, d]) as written by sla_marginal_states for that map.
+ * Outputs dq, dk, dv: contiguous fp32 [B, H, N, d], 16-byte aligned, fully overwritten; rows
+ * t >= n_valid are zero.  O_sparse is taken as o - O_linear.  Arithmetic: bf16 matrix-core
+ * operands, fp32 accumulation; deterministic (no atomics on gradients).  Smooth-K and a
+ * learned Proj are not differentiated here.
+ * workspace: sla_attn_bwd_workspace_bytes(B, H, N, d) bytes.
+ */
+sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
+                        const sla_tensor* o, const sla_tensor* dout, const float* lse, int32_t n_valid,
+                        float scale, const int32_t* crit_rowptr, const int32_t* crit_idx,
+                        const uint32_t* marg_bits, const void* S, const float* u,
+                        float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
                         void* stream);
 
 #ifdef __cplusplus

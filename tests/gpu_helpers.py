@@ -91,7 +91,9 @@ def oracle_csr(f: orc.Forward):
                 maps[(b, h, i)] = f.map_row(b, h, i)
     csr = orc.to_csr(maps, f.B, Hs, f.nb)
     csr["marg_bits"] = marg_bits_of(maps, f.B, Hs, f.nb, f.nb)
-    dev = {k: to_dev(v, torch.uint8 if k == "crit_flags" else torch.int32) for k, v in csr.items()}
+    # index arrays get at least one element (a device pointer is required even for empty lists)
+    pad = lambda v: v if np.asarray(v).size else np.zeros(1, np.asarray(v).dtype)
+    dev = {k: to_dev(pad(v), torch.uint8 if k == "crit_flags" else torch.int32) for k, v in csr.items()}
     return dev, maps
 
 

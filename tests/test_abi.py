@@ -170,7 +170,7 @@ def test_attn_fwd_validation(L):
              lin=0, H=None, z=None, Ha=None, za=None, wg=None, out=P, odt=0, ws=None, wsb=0, pw=None, pb=None,
              ph=0):
         return L.sla_attn_fwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), nv, scale, causal, win, group,
-                              crp, ci, cf, mb, lin, H, z, Ha, za, wg, pw, pb, ph, out, odt, ws, wsb, None)
+                              crp, ci, cf, mb, lin, H, z, Ha, za, wg, pw, pb, ph, out, odt, None, ws, wsb, None)
     assert call(out=None) == ENULL
     assert call(crp=None) == ENULL
     assert call(causal=1) == ENULL                   # causal needs the flags
@@ -191,3 +191,24 @@ def test_attn_fwd_validation(L):
     assert call(pw=P, ph=1) == EUNSUP                # Proj is for the SLA linear branch only
     assert call(lin=3, H=P, z=P, pw=P, ph=3) == ESHAPE
     assert call(lin=3, H=P, z=P, pw=ctypes.c_void_p(0x20004), ph=1) == EALIGN
+
+
+def test_attn_bwd_validation(L):
+    q = desc()
+    def call(qq=q, kk=q, vv=q, oo=q, gg=q, lse=P, nv=256, scale=0.1, crp=P, ci=P, mb=P, S=P, u=P, dq=P, dk=P,
+             dv=P, ws=None, wsb=0):
+        return L.sla_attn_bwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), ctypes.byref(oo),
+                              ctypes.byref(gg), lse, nv, scale, crp, ci, mb, S, u, dq, dk, dv, ws, wsb, None)
+    assert call(lse=None) == ENULL
+    assert call(mb=None) == ENULL
+    assert call(dq=None) == ENULL
+    assert call(kk=desc(H=1), vv=desc(H=1)) == EUNSUP          # one KV head per query head only
+    assert call(oo=desc(dtype=1)) == ESHAPE
+    assert call(gg=desc(N=512)) == ESHAPE
+    assert call(nv=100) == ERANGE
+    assert call(scale=-1.0) == ERANGE
+    assert call(dk=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call() == EWS                                       # workspace missing
+    assert call(ws=P, wsb=16) == EWS
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128) > 0
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 100, 128) == 0
