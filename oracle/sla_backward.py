@@ -42,11 +42,14 @@ def _phi(x: torch.Tensor) -> torch.Tensor:
     return torch.where(x > 0, x + 1.0, torch.exp(torch.clamp(x, max=0.0)))
 
 
-def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, proj_b=None) -> torch.Tensor:
+def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, proj_b=None,
+                  blocks: Optional[set] = None) -> torch.Tensor:
     """SLA output [B, H, N, d] for a fixed block map, in float64 torch ops (differentiable).
 
     Q, K, V: float64 tensors [B, H, N, d] (one KV head per query head).
     maps[(b, h, i)]: dict with the ascending lists "crit" and "marg" of query block i of head h.
+    blocks: if given, only these (b, h, i) query blocks are computed, the others output 0 (so a
+    loss over them is exact for every input row it depends on).
     """
     B, H, N, d = Q.shape
     nb = N // BLOCK
@@ -56,12 +59,18 @@ def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, 
     for b in range(B):
         heads = []
         for h in range(H):
+            if blocks is not None and not any((b, h, i) in blocks for i in range(nb)):
+                heads.append(torch.zeros_like(Q[b, h]))
+                continue
             q, k, v = Q[b, h], K[b, h], V[b, h]
             pk = _phi(k) * valid_k[:, None]                       # padded keys contribute nothing
             blocks_out = []
             for i in range(nb):
-                m = maps[(b, h, i)]
                 qi = q[BLOCK * i:BLOCK * (i + 1)]
+                if blocks is not None and (b, h, i) not in blocks:
+                    blocks_out.append(torch.zeros_like(qi))
+                    continue
+                m = maps[(b, h, i)]
                 # sparse branch: one softmax over the keys of the critical blocks
                 allowed = torch.zeros(N, dtype=torch.bool)
                 for j in m["crit"]:
@@ -97,12 +106,15 @@ def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, 
 
 
 def gradients(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, maps: Dict, n_valid: int,
-              scale: float, proj_w=None, proj_b=None):
-    """(O, dQ, dK, dV) as float64 numpy arrays: the output and the gradient of sum(dO * O)."""
+              scale: float, proj_w=None, proj_b=None, blocks: Optional[set] = None):
+    """(O, dQ, dK, dV) as float64 numpy arrays: the output and the gradient of sum(dO * O).
+
+    With `blocks`, the loss covers only those query blocks (see forward_torch).
+    """
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     q, k, v = t(Q), t(K), t(V)
     pw = None if proj_w is None else torch.tensor(np.asarray(proj_w, np.float64))
     pb = None if proj_b is None else torch.tensor(np.asarray(proj_b, np.float64))
-    O = forward_torch(q, k, v, maps, n_valid, scale, pw, pb)
+    O = forward_torch(q, k, v, maps, n_valid, scale, pw, pb, blocks)
     O.backward(torch.tensor(np.asarray(dO, dtype=np.float64)))
     return O.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()

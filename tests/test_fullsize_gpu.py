@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_linear_mean_amd as sla
+from oracle import sla_backward as obwd
 from oracle import sla_oracle as orc
 from tests.gpu_helpers import (MAX_ABS, REL_L2, gpu_map_rows, host, layer_for, oracle_for, say,
                                ulp_distance)
@@ -105,3 +107,54 @@ def test_full_size_sampled(name):
     mx = np.abs(d).max()
     say(f"  {name}: {n_rows} sampled blocks, rel-L2 {rel:.3e}, max-abs {mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def test_full_size_backward_sampled():
+    """The backward at the wan13b layer, in the configuration bench.py --backward times: dQ rows of
+    sampled query blocks and dK / dV rows of sampled key blocks, each recomputed by the gradient
+    oracle from exactly the query blocks that depend on them, on the first and last head."""
+    w = WORKLOADS["wan13b_sla"]
+    say("[full size backward] generating inputs")
+    q, k, v, wg = make_inputs(w)
+    layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, "sla", kh_bp=w.kh_bp, kl_bp=w.kl_bp, training=True)
+    layer.run()
+    r = np.random.default_rng(w.seed + 17)
+    dO = torch.from_numpy(r.standard_normal(q.shape, dtype=np.float32)).to(torch.bfloat16)
+    dq, dk, dv = layer.backward(dO.cuda())
+    torch.cuda.synchronize()
+    f = oracle_for(w, q, k, v, wg)
+    nb, nv = f.nb, w.Nv
+    for h in [0, w.Hq - 1]:
+        say(f"[full size backward] head {h}: oracle map")
+        maps_h = {(0, 0, i): f.map_row(0, h, i) for i in range(nb)}
+        got_rows = gpu_map_rows(layer.maps, [h * nb + i for i in range(nb)])
+        for i in range(nb):
+            crit, _, marg, _ = got_rows[h * nb + i]
+            assert crit == maps_h[(0, 0, i)]["crit"] and marg == maps_h[(0, 0, i)]["marg"], (h, i)
+        Qh, Kh, Vh = (X[:, h:h + 1] for X in (f.Q, f.K, f.V))
+        dOh = host(dO[:, h:h + 1]).astype(np.float64)
+        gq, gk, gv = (host(X[0, h]) for X in (dq, dk, dv))
+        diffs = {"dQ": [], "dK": [], "dV": []}
+        refs_ = {"dQ": [], "dK": [], "dV": []}
+        qblocks = sample_blocks(nb, 7 + h)
+        _, dQr, _, _ = obwd.gradients(Qh, Kh, Vh, dOh, maps_h, nv, f.scale, blocks={(0, 0, i) for i in qblocks})
+        for i in qblocks:
+            rows = slice(64 * i, min(64 * i + 64, nv))
+            diffs["dQ"].append(gq[rows] - dQr[0, 0, rows])
+            refs_["dQ"].append(dQr[0, 0, rows])
+        for j in [0, nb // 2, nb - 1]:
+            users = {key for key, m in maps_h.items() if j in m["crit"] or j in m["marg"]}
+            say(f"  key block {j}: {len(users)} query blocks use it")
+            _, _, dKr, dVr = obwd.gradients(Qh, Kh, Vh, dOh, maps_h, nv, f.scale, blocks=users)
+            rows = slice(64 * j, min(64 * j + 64, nv))
+            for name, g_, r_ in (("dK", gk, dKr), ("dV", gv, dVr)):
+                diffs[name].append(g_[rows] - r_[0, 0, rows])
+                refs_[name].append(r_[0, 0, rows])
+        for name in diffs:
+            d_ = np.concatenate(diffs[name])
+            r_ = np.concatenate(refs_[name])
+            rel = np.linalg.norm(d_) / np.linalg.norm(r_)
+            mx = np.abs(d_).max() / np.abs(r_).max()
+            say(f"  head {h} {name}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
+            assert rel <= REL_L2 and mx <= 3e-2, (h, name)
+    assert not dq[:, :, nv:].any() and not dk[:, :, nv:].any() and not dv[:, :, nv:].any()

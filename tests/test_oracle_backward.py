@@ -84,3 +84,19 @@ def test_nothing_critical_gradients_equal_closed_form_linear_autograd():
     o.backward(torch.tensor(dO[0, 0, :nv]))
     for G, ref in [(dQ, q.grad), (dK, k.grad), (dV, v.grad)]:
         assert np.allclose(G[0, 0, :nv], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_restricted_blocks_give_the_rows_they_cover():
+    """A loss over some query blocks only: dQ rows of those blocks, and dK/dV rows of a key block
+    used only by those blocks, equal the full gradient's rows."""
+    Q, K, V, dO, f, maps, _, _ = _setup(36)
+    _, dQ, dK, dV = bwd.gradients(Q, K, V, dO, maps, f.n_valid, f.scale)
+    j = 1
+    users = {key for key, m in maps.items() if key[1] == 0 and (j in m["crit"] or j in m["marg"])}
+    assert users
+    _, dQr, dKr, dVr = bwd.gradients(Q, K, V, dO, maps, f.n_valid, f.scale, blocks=users)
+    for (b, h, i) in users:
+        assert np.allclose(dQr[b, h, 64 * i:64 * i + 64], dQ[b, h, 64 * i:64 * i + 64], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dKr[0, 0, 64 * j:64 * j + 64], dK[0, 0, 64 * j:64 * j + 64], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dVr[0, 0, 64 * j:64 * j + 64], dV[0, 0, 64 * j:64 * j + 64], rtol=1e-12, atol=1e-14)
+    assert not dQr[0, 1].any()
