@@ -24,6 +24,7 @@
 // row's lists; the key-stationary ones (linear dK/dV and sparse dK/dV) over the transposed
 // lists, kept as one bit per (key block, query block); no atomics on gradients, so results
 // are deterministic.
+#include "attn_tiles.h"
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -362,17 +363,25 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ sparse branch, dQ
 
+// Zero rows r0 .. 63 of a tile (the padded rows of a partial block; a direct copy brings whatever
+// the caller's padding holds).
+template <int D>
+__device__ __forceinline__ void zero_rows(lds_u8* tile, int r0) {
+  constexpr int kChunks = D / 8;
+  for (int e = threadIdx.x; e < (kBlock - r0) * kChunks; e += kBwThreads)
+    lds_store16(tile + tpos<D>(r0 + e / kChunks, e % kChunks), zero8());
+}
+
 // One workgroup per (query block i, head); wavefront w owns query rows 64 i + 16 w + l % 16.
 // Over the row's critical blocks: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+// K and V tiles are double-buffered: the next block's direct-to-LDS copies run during this one.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
+  using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
   constexpr int kCt = D / 16;
-  constexpr int RB = 2 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char k_sm[kBlock * RB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_sm[kBlock * RB];
-  lds_u8* Kt = to_lds(k_sm);
-  lds_u8* Vt = to_lds(v_sm);
+  __shared__ __attribute__((aligned(1024))) unsigned char k_sm[2][Tl::kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_sm[2][Tl::kTileB];
 
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
@@ -383,6 +392,25 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   const T* Gr = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH + int64_t(tq) * p.dsN;
   const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(h) * p.ksH;
   const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(h) * p.vsH;
+  const StageOff<D, kBwWaves> koff = stage_offsets<D, false, kBwWaves>(p.ksN);
+  const StageOff<D, kBwWaves> voff = stage_offsets<D, false, kBwWaves>(p.vsN);
+
+  const int cbeg = p.crit_rowptr[row], cend = p.crit_rowptr[row + 1];
+  // the row's next valid block index at or after list position e (or -1), wave-uniform
+  auto next_block = [&](int& e) -> int {
+    while (e < cend) {
+      const int jraw = __builtin_amdgcn_readfirstlane(p.crit_idx[e]);
+      ++e;
+      if (unsigned(jraw) < unsigned(p.nb)) return jraw;   // malformed entries are skipped
+    }
+    return -1;
+  };
+  int epos = cbeg;
+  int cur = next_block(epos);
+  if (cur >= 0) {
+    stage_tile<T, D, false, kBwWaves>(K, p.ksN, cur, to_lds(k_sm[0]), koff);
+    stage_tile<T, D, false, kBwWaves>(V, p.vsN, cur, to_lds(v_sm[0]), voff);
+  }
   bf16x8 qf[kKc], gf[kKc];
 #pragma unroll
   for (int kc = 0; kc < kKc; ++kc) {
@@ -399,15 +427,25 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int rt = 0; rt < kCt; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int cbeg = p.crit_rowptr[row], cend = p.crit_rowptr[row + 1];
-  for (int e = cbeg; e < cend; ++e) {
-    const int jraw = __builtin_amdgcn_readfirstlane(p.crit_idx[e]);
-    if (unsigned(jraw) >= unsigned(p.nb)) continue;     // malformed entry: skipped by every wavefront
-    const int j = jraw;
-    __syncthreads();                                     // the previous block's tiles have been read
-    stage64<T, D>(K, p.ksN, kBlock * j, p.n_valid, Kt);
-    stage64<T, D>(V, p.vsN, kBlock * j, p.n_valid, Vt);
-    __syncthreads();
+  int buf = 0;
+  while (cur >= 0) {
+    const int nxt = next_block(epos);
+    lds_u8* Kt = to_lds(k_sm[buf]);
+    lds_u8* Vt = to_lds(v_sm[buf]);
+    SLA_WAIT_VMCNT(0);               // this block's copies have landed ...
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                   // ... for every wavefront, and the other buffer is free
+    const int rv = p.n_valid - kBlock * cur;
+    if (rv < kBlock) {               // padded keys: zero their K and V rows
+      zero_rows<D>(Kt, rv);
+      zero_rows<D>(Vt, rv);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+    }
+    if (nxt >= 0) {
+      stage_tile<T, D, false, kBwWaves>(K, p.ksN, nxt, to_lds(k_sm[buf ^ 1]), koff);
+      stage_tile<T, D, false, kBwWaves>(V, p.vsN, nxt, to_lds(v_sm[buf ^ 1]), voff);
+    }
     bf16x4 dsb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -421,9 +459,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
       f32x4 ds;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int sk = kBlock * j + 16 * st + 4 * g + e4;
-        const float pr = (has && sk < p.n_valid) ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -lse2)) : 0.f;
-        ds[e4] = pr * (pacc[e4] - Dt);
+        const bool ok = has && 16 * st + 4 * g + e4 < rv;
+        const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -lse2)) : 0.f;
+        ds[e4] = ok ? pr * (pacc[e4] - Dt) : 0.f;
       }
       dsb[st] = cvt4(ds);
     }
@@ -436,6 +474,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
                               lds_read_tr4(Kt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * rt, lane)));
         acc[rt] = mfma16(a, join(dsb[2 * pr], dsb[2 * pr + 1]), acc[rt]);
       }
+    cur = nxt;
+    buf ^= 1;
   }
   // lane holds dQ^T[r = 16 rt + 4 g + e][t]: add to the linear part
   if (qv) {
@@ -452,27 +492,59 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 
 // One workgroup per (key block j, head); wavefront w owns keys 64 j + 16 w + l % 16.  Over the
 // query blocks i that list j as critical: S = Q K^T, dP = dO V^T, dS = P (dP - D),
-// dV^T += dO^T P, dK^T += Q^T dS.
+// dV^T += dO^T P, dK^T += Q^T dS.  Q, dO tiles and the rows' log-sum-exp and D are
+// double-buffered: the next query block's direct-to-LDS copies run during this one.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
+  using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
   constexpr int kCt = D / 16;
-  constexpr int RB = 2 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char q_sm[kBlock * RB];
-  __shared__ __attribute__((aligned(1024))) unsigned char g_sm[kBlock * RB];
-  __shared__ __attribute__((aligned(16))) float lse_s[kBlock];
-  __shared__ __attribute__((aligned(16))) float d_s[kBlock];
-  lds_u8* Qt = to_lds(q_sm);
-  lds_u8* Gt = to_lds(g_sm);
+  __shared__ __attribute__((aligned(1024))) unsigned char q_sm[2][Tl::kTileB];
+  __shared__ __attribute__((aligned(1024))) unsigned char g_sm[2][Tl::kTileB];
+  __shared__ __attribute__((aligned(256))) float lse_s[2][kBlock];
+  __shared__ __attribute__((aligned(256))) float d_s[2][kBlock];
 
   const int j = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
-  const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
+  const int t = threadIdx.x, lane = t % kWave, l16 = lane % 16, g = lane / 16;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);
   const int s = kBlock * j + 16 * w + l16;
   const bool kv = s < p.n_valid;
   const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(h) * p.ksH + int64_t(s) * p.ksN;
   const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(h) * p.vsH + int64_t(s) * p.vsN;
   const T* Q = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
   const T* G = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH;
+  const float* lse_h = p.lse + int64_t(bh) * p.N;
+  const float* D_h = p.D + int64_t(bh) * p.N;
+  const StageOff<D, kBwWaves> qoff = stage_offsets<D, false, kBwWaves>(p.qsN);
+  const StageOff<D, kBwWaves> goff = stage_offsets<D, false, kBwWaves>(p.dsN);
+
+  // the query blocks that list j, ascending: a wave-uniform scan of the transposed bit row
+  const uint32_t* bits = p.critT + (int64_t(bh) * p.nb + j) * p.wq;
+  int word = 0;
+  uint32_t m = 0u;
+  auto next_block = [&]() -> int {
+    while (m == 0u) {
+      if (word >= p.wq) return -1;
+      m = __builtin_amdgcn_readfirstlane(bits[word]);
+      ++word;
+    }
+    const int i = 32 * (word - 1) + __builtin_ctz(m);
+    m &= m - 1u;
+    return i;
+  };
+  // copies of query block i into buffer bf: Q and dO tiles by every wavefront, the 64 rows'
+  // log-sum-exp and D (256 bytes each) by wavefront 0
+  auto stage = [&](int i, int bf) {
+    stage_tile<T, D, false, kBwWaves>(Q, p.qsN, i, to_lds(q_sm[bf]), qoff);
+    stage_tile<T, D, false, kBwWaves>(G, p.dsN, i, to_lds(g_sm[bf]), goff);
+    if (w == 0) {
+      load_lds4_sbase(lse_h + kBlock * i, uint32_t(4 * lane), to_lds(lse_s[bf]));
+      load_lds4_sbase(D_h + kBlock * i, uint32_t(4 * lane), to_lds(d_s[bf]));
+    }
+  };
+  int cur = next_block();
+  if (cur >= 0) stage(cur, 0);
+
   bf16x8 kf[kKc], vf[kKc];
 #pragma unroll
   for (int kc = 0; kc < kKc; ++kc) {
@@ -487,56 +559,58 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint32_t* bits = p.critT + (int64_t(bh) * p.nb + j) * p.wq;
-  for (int word = 0; word < p.wq; ++word) {
-    uint32_t m = __builtin_amdgcn_readfirstlane(bits[word]);
-    while (m != 0u) {
-      const int i = 32 * word + __builtin_ctz(m);
-      m &= m - 1u;
-      __syncthreads();                                   // the previous block's tiles have been read
-      stage64<T, D>(Q, p.qsN, kBlock * i, p.n_valid, Qt);
-      stage64<T, D>(G, p.dsN, kBlock * i, p.n_valid, Gt);
-      for (int e = t; e < kBlock; e += kBwThreads) {
-        const int tq = kBlock * i + e;
-        const float l = tq < p.n_valid ? p.lse[int64_t(bh) * p.N + tq] : -__builtin_inff();
-        lse_s[e] = l > -__builtin_inff() ? l * kLog2e : __builtin_inff();   // +inf: P = 0
-        d_s[e] = tq < p.n_valid ? p.D[int64_t(bh) * p.N + tq] : 0.f;
-      }
-      __syncthreads();
-      bf16x4 pb[4], db[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < kKc; ++kc) {
-          sacc = mfma16(lds_load16(Qt + tpos<D>(16 * tt + l16, 4 * kc + g)), kf[kc], sacc);
-          pacc = mfma16(lds_load16(Gt + tpos<D>(16 * tt + l16, 4 * kc + g)), vf[kc], pacc);
-        }
-        // lane holds S[t = 16 tt + 4 g + e][s]
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[16 * tt + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&d_s[16 * tt + 4 * g]);
-        f32x4 pr, ds;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          pr[e4] = kv ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -l4[e4])) : 0.f;
-          ds[e4] = pr[e4] * (pacc[e4] - d4[e4]);
-        }
-        pb[tt] = cvt4(pr);
-        db[tt] = cvt4(ds);
-      }
-      // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s]
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const bf16x8 ag = join(lds_read_tr4(Gt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
-                                 lds_read_tr4(Gt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
-          dv[ct] = mfma16(ag, join(pb[2 * pr], pb[2 * pr + 1]), dv[ct]);
-          const bf16x8 aq = join(lds_read_tr4(Qt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
-                                 lds_read_tr4(Qt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
-          dk[ct] = mfma16(aq, join(db[2 * pr], db[2 * pr + 1]), dk[ct]);
-        }
+  int buf = 0;
+  while (cur >= 0) {
+    const int nxt = next_block();
+    lds_u8* Qt = to_lds(q_sm[buf]);
+    lds_u8* Gt = to_lds(g_sm[buf]);
+    SLA_WAIT_VMCNT(0);               // this block's copies have landed ...
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                   // ... for every wavefront, and the other buffer is free
+    const int rq = p.n_valid - kBlock * cur;     // valid query rows of this block
+    if (rq < kBlock) {               // padded queries: zero their Q and dO rows
+      zero_rows<D>(Qt, rq);
+      zero_rows<D>(Gt, rq);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
     }
+    if (nxt >= 0) stage(nxt, buf ^ 1);
+    bf16x4 pb[4], db[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < kKc; ++kc) {
+        sacc = mfma16(lds_load16(Qt + tpos<D>(16 * tt + l16, 4 * kc + g)), kf[kc], sacc);
+        pacc = mfma16(lds_load16(Gt + tpos<D>(16 * tt + l16, 4 * kc + g)), vf[kc], pacc);
+      }
+      // lane holds S[t = 16 tt + 4 g + e][s]; rows without allowed keys or past n_valid get P = 0
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[buf][16 * tt + 4 * g]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&d_s[buf][16 * tt + 4 * g]);
+      f32x4 pr, ds;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const bool ok = kv && 16 * tt + 4 * g + e4 < rq && l4[e4] > -__builtin_inff();
+        pr[e4] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -l4[e4] * kLog2e)) : 0.f;
+        ds[e4] = ok ? pr[e4] * (pacc[e4] - d4[e4]) : 0.f;
+      }
+      pb[tt] = cvt4(pr);
+      db[tt] = cvt4(ds);
+    }
+    // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s]
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const bf16x8 ag = join(lds_read_tr4(Gt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
+                               lds_read_tr4(Gt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
+        dv[ct] = mfma16(ag, join(pb[2 * pr], pb[2 * pr + 1]), dv[ct]);
+        const bf16x8 aq = join(lds_read_tr4(Qt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
+                               lds_read_tr4(Qt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
+        dk[ct] = mfma16(aq, join(db[2 * pr], db[2 * pr + 1]), dk[ct]);
+      }
+    cur = nxt;
+    buf ^= 1;
   }
   if (kv) {
     float* dkr = p.dk + (int64_t(bh) * p.N + s) * D;

@@ -24,6 +24,7 @@
 //  * epilogue: 1/l normalisation, then the linear term phi(q)^T S / (phi(q) . u)
 //    as one more matrix-core product against S^T staged in LDS as bf16, and, with a
 //    projection, one more product against the staged weight.
+#include "attn_tiles.h"
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -54,94 +55,6 @@ struct AttnParams {
   void* out;
   int out_f32;
 };
-
-// Tile geometry of one 64-key block of K or V in LDS: row-major bf16, 16-byte chunks
-// permuted within each row so that both readers are free of bank conflicts:
-//  * K is read as the A operand of S^T = K Q^T (16 contiguous bytes per lane, 32 rows at a
-//    time): chunk c of row r sits at position c ^ (r % chunks);
-//  * V is read with the transposing LDS read (8 bytes per lane, 4 rows x 32 bytes per
-//    16-lane group): chunk c of row r sits at position c ^ 2 (r % 4).
-// The epilogue's S^T tile ([c][r], 128 x 128 bf16) reuses the K layout over both buffers.
-template <int D>
-struct AttnTile {
-  static constexpr int kRowB = 2 * D;             // bytes per row
-  static constexpr int kChunks = D / 8;           // 16-byte chunks per row
-  static constexpr int kTileB = kBlock * kRowB;   // one 64-row tile
-  static constexpr int kInst = kTileB / 1024;     // 1 KB direct-load steps per tile
-};
-
-template <int D>
-__device__ __forceinline__ int k_pos(int r, int c) {
-  return r * AttnTile<D>::kRowB + 16 * (c ^ (r % AttnTile<D>::kChunks));
-}
-template <int D>
-__device__ __forceinline__ int v_pos(int r, int c) {
-  return trs_pos<AttnTile<D>::kRowB>(r, c);
-}
-
-// Stage rows 64 j .. 64 j + 63 of X (row stride sN elements) into an LDS tile.  bf16 inputs go
-// straight from global memory to LDS: a 1 KB step q covers R = 1024 / rowbytes rows, and lane l
-// fetches the global chunk that belongs at LDS offset q * 1024 + 16 l.  With the swizzles above
-// that chunk's byte offset from the step's first row is a per-lane constant, except for the K
-// layout at d = 128 where it takes 4 values (q % 4); so each wavefront keeps at most four 32-bit
-// offsets and all other address arithmetic is wave-uniform.  fp32 inputs are converted through
-// registers.  The NW wavefronts of a workgroup split the tile's steps.
-template <int D, int NW>
-struct StageOff {
-  static constexpr int kSteps = AttnTile<D>::kInst / NW;   // steps per wavefront
-  static constexpr int kLanes = kSteps < 4 ? kSteps : 4;
-  uint32_t lane[kLanes];          // per-lane part of this wavefront's step n, index n % kLanes
-  uint32_t step[kSteps];          // this wavefront's steps: byte offset of the step's first row
-};
-
-template <int D, bool KLAYOUT, int NW>
-__device__ __forceinline__ StageOff<D, NW> stage_offsets(int64_t sN) {
-  using Tl = AttnTile<D>;
-  using SO = StageOff<D, NW>;
-  constexpr int R = 1024 / Tl::kRowB;             // rows per 1 KB step: 4 (d 128) or 8 (d 64)
-  const int lane = threadIdx.x % kWave;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int r = (16 * lane) / Tl::kRowB;          // row within the step
-  const int pc = lane % Tl::kChunks;              // physical chunk
-  SO o;
-#pragma unroll
-  for (int m = 0; m < SO::kLanes; ++m) {
-    const int q = w * SO::kSteps + m;             // q % 4 repeats with period 4 in m
-    const int c = KLAYOUT ? pc ^ ((q * R + r) % Tl::kChunks) : pc ^ (2 * (r % 4));
-    o.lane[m] = uint32_t(2 * (r * sN + 8 * c));
-  }
-#pragma unroll
-  for (int n = 0; n < SO::kSteps; ++n)
-    o.step[n] = uint32_t(int64_t(w * SO::kSteps + n) * R * sN * 2);
-  return o;
-}
-
-template <typename T, int D, bool KLAYOUT, int NW>
-__device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, int j, lds_u8* tile,
-                                           const StageOff<D, NW>& off) {
-  using Tl = AttnTile<D>;
-  using SO = StageOff<D, NW>;
-  const int t = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: the LDS base goes to M0
-  if constexpr (sizeof(T) == 2) {
-    // one 64-bit tile base per tile; each copy adds a wave-uniform step offset to a per-lane offset
-    const unsigned char* tb = reinterpret_cast<const unsigned char*>(X) + int64_t(kBlock * j) * sN * 2;
-#pragma unroll
-    for (int n = 0; n < SO::kSteps; ++n) {
-      const int q = w * SO::kSteps + n;
-      const uint32_t vo = off.lane[KLAYOUT ? n % SO::kLanes : 0] + off.step[n];
-      load_lds16_sbase(tb, vo, tile + q * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < Tl::kChunks * kBlock / (kWave * NW); ++n) {
-      const int e = t + kWave * NW * n;
-      const int r = e / Tl::kChunks, c = e % Tl::kChunks;
-      const bf16x8 x = In<T>::load8(X + int64_t(kBlock * j + r) * sN + 8 * c);
-      lds_store16(tile + (KLAYOUT ? k_pos<D>(r, c) : v_pos<D>(r, c)), x);
-    }
-  }
-}
 
 // Workgroup order.  Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
 // the hardware index is remapped: the workgroups one XCD receives form one contiguous range
