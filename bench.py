@@ -128,6 +128,30 @@ def cpu_baseline(w, q, k, v, wg, heads):
     }
 
 
+def captured_mass(w, qd, kd, vd):
+    """Mean over valid query rows of the dense softmax mass that falls on the row's critical
+    blocks, exp(lse_critical - lse_dense), with the tokens in row-major and in Hilbert order (the
+    reordering remark of the pages: a more coherent block raises the mass a fixed budget captures).
+    Both log-sum-exps come from the library's forward (the dense one with every block critical)."""
+    import torch
+    import block_sparse_linear_mean_amd as sla
+    if w.mode != "sla" or getattr(w, "grid", None) is None:
+        return None
+    out = {}
+    for name, order in (("row-major", None), ("hilbert", sla.sla_hilbert_order(*w.grid))):
+        lay = sla.SlaForward(qd, kd, vd, w.Nv, "sla", kh_bp=w.kh_bp, kl_bp=w.kl_bp, training=True, token_order=order)
+        lay.run()
+        dense = sla.SlaForward(qd, kd, vd, w.Nv, "sla", kh_bp=10000, kl_bp=0, training=True, token_order=order)
+        dense.run()
+        mass = torch.exp(lay.lse[:, :, :w.Nv] - dense.lse[:, :, :w.Nv])
+        out[name] = round(float(mass.mean()), 4)
+        out[name + "_p10"] = round(float(torch.quantile(mass.flatten()[::97].float(), 0.1)), 4)
+        del lay, dense
+        torch.cuda.empty_cache()
+        log(f"bench: captured dense mass ({name}) = {out[name]}")
+    return out
+
+
 def bench_backward(args, w, qd, kd, vd):
     """Time the backward (dQ, dK, dV of one SLA layer for its block map) and print one JSON line.
 
@@ -262,6 +286,10 @@ def main():
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead (sla workloads)")
+    ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",
+                    help="run the layer on Q, K, V gathered along a 3-D Hilbert curve of the latent grid")
+    ap.add_argument("--captured-mass", action="store_true",
+                    help="also report the dense attention mass the critical blocks capture (row-major and Hilbert)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a kernel-trace summary of a rocprofv3 run")
@@ -301,28 +329,34 @@ def main():
     if args.backward:
         bench_backward(args, w, qd, kd, vd)
         return
+    order = None
+    if args.token_order == "hilbert":
+        if getattr(w, "grid", None) is None:
+            raise SystemExit("--token-order hilbert needs a workload with a latent grid")
+        order = sla.sla_hilbert_order(*w.grid)
     layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
-                           window=w.window, w_gate=wg)
+                           window=w.window, w_gate=wg, token_order=order)
+    passes_run = (["reorder"] if order is not None else []) + PASSES + (["restore"] if order is not None else [])
     log(f"bench: {args.warmup} warm-up steps")
     for _ in range(args.warmup):
         layer.run()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PASSES) + 1)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(passes_run) + 1)] for _ in range(args.steps)]
     log(f"bench: {args.steps} timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         e = ev[s]
         e[0].record()
-        for i, name in enumerate(PASSES):
+        for i, name in enumerate(passes_run):
             getattr(layer, name)()
             e[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     pass_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-               for i, name in enumerate(PASSES)}
+               for i, name in enumerate(passes_run)}
     gpu_ms = sum(pass_ms.values())
     log("bench: per-pass ms " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in pass_ms.items()) +
         f"; wall {ms_step:.4f} ms/step")
@@ -343,8 +377,13 @@ def main():
     roof["algorithmic_per_launch"] = amount
     roof["avg_launch_ms"] = round(pass_ms[dom], 5)
 
+    if order is not None:
+        # a row gather of Q, K, V and a row scatter of O: 2 * bytes of each tensor
+        eb = 2 if w.dtype == "bf16" else 4
+        work["reorder"] = ("hbm", 3 * 2 * w.B * w.Hq * w.N * w.d * eb)
+        work["restore"] = ("hbm", 2 * w.B * w.Hq * w.N * w.d * eb)
     passes = {}
-    for name in PASSES:
+    for name in passes_run:
         b_, a_ = work[name]
         t_ = pass_ms[name] / 1e3
         if a_ and t_ > 0:
@@ -364,6 +403,8 @@ def main():
     else:
         cfg.update(n_sel=w.n_sel, window=w.window)
     cfg["critical_pairs"] = pairs
+    if order is not None:
+        cfg["token_order"] = "hilbert"
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -383,6 +424,8 @@ def main():
         "passes": passes,
         "gpu_ms_per_step": round(gpu_ms, 5),
     }
+    if args.captured_mass:
+        result["captured_mass"] = captured_mass(w, qd, kd, vd)
     if args.copy_calibration_mb:
         # an elementwise kernel that reads and writes exactly n * 4 bytes each (a plain DtoD copy
         # may go to a blit path that the counters do not see)

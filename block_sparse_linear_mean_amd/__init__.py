@@ -10,6 +10,8 @@ Entry points keep the C names (see include/sla.h):
     sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
     sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
     sla_attn_bwd         dQ, dK, dV of the SLA layer for a fixed block map
+    sla_hilbert_order    token order of a video latent grid along a 3-D Hilbert curve (host)
+    sla_permute_rows     apply / undo a token order on [B, H, N, d] rows
 
 `SlaForward` strings the four calls into one layer forward with every buffer
 allocated up front, so a step launches kernels only.
@@ -22,7 +24,8 @@ import torch
 
 from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
-    lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes, sla_block_map, sla_block_map_capacity,
+    lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes,
+    sla_hilbert_order, sla_permute_rows, sla_block_map, sla_block_map_capacity,
     sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
 )
@@ -37,13 +40,22 @@ class SlaForward:
     proj_w / proj_b (sla mode): the learned projection of the linear branch, [d, d] or [Hq, d, d]
     (out x in) and [d] or [Hq, d]; None = identity.  smooth_k (sla and salad modes): the linear
     branch uses the keys minus their mean over the valid tokens of each head.
+    token_order: optional int32 order of the n_valid tokens (e.g. sla_hilbert_order of the latent
+    grid): Q, K, V are gathered into that order before the layer and the output is scattered back.
     """
 
     def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_valid: int, mode: str,
                  kh_bp: int = 0, kl_bp: int = 0, n_sel: int = 0, window: int = 0,
                  w_gate: Optional[torch.Tensor] = None, scale: Optional[float] = None, out_dtype=None,
                  proj_w: Optional[torch.Tensor] = None, proj_b: Optional[torch.Tensor] = None,
-                 smooth_k: bool = False, training: bool = False):
+                 smooth_k: bool = False, training: bool = False, token_order: Optional[torch.Tensor] = None):
+        self.order = None
+        self.q_in, self.k_in, self.v_in = q, k, v
+        if token_order is not None:
+            if token_order.numel() != n_valid:
+                raise ValueError("token_order must order the n_valid tokens")
+            self.order = token_order.to(device=q.device, dtype=torch.int32).contiguous()
+            q, k, v = (torch.empty(x.shape, device=x.device, dtype=x.dtype) for x in (q, k, v))
         self.q, self.k, self.v = q, k, v
         self.n_valid = n_valid
         self.mode = mode
@@ -108,6 +120,20 @@ class SlaForward:
             self.row_states = (torch.empty((B * Hs * nb, d, d), device=dev, dtype=torch.bfloat16),
                                torch.empty((B * Hs * nb, d), **f))
         self.out = torch.empty(q.shape, device=dev, dtype=out_dtype or q.dtype)
+        # with a token order the layer writes its output in that order, then scatters it back
+        self.out_ordered = self.out if self.order is None else torch.empty_like(self.out)
+
+    def reorder(self):
+        """Gather Q, K, V into the token order (no-op without one)."""
+        if self.order is not None:
+            for src, dst in ((self.q_in, self.q), (self.k_in, self.k), (self.v_in, self.v)):
+                sla_permute_rows(src, self.order, out=dst)
+
+    def restore(self):
+        """Scatter the output back to the original token order (no-op without one)."""
+        if self.order is not None:
+            sla_permute_rows(self.out_ordered, self.order, inverse=True, out=self.out)
+        return self.out
 
     def pool_scores(self):
         return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
@@ -138,11 +164,11 @@ class SlaForward:
         if self.lin == SLA_LIN_MARGINAL:
             S, u = self.row_states
             return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps,
-                                lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out,
+                                lin_mode=SLA_LIN_ROW_STATES, scale=self.scale, H=S, z=u, out=self.out_ordered,
                                 proj_w=self.proj_w, proj_b=self.proj_b, lse=self.lse)
         return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
                             scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
-                            H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out)
+                            H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out_ordered)
 
     def backward(self, dout: torch.Tensor, maps=None, grads=None):
         """(dq, dk, dv) fp32 of sum(dout * out) after run() (or attention()) with training=True."""
@@ -153,13 +179,26 @@ class SlaForward:
             self.bwd_ws = torch.empty(sla_attn_bwd_workspace_bytes(B, H, N, d), device=self.q.device,
                                       dtype=torch.uint8)
         S, u = self.row_states
-        return sla_attn_bwd(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid, maps or self.maps, S, u,
-                            scale=self.scale, grads=grads, workspace=self.bwd_ws)
+        if self.order is None:
+            return sla_attn_bwd(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid, maps or self.maps,
+                                S, u, scale=self.scale, grads=grads, workspace=self.bwd_ws)
+        # in the token order, then scattered back (the order is a permutation: its gradient is the inverse)
+        dout_r = sla_permute_rows(dout, self.order)
+        g_r = sla_attn_bwd(self.q, self.k, self.v, self.out_ordered, dout_r, self.lse, self.n_valid,
+                           maps or self.maps, S, u, scale=self.scale, workspace=self.bwd_ws)
+        if grads is None:
+            grads = tuple(torch.empty_like(x) for x in g_r)
+        for src, dst in zip(g_r, grads):
+            sla_permute_rows(src, self.order, inverse=True, out=dst)
+        return grads
 
     def run(self) -> torch.Tensor:
-        """One full forward: pool + scores, block map, linear states, marginal sums, attention."""
+        """One full forward: (token order,) pool + scores, block map, linear states, marginal sums,
+        attention (, order undone)."""
+        self.reorder()
         self.pool_scores()
         self.block_map()
         self.kv_reduce()
         self.marginal_states()
-        return self.attention()
+        self.attention()
+        return self.restore()

@@ -57,6 +57,8 @@ _SIGS = {
     "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
                                c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P,
                                _P, _P, c_int32, _P, c_int32, _P, _P, c_size_t, _P]),
+    "sla_hilbert_order": (c_int32, [c_int32, c_int32, c_int32, _P]),
+    "sla_permute_rows": (c_int32, [POINTER(SlaTensor), _P, c_int32, c_int32, _P, _P]),
     "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 4),
     "sla_attn_bwd": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                           c_size_t, _P]),
@@ -322,3 +324,20 @@ def sla_attn_bwd(q, k, v, o, dout, lse, n_valid, maps, S, u, scale=None, grads=N
         _ptr(maps["crit_idx"]), _ptr(maps["marg_bits"]), _ptr(S), _ptr(u), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), ws_bytes, _stream(q.device)))
     return dq, dk, dv
+
+
+def sla_hilbert_order(T, H, W) -> torch.Tensor:
+    """Host int32 tensor [T*H*W]: row-major token indices in the order of a 3-D Hilbert curve."""
+    out = torch.empty(T * H * W, dtype=torch.int32)
+    _check("sla_hilbert_order", lib().sla_hilbert_order(T, H, W, ctypes.c_void_p(out.data_ptr())))
+    return out
+
+
+def sla_permute_rows(x, order, inverse=False, out=None):
+    """Gather (inverse=False) or scatter rows of x [B, H, N, d] by a device int32 order of n_order rows."""
+    _require_gpu(x, order)
+    if out is None:
+        out = torch.empty(x.shape, device=x.device, dtype=x.dtype)
+    _check("sla_permute_rows", lib().sla_permute_rows(ctypes.byref(tensor_desc(x)), _ptr(order), order.numel(),
+                                                      int(inverse), _ptr(out), _stream(x.device)))
+    return out

@@ -269,6 +269,30 @@ sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         void* out, int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Token order along a 3-D Hilbert curve ("2025稀疏注意力架构综述", section 11 SpargeAttn: reordering
+ * tokens along a Hilbert curve makes the tokens of a block more alike, raising the predicted
+ * sparsity).  For a T x H x W latent grid whose tokens are stored row-major (index (t H + h) W + w),
+ * order[n] = the row-major index of the n-th token along the curve: cells sorted by their Hilbert
+ * index on the cube of side 2^b >= max(T, H, W) (Skilling's transform, coordinates (t, h, w)).
+ * Host-only: `order` is a HOST array of T * H * W int32.  SLA_ERR_SHAPE unless T, H, W >= 1;
+ * SLA_ERR_RANGE if T H W > 2^31 - 1 or a side exceeds 2^21.
+ */
+sla_status sla_hilbert_order(int32_t T, int32_t H, int32_t W, int32_t* order);
+
+/*
+ * Apply (inverse == 0) or undo (inverse != 0) a token order on the rows of x [B, H, N, d]:
+ *   gather:  out[b,h,n,:] = x[b,h,order[n],:]   for n < n_order,
+ *   scatter: out[b,h,order[n],:] = x[b,h,n,:]   for n < n_order,
+ * rows n >= n_order are copied unchanged (padding stays at the end).  order: DEVICE int32
+ * [n_order], a permutation of 0 .. n_order - 1 (an entry out of range leaves its row in place;
+ * with repeated entries the scatter result is unspecified).  out: contiguous [B, H, N, d] in x's
+ * dtype, 16-byte aligned, not x itself.  n_order <= N.  A row copy: 2 N d (bf16: 2 bytes) bytes
+ * per head moved.  workspace: none.
+ */
+sla_status sla_permute_rows(const sla_tensor* x, const int32_t* order, int32_t n_order, int32_t inverse,
+                            void* out, void* stream);
+
 /* Workspace bytes sla_attn_bwd needs (0 for unsupported sizes). */
 size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
 
