@@ -488,3 +488,67 @@ class Forward:
 def forward(Q, K, V, **kw) -> np.ndarray:
     """Full output O [B, Hq, N, d] (float64) of the forward described in the module docstring."""
     return Forward(Q, K, V, **kw).output()
+
+
+# ----------------------------------------------------------------------------- NSA, three branches
+
+def compress_kv(X_head: np.ndarray, n_valid: int, block: int, stride: int) -> np.ndarray:
+    """Compressed tokens of one head (NSA's compressed branch: windows of `block` tokens every
+    `stride` tokens, "Sparse Attention 方法综述" section 2 and its key-parameter table): token m is
+    the mean of rows m*stride .. m*stride + block - 1, for every window inside the valid rows;
+    float64 [M, d] with M = (n_valid - block) // stride + 1 (0 if n_valid < block)."""
+    if n_valid < block:
+        return np.zeros((0, X_head.shape[1]), dtype=F64)
+    M = (n_valid - block) // stride + 1
+    return np.stack([X_head[m * stride:m * stride + block].astype(F64).mean(axis=0) for m in range(M)])
+
+
+def softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one query row over the given keys; 0 when there are none."""
+    if len(keys) == 0:
+        return np.zeros(vals.shape[1], dtype=F64)
+    x = (keys.astype(F64) @ q.astype(F64)) * float(scale)
+    p = np.exp(x - x.max())
+    return (p @ vals.astype(F64)) / p.sum()
+
+
+def nsa3_forward(Q, K, V, *, n_valid: int, n_sel: int, window: int, cmp_block: int, cmp_stride: int,
+                 w_gates, scale: Optional[float] = None) -> np.ndarray:
+    """NSA with its three parallel branches ("Sparse Attention 方法综述", section 2 NSA: compressed,
+    selected and sliding-window branches, merged), output [B, Hq, N, d] float64.
+
+    For query row t of head h (KV head g = h // (Hq/Hkv)), each branch is its own softmax attention:
+      compressed: over the compressed tokens m whose window ends at or before t
+                  (m * cmp_stride + cmp_block - 1 <= t);
+      selected:   over the keys s <= t of the row's selected blocks, the top min(n_sel, i+1) causal
+                  blocks of the GQA group's pooled scores (the NSA selection of Forward, no window);
+      window:     over the keys 0 <= t - s < window;
+    an empty branch gives 0.  O_t = sum over branches b of sigmoid(q_t . w_gates[b, h]) * O_b,
+    w_gates [3, Hq, d] in the order (compressed, selected, window).  Rows t >= n_valid are 0.
+    """
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    sel_fwd = Forward(Q, K, V, n_valid=n_valid, mode="nsa", n_sel=n_sel, window=0, scale=scale)
+    sc = sel_fwd.scale
+    W = np.asarray(w_gates, dtype=F64)
+    O = np.zeros((B, Hq, N, d), dtype=F64)
+    for b in range(B):
+        for g in range(Hkv):
+            Kg, Vg = K[b, g].astype(F64), V[b, g].astype(F64)
+            Kc = compress_kv(K[b, g], n_valid, cmp_block, cmp_stride)
+            Vc = compress_kv(V[b, g], n_valid, cmp_block, cmp_stride)
+            rows = {i: sel_fwd.map_row(b, g, i)["crit"] for i in range((n_valid + BLOCK - 1) // BLOCK)}
+            for h in range(g * G, (g + 1) * G):
+                for t in range(n_valid):
+                    q = Q[b, h, t].astype(F64)
+                    n_c = max(0, min(len(Kc), (t - cmp_block + 1) // cmp_stride + 1)) if t >= cmp_block - 1 else 0
+                    o_c = softmax_attend(q, Kc[:n_c], Vc[:n_c], sc)
+                    sel_keys = [s for j in rows[t // BLOCK] for s in range(BLOCK * j, BLOCK * (j + 1))
+                                if s <= t and s < n_valid]
+                    o_s = softmax_attend(q, Kg[sel_keys], Vg[sel_keys], sc)
+                    lo = max(0, t - window + 1)
+                    o_w = softmax_attend(q, Kg[lo:t + 1], Vg[lo:t + 1], sc) if window > 0 else np.zeros(d)
+                    gates = sigmoid(W[:, h] @ q)
+                    O[b, h, t] = gates[0] * o_c + gates[1] * o_s + gates[2] * o_w
+    return O
