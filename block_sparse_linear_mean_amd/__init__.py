@@ -11,6 +11,7 @@ Entry points keep the C names (see include/sla.h):
     sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
     sla_attn_bwd         dQ, dK, dV of the SLA layer for a fixed block map
     sla_hilbert_order    token order of a video latent grid along a 3-D Hilbert curve (host)
+    sla_nsa3_fwd         NSA with compressed, selected and window branches, gated
     sla_permute_rows     apply / undo a token order on [B, H, N, d] rows
 
 `SlaForward` strings the four calls into one layer forward with every buffer
@@ -25,7 +26,7 @@ import torch
 from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
     lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes,
-    sla_hilbert_order, sla_permute_rows, sla_block_map, sla_block_map_capacity,
+    sla_hilbert_order, sla_nsa3_fwd, sla_nsa3_workspace_bytes, sla_permute_rows, sla_block_map, sla_block_map_capacity,
     sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
 )

@@ -57,6 +57,9 @@ _SIGS = {
     "sla_attn_fwd": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_float,
                                c_int32, c_int32, c_int32, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P,
                                _P, _P, c_int32, _P, c_int32, _P, _P, c_size_t, _P]),
+    "sla_nsa3_workspace_bytes": (c_size_t, [c_int32] * 10),
+    "sla_nsa3_fwd": (c_int32, [POINTER(SlaTensor)] * 3 + [c_int32, c_float, _P, _P, _P, c_int32, c_int32, c_int32, _P,
+                                                          _P, c_int32, _P, c_size_t, _P]),
     "sla_hilbert_order": (c_int32, [c_int32, c_int32, c_int32, _P]),
     "sla_permute_rows": (c_int32, [POINTER(SlaTensor), _P, c_int32, c_int32, _P, _P]),
     "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 4),
@@ -340,4 +343,33 @@ def sla_permute_rows(x, order, inverse=False, out=None):
         out = torch.empty(x.shape, device=x.device, dtype=x.dtype)
     _check("sla_permute_rows", lib().sla_permute_rows(ctypes.byref(tensor_desc(x)), _ptr(order), order.numel(),
                                                       int(inverse), _ptr(out), _stream(x.device)))
+    return out
+
+
+def sla_nsa3_workspace_bytes(B, Hq, Hkv, N, d, dtype, n_valid, window, cmp_block, cmp_stride) -> int:
+    return int(lib().sla_nsa3_workspace_bytes(B, Hq, Hkv, N, d, dtype, n_valid, window, cmp_block, cmp_stride))
+
+
+def sla_nsa3_fwd(q, k, v, n_valid, sel_maps, w_gates, window=512, cmp_block=32, cmp_stride=16, scale=None,
+                 out=None, out_dtype=None, workspace=None):
+    """Three-branch NSA output [B, Hq, N, d]: gated compressed + selected + window attention.
+
+    sel_maps: the causal selection map of sla_block_map (group-summed scores, window 0);
+    w_gates: float32 [3, Hq, d] gate weights (compressed, selected, window).
+    """
+    _require_gpu(q, k, v, w_gates)
+    B, Hq, N, d = q.shape
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    odt = SLA_F32 if out.dtype == torch.float32 else SLA_BF16
+    dt = SLA_BF16 if q.dtype == torch.bfloat16 else SLA_F32
+    ws = sla_nsa3_workspace_bytes(B, Hq, k.shape[1], N, d, dt, n_valid, window, cmp_block, cmp_stride)
+    if workspace is None:
+        workspace = torch.empty(ws, device=q.device, dtype=torch.uint8)
+    qd, kd, vd = tensor_desc(q), tensor_desc(k), tensor_desc(v)
+    _check("sla_nsa3_fwd", lib().sla_nsa3_fwd(
+        ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), n_valid, float(scale), _ptr(sel_maps["crit_rowptr"]),
+        _ptr(sel_maps["crit_idx"]), _ptr(sel_maps["crit_flags"]), window, cmp_block, cmp_stride, _ptr(w_gates),
+        _ptr(out), odt, _ptr(workspace), ws, _stream(q.device)))
     return out

@@ -41,6 +41,9 @@ struct AttnParams {
   const void* v;
   int64_t qsB, qsH, qsN, ksB, ksH, ksN, vsB, vsH, vsN;
   int Hq, Hkv, Hs, N, nqb, n_valid, window, group_map;
+  int nkb, n_keys;      // key blocks and valid keys (= nqb, n_valid unless the keys are compressed tokens)
+  int cmp_block, cmp_stride;   // compressed keys (cmp_stride > 0): key m is visible to query t iff
+                               // m * cmp_stride + cmp_block - 1 <= t; otherwise key s iff s <= t (causal)
   float scale_log2;
   const int* crit_rowptr;
   const int* crit_idx;
@@ -109,6 +112,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int tq = kBlock * i + 32 * (w % 2) + l32; // this lane's query row
   const bool qvalid = tq < p.n_valid;
+  // causal limit: key s is visible iff s <= tlim (s <= tq; for compressed keys s * stride + block - 1 <= tq)
+  const int tlim = !CAUSAL || p.cmp_stride <= 0 ? tq
+                   : (tq >= p.cmp_block - 1 ? (tq - p.cmp_block + 1) / p.cmp_stride : -1);
   bf16x8 qf[kQs];
 #pragma unroll
   for (int ks = 0; ks < kQs; ++ks)
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto entry = [&](int n, int v0, int v1) {   // n = position relative to lbase, 0 <= n < 128
     return n < 64 ? __builtin_amdgcn_readlane(v0, n) : __builtin_amdgcn_readlane(v1, n - 64);
   };
-  auto safe_block = [&](int jraw) { return unsigned(jraw) < unsigned(p.nqb) ? jraw : 0; };
+  auto safe_block = [&](int jraw) { return unsigned(jraw) < unsigned(p.nkb) ? jraw : 0; };
   if (cbeg < cend) {
     const int j0 = safe_block(entry(0, lj0, lj1));
     stage_tile<T, D, true, NW>(K, p.ksN, j0, Kb, koff);
@@ -171,12 +177,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
     }
     const int jraw = entry(pi - lbase, lj0, lj1);
-    const bool jok = unsigned(jraw) < unsigned(p.nqb);   // a malformed entry reads block 0, fully masked
+    const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
     const int j = jok ? jraw : 0;
     const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
     const bool more = pi + 1 < cend;
     const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
-    const int rv = p.n_valid - kBlock * j;          // valid rows of this block (may exceed 64)
+    const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
 
     // ---- K_j resident (V_j may still be in flight): the previous block's last barrier
     // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
@@ -207,8 +213,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // key s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot: every test compares
       // C with a per-lane bound, so no per-slot key index has to live in registers
       const int rel = kBlock * j + 4 * lg;
-      const int lim_valid = jok ? p.n_valid - rel : 0;   // s < n_valid      <=> C < lim_valid
-      const int lim_causal = tq - rel;                    // s <= tq          <=> C <= lim_causal
+      const int lim_valid = jok ? p.n_keys - rel : 0;    // s < n_keys       <=> C < lim_valid
+      const int lim_causal = tlim - rel;                  // s <= tlim        <=> C <= lim_causal
       const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
       const bool sel = flag & 1;
 #pragma unroll
@@ -452,6 +458,38 @@ static void launch_attn(const AttnParams& p, int causal, int lin, int hg, dim3 g
   }
 }
 
+// One causal pass of the selected-block kernel over explicit block lists (group map rows), fp32
+// output: the building block of the three NSA branches.  k / v may be compressed tokens
+// (cmp_stride > 0, n_keys of them); window > 0 adds the sliding-window rule for blocks without
+// flag bit 0.
+sla_status launch_causal_pass(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int n_valid,
+                              int n_keys, float scale, int window, int cmp_block, int cmp_stride, const int* rowptr,
+                              const int* idx, const uint8_t* flags, float* out, hipStream_t st) {
+  const int nqb = q->N / kBlock;
+  AttnParams p{};
+  p.q = q->ptr; p.k = k->ptr; p.v = v->ptr;
+  p.qsB = q->sB; p.qsH = q->sH; p.qsN = q->sN;
+  p.ksB = k->sB; p.ksH = k->sH; p.ksN = k->sN;
+  p.vsB = v->sB; p.vsH = v->sH; p.vsN = v->sN;
+  p.Hq = q->H; p.Hkv = k->H; p.Hs = k->H; p.N = q->N; p.nqb = nqb; p.n_valid = n_valid;
+  p.nkb = k->N / kBlock; p.n_keys = n_keys; p.cmp_block = cmp_block; p.cmp_stride = cmp_stride;
+  p.window = window; p.group_map = 1;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.crit_rowptr = rowptr; p.crit_idx = idx; p.crit_flags = flags;
+  p.out = out; p.out_f32 = 1;
+  const int hg = (q->H / k->H) % kGroupHeads == 0 ? kGroupHeads : 1;
+  const dim3 grid(nqb * (q->H / hg) * q->B);
+  const bool bf = q->dtype == SLA_BF16;
+  if (q->d == 128) {
+    if (bf) launch_attn<bf16raw, 128>(p, 1, SLA_LIN_NONE, hg, grid, st);
+    else launch_attn<float, 128>(p, 1, SLA_LIN_NONE, hg, grid, st);
+  } else {
+    if (bf) launch_attn<bf16raw, 64>(p, 1, SLA_LIN_NONE, hg, grid, st);
+    else launch_attn<float, 64>(p, 1, SLA_LIN_NONE, hg, grid, st);
+  }
+  return launch_status();
+}
+
 }  // namespace sla
 
 extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
@@ -492,6 +530,7 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
   p.ksB = k->sB; p.ksH = k->sH; p.ksN = k->sN;
   p.vsB = v->sB; p.vsH = v->sH; p.vsN = v->sN;
   p.Hq = q->H; p.Hkv = k->H; p.Hs = Hs; p.N = q->N; p.nqb = nqb; p.n_valid = n_valid;
+  p.nkb = nqb; p.n_keys = n_valid; p.cmp_block = 0; p.cmp_stride = 0;
   p.window = window_tokens; p.group_map = group_map ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx; p.crit_flags = crit_flags;

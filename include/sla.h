@@ -293,6 +293,32 @@ sla_status sla_hilbert_order(int32_t T, int32_t H, int32_t W, int32_t* order);
 sla_status sla_permute_rows(const sla_tensor* x, const int32_t* order, int32_t n_order, int32_t inverse,
                             void* out, void* stream);
 
+/* Workspace bytes sla_nsa3_fwd needs (0 for unsupported arguments). */
+size_t sla_nsa3_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d, int32_t dtype,
+                                int32_t n_valid, int32_t window_tokens, int32_t cmp_block, int32_t cmp_stride);
+
+/*
+ * NSA with its three parallel branches ("Sparse Attention 方法综述", section 2 NSA: compressed,
+ * selected and sliding-window branches merged; key parameters: compression block 32 with stride
+ * 16, 16 selected blocks of 64, a 512-token window).  For query row t of head h (KV head g):
+ *   compressed: softmax attention over compressed tokens m, each the mean of K (and V) rows
+ *               m * cmp_stride .. m * cmp_stride + cmp_block - 1 (windows inside the valid rows),
+ *               visible when m * cmp_stride + cmp_block - 1 <= t;
+ *   selected:   softmax attention over keys s <= t of the blocks in the selection map (the
+ *               causal map sla_block_map writes with window_tokens = 0 from group-summed scores);
+ *   window:     softmax attention over keys 0 <= t - s < window_tokens;
+ *   O[t] = sum over the branches b = (compressed, selected, window) of
+ *          sigmoid(q_t . w_gates[b, h]) * O_b[t]   (w_gates: fp32 [3, Hq, d]; an empty branch is 0).
+ * Rows t >= n_valid are written as 0.  q [B, Hq, N, d], k, v [B, Hkv, N, d], one dtype; out
+ * contiguous [B, Hq, N, d] in out_dtype.  Arithmetic as sla_attn_fwd (bf16 matrix-core products,
+ * fp32 statistics); compressed tokens are fp32 means stored in the input dtype.
+ * workspace: sla_nsa3_workspace_bytes(...) bytes (compressed K/V, block lists, three fp32 outputs).
+ */
+sla_status sla_nsa3_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
+                        float scale, const int32_t* sel_rowptr, const int32_t* sel_idx, const uint8_t* sel_flags,
+                        int32_t window_tokens, int32_t cmp_block, int32_t cmp_stride, const float* w_gates,
+                        void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes sla_attn_bwd needs (0 for unsupported sizes). */
 size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
 

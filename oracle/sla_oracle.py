@@ -513,7 +513,8 @@ def softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: flo
 
 
 def nsa3_forward(Q, K, V, *, n_valid: int, n_sel: int, window: int, cmp_block: int, cmp_stride: int,
-                 w_gates, scale: Optional[float] = None) -> np.ndarray:
+                 w_gates, scale: Optional[float] = None, heads: Optional[Iterable[int]] = None,
+                 rows: Optional[Iterable[int]] = None) -> np.ndarray:
     """NSA with its three parallel branches ("Sparse Attention 方法综述", section 2 NSA: compressed,
     selected and sliding-window branches, merged), output [B, Hq, N, d] float64.
 
@@ -525,6 +526,7 @@ def nsa3_forward(Q, K, V, *, n_valid: int, n_sel: int, window: int, cmp_block: i
       window:     over the keys 0 <= t - s < window;
     an empty branch gives 0.  O_t = sum over branches b of sigmoid(q_t . w_gates[b, h]) * O_b,
     w_gates [3, Hq, d] in the order (compressed, selected, window).  Rows t >= n_valid are 0.
+    heads / rows: compute only these query heads and rows (the others stay 0).
     """
     B, Hq, N, d = Q.shape
     Hkv = K.shape[1]
@@ -538,13 +540,17 @@ def nsa3_forward(Q, K, V, *, n_valid: int, n_sel: int, window: int, cmp_block: i
             Kg, Vg = K[b, g].astype(F64), V[b, g].astype(F64)
             Kc = compress_kv(K[b, g], n_valid, cmp_block, cmp_stride)
             Vc = compress_kv(V[b, g], n_valid, cmp_block, cmp_stride)
-            rows = {i: sel_fwd.map_row(b, g, i)["crit"] for i in range((n_valid + BLOCK - 1) // BLOCK)}
-            for h in range(g * G, (g + 1) * G):
-                for t in range(n_valid):
+            hs = [h for h in range(g * G, (g + 1) * G) if heads is None or h in set(heads)]
+            if not hs:
+                continue
+            ts = [t for t in (range(n_valid) if rows is None else rows) if t < n_valid]
+            sel_rows = {i: sel_fwd.map_row(b, g, i)["crit"] for i in sorted({t // BLOCK for t in ts})}
+            for h in hs:
+                for t in ts:
                     q = Q[b, h, t].astype(F64)
                     n_c = max(0, min(len(Kc), (t - cmp_block + 1) // cmp_stride + 1)) if t >= cmp_block - 1 else 0
                     o_c = softmax_attend(q, Kc[:n_c], Vc[:n_c], sc)
-                    sel_keys = [s for j in rows[t // BLOCK] for s in range(BLOCK * j, BLOCK * (j + 1))
+                    sel_keys = [s for j in sel_rows[t // BLOCK] for s in range(BLOCK * j, BLOCK * (j + 1))
                                 if s <= t and s < n_valid]
                     o_s = softmax_attend(q, Kg[sel_keys], Vg[sel_keys], sc)
                     lo = max(0, t - window + 1)

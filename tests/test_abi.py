@@ -27,7 +27,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sla_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sla_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(L):
@@ -212,3 +212,23 @@ def test_attn_bwd_validation(L):
     assert call(ws=P, wsb=16) == EWS
     assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128) > 0
     assert L.sla_attn_bwd_workspace_bytes(1, 2, 100, 128) == 0
+
+
+def test_nsa3_validation(L):
+    q = desc(H=4)
+    kv = desc(H=1)
+    def call(qq=q, kk=kv, vv=kv, nv=256, scale=0.1, rp=P, ci=P, cf=P, win=512, blk=32, st=16, wg=P, out=P, odt=0,
+             ws=None, wsb=0):
+        return L.sla_nsa3_fwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), nv, scale, rp, ci, cf, win, blk, st,
+                              wg, out, odt, ws, wsb, None)
+    assert call(wg=None) == ENULL
+    assert call(cf=None) == ENULL
+    assert call(kk=desc(H=3), vv=desc(H=3)) == ESHAPE
+    assert call(blk=0) == ERANGE
+    assert call(st=0) == ERANGE
+    assert call(win=-1) == ERANGE
+    assert call(odt=3) == EUNSUP
+    assert call(wg=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call() == EWS
+    assert L.sla_nsa3_workspace_bytes(1, 4, 1, 256, 128, 0, 256, 512, 32, 16) > 0
+    assert L.sla_nsa3_workspace_bytes(1, 4, 3, 256, 128, 0, 256, 512, 32, 16) == 0
