@@ -152,6 +152,50 @@ def captured_mass(w, qd, kd, vd):
     return out
 
 
+def bench_nsa3(args, w, qd, kd, vd):
+    """Time NSA with its three branches (compressed 32/16 tokens, 16 selected blocks, 512-token window,
+    gated merge) on an NSA workload: pooled scores, the selection map and sla_nsa3_fwd per step."""
+    import torch
+    import block_sparse_linear_mean_amd as sla
+    if w.mode != "nsa":
+        raise SystemExit("--nsa-branches 3 needs an nsa workload")
+    layer = sla.SlaForward(qd, kd, vd, w.Nv, "nsa", n_sel=w.n_sel, window=0)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    wg = (torch.randn((3, w.Hq, w.d), generator=g) / w.d ** 0.5).to(qd.device)
+    B, Hq, N, d = qd.shape
+    ws = torch.empty(sla.sla_nsa3_workspace_bytes(B, Hq, w.Hkv, N, d, 0 if w.dtype == "bf16" else 1, w.Nv,
+                                                  w.window, 32, 16), device=qd.device, dtype=torch.uint8)
+    out = torch.empty_like(qd)
+    steps = {"pool_scores": layer.pool_scores, "block_map": layer.block_map,
+             "nsa3": lambda: sla.sla_nsa3_fwd(qd, kd, vd, w.Nv, layer.maps, wg, window=w.window, out=out, workspace=ws)}
+    for _ in range(args.warmup):
+        for fn in steps.values():
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record()
+        for i, fn in enumerate(steps.values()):
+            fn()
+            ev[s_][i + 1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    pass_ms = {name: sum(ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(args.steps)) / args.steps
+               for i, name in enumerate(steps)}
+    log("bench: per-pass ms " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in pass_ms.items()) + f"; wall {ms_step:.4f}")
+    print(json.dumps({
+        "metric": "NSA (compressed + selected + window, gated) fwd ms/layer + effective TFLOP/s",
+        "value": round(w.dense_flops() / (ms_step / 1e3) / 1e12, 3),
+        "unit": "TFLOP/s (effective, dense-equivalent causal)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "branches": 3, "cmp_block": 32, "cmp_stride": 16, "n_sel": w.n_sel,
+                   "window": w.window},
+        "passes": {k_: round(v_, 5) for k_, v_ in pass_ms.items()},
+    }))
+
+
 def bench_backward(args, w, qd, kd, vd):
     """Time the backward (dQ, dK, dV of one SLA layer for its block map) and print one JSON line.
 
@@ -288,6 +332,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead (sla workloads)")
     ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",
                     help="run the layer on Q, K, V gathered along a 3-D Hilbert curve of the latent grid")
+    ap.add_argument("--nsa-branches", type=int, choices=[2, 3], default=2,
+                    help="3: time NSA with its compressed branch and gated merge (nsa workloads)")
     ap.add_argument("--captured-mass", action="store_true",
                     help="also report the dense attention mass the critical blocks capture (row-major and Hilbert)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -328,6 +374,9 @@ def main():
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     if args.backward:
         bench_backward(args, w, qd, kd, vd)
+        return
+    if args.nsa_branches == 3:
+        bench_nsa3(args, w, qd, kd, vd)
         return
     order = None
     if args.token_order == "hilbert":

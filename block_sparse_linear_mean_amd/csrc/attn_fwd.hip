@@ -67,12 +67,18 @@ struct WgCoord {
   int i, h, b;
 };
 // hg heads per workgroup (hg divides the group size G): h is the workgroup's first head
-__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg) {
+// Causal rows do work that grows with i: there (heavy_first) each XCD's range takes every 8th
+// query block, largest i first, so the XCDs stay balanced and the longest blocks start first.
+__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg, bool heavy_first = false) {
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int G = Hq / Hkv, ng = G / hg;
   const int hh = logical % ng;
   const int rest = logical / ng;
-  const int i = rest % nqb;
+  int i = rest % nqb;
+  if (heavy_first) {
+    const int per = nqb / 8;
+    i = (per > 0 && i < 8 * per) ? nqb - 1 - ((i % per) * 8 + i / per) : nqb - 1 - i;
+  }
   const int bg = rest / nqb;
   const int g = bg % Hkv, b = bg / Hkv;
   return WgCoord{i, g * G + hh * hg, b};
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int t = threadIdx.x, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: head and K/V bases in SGPRs
-  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, NW / 2);
+  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, NW / 2, CAUSAL);
   const int i = wc.i, h = wc.h + w / 2, b = wc.b;  // this wavefront's head
   const int G = p.Hq / p.Hkv;
   const int g = h / G;

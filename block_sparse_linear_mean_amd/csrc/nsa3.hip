@@ -93,19 +93,46 @@ __device__ __forceinline__ int cmp_count(int i, int n_valid, int M, int block, i
   const int m = min((t - block + 1) / stride, M - 1);
   return m / kBlock + 1;
 }
+// Row offsets of one head's compressed lists: an exclusive prefix of the per-block counts, by one
+// workgroup of 1024 threads (4 query blocks per thread, then a scan of the thread sums in LDS);
+// head[i] for i = 0 .. nqb (head[nqb] = entries per head).  nqb <= 4096.
+__global__ __launch_bounds__(1024) void cmp_prefix_kernel(int nqb, int n_valid, int M, int block, int stride,
+                                                          int* __restrict__ head) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * t + k;
+    c[k] = i < nqb ? cmp_count(i, n_valid, M, block, stride) : 0;
+    sum += c[k];
+  }
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {       // inclusive scan (Hillis-Steele)
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - sum;                        // exclusive prefix of this thread's first block
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * t + k;
+    if (i < nqb) head[i] = run;
+    run += c[k];
+  }
+  if (t == 1023) head[nqb] = part[1023];           // entries per head
+}
+
+// Lists of every row from one head's offsets (head[0 .. nqb], written by cmp_prefix_kernel).
 __global__ __launch_bounds__(256) void cmp_lists_kernel(int rows, int nqb, int n_valid, int M, int block, int stride,
-                                                        int* __restrict__ rowptr, int* __restrict__ idx,
-                                                        uint8_t* __restrict__ flags) {
+                                                        const int* __restrict__ head, int* __restrict__ rowptr,
+                                                        int* __restrict__ idx, uint8_t* __restrict__ flags) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r > rows) return;
   const int bg = r / nqb, i = r % nqb;
-  int64_t per_head = 0, before = 0;
-  for (int i2 = 0; i2 < nqb; ++i2) {
-    const int c = cmp_count(i2, n_valid, M, block, stride);
-    per_head += c;
-    if (i2 < i) before += c;
-  }
-  const int64_t off = int64_t(bg) * per_head + before;
+  const int64_t off = int64_t(bg) * head[nqb] + head[i];
   rowptr[r] = int(off);
   if (r == rows) return;
   const int n = cmp_count(i, n_valid, M, block, stride);
@@ -178,7 +205,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 struct Nsa3Layout {
   int M, Mpad, reach, rows;
   int64_t n_win, n_cmp;
-  size_t kc, vc, wrp, widx, wfl, crp, cidx, cfl, oc, os, ow, total;
+  size_t kc, vc, wrp, widx, wfl, chead, crp, cidx, cfl, oc, os, ow, total;
 };
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -200,6 +227,7 @@ static Nsa3Layout nsa3_layout(int B, int Hq, int Hkv, int N, int d, int eb, int 
   L.wrp = take(size_t(L.rows + 1) * 4);
   L.widx = take(size_t(std::max<int64_t>(L.n_win, 1)) * 4);
   L.wfl = take(size_t(std::max<int64_t>(L.n_win, 1)));
+  L.chead = take(size_t(nqb + 1) * 4);
   L.crp = take(size_t(L.rows + 1) * 4);
   L.cidx = take(size_t(std::max<int64_t>(L.n_cmp, 1)) * 4);
   L.cfl = take(size_t(std::max<int64_t>(L.n_cmp, 1)));
@@ -243,6 +271,7 @@ extern "C" sla_status sla_nsa3_fwd(const sla_tensor* q, const sla_tensor* k, con
   if (!aligned16(out) || !aligned16(w_gates)) return SLA_ERR_ALIGN;
   if (out_dtype != SLA_BF16 && out_dtype != SLA_F32) return SLA_ERR_UNSUPPORTED;
   const int B = q->B, Hq = q->H, Hkv = k->H, N = q->N, d = q->d, nqb = N / kBlock;
+  if (nqb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
   const int eb = q->dtype == SLA_BF16 ? 2 : 4;
   const Nsa3Layout L = nsa3_layout(B, Hq, Hkv, N, d, eb, n_valid, window_tokens, cmp_block, cmp_stride);
   if (workspace == nullptr || workspace_bytes < L.total || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
@@ -272,9 +301,10 @@ extern "C" sla_status sla_nsa3_fwd(const sla_tensor* q, const sla_tensor* k, con
   if (L.reach >= 0)
     window_lists_kernel<<<lgrid, 256, 0, s>>>(L.rows, nqb, L.reach, reinterpret_cast<int*>(ws + L.wrp),
                                               reinterpret_cast<int*>(ws + L.widx), ws + L.wfl);
+  cmp_prefix_kernel<<<1, 1024, 0, s>>>(nqb, n_valid, L.M, cmp_block, cmp_stride, reinterpret_cast<int*>(ws + L.chead));
   cmp_lists_kernel<<<lgrid, 256, 0, s>>>(L.rows, nqb, n_valid, L.M, cmp_block, cmp_stride,
-                                         reinterpret_cast<int*>(ws + L.crp), reinterpret_cast<int*>(ws + L.cidx),
-                                         ws + L.cfl);
+                                         reinterpret_cast<const int*>(ws + L.chead), reinterpret_cast<int*>(ws + L.crp),
+                                         reinterpret_cast<int*>(ws + L.cidx), ws + L.cfl);
   // 3. the three branches, each normalised on its own, into fp32 buffers
   float* oc = reinterpret_cast<float*>(ws + L.oc);
   float* os = reinterpret_cast<float*>(ws + L.os);
