@@ -64,7 +64,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 __device__ __forceinline__ int tpos(int r, int c8) {
-  return trs_pos<2 * D>(r, c8);
+  return v_pos<D>(r, c8);      // the layout the direct-to-LDS tile copies write
 }
 
 // Byte offset, in a tpos tile, of the transposing read that gives lane l (group g = l / 16,

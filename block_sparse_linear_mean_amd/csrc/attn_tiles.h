@@ -25,9 +25,19 @@ template <int D>
 __device__ __forceinline__ int k_pos(int r, int c) {
   return r * AttnTile<D>::kRowB + 16 * (c ^ (r % AttnTile<D>::kChunks));
 }
+// V layout: the transposing-read swizzle c ^ 2 (r % 4); at d = 128 also the chunks whose bit 1
+// is set move to the other half of the row (c ^ 8): the two 16-lane groups of a 32-lane read
+// pass then touch disjoint banks (chunks 4 dt + {0, 1} and 4 dt + {2, 3} of the same 4 rows).
 template <int D>
 __device__ __forceinline__ int v_pos(int r, int c) {
+  if constexpr (D == 128) return r * AttnTile<D>::kRowB + 16 * (c ^ (2 * (r % 4)) ^ (8 * ((c >> 1) & 1)));
   return trs_pos<AttnTile<D>::kRowB>(r, c);
+}
+// The chunk that v_pos places at position pos of row r (its inverse within a row).
+template <int D>
+__device__ __forceinline__ int v_chunk_at(int r, int pos) {
+  if constexpr (D == 128) return pos ^ (2 * (r % 4)) ^ (8 * (((pos >> 1) & 1) ^ (r & 1)));
+  return pos ^ (2 * (r % 4));
 }
 
 // Stage rows 64 j .. 64 j + 63 of X (row stride sN elements) into an LDS tile.  bf16 inputs go
@@ -58,7 +68,7 @@ __device__ __forceinline__ StageOff<D, NW> stage_offsets(int64_t sN) {
 #pragma unroll
   for (int m = 0; m < SO::kLanes; ++m) {
     const int q = w * SO::kSteps + m;             // q % 4 repeats with period 4 in m
-    const int c = KLAYOUT ? pc ^ ((q * R + r) % Tl::kChunks) : pc ^ (2 * (r % 4));
+    const int c = KLAYOUT ? pc ^ ((q * R + r) % Tl::kChunks) : v_chunk_at<D>(r, pc);
     o.lane[m] = uint32_t(2 * (r * sN + 8 * c));
   }
 #pragma unroll
