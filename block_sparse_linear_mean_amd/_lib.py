@@ -42,7 +42,8 @@ _SIGS = {
     "sla_status_str": (c_char_p, [c_int32]),
     "sla_counts": (c_int32, [c_int32, c_int32, c_int32, _I32P, _I32P]),
     "sla_pool_scores": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_int32, c_int32, c_float,
-                                  _P, _P, _P, _P, _P]),
+                                  _P, _P, _P, _P, _P, c_size_t, _P]),
+    "sla_pool_scores_workspace_bytes": (c_size_t, [c_int32] * 6),
     "sla_block_map_capacity": (c_int64, [c_int32] * 9),
     "sla_block_map_workspace_bytes": (c_size_t, [c_int32] * 7),
     "sla_block_map": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -164,10 +165,14 @@ def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, wa
                    scores=torch.empty((B, Hs, nb, nb), **f))
         if want_probs:
             out["probs"] = torch.empty((B, Hs, nb, nb), **f)
+    ws = int(lib().sla_pool_scores_workspace_bytes(B, Hq, Hkv, N, d, int(group_sum)))
+    if ws and (out.get("workspace") is None or out["workspace"].numel() < ws):
+        out["workspace"] = torch.empty(ws, device=q.device, dtype=torch.uint8)
     qd, kd = tensor_desc(q), tensor_desc(k)
     _check("sla_pool_scores", lib().sla_pool_scores(
         ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale),
-        _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]), _ptr(out.get("probs")), _stream(q.device)))
+        _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]), _ptr(out.get("probs")),
+        _ptr(out.get("workspace")), ws, _stream(q.device)))
     return out
 
 

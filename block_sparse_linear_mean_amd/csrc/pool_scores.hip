@@ -73,48 +73,64 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int6
   }
 }
 
-// Pooled scores, one 64 (i) x 128 (j) tile of one score matrix per workgroup; each thread owns
-// 4 x 8 outputs.  scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a sequential
-// fp64 FMA chain over r; qsum sums the group's pooled queries in fp64 when group_sum is set.
-// The pooled vectors stream through LDS 32 features at a time, the next chunk's loads in flight
-// in registers while the current chunk is multiplied.
-constexpr int kScI = 64, kScJ = 128, kScR = 32;
+// Group sums of the pooled queries: qsum[b,g,i,r] = sum over the group's heads h (ascending) of
+// q_pool[b,h,i,r], in fp64 (exact for the fp32 pooled values in practice).  One thread per element.
+__global__ __launch_bounds__(256) void qsum_kernel(const float* __restrict__ qpool, int Hq, int Hkv, int nb, int d,
+                                                   double* __restrict__ qsum) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
+  if (e >= int64_t(nb) * d) return;
+  double s = 0.0;
+  for (int hh = 0; hh < G; ++hh) s += double(qpool[(int64_t(b) * Hq + g * G + hh) * nb * d + e]);
+  qsum[int64_t(bg) * nb * d + e] = s;
+}
 
-template <int D>
+// Pooled scores, one 64 (i) x TJ (j) tile of one score matrix per workgroup; each thread owns
+// 4 x TJ/16 outputs.  scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a
+// sequential fp64 FMA chain over r; with group_sum, qsum is the group's fp64 sum of pooled
+// queries (read from qsum_kernel's output when given, else summed here).  The pooled vectors stream through LDS 32 features at a time, the next
+// chunk's loads in flight in registers while the current chunk is multiplied.
+constexpr int kScI = 64, kScR = 32;
+
+template <int D, int TJ>
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qpool,
                                                      const float* __restrict__ kpool, int Hq, int Hkv,
                                                      int Hs, int nb, int group_sum, int causal,
-                                                     double scale, float* __restrict__ scores) {
+                                                     double scale, const double* __restrict__ qsum,
+                                                     float* __restrict__ scores) {
+  constexpr int kJ = TJ / 16;                    // outputs per thread along j
+  constexpr int kKl = TJ * kScR / 256;           // k-chunk elements per thread
   const int bs = blockIdx.z;
   const int b = bs / Hs, s = bs % Hs;
   const int G = Hq / Hkv;
   const int g = group_sum ? s : s / G;
-  const int i0 = blockIdx.y * kScI, j0 = blockIdx.x * kScJ;
+  const int i0 = blockIdx.y * kScI, j0 = blockIdx.x * TJ;
   const int t = threadIdx.x;
   const int tx = t % 16, ty = t / 16;
   float* out = scores + int64_t(bs) * nb * nb;
 
   if (causal && j0 > i0 + kScI - 1) {   // the whole tile lies above the diagonal
-    for (int e = t; e < kScI * kScJ; e += 256) {
-      const int ii = i0 + e / kScJ, jj = j0 + e % kScJ;
+    for (int e = t; e < kScI * TJ; e += 256) {
+      const int ii = i0 + e / TJ, jj = j0 + e % TJ;
       if (ii < nb && jj < nb) out[int64_t(ii) * nb + jj] = -__builtin_inff();
     }
     return;
   }
 
   __shared__ double qs[kScI][kScR + 1];
-  __shared__ float ks[kScJ][kScR + 1];
-  double acc[4][8];
+  __shared__ float ks[TJ][kScR + 1];
+  double acc[4][kJ];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0;
+    for (int c = 0; c < kJ; ++c) acc[a][c] = 0.0;
 
   const int gh0 = group_sum ? g * G : s;
   const int ngh = group_sum ? G : 1;
-  // staging map: q chunk 64 x 32 -> 8 elements per thread, k chunk 128 x 32 -> 16 per thread
+  const double* qs_row = qsum != nullptr ? qsum + int64_t(bs) * nb * D : nullptr;   // group sums, if given
+  // staging map: q chunk 64 x 32 -> 8 elements per thread, k chunk TJ x 32 -> kKl per thread
   double qreg[8];
-  float kreg[16];
+  float kreg[kKl];
   auto load = [&](int r0) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
@@ -122,12 +138,15 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
       const int row = e / kScR, col = e % kScR;
       const int ii = i0 + row;
       double qv = 0.0;
-      if (ii < nb)
-        for (int hh = 0; hh < ngh; ++hh) qv += double(qpool[((int64_t(b) * Hq + gh0 + hh) * nb + ii) * D + r0 + col]);
+      if (ii < nb) {
+        if (qs_row != nullptr) qv = qs_row[int64_t(ii) * D + r0 + col];
+        else
+          for (int hh = 0; hh < ngh; ++hh) qv += double(qpool[((int64_t(b) * Hq + gh0 + hh) * nb + ii) * D + r0 + col]);
+      }
       qreg[n] = qv;
     }
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
+    for (int n = 0; n < kKl; ++n) {
       const int e = t + 256 * n;
       const int row = e / kScR, col = e % kScR;
       const int jj = j0 + row;
@@ -140,27 +159,27 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 #pragma unroll
     for (int n = 0; n < 8; ++n) { const int e = t + 256 * n; qs[e / kScR][e % kScR] = qreg[n]; }
 #pragma unroll
-    for (int n = 0; n < 16; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = kreg[n]; }
+    for (int n = 0; n < kKl; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = kreg[n]; }
     __syncthreads();
     if (r0 + kScR < D) load(r0 + kScR);
 #pragma unroll 8
     for (int r = 0; r < kScR; ++r) {
-      double qa[4], kb[8];
+      double qa[4], kb[kJ];
 #pragma unroll
       for (int a = 0; a < 4; ++a) qa[a] = qs[ty + 16 * a][r];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) kb[c] = double(ks[tx + 16 * c][r]);
+      for (int c = 0; c < kJ; ++c) kb[c] = double(ks[tx + 16 * c][r]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[a][c] = __fma_rn(qa[a], kb[c], acc[a][c]);
+        for (int c = 0; c < kJ; ++c) acc[a][c] = __fma_rn(qa[a], kb[c], acc[a][c]);
     }
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int ii = i0 + ty + 16 * a;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kJ; ++c) {
       const int jj = j0 + tx + 16 * c;
       if (ii < nb && jj < nb) {
         const float v = (causal && jj > ii) ? -__builtin_inff() : float(acc[a][c] * scale);
@@ -170,7 +189,6 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
   }
 }
 
-// Row softmax of the score rows (diagnostic output): one wavefront per row.
 __global__ __launch_bounds__(64) void probs_kernel(const float* __restrict__ scores, int nb,
                                                    float* __restrict__ probs) {
   const int64_t row = blockIdx.x;
@@ -204,9 +222,16 @@ static void launch_pool(const sla_tensor* q, const sla_tensor* k, int n_valid, f
 
 }  // namespace sla
 
+extern "C" size_t sla_pool_scores_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                                                  int32_t group_sum) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || N < sla::kBlock || N % sla::kBlock || (d != 64 && d != 128)) return 0;
+  return (group_sum && Hq / Hkv > 1) ? size_t(B) * Hkv * (N / sla::kBlock) * d * sizeof(double) : 0;
+}
+
 extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
                                       int32_t group_sum, int32_t causal, float scale, float* q_pool,
-                                      float* k_pool, float* scores, float* probs, void* stream) {
+                                      float* k_pool, float* scores, float* probs, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(q);
   if (st != SLA_OK) return st;
@@ -215,18 +240,27 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if (q_pool == nullptr || k_pool == nullptr || scores == nullptr) return SLA_ERR_NULL;
   if ((st = check_valid_len(n_valid, q->N)) != SLA_OK) return st;
   if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
+  const size_t need = sla_pool_scores_workspace_bytes(q->B, q->H, k->H, q->N, q->d, group_sum);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) return SLA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = q->N / kBlock;
   if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, q_pool, k_pool, s);
   else launch_pool<float>(q, k, n_valid, q_pool, k_pool, s);
   const int Hs = group_sum ? k->H : q->H;
-  dim3 grid((nb + kScJ - 1) / kScJ, (nb + kScI - 1) / kScI, q->B * Hs);
+  const double* qsum = nullptr;
+  if (group_sum && q->H / k->H > 1) {             // the group sums once, instead of in every tile
+    double* qs = static_cast<double*>(workspace);
+    qsum_kernel<<<dim3(uint32_t((int64_t(nb) * q->d + 255) / 256), uint32_t(q->B * k->H)), 256, 0, s>>>(
+        q_pool, q->H, k->H, nb, q->d, qs);
+    qsum = qs;
+  }
+  dim3 grid((nb + 127) / 128, (nb + kScI - 1) / kScI, q->B * Hs);
   if (q->d == 128)
-    scores_kernel<128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
-                                            causal ? 1 : 0, double(scale), scores);
+    scores_kernel<128, 128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
+                                                 causal ? 1 : 0, double(scale), qsum, scores);
   else
-    scores_kernel<64><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
-                                           causal ? 1 : 0, double(scale), scores);
+    scores_kernel<64, 128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
+                                                causal ? 1 : 0, double(scale), qsum, scores);
   if (probs != nullptr) probs_kernel<<<dim3(q->B * Hs * nb), 64, 0, s>>>(scores, nb, probs);
   return launch_status();
 }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SLA_ABI_VERSION 2
+#define SLA_ABI_VERSION 3
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
 #define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
@@ -117,10 +117,17 @@ sla_status sla_counts(int32_t nb, int32_t kh_bp, int32_t kl_bp, int32_t* n_crit,
  *   probs (nullable) = row softmax of scores over the row's finite candidates (fp32,
  *     same shape as scores), for diagnostics; the classification ranks the scores.
  * q and k share dtype and d; n_valid as in the conventions; scale > 0 (normally 1/sqrt(d)).
+ * workspace: sla_pool_scores_workspace_bytes(...) bytes (the fp64 group sums of the pooled
+ * queries, non-zero only with group_sum and more than one query head per KV head).
  */
 sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
                            int32_t group_sum, int32_t causal, float scale,
-                           float* q_pool, float* k_pool, float* scores, float* probs, void* stream);
+                           float* q_pool, float* k_pool, float* scores, float* probs,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sla_pool_scores needs (B, Hq, Hkv, N, d, group_sum); 0 = none. */
+size_t sla_pool_scores_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                                       int32_t group_sum);
 
 /*
  * Smooth-K shift (SLA analysis page: the open-source code zero-means K, which the paper

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert sla.sla_abi_version() == 2
+    assert sla.sla_abi_version() == 3
     for s in range(9):
         assert len(sla.sla_status_str(s)) > 0
     assert sla.sla_status_str(12345) == "unknown status"
@@ -85,7 +85,7 @@ P = ctypes.c_void_p(0x20000)   # a fake, 16-byte aligned device address: never d
 
 
 def pool_call(L, q, k, n_valid=256, scale=0.1, qp=P, kp=P, sc=P):
-    return L.sla_pool_scores(ctypes.byref(q), ctypes.byref(k), n_valid, 0, 0, scale, qp, kp, sc, None, None)
+    return L.sla_pool_scores(ctypes.byref(q), ctypes.byref(k), n_valid, 0, 0, scale, qp, kp, sc, None, None, 0, None)
 
 
 def test_pool_scores_validation(L):
@@ -104,6 +104,11 @@ def test_pool_scores_validation(L):
     assert pool_call(L, good, good, scale=0.0) == ERANGE
     assert pool_call(L, good, good, scale=float("nan")) == ERANGE
     assert pool_call(L, desc(N=64 * 4097), desc(N=64 * 4097)) == EUNSUP
+    # group-summed scores of a GQA group need the workspace for the group sums
+    q4, k1 = desc(H=4), desc(H=1)
+    assert L.sla_pool_scores(ctypes.byref(q4), ctypes.byref(k1), 256, 1, 1, 0.1, P, P, P, None, None, 0, None) == EWS
+    assert L.sla_pool_scores_workspace_bytes(1, 4, 1, 256, 128, 1) == 4 * 128 * 8
+    assert L.sla_pool_scores_workspace_bytes(1, 4, 1, 256, 128, 0) == 0
 
 
 def test_block_map_validation(L):
