@@ -53,6 +53,7 @@ struct BwdParams {
   const u16* dH;                  // [B, H, nb][c][r] bf16: gradient of H_j
   const float* dz;                // [B, H, nb][r]
   const uint32_t* critT;          // [B, H, nb][wq]: bit i of row j = block j is critical for query block i
+  const int* kv_order;            // [B * H * nb]: key-block rows, most-used first (dK/dV dispatch order)
   float* dq;                      // [B, H, N, d] fp32
   float* dk;
   float* dv;
@@ -61,6 +62,7 @@ struct BwdParams {
 constexpr int kBwWaves = 4;
 constexpr int kBwThreads = kWave * kBwWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxKeyBlocksBwd = SLA_MAX_KEY_BLOCKS;
 
 template <int D>
 __device__ __forceinline__ int tpos(int r, int c8) {
@@ -122,15 +124,20 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 
 // One thread per map row (bh, i): set bit i of row (bh, j) of the transposed critical mask for
 // every listed block j (atomic OR: the result does not depend on the order).
+// Also counts, per key-block row, the query blocks that list it (the dK/dV workload of that row).
 __global__ __launch_bounds__(256) void crit_transpose_kernel(const int* __restrict__ rowptr, const int* __restrict__ idx,
-                                                             int rows, int nb, int wq, uint32_t* __restrict__ critT) {
+                                                             int rows, int nb, int wq, uint32_t* __restrict__ critT,
+                                                             int* __restrict__ counts) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= rows) return;
   const int bh = r / nb, i = r % nb;
   for (int e = rowptr[r]; e < rowptr[r + 1]; ++e) {
     const int j = idx[e];
-    if (unsigned(j) < unsigned(nb))
-      atomicOr(critT + (int64_t(bh) * nb + j) * wq + i / 32, 1u << (i % 32));
+    if (unsigned(j) < unsigned(nb)) {
+      const uint32_t bit = 1u << (i % 32);
+      // a repeated entry (a malformed list) is counted once
+      if ((atomicOr(critT + (int64_t(bh) * nb + j) * wq + i / 32, bit) & bit) == 0u) atomicAdd(counts + bh * nb + j, 1);
+    }
   }
 }
 
@@ -490,6 +497,31 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ sparse branch, dK and dV
 
+// Dispatch order of the dK/dV workgroups: key-block rows sorted by how many query blocks list them
+// (counted by crit_transpose_kernel), most-used first, so the longest workgroups start first and
+// the round-robin dispatch spreads them over the XCDs.  One workgroup: a histogram of the counts in
+// LDS, a descending scan, a scatter (the order within one count is arbitrary; results do not depend
+// on the order).  Counts are at most nb <= 4096.
+__global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ counts, int rows, int max_count,
+                                                        int* __restrict__ order) {
+  __shared__ int hist[kMaxKeyBlocksBwd + 2];
+  const int t = threadIdx.x;
+  for (int c = t; c <= max_count + 1; c += 1024) hist[c] = 0;
+  __syncthreads();
+  for (int r = t; r < rows; r += 1024) atomicAdd(&hist[counts[r]], 1);
+  __syncthreads();
+  if (t == 0) {                                   // exclusive scan from the largest count down
+    int run = 0;
+    for (int c = max_count; c >= 0; --c) {
+      const int h = hist[c];
+      hist[c] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  for (int r = t; r < rows; r += 1024) order[atomicAdd(&hist[counts[r]], 1)] = r;
+}
+
 // One workgroup per (key block j, head); wavefront w owns keys 64 j + 16 w + l % 16.  Over the
 // query blocks i that list j as critical: S = Q K^T, dP = dO V^T, dS = P (dP - D),
 // dV^T += dO^T P, dK^T += Q^T dS.  Q, dO tiles and the rows' log-sum-exp and D are
@@ -504,7 +536,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lse_s[2][kBlock];
   __shared__ __attribute__((aligned(256))) float d_s[2][kBlock];
 
-  const int j = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int krow = p.kv_order[blockIdx.x];        // (bh, j), most-used key blocks first
+  const int j = krow % p.nb, bh = krow / p.nb, b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t % kWave, l16 = lane % 16, g = lane / 16;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
   const int s = kBlock * j + 16 * w + l16;
@@ -633,6 +666,8 @@ struct BwdWs {
   float* dz;
   uint32_t* critT;
   uint32_t* margT;
+  int* kv_counts;
+  int* kv_order;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -652,6 +687,8 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
   const size_t odz = take(size_t(rows) * d * 4);
   const size_t oc = take(size_t(rows) * wq * 4);
   const size_t om = take(size_t(rows) * wq * 4);
+  const size_t okc = take(size_t(rows) * 4);
+  const size_t oko = take(size_t(rows) * 4);
   if (ws != nullptr) {
     unsigned char* p = static_cast<unsigned char*>(base);
     ws->D = reinterpret_cast<float*>(p + oD);
@@ -661,6 +698,8 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
     ws->dz = reinterpret_cast<float*>(p + odz);
     ws->critT = reinterpret_cast<uint32_t*>(p + oc);
     ws->margT = reinterpret_cast<uint32_t*>(p + om);
+    ws->kv_counts = reinterpret_cast<int*>(p + okc);
+    ws->kv_order = reinterpret_cast<int*>(p + oko);
   }
   return off;
 }
@@ -676,7 +715,7 @@ static void launch_bwd_k_side(const BwdParams& p, int BH, hipStream_t st) {
   const dim3 grid(p.nb, BH);
   bwd_lin_k_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
   bwd_dq_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
-  bwd_dkdv_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
+  bwd_dkdv_kernel<T, D><<<dim3(p.nb * BH), kBwThreads, 0, st>>>(p);
 }
 
 }  // namespace sla
@@ -728,6 +767,7 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
   p.lse = lse; p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx;
   p.S = static_cast<const u16*>(S); p.u = u;
   p.D = ws.D; p.dS = ws.dS; p.du = ws.du; p.dH = ws.dH; p.dz = ws.dz; p.critT = ws.critT;
+  p.kv_order = ws.kv_order;
   p.dq = dq; p.dk = dk; p.dv = dv;
 
   // transposed masks (cleared by a fill kernel, then set by atomic OR)
@@ -735,10 +775,14 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
   const int64_t nbits = int64_t(rows) * p.wq;
   fill_u32_kernel<<<dim3(uint32_t((nbits + 255) / 256)), 256, 0, s>>>(ws.critT, nbits, 0u);
   fill_u32_kernel<<<dim3(uint32_t((nbits + 255) / 256)), 256, 0, s>>>(ws.margT, nbits, 0u);
-  crit_transpose_kernel<<<dim3((rows + 255) / 256), 256, 0, s>>>(crit_rowptr, crit_idx, rows, nb, p.wq, ws.critT);
+  fill_u32_kernel<<<dim3(uint32_t((rows + 255) / 256)), 256, 0, s>>>(reinterpret_cast<uint32_t*>(ws.kv_counts),
+                                                                     rows, 0u);
+  crit_transpose_kernel<<<dim3((rows + 255) / 256), 256, 0, s>>>(crit_rowptr, crit_idx, rows, nb, p.wq, ws.critT,
+                                                                 ws.kv_counts);
   const int wk = (nb + 31) / 32;
   marg_transpose_kernel<<<dim3(uint32_t((int64_t(rows) * wk + 255) / 256)), 256, 0, s>>>(marg_bits, rows, nb, wk,
                                                                                         p.wq, ws.margT);
+  kv_order_kernel<<<1, 1024, 0, s>>>(ws.kv_counts, rows, nb, ws.kv_order);
   const bool bf = q->dtype == SLA_BF16;
   // 1. linear branch, query side: dQ (linear part), D, dS_i, du_i
   if (d == 128) {
