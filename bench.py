@@ -5,7 +5,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input already
 resident in HBM: pooled scores, block map, linear key states, marginal sums and the
-attention kernel with its fused linear epilogue.  Prints one JSON line.
+attention kernel with its fused linear epilogue, in that order on one stream (--overlap runs the
+key states and marginal sums on a second HIP stream beside the scores and the block map).  Prints
+one JSON line.
 
 value = effective TFLOP/s = dense-equivalent attention FLOPs (4 B Hq Nv^2 d, halved when
 causal) / measured time per layer; ms_per_step = milliseconds per layer forward.
@@ -330,6 +332,8 @@ def main():
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead (sla workloads)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the key states and marginal sums on a second stream, overlapping scores and map")
     ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",
                     help="run the layer on Q, K, V gathered along a 3-D Hilbert curve of the latent grid")
     ap.add_argument("--nsa-branches", type=int, choices=[2, 3], default=2,
@@ -388,27 +392,29 @@ def main():
     passes_run = (["reorder"] if order is not None else []) + PASSES + (["restore"] if order is not None else [])
     log(f"bench: {args.warmup} warm-up steps")
     for _ in range(args.warmup):
-        layer.run()
+        layer.run(overlap=args.overlap)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(passes_run) + 1)] for _ in range(args.steps)]
+    # every pass timed with an event pair on the stream it runs on
+    mk = lambda: {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in passes_run}
+    ev = [mk() for _ in range(args.steps)]
+    ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     log(f"bench: {args.steps} timed steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        e = ev[s]
-        e[0].record()
-        for i, name in enumerate(passes_run):
-            getattr(layer, name)()
-            e[i + 1].record()
+        ev_step[s][0].record()
+        layer.run(overlap=args.overlap, events=ev[s])
+        ev_step[s][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    pass_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-               for i, name in enumerate(passes_run)}
-    gpu_ms = sum(pass_ms.values())
+    pass_ms = {name: sum(ev[s][name][0].elapsed_time(ev[s][name][1]) for s in range(args.steps)) / args.steps
+               for name in passes_run}
+    step_gpu_ms = sum(a.elapsed_time(b) for a, b in ev_step) / args.steps
+    gpu_ms = step_gpu_ms
     log("bench: per-pass ms " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in pass_ms.items()) +
-        f"; wall {ms_step:.4f} ms/step")
+        f"; step {step_gpu_ms:.4f} (events); wall {ms_step:.4f} ms/step")
 
     work, pairs = pass_work(w, layer)
     dom = max(PASSES, key=lambda n: pass_ms[n])

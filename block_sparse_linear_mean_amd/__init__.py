@@ -193,13 +193,50 @@ class SlaForward:
             sla_permute_rows(src, self.order, inverse=True, out=dst)
         return grads
 
-    def run(self) -> torch.Tensor:
+    def run(self, overlap: bool = False, events=None) -> torch.Tensor:
         """One full forward: (token order,) pool + scores, block map, linear states, marginal sums,
-        attention (, order undone)."""
-        self.reorder()
-        self.pool_scores()
-        self.block_map()
-        self.kv_reduce()
-        self.marginal_states()
-        self.attention()
-        return self.restore()
+        attention (, order undone).
+
+        overlap: the linear key states depend only on K and V (and, with smooth-K, on the pooled
+        keys), so they can run on a second stream while the scores and the block map run; the
+        marginal sums follow on that stream once the map is there, and the attention waits for them.
+        (Measured at the wan13b layer: under 1% faster, the overlapped passes sharing HBM.)
+        events: optional dict pass name -> (start, end) torch.cuda.Event pairs, recorded around each
+        pass on the stream it runs on.
+        """
+        def timed(name, fn):
+            if events is not None and name in events:
+                events[name][0].record()
+                fn()
+                events[name][1].record()
+            else:
+                fn()
+        timed("reorder", self.reorder)
+        if not overlap or self.lin == SLA_LIN_NONE:
+            for name in ("pool_scores", "block_map", "kv_reduce", "marginal_states", "attention"):
+                timed(name, getattr(self, name))
+            timed("restore", self.restore)
+            return self.out
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(device=self.q.device)
+            self._ev = [torch.cuda.Event() for _ in range(3)]
+        main, side = torch.cuda.current_stream(self.q.device), self._side
+        e_in, e_map, e_marg = self._ev
+        if not self.smooth_k:
+            e_in.record(main)                  # inputs (and their reorder) are ready
+        timed("pool_scores", self.pool_scores)
+        if self.smooth_k:
+            e_in.record(main)                  # the key shift needs the pooled keys
+        with torch.cuda.stream(side):
+            side.wait_event(e_in)
+            timed("kv_reduce", self.kv_reduce)
+        timed("block_map", self.block_map)
+        e_map.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(e_map)
+            timed("marginal_states", self.marginal_states)
+            e_marg.record(side)
+        main.wait_event(e_marg)
+        timed("attention", self.attention)
+        timed("restore", self.restore)
+        return self.out
