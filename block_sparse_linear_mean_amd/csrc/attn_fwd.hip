@@ -233,11 +233,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
         }
     }
-    float mx = -__builtin_inff();
+    // block max and row sum in four independent chains (short dependency chains for the VALU)
+    float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+      for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
+    float mx = fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]));
     mx = xor32_max(mx);
     // lazy rescale: keep the running max unless the block's max exceeds it by 2^8 in exp2 units
     if (__any((mx - m_run) * c2 > 8.f)) {
@@ -250,17 +252,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
     bf16x8 pb[4];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x8 pv;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -mc));
-        l_run += x;
+        ls[m % 4] += x;
         pv[m] = x;
       }
       pb[u] = cvt8(pv);
     }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // ---- V_j resident
     if constexpr (kDirect) {
