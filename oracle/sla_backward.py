@@ -15,10 +15,13 @@ Readings (also listed in the design notes):
     where two pooled scores swap order), so it is held fixed: the gradient flows
     through the critical softmax branch and the marginal linear branch only,
     never through pooling, scores or classification;
-  * Proj (when given) is part of the forward, so dQ, dK, dV see it; the
-    gradients of the Proj weight itself are not part of this oracle;
+  * Proj (when given) is part of the forward, so dQ, dK, dV see it, and its
+    weight and bias get their own gradients (summed over every valid row of the
+    heads that share them);
   * padded positions (>= n_valid) get zero gradient;
-  * smooth-K is off.
+  * smooth-K (when on) shifts the keys of the linear branch by their mean over
+    the valid rows inside the differentiated forward, so dK carries the
+    gradient through that mean as well.
 
 The forward here restates the numpy oracle's steps with masks: a query row
 attends with one softmax to the keys of its critical blocks (s < n_valid), and
@@ -43,7 +46,7 @@ def _phi(x: torch.Tensor) -> torch.Tensor:
 
 
 def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, proj_b=None,
-                  blocks: Optional[set] = None) -> torch.Tensor:
+                  blocks: Optional[set] = None, smooth_k: bool = False) -> torch.Tensor:
     """SLA output [B, H, N, d] for a fixed block map, in float64 torch ops (differentiable).
 
     Q, K, V: float64 tensors [B, H, N, d] (one KV head per query head).
@@ -63,7 +66,8 @@ def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, 
                 heads.append(torch.zeros_like(Q[b, h]))
                 continue
             q, k, v = Q[b, h], K[b, h], V[b, h]
-            pk = _phi(k) * valid_k[:, None]                       # padded keys contribute nothing
+            kl = k - k[:n_valid].mean(dim=0) if smooth_k else k   # keys of the linear branch
+            pk = _phi(kl) * valid_k[:, None]                      # padded keys contribute nothing
             blocks_out = []
             for i in range(nb):
                 qi = q[BLOCK * i:BLOCK * (i + 1)]
@@ -106,15 +110,20 @@ def forward_torch(Q, K, V, maps: Dict, n_valid: int, scale: float, proj_w=None, 
 
 
 def gradients(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, maps: Dict, n_valid: int,
-              scale: float, proj_w=None, proj_b=None, blocks: Optional[set] = None):
-    """(O, dQ, dK, dV) as float64 numpy arrays: the output and the gradient of sum(dO * O).
+              scale: float, proj_w=None, proj_b=None, blocks: Optional[set] = None, smooth_k: bool = False,
+              with_proj_grads: bool = False):
+    """(O, dQ, dK, dV) as float64 numpy arrays: the output and the gradient of sum(dO * O);
+    with with_proj_grads also (dW, db) of the Proj weight and bias (db None without a bias).
 
     With `blocks`, the loss covers only those query blocks (see forward_torch).
     """
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
     q, k, v = t(Q), t(K), t(V)
-    pw = None if proj_w is None else torch.tensor(np.asarray(proj_w, np.float64))
-    pb = None if proj_b is None else torch.tensor(np.asarray(proj_b, np.float64))
-    O = forward_torch(q, k, v, maps, n_valid, scale, pw, pb, blocks)
+    pw = None if proj_w is None else t(proj_w)
+    pb = None if proj_b is None else t(proj_b)
+    O = forward_torch(q, k, v, maps, n_valid, scale, pw, pb, blocks, smooth_k)
     O.backward(torch.tensor(np.asarray(dO, dtype=np.float64)))
-    return O.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+    out = (O.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy())
+    if with_proj_grads:
+        out = out + (None if pw is None else pw.grad.numpy(), None if pb is None else pb.grad.numpy())
+    return out

@@ -100,3 +100,48 @@ def test_restricted_blocks_give_the_rows_they_cover():
     assert np.allclose(dKr[0, 0, 64 * j:64 * j + 64], dK[0, 0, 64 * j:64 * j + 64], rtol=1e-12, atol=1e-14)
     assert np.allclose(dVr[0, 0, 64 * j:64 * j + 64], dV[0, 0, 64 * j:64 * j + 64], rtol=1e-12, atol=1e-14)
     assert not dQr[0, 1].any()
+
+
+@pytest.mark.parametrize("shared_w", [False, True])
+def test_proj_weight_and_smooth_k_gradients_match_finite_differences(shared_w):
+    """Proj weight / bias gradients and smooth-K key gradients against central differences of the
+    numpy oracle (smooth-K makes every key's gradient depend on the mean over the valid keys)."""
+    N, nv, d, H = 256, 240, 8, 2
+    Q, K, V = rand_qkv(1, H, H, N, d, seed=37, n_valid=nv, garbage=True)
+    K = K + 0.3
+    r = np.random.default_rng(38)
+    W = r.standard_normal((d, d) if shared_w else (H, d, d)) / np.sqrt(d)
+    b = r.standard_normal(d if shared_w else (H, d))
+    dO = r.standard_normal(Q.shape)
+    kw = dict(n_valid=nv, mode="sla", kh_bp=2500, kl_bp=2500)
+    f = orc.Forward(Q, K, V, proj_w=W, proj_b=b, smooth_k=True, **kw)
+    maps = f.maps()
+    O, dQ, dK, dV, dW, db = bwd.gradients(Q, K, V, dO, maps, nv, f.scale, W, b, smooth_k=True,
+                                          with_proj_grads=True)
+    assert np.allclose(O, f.output(), rtol=1e-12, atol=1e-13)
+
+    def loss(Qx=Q, Kx=K, Vx=V, Wx=W, bx=b):
+        g = orc.Forward(Qx, Kx, Vx, proj_w=Wx, proj_b=bx, smooth_k=True, **kw)
+        return sum(float(np.sum(dO[bb, h, 64 * i:64 * i + 64] * g.output_block(bb, h, i, m)))
+                   for (bb, h, i), m in maps.items())
+    eps = 1e-6
+    for _ in range(6):
+        idx = tuple(int(r.integers(s_)) for s_ in W.shape)
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += eps
+        Wm[idx] -= eps
+        fd = (loss(Wx=Wp) - loss(Wx=Wm)) / (2 * eps)
+        assert abs(fd - dW[idx]) <= 1e-6 * (1 + abs(fd)), ("W", idx, fd, dW[idx])
+        bidx = tuple(int(r.integers(s_)) for s_ in b.shape)
+        bp, bm = b.copy(), b.copy()
+        bp[bidx] += eps
+        bm[bidx] -= eps
+        fd = (loss(bx=bp) - loss(bx=bm)) / (2 * eps)
+        assert abs(fd - db[bidx]) <= 1e-6 * (1 + abs(fd)), ("b", bidx, fd, db[bidx])
+        kidx = (0, int(r.integers(H)), int(r.integers(nv)), int(r.integers(d)))
+        Kp, Km = K.astype(np.float64).copy(), K.astype(np.float64).copy()
+        Kp[kidx] += eps
+        Km[kidx] -= eps
+        fd = (loss(Kx=Kp) - loss(Kx=Km)) / (2 * eps)
+        assert abs(fd - dK[kidx]) <= 1e-6 * (1 + abs(fd)), ("K", kidx, fd, dK[kidx])
+    assert np.all(dK[:, :, nv:] == 0.0)
