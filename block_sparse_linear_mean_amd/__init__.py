@@ -111,8 +111,8 @@ class SlaForward:
                            workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
         self.k_mean = torch.empty((B, Hkv, d), **f) if smooth_k else None
         # training: the forward also writes each row's log-sum-exp, which backward() reads
-        if training and (mode != "sla" or Hq != Hkv or proj_w is not None or smooth_k):
-            raise ValueError("backward is provided for the sla mode with Hq == Hkv, no Proj and no smooth-K")
+        if training and (mode != "sla" or Hq != Hkv):
+            raise ValueError("backward is provided for the sla mode with Hq == Hkv")
         self.lse = torch.empty((B, Hq, N), **f) if training else None
         self.bwd_ws = None
         self.row_states = None
@@ -172,26 +172,30 @@ class SlaForward:
                             H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out_ordered)
 
     def backward(self, dout: torch.Tensor, maps=None, grads=None):
-        """(dq, dk, dv) fp32 of sum(dout * out) after run() (or attention()) with training=True."""
+        """(dq, dk, dv) fp32 of sum(dout * out) after run() (or attention()) with training=True;
+        with a Proj weight (dq, dk, dv, dW, db), db None without a bias."""
         if self.lse is None:
             raise ValueError("construct the layer with training=True to keep what the backward needs")
+        proj_heads = 0 if self.proj_w is None else (1 if self.proj_w.dim() == 2 else self.proj_w.shape[0])
         if self.bwd_ws is None:
             B, H, N, d = self.q.shape
-            self.bwd_ws = torch.empty(sla_attn_bwd_workspace_bytes(B, H, N, d), device=self.q.device,
+            self.bwd_ws = torch.empty(sla_attn_bwd_workspace_bytes(B, H, N, d, proj_heads), device=self.q.device,
                                       dtype=torch.uint8)
         S, u = self.row_states
+        extra = dict(scale=self.scale, workspace=self.bwd_ws, k_shift=self.k_mean, proj_w=self.proj_w,
+                     proj_b=self.proj_b)
         if self.order is None:
             return sla_attn_bwd(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid, maps or self.maps,
-                                S, u, scale=self.scale, grads=grads, workspace=self.bwd_ws)
+                                S, u, grads=grads, **extra)
         # in the token order, then scattered back (the order is a permutation: its gradient is the inverse)
         dout_r = sla_permute_rows(dout, self.order)
         g_r = sla_attn_bwd(self.q, self.k, self.v, self.out_ordered, dout_r, self.lse, self.n_valid,
-                           maps or self.maps, S, u, scale=self.scale, workspace=self.bwd_ws)
+                           maps or self.maps, S, u, **extra)
         if grads is None:
-            grads = tuple(torch.empty_like(x) for x in g_r)
-        for src, dst in zip(g_r, grads):
+            grads = tuple(torch.empty_like(x) for x in g_r[:3])
+        for src, dst in zip(g_r[:3], grads):
             sla_permute_rows(src, self.order, inverse=True, out=dst)
-        return grads
+        return tuple(grads) + tuple(g_r[3:])
 
     def run(self, overlap: bool = False, events=None) -> torch.Tensor:
         """One full forward: (token order,) pool + scores, block map, linear states, marginal sums,

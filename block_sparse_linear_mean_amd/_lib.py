@@ -63,9 +63,9 @@ _SIGS = {
                                                           _P, c_int32, _P, c_size_t, _P]),
     "sla_hilbert_order": (c_int32, [c_int32, c_int32, c_int32, _P]),
     "sla_permute_rows": (c_int32, [POINTER(SlaTensor), _P, c_int32, c_int32, _P, _P]),
-    "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 4),
-    "sla_attn_bwd": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                                          c_size_t, _P]),
+    "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 5),
+    "sla_attn_bwd": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                          c_int32, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
 }
 
 
@@ -308,29 +308,53 @@ def sla_attn_fwd(q, k, v, n_valid, maps, lin_mode=SLA_LIN_NONE, scale=None, caus
     return out
 
 
-def sla_attn_bwd_workspace_bytes(B, H, N, d) -> int:
-    return int(lib().sla_attn_bwd_workspace_bytes(B, H, N, d))
+def sla_attn_bwd_workspace_bytes(B, H, N, d, proj_heads=0) -> int:
+    return int(lib().sla_attn_bwd_workspace_bytes(B, H, N, d, proj_heads))
 
 
-def sla_attn_bwd(q, k, v, o, dout, lse, n_valid, maps, S, u, scale=None, grads=None, workspace=None):
-    """(dq, dk, dv) fp32 [B, H, N, d]: gradients of sum(dout * o) for the SLA forward with the same map.
+def sla_attn_bwd(q, k, v, o, dout, lse, n_valid, maps, S, u, scale=None, grads=None, workspace=None, k_shift=None,
+                 proj_w=None, proj_b=None, proj_grads=None):
+    """(dq, dk, dv) fp32 [B, H, N, d]: gradients of sum(dout * o) for the SLA forward with the same map;
+    with proj_w, (dq, dk, dv, dW, db) with dW shaped like proj_w and db like it without the last axis
+    (db None when there is no bias and proj_grads does not supply one).
 
     o and lse come from sla_attn_fwd; S, u are that map's per-row marginal sums (sla_marginal_states).
+    k_shift: the smooth-K key mean [B, H, d] fp32 given to the forward (None: smooth-K off).
+    proj_w, proj_b: the forward's Proj weight and bias (None: identity).
     """
     _require_gpu(q, k, v, o, dout, lse)
     B, H, N, d = q.shape
     scale = (1.0 / d ** 0.5) if scale is None else scale
     if grads is None:
         grads = tuple(torch.empty((B, H, N, d), device=q.device, dtype=torch.float32) for _ in range(3))
-    ws_bytes = sla_attn_bwd_workspace_bytes(B, H, N, d)
+    proj_heads = 0
+    dW = db = None
+    if proj_w is not None:
+        if proj_w.dtype != torch.float32 or not proj_w.is_contiguous() or proj_w.shape[-2:] != (d, d):
+            raise ValueError("proj_w must be a contiguous float32 [d, d] or [H, d, d] tensor")
+        proj_heads = 1 if proj_w.dim() == 2 else proj_w.shape[0]
+        if proj_grads is not None:
+            dW, db = proj_grads
+        else:
+            dW = torch.empty_like(proj_w)
+            db = None if proj_b is None else torch.empty(proj_w.shape[:-1], device=q.device, dtype=torch.float32)
+    elif proj_b is not None:
+        raise ValueError("proj_b without proj_w")
+    if k_shift is not None and (k_shift.dtype != torch.float32 or not k_shift.is_contiguous()
+                                or tuple(k_shift.shape) != (B, H, d)):
+        raise ValueError("k_shift must be a contiguous float32 [B, H, d] tensor")
+    ws_bytes = sla_attn_bwd_workspace_bytes(B, H, N, d, proj_heads)
     if workspace is None:
         workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
     descs = [tensor_desc(x) for x in (q, k, v, o, dout)]
     dq, dk, dv = grads
     _check("sla_attn_bwd", lib().sla_attn_bwd(
         *[ctypes.byref(x) for x in descs], _ptr(lse), n_valid, float(scale), _ptr(maps["crit_rowptr"]),
-        _ptr(maps["crit_idx"]), _ptr(maps["marg_bits"]), _ptr(S), _ptr(u), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(workspace), ws_bytes, _stream(q.device)))
+        _ptr(maps["crit_idx"]), _ptr(maps["marg_bits"]), _ptr(S), _ptr(u), _ptr(k_shift), _ptr(proj_w),
+        _ptr(proj_b), proj_heads, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(db), _ptr(workspace), ws_bytes,
+        _stream(q.device)))
+    if proj_w is not None:
+        return dq, dk, dv, dW, db
     return dq, dk, dv
 
 

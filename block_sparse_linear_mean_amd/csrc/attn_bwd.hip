@@ -54,6 +54,12 @@ struct BwdParams {
   const float* dz;                // [B, H, nb][r]
   const uint32_t* critT;          // [B, H, nb][wq]: bit i of row j = block j is critical for query block i
   const int* kv_order;            // [B * H * nb]: key-block rows, most-used first (dK/dV dispatch order)
+  const float* k_shift;           // smooth-K: [B, H, d] key mean of the forward, or null
+  const float* dk_mean;           // smooth-K: [B, H, d] mean over valid rows of the linear-branch dK
+  const float* proj_w;            // Proj weight [heads][d][d] fp32 or null (identity)
+  const float* proj_b;            // Proj bias [heads][d] or null
+  int64_t proj_sH;                // elements between consecutive heads' weights (0: shared)
+  u16* xlin;                      // Proj: [B, H, N, d] bf16, the linear-branch output O_l per row
   float* dq;                      // [B, H, N, d] fp32
   float* dk;
   float* dv;
@@ -158,13 +164,20 @@ __global__ __launch_bounds__(256) void marg_transpose_kernel(const uint32_t* __r
 
 // ------------------------------------------------------------------ linear branch, query side
 
+__device__ __forceinline__ bf16x4 lds_load8(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x4*>(p);
+}
+
 // One workgroup per (query block i, head); wavefront w owns query rows 64 i + 16 w + l % 16.
 // Writes dQ (linear part, all rows), D_t, and the per-row gradients dS_i ([c][r], bf16), du_i.
-template <typename T, int D>
+// PROJ: O = O_s + O_l W^T + b, so O_s = O - O_l W^T - b, the gradient reaching O_l is dO W, and
+// O_l is written out (bf16) for the weight gradient.
+template <typename T, int D, bool PROJ>
 __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   constexpr int kKc = D / 32;     // 32-deep k-steps over features
   constexpr int kCt = D / 16;     // 16-wide feature tiles
   constexpr int RB = 2 * D;
+  __shared__ __attribute__((aligned(1024))) unsigned char w_sm[PROJ ? D * RB : 16];  // W: [o][c]
   __shared__ __attribute__((aligned(1024))) unsigned char st_sm[D * RB];      // S_i^T: [c][r]
   __shared__ __attribute__((aligned(1024))) unsigned char pq_sm[kBlock * RB]; // phi(Q_i): [t][r]
   __shared__ __attribute__((aligned(1024))) unsigned char dn_sm[kBlock * RB]; // dN_i: [t][c]
@@ -220,20 +233,66 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
     for (int kc = 0; kc < kKc; ++kc) acc = mfma16(lds_load16(St + tpos<D>(16 * ct + l16, 4 * kc + g)), pqf[kc], acc);
     xl[ct] = acc * inv_den;
   }
-  // D_t = dO . (O - O_l); dn = dO / den; dden = -(dO . O_l) / den
+  // D_t = dO . O_s; a = the gradient reaching O_l; dn = a / den; dden = -(a . O_l) / den
   float dsum = 0.f, ax = 0.f;
+  f32x4 go[kCt], ga[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) go[ct] = qv ? load4_f32(Gr + 16 * ct + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (PROJ) {
+    lds_u8* Wt = to_lds(w_sm);
+    const float* Wg = p.proj_w + int64_t(h) * p.proj_sH;
+    for (int e = t; e < D * D / 8; e += kBwThreads) {
+      const int o = e / (D / 8), c8 = e % (D / 8);
+      lds_store16(Wt + tpos<D>(o, c8), In<float>::load8(Wg + int64_t(o) * D + 8 * c8));
+    }
+    __syncthreads();
+    const float* bias = p.proj_b != nullptr ? p.proj_b + int64_t(h) * (p.proj_sH != 0 ? D : 0) : nullptr;
+#pragma unroll
+    for (int ot = 0; ot < kCt; ++ot) {
+      // Y^T[o][t] = sum_c W[o][c] O_l[t][c]: k-slots c = 32 kc + 4 g + {0..3} and + 16 (the lane's O_l)
+      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < kKc; ++kc) {
+        const int o = 16 * ot + l16;
+        const bf16x8 a = join(lds_load8(Wt + tpos<D>(o, 4 * kc + g / 2) + 8 * (g % 2)),
+                              lds_load8(Wt + tpos<D>(o, 4 * kc + 2 + g / 2) + 8 * (g % 2)));
+        y = mfma16(a, join(cvt4(xl[2 * kc]), cvt4(xl[2 * kc + 1])), y);
+      }
+      const int o0 = 16 * ot + 4 * g;        // lane holds Y[t][o0 + e]
+      const f32x4 oo = qv ? load4_f32(Or + o0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 bb = bias != nullptr ? *reinterpret_cast<const f32x4*>(bias + o0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsum += go[ot][e] * (oo[e] - y[e] - bb[e]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      // a^T[c][t] = sum_o W[o][c] dO[t][o]: A = W^T (transposing reads of rows o), B = the lane's dO
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ko = 0; ko < kKc; ++ko) {
+        const bf16x8 a = join(lds_read_tr4(Wt + tr_addr<D>(32 * ko + 4 * g, 16 * ct, lane)),
+                              lds_read_tr4(Wt + tr_addr<D>(32 * ko + 16 + 4 * g, 16 * ct, lane)));
+        acc = mfma16(a, join(cvt4(go[2 * ko]), cvt4(go[2 * ko + 1])), acc);
+      }
+      ga[ct] = acc;
+      *reinterpret_cast<bf16x4*>(p.xlin + (int64_t(bh) * p.N + tq) * D + 16 * ct + 4 * g) = cvt4(xl[ct]);
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      const f32x4 oo = qv ? load4_f32(Or + 16 * ct + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsum += go[ct][e] * (oo[e] - xl[ct][e]);
+      ga[ct] = go[ct];
+    }
+  }
   f32x4 dn[kCt];
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) {
     const int c = 16 * ct + 4 * g;
-    const f32x4 go = qv ? load4_f32(Gr + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 oo = qv ? load4_f32(Or + c) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dsum += go[e] * (oo[e] - xl[ct][e]);
-      ax += go[e] * xl[ct][e];
-    }
-    dn[ct] = go * inv_den;
+    for (int e = 0; e < 4; ++e) ax += ga[ct][e] * xl[ct][e];
+    dn[ct] = ga[ct] * inv_den;
     // dN tile [t][c]: 4 consecutive c = 8 bytes
     *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(Dn + tpos<D>(16 * w + l16, c / 8) + 2 * (c % 8)) =
         cvt4(dn[ct]);
@@ -302,7 +361,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 // ------------------------------------------------------------------ linear branch, key side
 
 // One workgroup per (key block j, head); wavefront w owns keys 64 j + 16 w + l % 16.
-// Writes dK and dV (linear part, all rows): dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k).
+// Writes dK and dV (linear part, all rows): dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k); with
+// smooth-K, phi and its derivative at the shifted key k - mean.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
   constexpr int kKc = D / 32;
@@ -335,7 +395,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
     if (kv) In<T>::load8_f32(Kr + 32 * kc + 8 * g, x);
     f32x8 ph;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) ph[m] = kv ? phi(x[m]) : 0.f;
+    for (int m = 0; m < 8; ++m) ph[m] = kv ? phi(x[m] - (p.k_shift ? p.k_shift[int64_t(bh) * D + 32 * kc + 8 * g + m] : 0.f)) : 0.f;
     pkf[kc] = cvt8(ph);
   }
   float* dkr = p.dk + (int64_t(bh) * p.N + s) * D;
@@ -351,8 +411,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
       acc = mfma16(a, vf[kc], acc);
     }
     const int r0 = 16 * rt + 4 * g;
-    const f32x4 kx = kv ? load4_f32(Kr + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 out;
+    f32x4 kx = kv ? load4_f32(Kr + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.k_shift != nullptr) kx -= *reinterpret_cast<const f32x4*>(p.k_shift + int64_t(bh) * D + r0);
+    f32x4 out;                       // the gradient with respect to the (shifted) key of the linear branch
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[e] = kv ? (acc[e] + dzs[r0 + e]) * dphi(kx[e]) : 0.f;
     *reinterpret_cast<f32x4*>(dkr + r0) = out;
@@ -366,6 +427,108 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
     const int c0 = 16 * ct + 4 * g;
     *reinterpret_cast<f32x4*>(dvr + c0) = kv ? acc : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
+
+// ------------------------------------------------------------------ Proj weight gradient
+
+// Partial dW[o][c] = sum_t dO[t][o] O_l[t][c] and db[o] = sum_t dO[t][o] over one chunk of 16
+// query blocks of one (batch, head): grid x = chunk (of the rows that share weight y), y = weight.
+// Rows past n_valid take no part.  Partials are summed by proj_reduce_kernel in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(kBwThreads) void proj_grad_kernel(BwdParams p, int B, int per_head, int chunks_per_bh,
+                                                               float* __restrict__ partW, float* __restrict__ partB) {
+  constexpr int kCt = D / 16;
+  constexpr int kTiles = kCt * kCt / kBwWaves;   // 16 x 16 output tiles per wavefront
+  __shared__ __attribute__((aligned(1024))) unsigned char g_sm[kBlock * 2 * D];   // dO: [t][o]
+  __shared__ __attribute__((aligned(1024))) unsigned char x_sm[kBlock * 2 * D];   // O_l: [t][c]
+  lds_u8* Gt = to_lds(g_sm);
+  lds_u8* Xt = to_lds(x_sm);
+  const int t = threadIdx.x, lane = t % kWave, w = t / kWave, g = lane / 16;
+  const int y = blockIdx.y, x = blockIdx.x;
+  const int bh_idx = x / chunks_per_bh, chunk = x % chunks_per_bh;
+  const int b = per_head ? bh_idx : bh_idx / p.H, h = per_head ? y : bh_idx % p.H;
+  const int bh = b * p.H + h;
+  const T* G = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH;
+  const bf16raw* X = reinterpret_cast<const bf16raw*>(p.xlin) + int64_t(bh) * p.N * D;
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int n = 0; n < kTiles; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float bsum = 0.f;
+  const int i0 = chunk * 16, i1 = min(p.nb, i0 + 16);
+  for (int i = i0; i < i1; ++i) {
+    __syncthreads();
+    stage64<T, D>(G, p.dsN, kBlock * i, p.n_valid, Gt);
+    stage64<bf16raw, D>(X, D, kBlock * i, p.n_valid, Xt);
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < kTiles; ++n) {
+      const int tile = w * kTiles + n, ot = tile / kCt, ct = tile % kCt;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 a = join(lds_read_tr4(Gt + tr_addr<D>(32 * kt + 8 * g, 16 * ot, lane)),
+                              lds_read_tr4(Gt + tr_addr<D>(32 * kt + 8 * g + 4, 16 * ot, lane)));
+        const bf16x8 bb = join(lds_read_tr4(Xt + tr_addr<D>(32 * kt + 8 * g, 16 * ct, lane)),
+                               lds_read_tr4(Xt + tr_addr<D>(32 * kt + 8 * g + 4, 16 * ct, lane)));
+        acc[n] = mfma16(a, bb, acc[n]);
+      }
+    }
+    if (t < D) {
+      for (int tt = 0; tt < kBlock; ++tt)
+        bsum += bf16_to_f32(*reinterpret_cast<const __attribute__((address_space(3))) u16*>(
+            Gt + tpos<D>(tt, t / 8) + 2 * (t % 8)));
+    }
+  }
+  const int64_t part = int64_t(y) * gridDim.x + x;
+#pragma unroll
+  for (int n = 0; n < kTiles; ++n) {
+    const int tile = w * kTiles + n, ot = tile / kCt, ct = tile % kCt;
+    // lane holds dW[o = 16 ot + 4 g + e][c = 16 ct + lane % 16]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) partW[(part * D + 16 * ot + 4 * g + e) * D + 16 * ct + lane % 16] = acc[n][e];
+  }
+  if (t < D) partB[part * D + t] = bsum;
+}
+
+// out[y][e] = sum over the parts of weight y, in order.
+__global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int parts, int len,
+                                                          float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x, y = blockIdx.y;
+  if (e >= len) return;
+  float s = 0.f;
+  for (int q = 0; q < parts; ++q) s += part[(int64_t(y) * parts + q) * len + e];
+  out[int64_t(y) * len + e] = s;
+}
+
+// Smooth-K: the mean over the valid rows of the linear-branch dK of each head (the gradient that
+// flows back through the key mean).  One workgroup per (8 features, head), strided fp32 sums then
+// a fixed-order LDS tree.
+__global__ __launch_bounds__(256) void dk_mean_kernel(const float* __restrict__ dk, int N, int d, int n_valid,
+                                                      float* __restrict__ mean) {
+  const int bh = blockIdx.y, r0 = 8 * blockIdx.x, t = threadIdx.x;
+  float s[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) s[m] = 0.f;
+  for (int row = t; row < n_valid; row += 256) {
+    const float* src = dk + (int64_t(bh) * N + row) * d + r0;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src), b4 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s[m] += a[m];
+      s[4 + m] += b4[m];
+    }
+  }
+  __shared__ float red[256][9];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) red[t][m] = s[m];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) red[t][m] += red[t + w][m];
+    }
+    __syncthreads();
+  }
+  if (t < 8) mean[int64_t(bh) * d + r0 + t] = n_valid > 0 ? red[0][t] / float(n_valid) : 0.f;
 }
 
 // ------------------------------------------------------------------ sparse branch, dQ
@@ -652,7 +815,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     for (int ct = 0; ct < kCt; ++ct) {
       f32x4* k4 = reinterpret_cast<f32x4*>(dkr + 16 * ct + 4 * g);
       f32x4* v4 = reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g);
-      *k4 = *k4 + dk[ct] * p.scale;
+      f32x4 add = dk[ct] * p.scale;
+      // smooth-K: the linear branch saw k - mean(k), so its dK loses its own mean over the valid rows
+      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bh) * D + 16 * ct + 4 * g);
+      *k4 = *k4 + add;
       *v4 = *v4 + dv[ct];
     }
   }
@@ -668,12 +834,19 @@ struct BwdWs {
   uint32_t* margT;
   int* kv_counts;
   int* kv_order;
+  float* dk_mean;
+  u16* xlin;
+  float* partW;
+  float* partB;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
+constexpr int kProjChunk = 16;   // query blocks per partial of the Proj weight gradient
+
+static size_t bwd_ws_layout(int B, int H, int N, int d, bool proj, BwdWs* ws, void* base) {
   const int64_t nb = N / kBlock, rows = int64_t(B) * H * nb, wq = (nb + 31) / 32;
+  const int64_t parts = proj ? int64_t(B) * H * ((nb + kProjChunk - 1) / kProjChunk) : 0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -689,6 +862,10 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
   const size_t om = take(size_t(rows) * wq * 4);
   const size_t okc = take(size_t(rows) * 4);
   const size_t oko = take(size_t(rows) * 4);
+  const size_t okm = take(size_t(B) * H * d * 4);
+  const size_t ox = take(proj ? size_t(B) * H * N * d * 2 : 0);
+  const size_t opw = take(size_t(parts) * d * d * 4);
+  const size_t opb = take(size_t(parts) * d * 4);
   if (ws != nullptr) {
     unsigned char* p = static_cast<unsigned char*>(base);
     ws->D = reinterpret_cast<float*>(p + oD);
@@ -700,6 +877,10 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
     ws->margT = reinterpret_cast<uint32_t*>(p + om);
     ws->kv_counts = reinterpret_cast<int*>(p + okc);
     ws->kv_order = reinterpret_cast<int*>(p + oko);
+    ws->dk_mean = reinterpret_cast<float*>(p + okm);
+    ws->xlin = reinterpret_cast<u16*>(p + ox);
+    ws->partW = reinterpret_cast<float*>(p + opw);
+    ws->partB = reinterpret_cast<float*>(p + opb);
   }
   return off;
 }
@@ -707,29 +888,47 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, BwdWs* ws, void* base) {
 template <typename T, int D>
 static void launch_bwd_kernels(const BwdParams& p, int BH, hipStream_t st) {
   const dim3 grid(p.nb, BH);
-  bwd_lin_q_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
+  if (p.proj_w != nullptr) bwd_lin_q_kernel<T, D, true><<<grid, kBwThreads, 0, st>>>(p);
+  else bwd_lin_q_kernel<T, D, false><<<grid, kBwThreads, 0, st>>>(p);
 }
 
 template <typename T, int D>
 static void launch_bwd_k_side(const BwdParams& p, int BH, hipStream_t st) {
   const dim3 grid(p.nb, BH);
   bwd_lin_k_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
+  if (p.dk_mean != nullptr)
+    dk_mean_kernel<<<dim3(D / 8, BH), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
   bwd_dq_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
   bwd_dkdv_kernel<T, D><<<dim3(p.nb * BH), kBwThreads, 0, st>>>(p);
 }
 
+// dW (and db) of the Proj layer: partials over chunks of query blocks, then their ordered sums.
+template <typename T, int D>
+static void launch_proj_grad(const BwdParams& p, int B, int per_head, const BwdWs& ws, float* dw, float* db,
+                             hipStream_t st) {
+  const int chunks = (p.nb + kProjChunk - 1) / kProjChunk;
+  const int weights = per_head ? p.H : 1;
+  const int parts = (per_head ? B : B * p.H) * chunks;
+  proj_grad_kernel<T, D><<<dim3(parts, weights), kBwThreads, 0, st>>>(p, B, per_head, chunks, ws.partW, ws.partB);
+  proj_reduce_kernel<<<dim3((D * D + 255) / 256, weights), 256, 0, st>>>(ws.partW, parts, D * D, dw);
+  if (db != nullptr) proj_reduce_kernel<<<dim3(1, weights), 256, 0, st>>>(ws.partB, parts, D, db);
+}
+
 }  // namespace sla
 
-extern "C" size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
+extern "C" size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, int32_t proj_heads) {
   if (B < 1 || H < 1 || N < sla::kBlock || N % sla::kBlock != 0 || (d != 64 && d != 128)) return 0;
-  return sla::bwd_ws_layout(B, H, N, d, nullptr, nullptr);
+  if (proj_heads != 0 && proj_heads != 1 && proj_heads != H) return 0;
+  return sla::bwd_ws_layout(B, H, N, d, proj_heads != 0, nullptr, nullptr);
 }
 
 extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
                                    const sla_tensor* o, const sla_tensor* dout, const float* lse, int32_t n_valid,
                                    float scale, const int32_t* crit_rowptr, const int32_t* crit_idx,
-                                   const uint32_t* marg_bits, const void* S, const float* u, float* dq, float* dk,
-                                   float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+                                   const uint32_t* marg_bits, const void* S, const float* u, const float* k_shift,
+                                   const float* proj_w, const float* proj_b, int32_t proj_heads, float* dq,
+                                   float* dk, float* dv, float* dproj_w, float* dproj_b, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(q);
   if (st != SLA_OK) return st;
@@ -747,12 +946,22 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
       u == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return SLA_ERR_NULL;
   if (!aligned16(S) || !aligned16(u) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return SLA_ERR_ALIGN;
+  const bool proj = proj_w != nullptr;
+  if (!proj && (proj_b != nullptr || dproj_w != nullptr || dproj_b != nullptr)) return SLA_ERR_NULL;
+  if (proj) {
+    if (dproj_w == nullptr) return SLA_ERR_NULL;
+    if (proj_heads != 1 && proj_heads != q->H) return SLA_ERR_SHAPE;
+    if (!aligned16(proj_w) || !aligned16(dproj_w) || (proj_b != nullptr && !aligned16(proj_b)) ||
+        (dproj_b != nullptr && !aligned16(dproj_b)))
+      return SLA_ERR_ALIGN;
+  }
+  if (k_shift != nullptr && !aligned16(k_shift)) return SLA_ERR_ALIGN;
   const int d = q->d, B = q->B, H = q->H, N = q->N, nb = N / kBlock;
   if (nb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
-  const size_t need = bwd_ws_layout(B, H, N, d, nullptr, nullptr);
+  const size_t need = bwd_ws_layout(B, H, N, d, proj, nullptr, nullptr);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
   BwdWs ws{};
-  bwd_ws_layout(B, H, N, d, &ws, workspace);
+  bwd_ws_layout(B, H, N, d, proj, &ws, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   BwdParams p{};
@@ -768,6 +977,13 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
   p.S = static_cast<const u16*>(S); p.u = u;
   p.D = ws.D; p.dS = ws.dS; p.du = ws.du; p.dH = ws.dH; p.dz = ws.dz; p.critT = ws.critT;
   p.kv_order = ws.kv_order;
+  p.k_shift = k_shift;
+  p.dk_mean = k_shift != nullptr ? ws.dk_mean : nullptr;
+  if (proj) {
+    p.proj_w = proj_w; p.proj_b = proj_b;
+    p.proj_sH = proj_heads != 1 ? int64_t(d) * d : 0;
+    p.xlin = ws.xlin;
+  }
   p.dq = dq; p.dk = dk; p.dv = dv;
 
   // transposed masks (cleared by a fill kernel, then set by atomic OR)
@@ -784,7 +1000,7 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
                                                                                         p.wq, ws.margT);
   kv_order_kernel<<<1, 1024, 0, s>>>(ws.kv_counts, rows, nb, ws.kv_order);
   const bool bf = q->dtype == SLA_BF16;
-  // 1. linear branch, query side: dQ (linear part), D, dS_i, du_i
+  // 1. linear branch, query side: dQ (linear part), D, dS_i, du_i (and O_l with Proj)
   if (d == 128) {
     if (bf) launch_bwd_kernels<bf16raw, 128>(p, B * H, s);
     else launch_bwd_kernels<float, 128>(p, B * H, s);
@@ -792,11 +1008,22 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
     if (bf) launch_bwd_kernels<bf16raw, 64>(p, B * H, s);
     else launch_bwd_kernels<float, 64>(p, B * H, s);
   }
+  if (proj) {
+    const int per_head = proj_heads != 1;
+    if (d == 128) {
+      if (bf) launch_proj_grad<bf16raw, 128>(p, B, per_head, ws, dproj_w, dproj_b, s);
+      else launch_proj_grad<float, 128>(p, B, per_head, ws, dproj_w, dproj_b, s);
+    } else {
+      if (bf) launch_proj_grad<bf16raw, 64>(p, B, per_head, ws, dproj_w, dproj_b, s);
+      else launch_proj_grad<float, 64>(p, B, per_head, ws, dproj_w, dproj_b, s);
+    }
+  }
   // 2. dH_j = sum of dS_i, dz_j = sum of du_i over the query blocks i with j marginal: the
   //    marginal aggregation with the mask transposed (rows = key blocks, summed items = query blocks)
   if ((st = launch_marginal_states(ws.dS, ws.du, B, H, H, nb, nb, d, 0, ws.margT, ws.dH, ws.dz, s)) != SLA_OK)
     return st;
-  // 3. linear branch, key side (dK, dV written), then the sparse branch (dQ, dK, dV accumulated)
+  // 3. linear branch, key side (dK, dV written; with smooth-K the mean of that dK), then the sparse
+  //    branch (dQ, dK, dV accumulated)
   if (d == 128) {
     if (bf) launch_bwd_k_side<bf16raw, 128>(p, B * H, s);
     else launch_bwd_k_side<float, 128>(p, B * H, s);

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SLA_ABI_VERSION 3
+#define SLA_ABI_VERSION 4
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
 #define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
@@ -326,34 +326,49 @@ sla_status sla_nsa3_fwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         int32_t window_tokens, int32_t cmp_block, int32_t cmp_stride, const float* w_gates,
                         void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sla_attn_bwd needs (0 for unsupported sizes). */
-size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
+/* Workspace bytes sla_attn_bwd needs (0 for unsupported sizes); proj_heads as passed to
+ * sla_attn_bwd (0 without Proj: the Proj buffers are then left out). */
+size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, int32_t proj_heads);
 
 /*
  * Backward of the SLA layer (the method is fine-tuned: SLA analysis page for arXiv
  * 2509.24006, the learned Proj and linear path).  Gradients of sum(dout * O) with respect to
- * Q, K and V, where O is the sla_attn_fwd output in SLA mode with Proj the identity, for the
- * SAME block map (held fixed: it is piecewise constant in Q and K):
+ * Q, K, V (and the Proj weight and bias), where O is the sla_attn_fwd output in SLA mode, for
+ * the SAME block map (held fixed: it is piecewise constant in Q and K):
  *   critical branch:  P = exp(scale q.k - lse), dP = dO V^T, D_t = dO_t . O_sparse_t,
  *                     dS = P (dP - D); dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO;
  *   marginal branch:  through O_linear[t] = phi(q_t)^T S_r / (phi(q_t) . u_r), S_r and u_r the
- *                     sums of H_j = phi(K_j)^T V_j and z_j over row r's marginal blocks.
+ *                     sums of H_j = phi(K_j)^T V_j and z_j over row r's marginal blocks;
+ *   Proj (proj_w non-NULL): O = O_sparse + W_h O_linear + b_h on valid rows, so the gradient
+ *                     reaching O_linear is W_h^T dO, dW_h = sum_t dO_t O_linear_t^T and
+ *                     db_h = sum_t dO_t over the valid rows (summed over the heads and
+ *                     sequences that share the weight when proj_heads == 1);
+ *   smooth-K (k_shift non-NULL): the linear branch used K - mean(K) (mean over the valid rows);
+ *                     its key gradient G is evaluated at the shifted keys and becomes
+ *                     G - mean over valid rows of G, the path through the mean.
  * Inputs: q, k, v and o (the forward output), dout: [B, H, N, d], one dtype (bf16 or fp32),
  * one KV head per query head (Hq == Hkv, else SLA_ERR_UNSUPPORTED); lse [B, H, N] from
  * sla_attn_fwd; the block map's critical CSR lists and marginal bit masks; S (bf16 bits
- * [rows, d, d]) and u (fp32 [rows, d]) as written by sla_marginal_states for that map.
+ * [rows, d, d]) and u (fp32 [rows, d]) as written by sla_marginal_states for that map (from
+ * the shifted keys' states under smooth-K).  k_shift: fp32 [B, H, d] (16-byte aligned) as
+ * given to the forward's sla_linear_kv_reduce, or NULL.  proj_w, proj_b, proj_heads: as given
+ * to sla_attn_fwd (NULL, NULL, any: no Proj).
  * Outputs dq, dk, dv: contiguous fp32 [B, H, N, d], 16-byte aligned, fully overwritten; rows
- * t >= n_valid are zero.  O_sparse is taken as o - O_linear.  Arithmetic: bf16 matrix-core
- * operands, fp32 accumulation; deterministic (no atomics on gradients).  Smooth-K and a
- * learned Proj are not differentiated here.
- * workspace: sla_attn_bwd_workspace_bytes(B, H, N, d) bytes.
+ * t >= n_valid are zero.  dproj_w (required with Proj, else NULL): fp32 [proj_heads, d, d],
+ * fully overwritten; dproj_b (nullable; NULL without Proj): fp32 [proj_heads, d].
+ * O_sparse is taken as o - Proj(O_linear).  Arithmetic: bf16 matrix-core operands (the Proj
+ * weight rounded to bf16), fp32 accumulation; deterministic (no atomics on gradients).
+ * Errors: SLA_ERR_NULL for a missing required pointer or a Proj output without proj_w,
+ * SLA_ERR_SHAPE for proj_heads not 1 or H, SLA_ERR_ALIGN, SLA_ERR_WORKSPACE.
+ * workspace: sla_attn_bwd_workspace_bytes(B, H, N, d, proj_w ? proj_heads : 0) bytes.
  */
 sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
                         const sla_tensor* o, const sla_tensor* dout, const float* lse, int32_t n_valid,
                         float scale, const int32_t* crit_rowptr, const int32_t* crit_idx,
-                        const uint32_t* marg_bits, const void* S, const float* u,
-                        float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                        void* stream);
+                        const uint32_t* marg_bits, const void* S, const float* u, const float* k_shift,
+                        const float* proj_w, const float* proj_b, int32_t proj_heads,
+                        float* dq, float* dk, float* dv, float* dproj_w, float* dproj_b,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

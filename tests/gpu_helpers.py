@@ -39,9 +39,10 @@ def layer_for(w, q, k, v, wg):
                           n_sel=w.n_sel, window=w.window, w_gate=wg)
 
 
-def make_case(w, proj_w=None, proj_b=None, smooth_k=False):
+def make_case(w, proj_w=None, proj_b=None, smooth_k=False, training=False):
     """Seeded inputs of workload w, the oracle Forward and the library layer, both with the given
-    Proj weights (float32 numpy) and smooth-K setting."""
+    Proj weights (float32 numpy) and smooth-K setting (training: the layer keeps what its backward
+    needs)."""
     q, k, v, wg = make_inputs(w)
     f = orc.Forward(host(q), host(k), host(v), n_valid=w.Nv, mode=w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp,
                     n_sel=w.n_sel, window=w.window, w_gate=None if wg is None else wg.numpy(),
@@ -49,7 +50,7 @@ def make_case(w, proj_w=None, proj_b=None, smooth_k=False):
     t = lambda x: None if x is None else torch.as_tensor(x)
     layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp,
                            n_sel=w.n_sel, window=w.window, w_gate=wg, proj_w=t(proj_w), proj_b=t(proj_b),
-                           smooth_k=smooth_k)
+                           smooth_k=smooth_k, training=training)
     return q, k, v, wg, f, layer
 
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert sla.sla_abi_version() == 3
+    assert sla.sla_abi_version() == 4
     for s in range(9):
         assert len(sla.sla_status_str(s)) > 0
     assert sla.sla_status_str(12345) == "unknown status"
@@ -200,10 +200,11 @@ def test_attn_fwd_validation(L):
 
 def test_attn_bwd_validation(L):
     q = desc()
-    def call(qq=q, kk=q, vv=q, oo=q, gg=q, lse=P, nv=256, scale=0.1, crp=P, ci=P, mb=P, S=P, u=P, dq=P, dk=P,
-             dv=P, ws=None, wsb=0):
+    def call(qq=q, kk=q, vv=q, oo=q, gg=q, lse=P, nv=256, scale=0.1, crp=P, ci=P, mb=P, S=P, u=P, ks=None,
+             pw=None, pb=None, ph=0, dq=P, dk=P, dv=P, dw=None, db=None, ws=None, wsb=0):
         return L.sla_attn_bwd(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), ctypes.byref(oo),
-                              ctypes.byref(gg), lse, nv, scale, crp, ci, mb, S, u, dq, dk, dv, ws, wsb, None)
+                              ctypes.byref(gg), lse, nv, scale, crp, ci, mb, S, u, ks, pw, pb, ph, dq, dk, dv, dw,
+                              db, ws, wsb, None)
     assert call(lse=None) == ENULL
     assert call(mb=None) == ENULL
     assert call(dq=None) == ENULL
@@ -215,8 +216,17 @@ def test_attn_bwd_validation(L):
     assert call(dk=ctypes.c_void_p(0x20004)) == EALIGN
     assert call() == EWS                                       # workspace missing
     assert call(ws=P, wsb=16) == EWS
-    assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128) > 0
-    assert L.sla_attn_bwd_workspace_bytes(1, 2, 100, 128) == 0
+    assert call(pb=P) == ENULL                                 # Proj bias without the weight
+    assert call(dw=P) == ENULL                                 # Proj gradient without the weight
+    assert call(pw=P, ph=1) == ENULL                           # Proj needs its weight gradient
+    assert call(pw=P, ph=3, dw=P) == ESHAPE                    # proj_heads is 1 or H
+    assert call(pw=P, ph=2, dw=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call(ks=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call(pw=P, ph=1, dw=P, ws=P, wsb=L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 0)) == EWS
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 0) > 0
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 1) > L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 0)
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 3) == 0
+    assert L.sla_attn_bwd_workspace_bytes(1, 2, 100, 128, 0) == 0
 
 
 def test_nsa3_validation(L):
