@@ -116,6 +116,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(g) * p.ksH;
   const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(g) * p.vsH;
 
+  if constexpr (LIN == SLA_LIN_MARGINAL) {
+    if (t < D) lin_u[t] = p.u[mrow * D + t];
+  } else if constexpr (LIN != SLA_LIN_NONE) {
+    if (t < D) lin_u[t] = p.u[(int64_t(b) * p.Hkv + g) * D + t];
+  }
   const int tq = kBlock * i + 32 * (w % 2) + l32; // this lane's query row
   const bool qvalid = tq < p.n_valid;
   // causal limit: key s is visible iff s <= tlim (s <= tq; for compressed keys s * stride + block - 1 <= tq)
@@ -211,7 +216,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     SLA_WAIT_LGKM0();
     SLA_BARRIER();                                   // every wavefront has read K_j
-    if (more) stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
+    if (more) {
+      stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
+    } else if constexpr (LIN == SLA_LIN_MARGINAL) {
+      // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
+      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
+                                       D, 0, Kb, stage_offsets<D, true, NW>(D));
+    }
 
     // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
     const bool full = jok && rv >= kBlock && !CAUSAL;
@@ -251,24 +262,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
     }
     const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
+    // the row sum is taken over the bf16 P that the P.V product uses (two per dot instruction)
     bf16x8 pb[4];
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float ls[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x8 pv;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -mc));
-        ls[m % 4] += x;
-        pv[m] = x;
-      }
+      for (int m = 0; m < 8; ++m) pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -mc));
       pb[u] = cvt8(pv);
+      ls[u] = sum8_bf16(pb[u]);
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // ---- V_j resident
+    // ---- V_j resident (the one copy issued after it, K_{j+1} or S^T rows 0..63, may be in flight)
     if constexpr (kDirect) {
-      if (more) SLA_WAIT_VMCNT(kWaitK);
+      if (more || LIN == SLA_LIN_MARGINAL) SLA_WAIT_VMCNT(kWaitK);
       else SLA_WAIT_VMCNT(0);
     }
     SLA_WAIT_LGKM0();
@@ -306,6 +315,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
       stage_tile<T, D, false, NW>(V, p.vsN, jn, Vb, voff);
+    } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                                 // every wavefront has read V_j
+      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
+                                       D, 1, Vb, stage_offsets<D, true, NW>(D));
     }
   }
 
@@ -320,28 +334,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // ---- linear branch: phi(q)^T S / (phi(q) . u) with S^T staged in LDS ([c][r], K layout)
   if constexpr (LIN != SLA_LIN_NONE) {
-    const float* ug;
-    SLA_WAIT_VMCNT(0);
-    SLA_WAIT_LGKM0();
-    SLA_BARRIER();
     // S^T rows (c) 0..63 go to the K buffer, rows 64..D-1 to the V buffer, both in the K layout
+    // (for per-row states already issued during the last critical block, if the row has one)
     auto st_tile = [&](int r) { return r < kBlock ? Kb : Vb; };
-    if constexpr (LIN == SLA_LIN_MARGINAL) {
-      const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
-      ug = p.u + mrow * D;
-      const StageOff<D, NW> soff = stage_offsets<D, true, NW>(D);
-      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
-      if constexpr (D == 128) stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
-    } else {
-      const float* Sg = static_cast<const float*>(p.S) + (int64_t(b) * p.Hkv + g) * D * D;
-      ug = p.u + (int64_t(b) * p.Hkv + g) * D;
-      for (int e = t; e < D * Tl::kChunks; e += kThreads) {
-        const int r = e / Tl::kChunks, c = e % Tl::kChunks;
-        const bf16x8 x = In<float>::load8(Sg + r * D + 8 * c);
-        lds_store16(st_tile(r) + k_pos<D>(r % kBlock, c), x);
+    if (LIN != SLA_LIN_MARGINAL || cbeg >= cend) {
+      SLA_WAIT_VMCNT(0);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      if constexpr (LIN == SLA_LIN_MARGINAL) {
+        const u16* Sg = static_cast<const u16*>(p.S) + mrow * D * D;
+        const StageOff<D, NW> soff = stage_offsets<D, true, NW>(D);
+        stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 0, Kb, soff);
+        if constexpr (D == 128) stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(Sg), D, 1, Vb, soff);
+      } else {
+        const float* Sg = static_cast<const float*>(p.S) + (int64_t(b) * p.Hkv + g) * D * D;
+        for (int e = t; e < D * Tl::kChunks; e += kThreads) {
+          const int r = e / Tl::kChunks, c = e % Tl::kChunks;
+          const bf16x8 x = In<float>::load8(Sg + r * D + 8 * c);
+          lds_store16(st_tile(r) + k_pos<D>(r % kBlock, c), x);
+        }
       }
     }
-    if (t < D) lin_u[t] = ug[t];
     SLA_WAIT_VMCNT(0);
     SLA_WAIT_LGKM0();
     SLA_BARRIER();
@@ -435,6 +448,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   // ---- store: lane holds O[tq][32 dt + 8 (e / 4) + 4 lg + e % 4]; padded query rows are zero
+  if constexpr (NW == 2) {
+    if (!p.out_f32) {
+      // bf16 output of one head: re-staged through the K buffer (64 rows of 2 D bytes, 16-byte
+      // chunk c of row r at c ^ (r % chunks)) so that every store writes whole rows, 16 bytes a lane
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                                 // every wavefront is done with the buffers
+      const int r = 32 * (w % 2) + l32;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 o = {oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
+          const int c = 4 * dt + e4;
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+              Kb + r * Tl::kRowB + 16 * (c ^ (r % Tl::kChunks)) + 8 * lg) = __builtin_convertvector(o, bf16x4);
+        }
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      u16* ob = static_cast<u16*>(p.out) + ((int64_t(b) * p.Hq + h) * p.N + kBlock * i) * D;
+#pragma unroll
+      for (int n = 0; n < kBlock * Tl::kChunks / kThreads; ++n) {
+        const int e = t + kThreads * n;
+        const int rr = e / Tl::kChunks, c = e % Tl::kChunks;
+        bf16x8 x = lds_load16(Kb + rr * Tl::kRowB + 16 * (c ^ (rr % Tl::kChunks)));
+        if (kBlock * i + rr >= p.n_valid) x = zero8();
+        *reinterpret_cast<bf16x8*>(ob + rr * D + 8 * c) = x;
+      }
+      return;
+    }
+  }
   const int64_t obase = ((int64_t(b) * p.Hq + h) * p.N + tq) * D;
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt)

@@ -30,6 +30,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ bf16x8 cvt8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum of 8 bf16 values in fp32: four two-element dot products against (1, 1)
+__device__ __forceinline__ float sum8_bf16(bf16x8 x) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, s, false);
+}
 
 // 32x32x16 bf16 matrix-core product: D = A(32x16) * B(16x32) + C.
 // Lane l holds A[l % 32][8 * (l / 32) .. +8], B[8 * (l / 32) .. +8][l % 32],
