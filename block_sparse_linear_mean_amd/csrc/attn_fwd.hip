@@ -136,6 +136,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  // running row offset M in exp2 units (P = exp2(c2 s - M)), -inf until the row has seen a key
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   const float c2 = p.scale_log2;
@@ -244,36 +245,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
         }
     }
-    // block max and row sum in four independent chains (short dependency chains for the VALU)
-    float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
-    float mx = fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]));
-    mx = xor32_max(mx);
-    // lazy rescale: keep the running max unless the block's max exceeds it by 2^8 in exp2 units
-    if (__any((mx - m_run) * c2 > 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
-    }
-    const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
-    // the row sum is taken over the bf16 P that the P.V product uses (two per dot instruction)
+    // P = exp2(c2 s - M); its row sums from the bf16 P that the P.V product uses (two per dot
+    // instruction).  The offset M is only moved when the row has none yet or this block's sum
+    // passes 2^16 (then the row max sets it and the block's P are recomputed): every P stays
+    // below 2^16, far from overflow, without a row max per block.
     bf16x8 pb[4];
     float ls[4];
+    auto probs = [&](float off) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f32x8 pv;
+      for (int u = 0; u < 4; ++u) {
+        f32x8 pv;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -mc));
-      pb[u] = cvt8(pv);
-      ls[u] = sum8_bf16(pb[u]);
+        for (int m = 0; m < 8; ++m)
+          pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -off));
+        pb[u] = cvt8(pv);
+        ls[u] = sum8_bf16(pb[u]);
+      }
+    };
+    probs(m_run == -__builtin_inff() ? 0.f : m_run);
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if (__any(m_run == -__builtin_inff() || !(lsum <= 65536.f))) {
+      float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
+      const float mx = xor32_max(fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]))) * c2;
+      const float m_new = fmaxf(m_run, mx);          // -inf while the row has no key
+      if (m_new != m_run) {
+        const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+      probs(m_run == -__builtin_inff() ? 0.f : m_run);
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    l_run += lsum;
 
     // ---- V_j resident (the one copy issued after it, K_{j+1} or S^T rows 0..63, may be in flight)
     if constexpr (kDirect) {
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (p.lse != nullptr && lg == 0)   // ln sum_s exp(scale q.k_s) = (m c2 + log2 l) ln 2; -inf without keys
     p.lse[(int64_t(b) * p.Hq + h) * p.N + tq] =
-        (qvalid && l_tot > 0.f) ? (m_run * c2 + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
+        (qvalid && l_tot > 0.f) ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -__builtin_inff();
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= inv_l;
 
