@@ -90,6 +90,22 @@ __device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg, bo
 // online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
 // transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU): the next
 // K block streams into LDS during softmax and P.V, the next V block during the next S^T.
+// Step k of NSTEP of the softmax of a 32-key half (scores sc, 16 per lane): elements
+// E k .. E k + E - 1 (E = 16 / NSTEP) of P = exp2(c2 s - off); each time eight are done they are
+// packed into a bf16 B operand (p0, then p1) and added to the row sum (of those bf16 values, two
+// per dot instruction).
+#define SOFTMAX_STEP(NSTEP, sc, k, pv, p0, p1, lsum, off)                                       \
+  do {                                                                                          \
+    constexpr int kE_ = 16 / (NSTEP);                                                           \
+    _Pragma("unroll") for (int m_ = 0; m_ < kE_; ++m_)                                          \
+      pv[(kE_ * (k) + m_) % 8] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kE_ * (k) + m_], c2, -(off))); \
+    if ((kE_ * (k) + kE_) % 8 == 0) {                                                           \
+      bf16x8& dst_ = kE_ * (k) < 8 ? (p0) : (p1);                                               \
+      dst_ = cvt8(pv);                                                                          \
+      lsum += sum8_bf16(dst_);                                                                  \
+    }                                                                                           \
+  } while (0)
+
 template <typename T, int D, bool CAUSAL, int LIN, int NW, bool PROJ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
   using Tl = AttnTile<D>;
@@ -171,105 +187,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     return n < 64 ? __builtin_amdgcn_readlane(v0, n) : __builtin_amdgcn_readlane(v1, n - 64);
   };
   auto safe_block = [&](int jraw) { return unsigned(jraw) < unsigned(p.nkb) ? jraw : 0; };
-  if (cbeg < cend) {
-    const int j0 = safe_block(entry(0, lj0, lj1));
-    stage_tile<T, D, true, NW>(K, p.ksN, j0, Kb, koff);
-    stage_tile<T, D, false, NW>(V, p.vsN, j0, Vb, voff);
-    if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);   // K_0 resident (V_0 may still be in flight)
-    SLA_WAIT_LGKM0();
-    SLA_BARRIER();
-  }
-  for (int pi = cbeg; pi < cend; ++pi) {
-    if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
-      lbase += 64;
-      lj0 = lj1;
-      lf0 = lf1;
-      const int e1 = lbase + 64 + lane;
-      lj1 = e1 < cend ? p.crit_idx[e1] : 0;
-      if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
+  // scores of keys that may not be attended (padded, malformed, causal, window) become -inf; key
+  // s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot, so every test compares C
+  // with a per-lane bound and no per-slot key index has to live in registers
+  auto mask_scores = [&](f32x16& sc, int kt, int j, bool jok, int flag) {
+    const int rel = kBlock * j + 4 * lg;
+    const int lim_valid = jok ? p.n_keys - rel : 0;    // s < n_keys       <=> C < lim_valid
+    const int lim_causal = tlim - rel;                  // s <= tlim        <=> C <= lim_causal
+    const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
+    const bool sel = flag & 1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int C = 32 * kt + 8 * (e / 4) + (e % 4);
+      bool ok = C < lim_valid;
+      if constexpr (CAUSAL) ok = ok && C <= lim_causal && (sel || C > lim_win);
+      sc[e] = ok ? sc[e] : -__builtin_inff();
     }
-    const int jraw = entry(pi - lbase, lj0, lj1);
-    const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
-    const int j = jok ? jraw : 0;
-    const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
-    const bool more = pi + 1 < cend;
-    const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
-    const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
-
-    // ---- K_j resident (V_j may still be in flight): the previous block's last barrier
-    // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
-    f32x16 sacc[2];
+  };
+  // softmax of one 32-key half: P = exp2(c2 s - M) as two bf16 B operands and their row sum (of the
+  // bf16 values the P.V product uses, two per dot instruction)
+  auto half_probs = [&](const f32x16& sc, bf16x8& p0, bf16x8& p1, float off) {
+    f32x8 a, b2;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-    bf16x8 ka[2][2];
-    ka[0][0] = lds_load16(Kb + kread[0]);
-    ka[0][1] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
-#pragma unroll
-    for (int ks = 0; ks < kQs; ++ks) {
-      if (ks + 1 < kQs) {
-        ka[(ks + 1) & 1][0] = lds_load16(Kb + kread[ks + 1]);
-        ka[(ks + 1) & 1][1] = lds_load16(Kb + kread[ks + 1] + 32 * Tl::kRowB);
-      }
-      sacc[0] = mfma32(ka[ks & 1][0], qf[ks], sacc[0]);
-      sacc[1] = mfma32(ka[ks & 1][1], qf[ks], sacc[1]);
+    for (int m = 0; m < 8; ++m) {
+      a[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[m], c2, -off));
+      b2[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 + m], c2, -off));
     }
-    SLA_WAIT_LGKM0();
-    SLA_BARRIER();                                   // every wavefront has read K_j
-    if (more) {
-      stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
-    } else if constexpr (LIN == SLA_LIN_MARGINAL) {
-      // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
-      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
-                                       D, 0, Kb, stage_offsets<D, true, NW>(D));
-    }
-
-    // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
-    const bool full = jok && rv >= kBlock && !CAUSAL;
-    if (!full) {                                     // padded, malformed or causal block
-      // key s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot: every test compares
-      // C with a per-lane bound, so no per-slot key index has to live in registers
-      const int rel = kBlock * j + 4 * lg;
-      const int lim_valid = jok ? p.n_keys - rel : 0;    // s < n_keys       <=> C < lim_valid
-      const int lim_causal = tlim - rel;                  // s <= tlim        <=> C <= lim_causal
-      const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
-      const bool sel = flag & 1;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int C = 32 * kt + 8 * (e / 4) + (e % 4);
-          bool ok = C < lim_valid;
-          if constexpr (CAUSAL) ok = ok && C <= lim_causal && (sel || C > lim_win);
-          sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
-        }
-    }
-    // P = exp2(c2 s - M); its row sums from the bf16 P that the P.V product uses (two per dot
-    // instruction).  The offset M is only moved when the row has none yet or this block's sum
-    // passes 2^16 (then the row max sets it and the block's P are recomputed): every P stays
-    // below 2^16, far from overflow, without a row max per block.
-    bf16x8 pb[4];
-    float ls[4];
-    auto probs = [&](float off) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        f32x8 pv;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -off));
-        pb[u] = cvt8(pv);
-        ls[u] = sum8_bf16(pb[u]);
-      }
-    };
-    probs(m_run == -__builtin_inff() ? 0.f : m_run);
-    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    p0 = cvt8(a);
+    p1 = cvt8(b2);
+    return sum8_bf16(p0) + sum8_bf16(p1);
+  };
+  // the running offset M moves only when the row has none yet or a half's P sum passes 2^16: then
+  // the half's row max sets it, the accumulators are rescaled and the half's P recomputed.  Every P
+  // stays below 2^16, far from overflow, without a row max per block.
+  auto settle = [&](const f32x16& sc, bf16x8& p0, bf16x8& p1, float& lsum) {
     if (__any(m_run == -__builtin_inff() || !(lsum <= 65536.f))) {
       float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
+      for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sc[e]);
       const float mx = xor32_max(fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]))) * c2;
       const float m_new = fmaxf(m_run, mx);          // -inf while the row has no key
       if (m_new != m_run) {
@@ -279,56 +234,341 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
       }
-      probs(m_run == -__builtin_inff() ? 0.f : m_run);
-      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      lsum = half_probs(sc, p0, p1, m_run == -__builtin_inff() ? 0.f : m_run);
     }
     l_run += lsum;
-
-    // ---- V_j resident (the one copy issued after it, K_{j+1} or S^T rows 0..63, may be in flight)
-    if constexpr (kDirect) {
-      if (more || LIN == SLA_LIN_MARGINAL) SLA_WAIT_VMCNT(kWaitK);
-      else SLA_WAIT_VMCNT(0);
+  };
+  // O^T += V^T P^T over keys 16 u .. 16 u + 15: slot m of P holds key 16 u + 8 (m / 4) + 4 lg + m % 4;
+  // each 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
+  // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
+  auto vop = [&](int u, int dt) {
+    const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
+    const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  // padded keys: zero the V rows r0 .. r1 - 1 (every wavefront waits for the others afterwards)
+  auto zero_v_rows = [&](int r0, int r1) {
+    for (int e = t; e < (r1 - r0) * Tl::kChunks; e += kThreads) {
+      const int r = r0 + e / Tl::kChunks;
+      lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
     }
     SLA_WAIT_LGKM0();
     SLA_BARRIER();
-    if (!jok || rv < kBlock) {                       // padded keys: zero their V rows
-      const int r0 = jok ? max(rv, 0) : 0;
-      for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += kThreads) {
-        const int r = r0 + e / Tl::kChunks;
-        lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
+  };
+  const bf16raw* Srow = reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S)) + mrow * D * D;
+
+  if constexpr (NW == 2) {
+    // Each key block is taken as two 32-key halves (h = 0, 1), and the matrix-core products of one
+    // half are issued among the VALU work of the other: on gfx950 a wavefront's own independent
+    // VALU instructions run largely in the shadow of its MFMAs, while another wavefront's barely do.
+    //   R0: S0 = K[0:32] Q^T                          (K rows 0..31 then free: K_{j+1}[0:32] streams in)
+    //   R1: S1 = K[32:64] Q^T  |  softmax(S0)         (K rows 32..63 free: K_{j+1}[32:64])
+    //   R2: O += V[0:32] P0    |  softmax(S1)
+    //   R3: O += V[32:64] P1                          (V free: V_{j+1} streams in)
+    // K goes by half tiles (kHS direct loads per wavefront each), so each half has about a block's
+    // time to land; V, needed only from R2 on, has R0 and R1.  The waits name how many of this
+    // wavefront's copies may stay in flight.
+    constexpr int kHS = HalfSteps<D, NW>::kSteps;
+    const HalfSteps<D, NW> khs = half_steps<D, NW>(p.ksN);
+    const HalfSteps<D, NW> vhs = half_steps<D, NW>(p.vsN);
+    if (cbeg < cend) {
+      const int j0 = safe_block(entry(0, lj0, lj1));
+      stage_half<T, D, true, NW>(K, p.ksN, j0, 0, Kb, koff, khs);
+      stage_half<T, D, true, NW>(K, p.ksN, j0, 1, Kb, koff, khs);
+      stage_half<T, D, false, NW>(V, p.vsN, j0, 0, Vb, voff, vhs);
+      stage_half<T, D, false, NW>(V, p.vsN, j0, 1, Vb, voff, vhs);
+      if constexpr (kDirect) SLA_WAIT_VMCNT(2 * kHS);  // K_0 resident (V_0 may still be in flight)
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+    }
+    for (int pi = cbeg; pi < cend; ++pi) {
+      if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
+        lbase += 64;
+        lj0 = lj1;
+        lf0 = lf1;
+        const int e1 = lbase + 64 + lane;
+        lj1 = e1 < cend ? p.crit_idx[e1] : 0;
+        if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
+      }
+      const int jraw = entry(pi - lbase, lj0, lj1);
+      const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
+      const int j = jok ? jraw : 0;
+      const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
+      const bool more = pi + 1 < cend;
+      const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
+      const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
+      const bool full = jok && rv >= kBlock && !CAUSAL;
+      const int vz = jok ? max(rv, 0) : 0;             // V rows from vz on are padding
+
+      // ---- R0: S0 = K rows 0..31 x Q^T (one accumulation chain, operands a step ahead)
+      f32x16 s0, s1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s0[e] = 0.f;
+        s1[e] = 0.f;
+      }
+      {
+        bf16x8 ka[3];                                  // operands two steps ahead
+        ka[0] = lds_load16(Kb + kread[0]);
+        ka[1] = lds_load16(Kb + kread[1]);
+#pragma unroll
+        for (int ks = 0; ks < kQs; ++ks) {
+          if (ks + 2 < kQs) ka[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2]);
+          s0 = mfma32(ka[ks % 3], qf[ks], s0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                                   // A: every wavefront has read K rows 0..31
+      if (more) stage_half<T, D, true, NW>(K, p.ksN, jn, 0, Kb, koff, khs);
+      if (!full) mask_scores(s0, 0, j, jok, flag);
+
+      // ---- R1: S1 = K rows 32..63 x Q^T among the softmax of S0
+      bf16x8 pb[4];
+      const float off1 = m_run == -__builtin_inff() ? 0.f : m_run;
+      // step ks: one product, the next K operand and 1/8 of the softmax (scheduling barriers keep
+      // the compiler from regrouping them)
+      float lsum0 = 0.f;
+      {
+        f32x8 pv;
+        bf16x8 kb3[3];                                 // operands two steps ahead
+        kb3[0] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
+        kb3[1] = lds_load16(Kb + kread[1] + 32 * Tl::kRowB);
+#pragma unroll
+        for (int ks = 0; ks < kQs; ++ks) {
+          if (ks + 2 < kQs) kb3[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2] + 32 * Tl::kRowB);
+          s1 = mfma32(kb3[ks % 3], qf[ks], s1);
+          SOFTMAX_STEP(kQs, s0, ks, pv, pb[0], pb[1], lsum0, off1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      settle(s0, pb[0], pb[1], lsum0);
+
+      // ---- B: K rows 32..63 read by every wavefront; V_j resident (the copy after it: with a next
+      // block, its K rows 0..31)
+      if constexpr (kDirect) {
+        if (more) SLA_WAIT_VMCNT(kHS);
+        else SLA_WAIT_VMCNT(0);
       }
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
-    }
-    // O^T += V^T P^T: 16-key step u holds keys 16 u + 8 (m / 4) + 4 lg + m % 4 in slot m; each
-    // 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
-    // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
-    // kDt independent accumulation chains; operands read one step ahead
-    auto vop = [&](int u, int dt) {
-      const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
-      const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    bf16x8 va[2];
-    va[0] = vop(0, 0);
+      if (more) {
+        stage_half<T, D, true, NW>(K, p.ksN, jn, 1, Kb, koff, khs);
+      } else if constexpr (LIN == SLA_LIN_MARGINAL) {
+        // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
+        stage_tile<bf16raw, D, true, NW>(Srow, D, 0, Kb, stage_offsets<D, true, NW>(D));
+      }
+      if (vz < kBlock) zero_v_rows(vz, kBlock);
+      if (!full) mask_scores(s1, 1, j, jok, flag);
+
+      // ---- R2: O += V rows 0..31 x P0 among the softmax of S1
+      const float off2 = m_run == -__builtin_inff() ? 0.f : m_run;
+      float lsum1 = 0.f;
+      {
+        static_assert(2 * kDt == kQs, "the P.V steps of a half pair with the softmax steps");
+        f32x8 pv;
+        bf16x8 va[3];                                  // operands two steps ahead
+        va[0] = vop(0, 0);
+        va[1] = vop(1 / kDt, 1 % kDt);
 #pragma unroll
-    for (int st = 0; st < 4 * kDt; ++st) {
-      const int u = st / kDt, dt = st % kDt;
-      if (st + 1 < 4 * kDt) va[(st + 1) & 1] = vop((st + 1) / kDt, (st + 1) % kDt);
-      oacc[dt] = mfma32(va[st & 1], pb[u], oacc[dt]);
-    }
-    if (more) {
-      // one barrier for both: every wavefront has read V_j, and K_{j+1} (the only copy in flight)
-      // has landed
-      if constexpr (kDirect) SLA_WAIT_VMCNT(0);
+        for (int st = 0; st < 2 * kDt; ++st) {
+          const int u = st / kDt, dt = st % kDt;
+          if (st + 2 < 2 * kDt) va[(st + 2) % 3] = vop((st + 2) / kDt, (st + 2) % kDt);
+          oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
+          SOFTMAX_STEP(2 * kDt, s1, st, pv, pb[2], pb[3], lsum1, off2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      settle(s1, pb[2], pb[3], lsum1);
+
+      // ---- R3: O += V rows 32..63 x P1
+      {
+        constexpr int kSt = 2 * kDt;
+        bf16x8 va[3];                                  // operands two steps ahead
+        va[0] = vop(2, 0);
+        va[1] = vop(2 + 1 / kDt, 1 % kDt);
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+          const int u = 2 + st / kDt, dt = st % kDt;
+          if (st + 2 < kSt) va[(st + 2) % 3] = vop(2 + (st + 2) / kDt, (st + 2) % kDt);
+          oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- D: V_j read by every wavefront; the next block's K resident (no copy after it)
+      if constexpr (kDirect) {
+        if (more) SLA_WAIT_VMCNT(0);
+      }
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
-      stage_tile<T, D, false, NW>(V, p.vsN, jn, Vb, voff);
-    } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
+      if (more) {
+        stage_half<T, D, false, NW>(V, p.vsN, jn, 0, Vb, voff, vhs);
+        stage_half<T, D, false, NW>(V, p.vsN, jn, 1, Vb, voff, vhs);
+      } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
+        stage_tile<bf16raw, D, true, NW>(Srow, D, 1, Vb, stage_offsets<D, true, NW>(D));
+      }
+    }
+  } else {
+    if (cbeg < cend) {
+      const int j0 = safe_block(entry(0, lj0, lj1));
+      stage_tile<T, D, true, NW>(K, p.ksN, j0, Kb, koff);
+      stage_tile<T, D, false, NW>(V, p.vsN, j0, Vb, voff);
+      if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);   // K_0 resident (V_0 may still be in flight)
       SLA_WAIT_LGKM0();
-      SLA_BARRIER();                                 // every wavefront has read V_j
-      stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
-                                       D, 1, Vb, stage_offsets<D, true, NW>(D));
+      SLA_BARRIER();
+    }
+    for (int pi = cbeg; pi < cend; ++pi) {
+      if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
+        lbase += 64;
+        lj0 = lj1;
+        lf0 = lf1;
+        const int e1 = lbase + 64 + lane;
+        lj1 = e1 < cend ? p.crit_idx[e1] : 0;
+        if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
+      }
+      const int jraw = entry(pi - lbase, lj0, lj1);
+      const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
+      const int j = jok ? jraw : 0;
+      const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
+      const bool more = pi + 1 < cend;
+      const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
+      const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
+
+      // ---- K_j resident (V_j may still be in flight): the previous block's last barrier
+      // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
+      f32x16 sacc[2];
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+      bf16x8 ka[2][2];
+      ka[0][0] = lds_load16(Kb + kread[0]);
+      ka[0][1] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
+  #pragma unroll
+      for (int ks = 0; ks < kQs; ++ks) {
+        if (ks + 1 < kQs) {
+          ka[(ks + 1) & 1][0] = lds_load16(Kb + kread[ks + 1]);
+          ka[(ks + 1) & 1][1] = lds_load16(Kb + kread[ks + 1] + 32 * Tl::kRowB);
+        }
+        sacc[0] = mfma32(ka[ks & 1][0], qf[ks], sacc[0]);
+        sacc[1] = mfma32(ka[ks & 1][1], qf[ks], sacc[1]);
+      }
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                                   // every wavefront has read K_j
+      if (more) {
+        stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
+      } else if constexpr (LIN == SLA_LIN_MARGINAL) {
+        // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
+        stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
+                                         D, 0, Kb, stage_offsets<D, true, NW>(D));
+      }
+
+      // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
+      const bool full = jok && rv >= kBlock && !CAUSAL;
+      if (!full) {                                     // padded, malformed or causal block
+        // key s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot: every test compares
+        // C with a per-lane bound, so no per-slot key index has to live in registers
+        const int rel = kBlock * j + 4 * lg;
+        const int lim_valid = jok ? p.n_keys - rel : 0;    // s < n_keys       <=> C < lim_valid
+        const int lim_causal = tlim - rel;                  // s <= tlim        <=> C <= lim_causal
+        const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
+        const bool sel = flag & 1;
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int C = 32 * kt + 8 * (e / 4) + (e % 4);
+            bool ok = C < lim_valid;
+            if constexpr (CAUSAL) ok = ok && C <= lim_causal && (sel || C > lim_win);
+            sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
+          }
+      }
+      // P = exp2(c2 s - M); its row sums from the bf16 P that the P.V product uses (two per dot
+      // instruction).  The offset M is only moved when the row has none yet or this block's sum
+      // passes 2^16 (then the row max sets it and the block's P are recomputed): every P stays
+      // below 2^16, far from overflow, without a row max per block.
+      bf16x8 pb[4];
+      float ls[4];
+      auto probs = [&](float off) {
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          f32x8 pv;
+  #pragma unroll
+          for (int m = 0; m < 8; ++m)
+            pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -off));
+          pb[u] = cvt8(pv);
+          ls[u] = sum8_bf16(pb[u]);
+        }
+      };
+      probs(m_run == -__builtin_inff() ? 0.f : m_run);
+      float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if (__any(m_run == -__builtin_inff() || !(lsum <= 65536.f))) {
+        float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
+        const float mx = xor32_max(fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]))) * c2;
+        const float m_new = fmaxf(m_run, mx);          // -inf while the row has no key
+        if (m_new != m_run) {
+          const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+  #pragma unroll
+          for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
+          m_run = m_new;
+        }
+        probs(m_run == -__builtin_inff() ? 0.f : m_run);
+        lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      }
+      l_run += lsum;
+
+      // ---- V_j resident (the one copy issued after it, K_{j+1} or S^T rows 0..63, may be in flight)
+      if constexpr (kDirect) {
+        if (more || LIN == SLA_LIN_MARGINAL) SLA_WAIT_VMCNT(kWaitK);
+        else SLA_WAIT_VMCNT(0);
+      }
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      if (!jok || rv < kBlock) {                       // padded keys: zero their V rows
+        const int r0 = jok ? max(rv, 0) : 0;
+        for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += kThreads) {
+          const int r = r0 + e / Tl::kChunks;
+          lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
+        }
+        SLA_WAIT_LGKM0();
+        SLA_BARRIER();
+      }
+      // O^T += V^T P^T: 16-key step u holds keys 16 u + 8 (m / 4) + 4 lg + m % 4 in slot m; each
+      // 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
+      // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
+      // kDt independent accumulation chains; operands read one step ahead
+      auto vop = [&](int u, int dt) {
+        const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
+        const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      bf16x8 va[2];
+      va[0] = vop(0, 0);
+  #pragma unroll
+      for (int st = 0; st < 4 * kDt; ++st) {
+        const int u = st / kDt, dt = st % kDt;
+        if (st + 1 < 4 * kDt) va[(st + 1) & 1] = vop((st + 1) / kDt, (st + 1) % kDt);
+        oacc[dt] = mfma32(va[st & 1], pb[u], oacc[dt]);
+      }
+      if (more) {
+        // one barrier for both: every wavefront has read V_j, and K_{j+1} (the only copy in flight)
+        // has landed
+        if constexpr (kDirect) SLA_WAIT_VMCNT(0);
+        SLA_WAIT_LGKM0();
+        SLA_BARRIER();
+        stage_tile<T, D, false, NW>(V, p.vsN, jn, Vb, voff);
+      } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
+        SLA_WAIT_LGKM0();
+        SLA_BARRIER();                                 // every wavefront has read V_j
+        stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
+                                         D, 1, Vb, stage_offsets<D, true, NW>(D));
+      }
     }
   }
 

@@ -104,4 +104,57 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ X, int64_t sN, 
   }
 }
 
+// Half tiles: rows 32 h .. 32 h + 31 of a tile are 1 KB steps h * kInst / 2 ... of it, shared by
+// the NW wavefronts (kInst / 2 / NW steps each).  The per-lane part of a step's offset is that of
+// the full-tile copy (it depends on the step only through step % 4, which both orders share);
+// the wave-uniform part is the step's first row relative to the half's first row.
+template <int D, int NW>
+struct HalfSteps {
+  static constexpr int kSteps = AttnTile<D>::kInst / 2 / NW;
+  uint32_t step[kSteps];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ HalfSteps<D, NW> half_steps(int64_t sN) {
+  constexpr int R = 1024 / AttnTile<D>::kRowB;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  HalfSteps<D, NW> o;
+#pragma unroll
+  for (int n = 0; n < HalfSteps<D, NW>::kSteps; ++n)
+    o.step[n] = uint32_t(int64_t(HalfSteps<D, NW>::kSteps * w + n) * R * sN * 2);
+  return o;
+}
+
+// Stage rows 32 h .. 32 h + 31 of key block j of X into the same rows of an LDS tile (the
+// layout of stage_tile).
+template <typename T, int D, bool KLAYOUT, int NW>
+__device__ __forceinline__ void stage_half(const T* __restrict__ X, int64_t sN, int j, int h, lds_u8* tile,
+                                           const StageOff<D, NW>& off, const HalfSteps<D, NW>& hs) {
+  using Tl = AttnTile<D>;
+  using SO = StageOff<D, NW>;
+  constexpr int kHS = HalfSteps<D, NW>::kSteps;
+  // the K layout's per-lane offset depends on the step only at d = 128, through step % 4; with
+  // four steps per wavefront per half (NW = 2) the half's step n has the remainder of full step n
+  static_assert(kHS >= 1 && (D == 64 || kHS % 4 == 0), "half tiles: unsupported wavefront count");
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t / kWave);
+  if constexpr (sizeof(T) == 2) {
+    const unsigned char* tb = reinterpret_cast<const unsigned char*>(X) + int64_t(kBlock * j + 32 * h) * sN * 2;
+#pragma unroll
+    for (int n = 0; n < kHS; ++n) {
+      const int q = h * (Tl::kInst / 2) + kHS * w + n;
+      const uint32_t vo = off.lane[KLAYOUT && D == 128 ? n % SO::kLanes : 0] + hs.step[n];
+      load_lds16_sbase(tb, vo, tile + q * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < Tl::kChunks * 32 / (kWave * NW); ++n) {
+      const int e = t + kWave * NW * n;
+      const int r = 32 * h + e / Tl::kChunks, c = e % Tl::kChunks;
+      const bf16x8 x = In<T>::load8(X + int64_t(kBlock * j + r) * sN + 8 * c);
+      lds_store16(tile + (KLAYOUT ? k_pos<D>(r, c) : v_pos<D>(r, c)), x);
+    }
+  }
+}
+
 }  // namespace sla
