@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void qsum_kernel(const float* __restrict__ qpo
   qsum[int64_t(bg) * nb * d + e] = s;
 }
 
-// Pooled scores, one 64 (i) x TJ (j) tile of one score matrix per workgroup; each thread owns
+// Pooled scores, one 64 (i) x TJ (j) tile of one score matrix per workgroup (TJ = 64: twice the
+// workgroups of 128-wide tiles, for more wavefronts in flight); each thread owns
 // 4 x TJ/16 outputs.  scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a
 // sequential fp64 FMA chain over r; with group_sum, qsum is the group's fp64 sum of pooled
 // queries (read from qsum_kernel's output when given, else summed here).  The pooled vectors stream through LDS 32 features at a time, the next
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
   }
 
   __shared__ double qs[kScI][kScR + 1];
-  __shared__ float ks[TJ][kScR + 1];
+  __shared__ double ks[TJ][kScR + 1];       // converted once here, not by every reader
   double acc[4][kJ];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 #pragma unroll
     for (int n = 0; n < 8; ++n) { const int e = t + 256 * n; qs[e / kScR][e % kScR] = qreg[n]; }
 #pragma unroll
-    for (int n = 0; n < kKl; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = kreg[n]; }
+    for (int n = 0; n < kKl; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = double(kreg[n]); }
     __syncthreads();
     if (r0 + kScR < D) load(r0 + kScR);
 #pragma unroll 8
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 #pragma unroll
       for (int a = 0; a < 4; ++a) qa[a] = qs[ty + 16 * a][r];
 #pragma unroll
-      for (int c = 0; c < kJ; ++c) kb[c] = double(ks[tx + 16 * c][r]);
+      for (int c = 0; c < kJ; ++c) kb[c] = ks[tx + 16 * c][r];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -254,12 +255,13 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
         q_pool, q->H, k->H, nb, q->d, qs);
     qsum = qs;
   }
-  dim3 grid((nb + 127) / 128, (nb + kScI - 1) / kScI, q->B * Hs);
+  constexpr int kTJ = 64;
+  dim3 grid((nb + kTJ - 1) / kTJ, (nb + kScI - 1) / kScI, q->B * Hs);
   if (q->d == 128)
-    scores_kernel<128, 128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
+    scores_kernel<128, kTJ><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
                                                  causal ? 1 : 0, double(scale), qsum, scores);
   else
-    scores_kernel<64, 128><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
+    scores_kernel<64, kTJ><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
                                                 causal ? 1 : 0, double(scale), qsum, scores);
   if (probs != nullptr) probs_kernel<<<dim3(q->B * Hs * nb), 64, 0, s>>>(scores, nb, probs);
   return launch_status();
