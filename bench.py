@@ -323,6 +323,57 @@ def summarize_counters(fetch_dir, write_dir, kernel_pass, workload, copy_mib, co
     return "\n".join(out) + "\n"
 
 
+def cold_steps(layer, args, dev):
+    """Layer time with the caches cold: before each step a 512 MiB scratch write evicts L2 and
+    MALL (256 MB), so the inputs come from HBM.  Median over the steps (HIP events)."""
+    import torch
+    scratch = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev_att = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        scratch.fill_(s_ & 255)
+        ev[s_][0].record()
+        layer.run(events={"attention": ev_att[s_]})
+        ev[s_][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    att = sorted(a.elapsed_time(b) for a, b in ev_att)
+    del scratch
+    return {"ms_per_step_median": round(ms[len(ms) // 2], 5), "attention_ms_median": round(att[len(att) // 2], 5),
+            "flush": "512 MiB scratch write before each step"}
+
+
+def achievable_peaks(dev, attention_ms, attention_flops):
+    """Context for the roofline fractions, measured in the same process: a device copy of 1 GiB
+    (read + write) and a large bf16 GEMM (8192^3, the vendor library), with the attention pass's
+    rate as a fraction of the GEMM's."""
+    import torch
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    n = 1 << 28
+    src = torch.ones(n, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    copy_ms = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    gemm_ms = timed(lambda: torch.matmul(a, b), 10)
+    del a, b
+    gemm_tf = 2 * m ** 3 / (gemm_ms / 1e3) / 1e12
+    att_tf = attention_flops / (attention_ms / 1e3) / 1e12
+    return {"copy_GBps": round(2 * n * 4 / (copy_ms / 1e3) / 1e9, 1), "gemm_bf16_TFLOPs": round(gemm_tf, 1),
+            "gemm_shape": [m, m, m], "attention_frac_of_gemm": round(att_tf / gemm_tf, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +382,8 @@ def main():
     ap.add_argument("--workload", default="wan13b_sla")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the cold-cache steps and the copy / GEMM reference measurements")
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead (sla workloads)")
     ap.add_argument("--overlap", action="store_true",
                     help="run the key states and marginal sums on a second stream, overlapping scores and map")
@@ -479,6 +532,12 @@ def main():
         "passes": passes,
         "gpu_ms_per_step": round(gpu_ms, 5),
     }
+    per_step = sorted(a.elapsed_time(b) for a, b in ev_step)
+    result["gpu_ms_per_step_median"] = round(per_step[len(per_step) // 2], 5)
+    result["gpu_ms_per_step_min"] = round(per_step[0], 5)
+    if not args.no_context:
+        result["cold"] = cold_steps(layer, args, dev)
+        result["achievable"] = achievable_peaks(dev, pass_ms["attention"], work["attention"][1])
     if args.captured_mass:
         result["captured_mass"] = captured_mass(w, qd, kd, vd)
     if args.copy_calibration_mb:
