@@ -11,8 +11,8 @@
 // heads of a GQA group share the selection ("Sparse Attention 方法综述", section 2 NSA).
 //
 // Design (gfx950, wave64, 32x32x16 bf16 matrix cores):
-//  * one workgroup = one 64-row query block of one head (2 wavefronts x 32 query rows),
-//    or of four heads of a GQA group that share the block map (8 wavefronts);
+//  * one workgroup = one 64-row query block of one head (2 wavefronts x 32 query rows); the
+//    heads of a GQA group that share the block map run on one XCD back to back (shared L2);
 //  * the query fragment stays in registers for the whole block list;
 //  * per critical key block, K and V tiles are copied global -> LDS by the direct-to-LDS
 //    loads; scores are computed transposed (S^T = K Q^T), so each lane owns one query
@@ -20,7 +20,10 @@
 //    rescale of the (transposed) output accumulators is per lane;
 //  * P^T feeds the P.V product directly from registers, V^T comes from the transposing
 //    LDS read;
-//  * exp2 with scale*log2(e) folded in; fp32 running max / sum / accumulators;
+//  * each key block as two 32-key halves: the scores of one half and the P.V of the other are
+//    issued among the half's softmax instructions (a wavefront's own VALU work runs in the shadow
+//    of its matrix-core products; another wavefront's barely does);
+//  * exp2 with scale*log2(e) folded in; fp32 running offset / sum / accumulators;
 //  * epilogue: 1/l normalisation, then the linear term phi(q)^T S / (phi(q) . u)
 //    as one more matrix-core product against S^T staged in LDS as bf16, and, with a
 //    projection, one more product against the staged weight.
@@ -32,8 +35,6 @@ namespace sla {
 
 sla_status launch_marginal_states(const u16* H, const float* z, int B, int Hq, int Hkv, int nqb, int nkb, int d,
                                   int group_map, const uint32_t* bits, u16* S, float* u, hipStream_t st);
-
-constexpr int kGroupHeads = 4;   // heads per workgroup when a GQA group shares the block map
 
 struct AttnParams {
   const void* q;
@@ -60,20 +61,19 @@ struct AttnParams {
 };
 
 // Workgroup order.  Workgroups are dealt round-robin to the 8 XCDs, each with its own L2, so
-// the hardware index is remapped: the workgroups one XCD receives form one contiguous range
-// of the logical order, in which the query heads of a GQA group (same map row, same K/V
-// blocks) come first, then neighbouring query blocks (largely the same critical blocks).
+// the hardware index is remapped: the workgroups one XCD receives form one contiguous range of
+// the logical order, in which the query heads of a GQA group (same map row, same K/V blocks)
+// come first, then neighbouring query blocks (largely the same critical blocks).
 struct WgCoord {
   int i, h, b;
 };
-// hg heads per workgroup (hg divides the group size G): h is the workgroup's first head
 // Causal rows do work that grows with i: there (heavy_first) each XCD's range takes every 8th
 // query block, largest i first, so the XCDs stay balanced and the longest blocks start first.
-__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg, bool heavy_first = false) {
+__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, bool heavy_first = false) {
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int G = Hq / Hkv, ng = G / hg;
-  const int hh = logical % ng;
-  const int rest = logical / ng;
+  const int G = Hq / Hkv;
+  const int hh = logical % G;
+  const int rest = logical / G;
   int i = rest % nqb;
   if (heavy_first) {
     const int per = nqb / 8;
@@ -81,15 +81,15 @@ __device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, int hg, bo
   }
   const int bg = rest / nqb;
   const int g = bg % Hkv, b = bg / Hkv;
-  return WgCoord{i, g * G + hh * hg, b};
+  return WgCoord{i, g * G + hh, b};
 }
 
-// One workgroup = one 64-row query block of NW / 2 heads (heads of one GQA group sharing the
-// block map, so they share every staged K/V tile): 2 wavefronts x 32 query rows per head, 32x32x16
+// One workgroup = one 64-row query block of one head: 2 wavefronts x 32 query rows, 32x32x16
 // bf16 matrix cores.  Per critical key block: S^T = K Q^T (lane = one query column, 32 keys),
 // online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
-// transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU): the next
-// K block streams into LDS during softmax and P.V, the next V block during the next S^T.
+// transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU).  (Four heads
+// of a GQA group sharing each staged tile in one 8-wavefront workgroup measured slower at the
+// NSA prefill: 1.31 ms against 1.08 ms, one workgroup per CU against four.)
 // Step k of NSTEP of the softmax of a 32-key half (scores sc, 16 per lane): elements
 // E k .. E k + E - 1 (E = 16 / NSTEP) of P = exp2(c2 s - off); each time eight are done they are
 // packed into a bf16 B operand (p0, then p1) and added to the row sum (of those bf16 values, two
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int t = threadIdx.x, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: head and K/V bases in SGPRs
-  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, NW / 2, CAUSAL);
+  static_assert(NW == 2, "one head per workgroup: two wavefronts of 32 query rows");
+  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, CAUSAL);
   const int i = wc.i, h = wc.h + w / 2, b = wc.b;  // this wavefront's head
   const int G = p.Hq / p.Hkv;
   const int g = h / G;
@@ -257,318 +258,155 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   const bf16raw* Srow = reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S)) + mrow * D * D;
 
-  if constexpr (NW == 2) {
-    // Each key block is taken as two 32-key halves (h = 0, 1), and the matrix-core products of one
-    // half are issued among the VALU work of the other: on gfx950 a wavefront's own independent
-    // VALU instructions run largely in the shadow of its MFMAs, while another wavefront's barely do.
-    //   R0: S0 = K[0:32] Q^T                          (K rows 0..31 then free: K_{j+1}[0:32] streams in)
-    //   R1: S1 = K[32:64] Q^T  |  softmax(S0)         (K rows 32..63 free: K_{j+1}[32:64])
-    //   R2: O += V[0:32] P0    |  softmax(S1)
-    //   R3: O += V[32:64] P1                          (V free: V_{j+1} streams in)
-    // K goes by half tiles (kHS direct loads per wavefront each), so each half has about a block's
-    // time to land; V, needed only from R2 on, has R0 and R1.  The waits name how many of this
-    // wavefront's copies may stay in flight.
-    constexpr int kHS = HalfSteps<D, NW>::kSteps;
-    const HalfSteps<D, NW> khs = half_steps<D, NW>(p.ksN);
-    const HalfSteps<D, NW> vhs = half_steps<D, NW>(p.vsN);
-    if (cbeg < cend) {
-      const int j0 = safe_block(entry(0, lj0, lj1));
-      stage_half<T, D, true, NW>(K, p.ksN, j0, 0, Kb, koff, khs);
-      stage_half<T, D, true, NW>(K, p.ksN, j0, 1, Kb, koff, khs);
-      stage_half<T, D, false, NW>(V, p.vsN, j0, 0, Vb, voff, vhs);
-      stage_half<T, D, false, NW>(V, p.vsN, j0, 1, Vb, voff, vhs);
-      if constexpr (kDirect) SLA_WAIT_VMCNT(2 * kHS);  // K_0 resident (V_0 may still be in flight)
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();
+  // Each key block is taken as two 32-key halves (h = 0, 1), and the matrix-core products of one
+  // half are issued among the VALU work of the other: on gfx950 a wavefront's own independent
+  // VALU instructions run largely in the shadow of its MFMAs, while another wavefront's barely do.
+  //   R0: S0 = K[0:32] Q^T                          (K rows 0..31 then free: K_{j+1}[0:32] streams in)
+  //   R1: S1 = K[32:64] Q^T  |  softmax(S0)         (K rows 32..63 free: K_{j+1}[32:64])
+  //   R2: O += V[0:32] P0    |  softmax(S1)
+  //   R3: O += V[32:64] P1                          (V free: V_{j+1} streams in)
+  // K goes by half tiles (kHS direct loads per wavefront each), so each half has about a block's
+  // time to land; V, needed only from R2 on, has R0 and R1.  The waits name how many of this
+  // wavefront's copies may stay in flight.
+  constexpr int kHS = HalfSteps<D, NW>::kSteps;
+  const HalfSteps<D, NW> khs = half_steps<D, NW>(p.ksN);
+  const HalfSteps<D, NW> vhs = half_steps<D, NW>(p.vsN);
+  if (cbeg < cend) {
+    const int j0 = safe_block(entry(0, lj0, lj1));
+    stage_half<T, D, true, NW>(K, p.ksN, j0, 0, Kb, koff, khs);
+    stage_half<T, D, true, NW>(K, p.ksN, j0, 1, Kb, koff, khs);
+    stage_half<T, D, false, NW>(V, p.vsN, j0, 0, Vb, voff, vhs);
+    stage_half<T, D, false, NW>(V, p.vsN, j0, 1, Vb, voff, vhs);
+    if constexpr (kDirect) SLA_WAIT_VMCNT(2 * kHS);  // K_0 resident (V_0 may still be in flight)
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+  }
+  for (int pi = cbeg; pi < cend; ++pi) {
+    if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
+      lbase += 64;
+      lj0 = lj1;
+      lf0 = lf1;
+      const int e1 = lbase + 64 + lane;
+      lj1 = e1 < cend ? p.crit_idx[e1] : 0;
+      if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
     }
-    for (int pi = cbeg; pi < cend; ++pi) {
-      if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
-        lbase += 64;
-        lj0 = lj1;
-        lf0 = lf1;
-        const int e1 = lbase + 64 + lane;
-        lj1 = e1 < cend ? p.crit_idx[e1] : 0;
-        if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
-      }
-      const int jraw = entry(pi - lbase, lj0, lj1);
-      const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
-      const int j = jok ? jraw : 0;
-      const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
-      const bool more = pi + 1 < cend;
-      const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
-      const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
-      const bool full = jok && rv >= kBlock && !CAUSAL;
-      const int vz = jok ? max(rv, 0) : 0;             // V rows from vz on are padding
+    const int jraw = entry(pi - lbase, lj0, lj1);
+    const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
+    const int j = jok ? jraw : 0;
+    const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
+    const bool more = pi + 1 < cend;
+    const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
+    const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
+    const bool full = jok && rv >= kBlock && !CAUSAL;
+    const int vz = jok ? max(rv, 0) : 0;             // V rows from vz on are padding
 
-      // ---- R0: S0 = K rows 0..31 x Q^T (one accumulation chain, operands a step ahead)
-      f32x16 s0, s1;
+    // ---- R0: S0 = K rows 0..31 x Q^T (one accumulation chain, operands a step ahead)
+    f32x16 s0, s1;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s0[e] = 0.f;
-        s1[e] = 0.f;
-      }
-      {
-        bf16x8 ka[3];                                  // operands two steps ahead
-        ka[0] = lds_load16(Kb + kread[0]);
-        ka[1] = lds_load16(Kb + kread[1]);
-#pragma unroll
-        for (int ks = 0; ks < kQs; ++ks) {
-          if (ks + 2 < kQs) ka[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2]);
-          s0 = mfma32(ka[ks % 3], qf[ks], s0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();                                   // A: every wavefront has read K rows 0..31
-      if (more) stage_half<T, D, true, NW>(K, p.ksN, jn, 0, Kb, koff, khs);
-      if (!full) mask_scores(s0, 0, j, jok, flag);
-
-      // ---- R1: S1 = K rows 32..63 x Q^T among the softmax of S0
-      bf16x8 pb[4];
-      const float off1 = m_run == -__builtin_inff() ? 0.f : m_run;
-      // step ks: one product, the next K operand and 1/8 of the softmax (scheduling barriers keep
-      // the compiler from regrouping them)
-      float lsum0 = 0.f;
-      {
-        f32x8 pv;
-        bf16x8 kb3[3];                                 // operands two steps ahead
-        kb3[0] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
-        kb3[1] = lds_load16(Kb + kread[1] + 32 * Tl::kRowB);
-#pragma unroll
-        for (int ks = 0; ks < kQs; ++ks) {
-          if (ks + 2 < kQs) kb3[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2] + 32 * Tl::kRowB);
-          s1 = mfma32(kb3[ks % 3], qf[ks], s1);
-          SOFTMAX_STEP(kQs, s0, ks, pv, pb[0], pb[1], lsum0, off1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      settle(s0, pb[0], pb[1], lsum0);
-
-      // ---- B: K rows 32..63 read by every wavefront; V_j resident (the copy after it: with a next
-      // block, its K rows 0..31)
-      if constexpr (kDirect) {
-        if (more) SLA_WAIT_VMCNT(kHS);
-        else SLA_WAIT_VMCNT(0);
-      }
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();
-      if (more) {
-        stage_half<T, D, true, NW>(K, p.ksN, jn, 1, Kb, koff, khs);
-      } else if constexpr (LIN == SLA_LIN_MARGINAL) {
-        // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
-        stage_tile<bf16raw, D, true, NW>(Srow, D, 0, Kb, stage_offsets<D, true, NW>(D));
-      }
-      if (vz < kBlock) zero_v_rows(vz, kBlock);
-      if (!full) mask_scores(s1, 1, j, jok, flag);
-
-      // ---- R2: O += V rows 0..31 x P0 among the softmax of S1
-      const float off2 = m_run == -__builtin_inff() ? 0.f : m_run;
-      float lsum1 = 0.f;
-      {
-        static_assert(2 * kDt == kQs, "the P.V steps of a half pair with the softmax steps");
-        f32x8 pv;
-        bf16x8 va[3];                                  // operands two steps ahead
-        va[0] = vop(0, 0);
-        va[1] = vop(1 / kDt, 1 % kDt);
-#pragma unroll
-        for (int st = 0; st < 2 * kDt; ++st) {
-          const int u = st / kDt, dt = st % kDt;
-          if (st + 2 < 2 * kDt) va[(st + 2) % 3] = vop((st + 2) / kDt, (st + 2) % kDt);
-          oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
-          SOFTMAX_STEP(2 * kDt, s1, st, pv, pb[2], pb[3], lsum1, off2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      settle(s1, pb[2], pb[3], lsum1);
-
-      // ---- R3: O += V rows 32..63 x P1
-      {
-        constexpr int kSt = 2 * kDt;
-        bf16x8 va[3];                                  // operands two steps ahead
-        va[0] = vop(2, 0);
-        va[1] = vop(2 + 1 / kDt, 1 % kDt);
-#pragma unroll
-        for (int st = 0; st < kSt; ++st) {
-          const int u = 2 + st / kDt, dt = st % kDt;
-          if (st + 2 < kSt) va[(st + 2) % 3] = vop(2 + (st + 2) / kDt, (st + 2) % kDt);
-          oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- D: V_j read by every wavefront; the next block's K resident (no copy after it)
-      if constexpr (kDirect) {
-        if (more) SLA_WAIT_VMCNT(0);
-      }
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();
-      if (more) {
-        stage_half<T, D, false, NW>(V, p.vsN, jn, 0, Vb, voff, vhs);
-        stage_half<T, D, false, NW>(V, p.vsN, jn, 1, Vb, voff, vhs);
-      } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
-        stage_tile<bf16raw, D, true, NW>(Srow, D, 1, Vb, stage_offsets<D, true, NW>(D));
-      }
+    for (int e = 0; e < 16; ++e) {
+      s0[e] = 0.f;
+      s1[e] = 0.f;
     }
-  } else {
-    if (cbeg < cend) {
-      const int j0 = safe_block(entry(0, lj0, lj1));
-      stage_tile<T, D, true, NW>(K, p.ksN, j0, Kb, koff);
-      stage_tile<T, D, false, NW>(V, p.vsN, j0, Vb, voff);
-      if constexpr (kDirect) SLA_WAIT_VMCNT(kWaitK);   // K_0 resident (V_0 may still be in flight)
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();
-    }
-    for (int pi = cbeg; pi < cend; ++pi) {
-      if (pi - lbase == 64) {                          // slide the list window (rare: > 64 entries)
-        lbase += 64;
-        lj0 = lj1;
-        lf0 = lf1;
-        const int e1 = lbase + 64 + lane;
-        lj1 = e1 < cend ? p.crit_idx[e1] : 0;
-        if constexpr (CAUSAL) lf1 = e1 < cend ? int(p.crit_flags[e1]) : 0;
-      }
-      const int jraw = entry(pi - lbase, lj0, lj1);
-      const bool jok = unsigned(jraw) < unsigned(p.nkb);   // a malformed entry reads block 0, fully masked
-      const int j = jok ? jraw : 0;
-      const int flag = CAUSAL ? entry(pi - lbase, lf0, lf1) : 1;
-      const bool more = pi + 1 < cend;
-      const int jn = more ? safe_block(entry(pi + 1 - lbase, lj0, lj1)) : 0;
-      const int rv = p.n_keys - kBlock * j;           // valid rows of this block (may exceed 64)
-
-      // ---- K_j resident (V_j may still be in flight): the previous block's last barrier
-      // two independent accumulation chains (key halves kt = 0, 1); operands read one step ahead
-      f32x16 sacc[2];
-  #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-      bf16x8 ka[2][2];
-      ka[0][0] = lds_load16(Kb + kread[0]);
-      ka[0][1] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
-  #pragma unroll
+    {
+      bf16x8 ka[3];                                  // operands two steps ahead
+      ka[0] = lds_load16(Kb + kread[0]);
+      ka[1] = lds_load16(Kb + kread[1]);
+#pragma unroll
       for (int ks = 0; ks < kQs; ++ks) {
-        if (ks + 1 < kQs) {
-          ka[(ks + 1) & 1][0] = lds_load16(Kb + kread[ks + 1]);
-          ka[(ks + 1) & 1][1] = lds_load16(Kb + kread[ks + 1] + 32 * Tl::kRowB);
-        }
-        sacc[0] = mfma32(ka[ks & 1][0], qf[ks], sacc[0]);
-        sacc[1] = mfma32(ka[ks & 1][1], qf[ks], sacc[1]);
+        if (ks + 2 < kQs) ka[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2]);
+        s0 = mfma32(ka[ks % 3], qf[ks], s0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();                                   // every wavefront has read K_j
-      if (more) {
-        stage_tile<T, D, true, NW>(K, p.ksN, jn, Kb, koff);
-      } else if constexpr (LIN == SLA_LIN_MARGINAL) {
-        // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
-        stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
-                                         D, 0, Kb, stage_offsets<D, true, NW>(D));
-      }
+    }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                                   // A: every wavefront has read K rows 0..31
+    if (more) stage_half<T, D, true, NW>(K, p.ksN, jn, 0, Kb, koff, khs);
+    if (!full) mask_scores(s0, 0, j, jok, flag);
 
-      // ---- online softmax over the 32 keys this lane holds: key = 32 kt + 8 (e / 4) + 4 lg + e % 4
-      const bool full = jok && rv >= kBlock && !CAUSAL;
-      if (!full) {                                     // padded, malformed or causal block
-        // key s = rel + C with C = 32 kt + 8 (e / 4) + e % 4 a constant per slot: every test compares
-        // C with a per-lane bound, so no per-slot key index has to live in registers
-        const int rel = kBlock * j + 4 * lg;
-        const int lim_valid = jok ? p.n_keys - rel : 0;    // s < n_keys       <=> C < lim_valid
-        const int lim_causal = tlim - rel;                  // s <= tlim        <=> C <= lim_causal
-        const int lim_win = tq - rel - p.window;            // tq - s < window  <=> C > lim_win
-        const bool sel = flag & 1;
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int C = 32 * kt + 8 * (e / 4) + (e % 4);
-            bool ok = C < lim_valid;
-            if constexpr (CAUSAL) ok = ok && C <= lim_causal && (sel || C > lim_win);
-            sacc[kt][e] = ok ? sacc[kt][e] : -__builtin_inff();
-          }
+    // ---- R1: S1 = K rows 32..63 x Q^T among the softmax of S0
+    bf16x8 pb[4];
+    const float off1 = m_run == -__builtin_inff() ? 0.f : m_run;
+    // step ks: one product, the next K operand and 1/8 of the softmax (scheduling barriers keep
+    // the compiler from regrouping them)
+    float lsum0 = 0.f;
+    {
+      f32x8 pv;
+      bf16x8 kb3[3];                                 // operands two steps ahead
+      kb3[0] = lds_load16(Kb + kread[0] + 32 * Tl::kRowB);
+      kb3[1] = lds_load16(Kb + kread[1] + 32 * Tl::kRowB);
+#pragma unroll
+      for (int ks = 0; ks < kQs; ++ks) {
+        if (ks + 2 < kQs) kb3[(ks + 2) % 3] = lds_load16(Kb + kread[ks + 2] + 32 * Tl::kRowB);
+        s1 = mfma32(kb3[ks % 3], qf[ks], s1);
+        SOFTMAX_STEP(kQs, s0, ks, pv, pb[0], pb[1], lsum0, off1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // P = exp2(c2 s - M); its row sums from the bf16 P that the P.V product uses (two per dot
-      // instruction).  The offset M is only moved when the row has none yet or this block's sum
-      // passes 2^16 (then the row max sets it and the block's P are recomputed): every P stays
-      // below 2^16, far from overflow, without a row max per block.
-      bf16x8 pb[4];
-      float ls[4];
-      auto probs = [&](float off) {
-  #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          f32x8 pv;
-  #pragma unroll
-          for (int m = 0; m < 8; ++m)
-            pv[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u / 2][8 * (u % 2) + m], c2, -off));
-          pb[u] = cvt8(pv);
-          ls[u] = sum8_bf16(pb[u]);
-        }
-      };
-      probs(m_run == -__builtin_inff() ? 0.f : m_run);
-      float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      if (__any(m_run == -__builtin_inff() || !(lsum <= 65536.f))) {
-        float mxs[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-  #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) mxs[e % 4] = fmaxf(mxs[e % 4], sacc[kt][e]);
-        const float mx = xor32_max(fmaxf(fmaxf(mxs[0], mxs[1]), fmaxf(mxs[2], mxs[3]))) * c2;
-        const float m_new = fmaxf(m_run, mx);          // -inf while the row has no key
-        if (m_new != m_run) {
-          const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-  #pragma unroll
-          for (int dt = 0; dt < kDt; ++dt) oacc[dt] *= alpha;
-          m_run = m_new;
-        }
-        probs(m_run == -__builtin_inff() ? 0.f : m_run);
-        lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      }
-      l_run += lsum;
+    }
+    settle(s0, pb[0], pb[1], lsum0);
 
-      // ---- V_j resident (the one copy issued after it, K_{j+1} or S^T rows 0..63, may be in flight)
-      if constexpr (kDirect) {
-        if (more || LIN == SLA_LIN_MARGINAL) SLA_WAIT_VMCNT(kWaitK);
-        else SLA_WAIT_VMCNT(0);
-      }
-      SLA_WAIT_LGKM0();
-      SLA_BARRIER();
-      if (!jok || rv < kBlock) {                       // padded keys: zero their V rows
-        const int r0 = jok ? max(rv, 0) : 0;
-        for (int e = t; e < (kBlock - r0) * Tl::kChunks; e += kThreads) {
-          const int r = r0 + e / Tl::kChunks;
-          lds_store16(Vb + v_pos<D>(r, e % Tl::kChunks), zero8());
-        }
-        SLA_WAIT_LGKM0();
-        SLA_BARRIER();
-      }
-      // O^T += V^T P^T: 16-key step u holds keys 16 u + 8 (m / 4) + 4 lg + m % 4 in slot m; each
-      // 16-lane group reads 4 consecutive keys of one 16-column strip with the transposing read
-      // (row r0 + 8 has the same swizzle as r0, since both leave the same remainder mod 4)
-      // kDt independent accumulation chains; operands read one step ahead
-      auto vop = [&](int u, int dt) {
-        const bf16x4 lo = lds_read_tr4(Vb + vread[dt] + 16 * u * Tl::kRowB);
-        const bf16x4 hi = lds_read_tr4(Vb + vread[dt] + (16 * u + 8) * Tl::kRowB);
-        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      bf16x8 va[2];
+    // ---- B: K rows 32..63 read by every wavefront; V_j resident (the copy after it: with a next
+    // block, its K rows 0..31)
+    if constexpr (kDirect) {
+      if (more) SLA_WAIT_VMCNT(kHS);
+      else SLA_WAIT_VMCNT(0);
+    }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    if (more) {
+      stage_half<T, D, true, NW>(K, p.ksN, jn, 1, Kb, koff, khs);
+    } else if constexpr (LIN == SLA_LIN_MARGINAL) {
+      // last block: the linear epilogue's S^T rows 0..63 stream into the free K buffer now
+      stage_tile<bf16raw, D, true, NW>(Srow, D, 0, Kb, stage_offsets<D, true, NW>(D));
+    }
+    if (vz < kBlock) zero_v_rows(vz, kBlock);
+    if (!full) mask_scores(s1, 1, j, jok, flag);
+
+    // ---- R2: O += V rows 0..31 x P0 among the softmax of S1
+    const float off2 = m_run == -__builtin_inff() ? 0.f : m_run;
+    float lsum1 = 0.f;
+    {
+      static_assert(2 * kDt == kQs, "the P.V steps of a half pair with the softmax steps");
+      f32x8 pv;
+      bf16x8 va[3];                                  // operands two steps ahead
       va[0] = vop(0, 0);
-  #pragma unroll
-      for (int st = 0; st < 4 * kDt; ++st) {
+      va[1] = vop(1 / kDt, 1 % kDt);
+#pragma unroll
+      for (int st = 0; st < 2 * kDt; ++st) {
         const int u = st / kDt, dt = st % kDt;
-        if (st + 1 < 4 * kDt) va[(st + 1) & 1] = vop((st + 1) / kDt, (st + 1) % kDt);
-        oacc[dt] = mfma32(va[st & 1], pb[u], oacc[dt]);
+        if (st + 2 < 2 * kDt) va[(st + 2) % 3] = vop((st + 2) / kDt, (st + 2) % kDt);
+        oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
+        SOFTMAX_STEP(2 * kDt, s1, st, pv, pb[2], pb[3], lsum1, off2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (more) {
-        // one barrier for both: every wavefront has read V_j, and K_{j+1} (the only copy in flight)
-        // has landed
-        if constexpr (kDirect) SLA_WAIT_VMCNT(0);
-        SLA_WAIT_LGKM0();
-        SLA_BARRIER();
-        stage_tile<T, D, false, NW>(V, p.vsN, jn, Vb, voff);
-      } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
-        SLA_WAIT_LGKM0();
-        SLA_BARRIER();                                 // every wavefront has read V_j
-        stage_tile<bf16raw, D, true, NW>(reinterpret_cast<const bf16raw*>(static_cast<const u16*>(p.S) + mrow * D * D),
-                                         D, 1, Vb, stage_offsets<D, true, NW>(D));
+    }
+    settle(s1, pb[2], pb[3], lsum1);
+
+    // ---- R3: O += V rows 32..63 x P1
+    {
+      constexpr int kSt = 2 * kDt;
+      bf16x8 va[3];                                  // operands two steps ahead
+      va[0] = vop(2, 0);
+      va[1] = vop(2 + 1 / kDt, 1 % kDt);
+#pragma unroll
+      for (int st = 0; st < kSt; ++st) {
+        const int u = 2 + st / kDt, dt = st % kDt;
+        if (st + 2 < kSt) va[(st + 2) % 3] = vop(2 + (st + 2) / kDt, (st + 2) % kDt);
+        oacc[dt] = mfma32(va[st % 3], pb[u], oacc[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+
+    // ---- D: V_j read by every wavefront; the next block's K resident (no copy after it)
+    if constexpr (kDirect) {
+      if (more) SLA_WAIT_VMCNT(0);
+    }
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();
+    if (more) {
+      stage_half<T, D, false, NW>(V, p.vsN, jn, 0, Vb, voff, vhs);
+      stage_half<T, D, false, NW>(V, p.vsN, jn, 1, Vb, voff, vhs);
+    } else if constexpr (LIN == SLA_LIN_MARGINAL && D == 128) {
+      stage_tile<bf16raw, D, true, NW>(Srow, D, 1, Vb, stage_offsets<D, true, NW>(D));
     }
   }
 
@@ -697,7 +535,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   // ---- store: lane holds O[tq][32 dt + 8 (e / 4) + 4 lg + e % 4]; padded query rows are zero
-  if constexpr (NW == 2) {
+  {
     if (!p.out_f32) {
       // bf16 output of one head: re-staged through the K buffer (64 rows of 2 D bytes, 16-byte
       // chunk c of row r at c ^ (r % chunks)) so that every store writes whole rows, 16 bytes a lane
@@ -744,11 +582,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 template <typename T, int D>
-static void launch_attn(const AttnParams& p, int causal, int lin, int hg, dim3 grid, hipStream_t st) {
-  if (hg == kGroupHeads) {   // GQA heads sharing one map: NW = 2 * kGroupHeads wavefronts
-    if (causal) attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2 * kGroupHeads><<<grid, 128 * kGroupHeads, 0, st>>>(p);
-    else attn_fwd_kernel<T, D, false, SLA_LIN_NONE, 2 * kGroupHeads><<<grid, 128 * kGroupHeads, 0, st>>>(p);
-  } else if (causal) {
+static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hipStream_t st) {
+  if (causal) {
     attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
     if (p.proj_w != nullptr) attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2, true><<<grid, 128, 0, st>>>(p);
@@ -779,15 +614,14 @@ sla_status launch_causal_pass(const sla_tensor* q, const sla_tensor* k, const sl
   p.scale_log2 = scale * 1.4426950408889634f;
   p.crit_rowptr = rowptr; p.crit_idx = idx; p.crit_flags = flags;
   p.out = out; p.out_f32 = 1;
-  const int hg = (q->H / k->H) % kGroupHeads == 0 ? kGroupHeads : 1;
-  const dim3 grid(nqb * (q->H / hg) * q->B);
+  const dim3 grid(nqb * q->H * q->B);
   const bool bf = q->dtype == SLA_BF16;
   if (q->d == 128) {
-    if (bf) launch_attn<bf16raw, 128>(p, 1, SLA_LIN_NONE, hg, grid, st);
-    else launch_attn<float, 128>(p, 1, SLA_LIN_NONE, hg, grid, st);
+    if (bf) launch_attn<bf16raw, 128>(p, 1, SLA_LIN_NONE, grid, st);
+    else launch_attn<float, 128>(p, 1, SLA_LIN_NONE, grid, st);
   } else {
-    if (bf) launch_attn<bf16raw, 64>(p, 1, SLA_LIN_NONE, hg, grid, st);
-    else launch_attn<float, 64>(p, 1, SLA_LIN_NONE, hg, grid, st);
+    if (bf) launch_attn<bf16raw, 64>(p, 1, SLA_LIN_NONE, grid, st);
+    else launch_attn<float, 64>(p, 1, SLA_LIN_NONE, grid, st);
   }
   return launch_status();
 }
@@ -864,16 +698,14 @@ extern "C" sla_status sla_attn_fwd(const sla_tensor* q, const sla_tensor* k, con
     p.u = z_all;
     p.w_gate = w_gate;
   }
-  // heads of a GQA group that share the map (and so every K/V tile) run in one workgroup
-  const int hg = (p.group_map && lin_mode == SLA_LIN_NONE && (q->H / k->H) % kGroupHeads == 0) ? kGroupHeads : 1;
-  dim3 grid(nqb * (q->H / hg) * q->B);
+  dim3 grid(nqb * q->H * q->B);
   const bool bf = q->dtype == SLA_BF16;
   if (d == 128) {
-    if (bf) launch_attn<bf16raw, 128>(p, causal, lin_mode, hg, grid, s);
-    else launch_attn<float, 128>(p, causal, lin_mode, hg, grid, s);
+    if (bf) launch_attn<bf16raw, 128>(p, causal, lin_mode, grid, s);
+    else launch_attn<float, 128>(p, causal, lin_mode, grid, s);
   } else {
-    if (bf) launch_attn<bf16raw, 64>(p, causal, lin_mode, hg, grid, s);
-    else launch_attn<float, 64>(p, causal, lin_mode, hg, grid, s);
+    if (bf) launch_attn<bf16raw, 64>(p, causal, lin_mode, grid, s);
+    else launch_attn<float, 64>(p, causal, lin_mode, grid, s);
   }
   return launch_status();
 }

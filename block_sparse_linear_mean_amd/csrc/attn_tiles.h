@@ -133,9 +133,10 @@ __device__ __forceinline__ void stage_half(const T* __restrict__ X, int64_t sN, 
   using Tl = AttnTile<D>;
   using SO = StageOff<D, NW>;
   constexpr int kHS = HalfSteps<D, NW>::kSteps;
-  // the K layout's per-lane offset depends on the step only at d = 128, through step % 4; with
-  // four steps per wavefront per half (NW = 2) the half's step n has the remainder of full step n
-  static_assert(kHS >= 1 && (D == 64 || kHS % 4 == 0), "half tiles: unsupported wavefront count");
+  // the K layout's per-lane offset depends on the step only at d = 128, through step % 4: the
+  // half's step q = h kInst/2 + kHS w + n has the remainder of this wavefront's full-tile step
+  // m = (q - kSteps w) % 4 = (n + (kHS - kSteps) w) % 4, which is n (kHS = 4) or n + 2 w (kHS = 2)
+  static_assert(kHS >= 1 && (D == 64 || kHS == 4 || kHS == 2), "half tiles: unsupported wavefront count");
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
   if constexpr (sizeof(T) == 2) {
@@ -143,7 +144,12 @@ __device__ __forceinline__ void stage_half(const T* __restrict__ X, int64_t sN, 
 #pragma unroll
     for (int n = 0; n < kHS; ++n) {
       const int q = h * (Tl::kInst / 2) + kHS * w + n;
-      const uint32_t vo = off.lane[KLAYOUT && D == 128 ? n % SO::kLanes : 0] + hs.step[n];
+      uint32_t lo = off.lane[0];
+      if constexpr (KLAYOUT && D == 128) {
+        if constexpr (kHS == 4) lo = off.lane[n];
+        else lo = (w & 1) ? off.lane[(n + 2) & 3] : off.lane[n & 3];
+      }
+      const uint32_t vo = lo + hs.step[n];
       load_lds16_sbase(tb, vo, tile + q * 1024);
     }
   } else {
