@@ -6,9 +6,11 @@
 // prediction that turns the N x N problem into an (N/b)^2 classification).
 //
 // Both passes are small next to attention: pooling is HBM-bound (Q and K read once),
-// scoring is fp64 FMA work on the pooled vectors.  The classification ranks these
+// scoring is fp64 matrix-core work on the pooled vectors.  The classification ranks these
 // scores, so they are computed in fp64 from the fp32 pooled vectors and rounded once:
 // each stored score is the correctly rounded fp32 of a near-exact fp64 dot product.
+#include <type_traits>
+
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -85,109 +87,111 @@ __global__ __launch_bounds__(256) void qsum_kernel(const float* __restrict__ qpo
   qsum[int64_t(bg) * nb * d + e] = s;
 }
 
-// Pooled scores, one 64 (i) x TJ (j) tile of one score matrix per workgroup (TJ = 64: twice the
-// workgroups of 128-wide tiles, for more wavefronts in flight); each thread owns
-// 4 x TJ/16 outputs.  scores[b,s,i,j] = fp32(scale * sum_r qsum[i,r] * kpool[j,r]) with a
-// sequential fp64 FMA chain over r; with group_sum, qsum is the group's fp64 sum of pooled
-// queries (read from qsum_kernel's output when given, else summed here).  The pooled vectors stream through LDS 32 features at a time, the next
-// chunk's loads in flight in registers while the current chunk is multiplied.
-constexpr int kScI = 64, kScR = 32;
+// Pooled scores on the fp64 matrix cores: one 64 (i) x 64 (j) tile of one score matrix per
+// workgroup, each wavefront a 32 x 32 quarter as 2 x 2 products of the 16x16x4 fp64 instruction.
+// scores[b,s,i,j] = fp32(scale * sum_r qv[i,r] * kpool[j,r]) with the sum in fp64; qv is the
+// fp64 group sum of the pooled queries (QSUM: qsum_kernel's output, one row per (b, s)) or, for
+// a single query head per score matrix (no group sum, or groups of one head), that head's pooled
+// queries: s is then the query head.  The operands come straight from global memory (the pooled
+// vectors are small and stay in cache): in 16-feature chunk c, lane group g = lane / 16 holds
+// features 16 c + 4 g .. 16 c + 4 g + 3 of its row and feeds them to four consecutive k-steps,
+// so one 16-byte load per row and chunk serves four instructions; A and B use the same feature
+// order, so every product pairs matching features.  The sum is taken in a different order from
+// the oracle's, so the fp64 values differ in their last bits; rounded to fp32 they agree except
+// on an fp32 rounding boundary.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+constexpr int kScI = 64, kScJ = 64;
 
-template <int D, int TJ>
+template <int D, bool QSUM>
 __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qpool,
                                                      const float* __restrict__ kpool, int Hq, int Hkv,
                                                      int Hs, int nb, int group_sum, int causal,
                                                      double scale, const double* __restrict__ qsum,
                                                      float* __restrict__ scores) {
-  constexpr int kJ = TJ / 16;                    // outputs per thread along j
-  constexpr int kKl = TJ * kScR / 256;           // k-chunk elements per thread
+  constexpr int kC = D / 16;                     // 16-feature chunks
   const int bs = blockIdx.z;
   const int b = bs / Hs, s = bs % Hs;
   const int G = Hq / Hkv;
   const int g = group_sum ? s : s / G;
-  const int i0 = blockIdx.y * kScI, j0 = blockIdx.x * TJ;
+  const int i0 = blockIdx.y * kScI, j0 = blockIdx.x * kScJ;
   const int t = threadIdx.x;
-  const int tx = t % 16, ty = t / 16;
   float* out = scores + int64_t(bs) * nb * nb;
 
   if (causal && j0 > i0 + kScI - 1) {   // the whole tile lies above the diagonal
-    for (int e = t; e < kScI * TJ; e += 256) {
-      const int ii = i0 + e / TJ, jj = j0 + e % TJ;
+    for (int e = t; e < kScI * kScJ; e += 256) {
+      const int ii = i0 + e / kScJ, jj = j0 + e % kScJ;
       if (ii < nb && jj < nb) out[int64_t(ii) * nb + jj] = -__builtin_inff();
     }
     return;
   }
 
-  __shared__ double qs[kScI][kScR + 1];
-  __shared__ double ks[TJ][kScR + 1];       // converted once here, not by every reader
-  double acc[4][kJ];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < kJ; ++c) acc[a][c] = 0.0;
+  const int lane = t % kWave, w = t / kWave;
+  const int li = lane % 16, lg = lane / 16;
+  const int wi = i0 + 32 * (w / 2), wj = j0 + 32 * (w % 2);
 
-  const int gh0 = group_sum ? g * G : s;
-  const int ngh = group_sum ? G : 1;
-  const double* qs_row = qsum != nullptr ? qsum + int64_t(bs) * nb * D : nullptr;   // group sums, if given
-  // staging map: q chunk 64 x 32 -> 8 elements per thread, k chunk TJ x 32 -> kKl per thread
-  double qreg[8];
-  float kreg[kKl];
-  auto load = [&](int r0) {
+  // a[tt][c]: features 16 c + 4 lg + 0..3 of query row wi + 16 tt + li; kv[uu][c] likewise for key
+  // row wj + 16 uu + li (rows past nb read row nb - 1 and are not stored); all loads are issued
+  // before the first product
+  typedef typename std::conditional<QSUM, f64x4, f32x4>::type AVec;
+  AVec a[2][kC];
+  f32x4 kv[2][kC];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int e = t + 256 * n;
-      const int row = e / kScR, col = e % kScR;
-      const int ii = i0 + row;
-      double qv = 0.0;
-      if (ii < nb) {
-        if (qs_row != nullptr) qv = qs_row[int64_t(ii) * D + r0 + col];
-        else
-          for (int hh = 0; hh < ngh; ++hh) qv += double(qpool[((int64_t(b) * Hq + gh0 + hh) * nb + ii) * D + r0 + col]);
-      }
-      qreg[n] = qv;
-    }
+  for (int uu = 0; uu < 2; ++uu) {
+    const int jj = min(wj + 16 * uu + li, nb - 1);
+    const float* kp = kpool + ((int64_t(b) * Hkv + g) * nb + jj) * D + 4 * lg;
 #pragma unroll
-    for (int n = 0; n < kKl; ++n) {
-      const int e = t + 256 * n;
-      const int row = e / kScR, col = e % kScR;
-      const int jj = j0 + row;
-      kreg[n] = jj < nb ? kpool[((int64_t(b) * Hkv + g) * nb + jj) * D + r0 + col] : 0.f;
-    }
-  };
-  load(0);
-  for (int r0 = 0; r0 < D; r0 += kScR) {
-    __syncthreads();                      // the previous chunk has been read
-#pragma unroll
-    for (int n = 0; n < 8; ++n) { const int e = t + 256 * n; qs[e / kScR][e % kScR] = qreg[n]; }
-#pragma unroll
-    for (int n = 0; n < kKl; ++n) { const int e = t + 256 * n; ks[e / kScR][e % kScR] = double(kreg[n]); }
-    __syncthreads();
-    if (r0 + kScR < D) load(r0 + kScR);
-#pragma unroll 8
-    for (int r = 0; r < kScR; ++r) {
-      double qa[4], kb[kJ];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qa[a] = qs[ty + 16 * a][r];
-#pragma unroll
-      for (int c = 0; c < kJ; ++c) kb[c] = ks[tx + 16 * c][r];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < kJ; ++c) acc[a][c] = __fma_rn(qa[a], kb[c], acc[a][c]);
-    }
+    for (int c = 0; c < kC; ++c) kv[uu][c] = *reinterpret_cast<const f32x4*>(kp + 16 * c);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int ii = i0 + ty + 16 * a;
+  for (int tt = 0; tt < 2; ++tt) {
+    const int ii = min(wi + 16 * tt + li, nb - 1);
+    if constexpr (QSUM) {
+      const double* qp = qsum + (int64_t(bs) * nb + ii) * D + 4 * lg;
 #pragma unroll
-    for (int c = 0; c < kJ; ++c) {
-      const int jj = j0 + tx + 16 * c;
-      if (ii < nb && jj < nb) {
-        const float v = (causal && jj > ii) ? -__builtin_inff() : float(acc[a][c] * scale);
-        out[int64_t(ii) * nb + jj] = v;
+      for (int c = 0; c < kC; ++c) {
+        const f64x2 lo = *reinterpret_cast<const f64x2*>(qp + 16 * c);
+        const f64x2 hi = *reinterpret_cast<const f64x2*>(qp + 16 * c + 2);
+        a[tt][c] = f64x4{lo[0], lo[1], hi[0], hi[1]};
       }
+    } else {
+      const float* qp = qpool + ((int64_t(b) * Hq + s) * nb + ii) * D + 4 * lg;
+#pragma unroll
+      for (int c = 0; c < kC; ++c) a[tt][c] = *reinterpret_cast<const f32x4*>(qp + 16 * c);
     }
   }
+
+  __builtin_amdgcn_sched_barrier(0);           // keep every load ahead of the products
+
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) acc[tt][uu] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int c = 0; c < kC; ++c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+          acc[tt][uu] = __builtin_amdgcn_mfma_f64_16x16x4f64(double(a[tt][c][m]), double(kv[uu][c][m]), acc[tt][uu],
+                                                            0, 0, 0);
+
+  // lane holds rows wi + 16 tt + 4 e + lg, column wj + 16 uu + li of the tile in acc[tt][uu][e]
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int jj = wj + 16 * uu + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = wi + 16 * tt + 4 * e + lg;
+        if (ii < nb && jj < nb)
+          out[int64_t(ii) * nb + jj] = (causal && jj > ii) ? -__builtin_inff() : float(acc[tt][uu][e] * scale);
+      }
+    }
 }
 
 __global__ __launch_bounds__(64) void probs_kernel(const float* __restrict__ scores, int nb,
@@ -239,6 +243,7 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if ((st = check_tensor(k)) != SLA_OK) return st;
   if (!same_geometry(q, k) || q->H % k->H != 0) return SLA_ERR_SHAPE;
   if (q_pool == nullptr || k_pool == nullptr || scores == nullptr) return SLA_ERR_NULL;
+  if (!aligned16(q_pool) || !aligned16(k_pool)) return SLA_ERR_ALIGN;
   if ((st = check_valid_len(n_valid, q->N)) != SLA_OK) return st;
   if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
   const size_t need = sla_pool_scores_workspace_bytes(q->B, q->H, k->H, q->N, q->d, group_sum);
@@ -255,14 +260,15 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
         q_pool, q->H, k->H, nb, q->d, qs);
     qsum = qs;
   }
-  constexpr int kTJ = 64;
-  dim3 grid((nb + kTJ - 1) / kTJ, (nb + kScI - 1) / kScI, q->B * Hs);
-  if (q->d == 128)
-    scores_kernel<128, kTJ><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
-                                                 causal ? 1 : 0, double(scale), qsum, scores);
-  else
-    scores_kernel<64, kTJ><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, group_sum ? 1 : 0,
-                                                causal ? 1 : 0, double(scale), qsum, scores);
+  dim3 grid((nb + kScJ - 1) / kScJ, (nb + kScI - 1) / kScI, q->B * Hs);
+  const int gs = group_sum ? 1 : 0, ca = causal ? 1 : 0;
+  if (q->d == 128) {
+    if (qsum) scores_kernel<128, true><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, gs, ca, double(scale), qsum, scores);
+    else scores_kernel<128, false><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, gs, ca, double(scale), qsum, scores);
+  } else {
+    if (qsum) scores_kernel<64, true><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, gs, ca, double(scale), qsum, scores);
+    else scores_kernel<64, false><<<grid, 256, 0, s>>>(q_pool, k_pool, q->H, k->H, Hs, nb, gs, ca, double(scale), qsum, scores);
+  }
   if (probs != nullptr) probs_kernel<<<dim3(q->B * Hs * nb), 64, 0, s>>>(scores, nb, probs);
   return launch_status();
 }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SLA_ABI_VERSION 4
+#define SLA_ABI_VERSION 5
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
 #define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
@@ -117,6 +117,7 @@ sla_status sla_counts(int32_t nb, int32_t kh_bp, int32_t kl_bp, int32_t* n_crit,
  *   probs (nullable) = row softmax of scores over the row's finite candidates (fp32,
  *     same shape as scores), for diagnostics; the classification ranks the scores.
  * q and k share dtype and d; n_valid as in the conventions; scale > 0 (normally 1/sqrt(d)).
+ * q_pool and k_pool are 16-byte aligned (SLA_ERR_ALIGN otherwise).
  * workspace: sla_pool_scores_workspace_bytes(...) bytes (the fp64 group sums of the pooled
  * queries, non-zero only with group_sum and more than one query head per KV head).
  */

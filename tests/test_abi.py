@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert sla.sla_abi_version() == 4
+    assert sla.sla_abi_version() == 5
     for s in range(9):
         assert len(sla.sla_status_str(s)) > 0
     assert sla.sla_status_str(12345) == "unknown status"
@@ -92,6 +92,8 @@ def test_pool_scores_validation(L):
     good = desc()
     assert pool_call(L, desc(ptr=0), good) == ENULL
     assert pool_call(L, good, good, qp=None) == ENULL
+    assert pool_call(L, good, good, qp=ctypes.c_void_p(0x20004)) == EALIGN   # pooled vectors are read 16 bytes at a time
+    assert pool_call(L, good, good, kp=ctypes.c_void_p(0x20008)) == EALIGN
     assert pool_call(L, desc(d=96), desc(d=96)) == EUNSUP
     assert pool_call(L, desc(dtype=7), good) == EUNSUP
     assert pool_call(L, desc(N=200), desc(N=200)) == ESHAPE
