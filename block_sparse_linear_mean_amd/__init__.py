@@ -110,6 +110,10 @@ class SlaForward:
             self.kv = dict(H_all=torch.empty((B, Hkv, d, d), **f), z_all=torch.empty((B, Hkv, d), **f),
                            workspace=torch.empty(ws, device=dev, dtype=torch.uint8), workspace_bytes=ws)
         self.k_mean = torch.empty((B, Hkv, d), **f) if smooth_k else None
+        # The key-state pass reads K anyway: when it runs without a shift, it also writes the key
+        # block means, and the pooling pass reads only Q.  For bf16 K (exact fp64 block sums) the
+        # means are the pooling pass's bit for bit, so the block map does not change.
+        self.fuse_key_pooling = self.lin != SLA_LIN_NONE and not smooth_k and k.dtype == torch.bfloat16
         # training: the forward also writes each row's log-sum-exp, which backward() reads
         if training and (mode != "sla" or Hq != Hkv):
             raise ValueError("backward is provided for the sla mode with Hq == Hkv")
@@ -136,20 +140,24 @@ class SlaForward:
             sla_permute_rows(self.out_ordered, self.order, inverse=True, out=self.out)
         return self.out
 
-    def pool_scores(self):
+    def pool_scores(self, k_pooled: bool = False):
+        """Pooled Q and K and the pooled scores; k_pooled: the key block means are already in
+        self.pool["k_pool"] (from kv_reduce(k_pool=True)), so only Q is pooled."""
         return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
-                               scale=self.scale, out=self.pool)
+                               scale=self.scale, out=self.pool, k_pooled=k_pooled)
 
     def block_map(self):
         return sla_block_map(self.pool["scores"], self.n_crit, self.n_negl, causal=self.causal,
                              window=self.window, out=self.maps)
 
-    def kv_reduce(self):
-        """Linear-branch key states (after pool_scores when smooth_k: the shift comes from k_pool)."""
+    def kv_reduce(self, k_pool: bool = False):
+        """Linear-branch key states (after pool_scores when smooth_k: the shift comes from k_pool).
+        k_pool: also write the key block means into self.pool["k_pool"] (K is read once for both)."""
         if self.lin != SLA_LIN_NONE:
             if self.smooth_k:
                 sla_key_mean(self.pool["k_pool"], self.n_valid, out=self.k_mean)
-            sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv, k_shift=self.k_mean)
+            sla_linear_kv_reduce(self.k, self.v, self.n_valid, out=self.kv, k_shift=self.k_mean,
+                                 k_pool=self.pool["k_pool"] if k_pool else None)
         return self.kv
 
     def marginal_states(self, maps=None):
@@ -199,7 +207,8 @@ class SlaForward:
 
     def run(self, overlap: bool = False, events=None) -> torch.Tensor:
         """One full forward: (token order,) pool + scores, block map, linear states, marginal sums,
-        attention (, order undone).
+        attention (, order undone).  With fuse_key_pooling the linear key states come first and also
+        write the key block means, and the pooling pass reads only Q.
 
         overlap: the linear key states depend only on K and V (and, with smooth-K, on the pooled
         keys), so they can run on a second stream while the scores and the block map run; the
@@ -216,6 +225,13 @@ class SlaForward:
             else:
                 fn()
         timed("reorder", self.reorder)
+        if self.fuse_key_pooling and not overlap:
+            timed("kv_reduce", lambda: self.kv_reduce(k_pool=True))
+            timed("pool_scores", lambda: self.pool_scores(k_pooled=True))
+            for name in ("block_map", "marginal_states", "attention"):
+                timed(name, getattr(self, name))
+            timed("restore", self.restore)
+            return self.out
         if not overlap or self.lin == SLA_LIN_NONE:
             for name in ("pool_scores", "block_map", "kv_reduce", "marginal_states", "attention"):
                 timed(name, getattr(self, name))

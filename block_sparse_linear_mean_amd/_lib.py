@@ -42,7 +42,7 @@ _SIGS = {
     "sla_status_str": (c_char_p, [c_int32]),
     "sla_counts": (c_int32, [c_int32, c_int32, c_int32, _I32P, _I32P]),
     "sla_pool_scores": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, c_int32, c_int32, c_float,
-                                  _P, _P, _P, _P, _P, c_size_t, _P]),
+                                  c_int32, _P, _P, _P, _P, _P, c_size_t, _P]),
     "sla_pool_scores_workspace_bytes": (c_size_t, [c_int32] * 6),
     "sla_block_map_capacity": (c_int64, [c_int32] * 9),
     "sla_block_map_workspace_bytes": (c_size_t, [c_int32] * 7),
@@ -51,7 +51,7 @@ _SIGS = {
     "sla_kv_reduce_workspace_bytes": (c_size_t, [c_int32] * 6),
     "sla_key_mean": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, _P, _P]),
     "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P, _P,
-                                       c_size_t, _P]),
+                                       _P, c_size_t, _P]),
     "sla_marginal_states": (c_int32, [_P, _P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                       _P, _P, _P, _P]),
     "sla_attn_workspace_bytes": (c_size_t, [c_int32] * 5),
@@ -151,8 +151,13 @@ def sla_attn_workspace_bytes(B, Hs, nqb, d, lin_mode) -> int:
 
 # ----------------------------------------------------------------------------- GPU calls
 
-def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, want_probs=False, out=None):
-    """Returns dict(q_pool, k_pool, scores[, probs]); `out` may hold preallocated tensors."""
+def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, want_probs=False, out=None,
+                    k_pooled=False):
+    """Returns dict(q_pool, k_pool, scores[, probs]); `out` may hold preallocated tensors.
+
+    k_pooled: out["k_pool"] already holds the key block means (sla_linear_kv_reduce's k_pool output);
+    only Q is pooled.
+    """
     _require_gpu(q, k)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -170,7 +175,7 @@ def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, wa
         out["workspace"] = torch.empty(ws, device=q.device, dtype=torch.uint8)
     qd, kd = tensor_desc(q), tensor_desc(k)
     _check("sla_pool_scores", lib().sla_pool_scores(
-        ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale),
+        ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale), int(bool(k_pooled)),
         _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]), _ptr(out.get("probs")),
         _ptr(out.get("workspace")), ws, _stream(q.device)))
     return out
@@ -221,16 +226,20 @@ def sla_key_mean(k_pool, n_valid, out=None):
     return out
 
 
-def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None, k_shift=None):
+def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None, k_shift=None, k_pool=None):
     """Returns dict(H, z[, H_all, z_all]): per-block states H in bf16, everything else fp32.
 
     k_shift [B, Hkv, d] fp32 (smooth-K, e.g. from sla_key_mean): states of phi(K - k_shift).
+    k_pool [B, Hkv, nb, d] fp32 (optional output): also the key block means of the prediction step.
     """
     _require_gpu(k, v)
     if k_shift is not None and (k_shift.dtype != torch.float32 or not k_shift.is_contiguous()):
         raise ValueError("k_shift must be a contiguous float32 [B, Hkv, d] tensor")
     B, Hkv, N, d = k.shape
     nb = N // BLOCK
+    if k_pool is not None and (k_pool.dtype != torch.float32 or not k_pool.is_contiguous()
+                               or tuple(k_pool.shape) != (B, Hkv, nb, d)):
+        raise ValueError("k_pool must be a contiguous float32 [B, Hkv, nb, d] tensor")
     if out is None:
         f = dict(device=k.device, dtype=torch.float32)
         out = {}
@@ -246,8 +255,8 @@ def sla_linear_kv_reduce(k, v, n_valid, per_block=True, want_all=False, out=None
     kd, vd = tensor_desc(k), tensor_desc(v)
     _check("sla_linear_kv_reduce", lib().sla_linear_kv_reduce(
         ctypes.byref(kd), ctypes.byref(vd), n_valid, _ptr(k_shift), _ptr(out.get("H")), _ptr(out.get("z")),
-        _ptr(out.get("H_all")), _ptr(out.get("z_all")), _ptr(out.get("workspace")), out.get("workspace_bytes", 0),
-        _stream(k.device)))
+        _ptr(out.get("H_all")), _ptr(out.get("z_all")), _ptr(k_pool), _ptr(out.get("workspace")),
+        out.get("workspace_bytes", 0), _stream(k.device)))
     return out
 
 

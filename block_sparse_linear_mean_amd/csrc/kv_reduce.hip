@@ -22,7 +22,8 @@
 // a B operand of ones, so z sums exactly the rounded phi(K) values H uses.  A lane's accumulator
 // holds 4 consecutive r for one c; bf16 states are re-staged through LDS and written with
 // 1 KB-contiguous wavefront stores, fp32 run sums with 16-byte stores.  The pass is HBM-bound:
-// K and V in, one state per block out.
+// K and V in, one state per block out.  Optionally it also writes the key block means of the
+// prediction step from the same registers, so the pooling pass need not read K again.
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -77,13 +78,26 @@ struct KvPiece {
   }
   // phi(K - shift) rounded to bf16 and V (zero for padded rows), into trs-layout tiles.  A
   // thread's pieces all cover features 8 (t % kChunks) .. + 7, the 8 entries of `shift`.
-  __device__ __forceinline__ void store(lds_u8* kt, lds_u8* vt, const float* shift) const {
+  // POOL: ps = this thread's fp64 sums of its valid rows of raw K (before the shift), the
+  // partial sums of the key block mean.
+  template <bool POOL>
+  __device__ __forceinline__ void store(lds_u8* kt, lds_u8* vt, const float* shift, double (&ps)[8]) const {
+    if constexpr (POOL) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ps[m] = 0.0;
+    }
 #pragma unroll
     for (int n = 0; n < kPer; ++n) {
       const int e = threadIdx.x + 256 * n;
       const int r = e / kChunks, c = e % kChunks;
       float kf[8];
       unpack(k[n], kf);
+      if constexpr (POOL) {
+        if ((valid >> n) & 1u) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) ps[m] += double(kf[m]);
+        }
+      }
       f32x8 f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) f[m] = phi(kf[m] - shift[m]);
@@ -104,18 +118,24 @@ struct KvPiece {
 
 // grid: x = run of cb key blocks, y = b * Hkv + g.  PER_BLOCK: every block's state goes to
 // Hb (bf16) and z; otherwise the run's sum goes to Hf (fp32) and z at index y * gridDim.x + x.
-template <typename T, int D, bool PER_BLOCK>
+// POOL: also kpool, each block's mean of the valid rows of K, [B, Hkv, nb, D] fp32, from fp64
+// sums (each thread's rows, then the threads of a feature in a fixed order through LDS) and one
+// rounding: the pooled keys of the prediction step, read here from the registers that already
+// hold K, so K is read from memory once for both.
+template <typename T, int D, bool PER_BLOCK, bool POOL>
 __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, int64_t ksB, int64_t ksH,
                                                        int64_t ksN, const T* __restrict__ v, int64_t vsB,
                                                        int64_t vsH, int64_t vsN, int Hkv, int nb, int n_valid,
                                                        int cb, const float* __restrict__ kshift,
                                                        u16* __restrict__ Hb, float* __restrict__ Hf,
-                                                       float* __restrict__ zout) {
+                                                       float* __restrict__ zout, float* __restrict__ kpool) {
   constexpr int RB = 2 * D;
   constexpr int kCt = D == 128 ? 4 : 1;          // 32-column tiles of c per wavefront
   constexpr int kChunks = D / 8;                 // 16-byte chunks per 2D-byte row
   // phi(K) and V tiles; after a block's products the same 2 x 64 x 2D bytes stage its D x D bf16 state
   __shared__ __attribute__((aligned(1024))) unsigned char tsm[2 * kBlock * RB];
+  constexpr int kRowGroups = 256 / kChunks;     // threads sharing one 8-feature chunk
+  __shared__ double kred[POOL ? kRowGroups : 1][D];   // per-thread partial sums of the key block mean
   lds_u8* Kt = to_lds(tsm);
   lds_u8* Vt = Kt + kBlock * RB;
   const int x = blockIdx.x, bg = blockIdx.y;
@@ -197,9 +217,22 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   if (j0 < j1) pc.load(K, ksN, V, vsN, j0, n_valid);
   for (int j = j0; j < j1; ++j) {
     __syncthreads();                    // the previous block's operands (and staged state) have been read
-    pc.store(Kt, Vt, shift);
+    double ps[8];
+    pc.template store<POOL>(Kt, Vt, shift, ps);
+    if constexpr (POOL) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kred[t / kChunks][8 * (t % kChunks) + m] = ps[m];
+    }
     __syncthreads();
     if (j + 1 < j1) pc.load(K, ksN, V, vsN, j + 1, n_valid);
+    if (POOL && t < D) {                // after the next block's loads are issued; kred is rewritten
+                                        // only after the next block's first barrier
+      double tot = kred[0][t];
+#pragma unroll
+      for (int i = 1; i < kRowGroups; ++i) tot += kred[i][t];
+      const int rows = min(kBlock, n_valid - kBlock * j);
+      kpool[(int64_t(bg) * nb + j) * D + t] = float(rows == kBlock ? tot * (1.0 / kBlock) : tot / double(rows));
+    }
 #pragma unroll
     for (int ks = 0; ks < kBlock / 16; ++ks) {
       lds_u8* kk0 = Kt + 16 * ks * RB;
@@ -235,20 +268,21 @@ __global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict
 
 template <typename T>
 static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int cb, int nch, const float* kshift,
-                      u16* Hb, float* Hf, float* z, hipStream_t st) {
+                      u16* Hb, float* Hf, float* z, float* kpool, hipStream_t st) {
   const int nb = k->N / kBlock;
   dim3 grid(nch, k->B * k->H);
   const T* kp = static_cast<const T*>(k->ptr);
   const T* vp = static_cast<const T*>(v->ptr);
-#define SLA_KV_LAUNCH(DD, PB)                                                                                    \
-  kv_state_kernel<T, DD, PB><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, nb, \
-                                                   n_valid, cb, kshift, Hb, Hf, z)
+#define SLA_KV_LAUNCH(DD, PB, PL)                                                                                \
+  kv_state_kernel<T, DD, PB, PL><<<grid, 256, 0, st>>>(kp, k->sB, k->sH, k->sN, vp, v->sB, v->sH, v->sN, k->H, \
+                                                       nb, n_valid, cb, kshift, Hb, Hf, z, kpool)
+  const bool pool = kpool != nullptr;
   if (k->d == 128) {
-    if (Hb != nullptr) SLA_KV_LAUNCH(128, true);
-    else SLA_KV_LAUNCH(128, false);
+    if (Hb != nullptr) { if (pool) SLA_KV_LAUNCH(128, true, true); else SLA_KV_LAUNCH(128, true, false); }
+    else { if (pool) SLA_KV_LAUNCH(128, false, true); else SLA_KV_LAUNCH(128, false, false); }
   } else {
-    if (Hb != nullptr) SLA_KV_LAUNCH(64, true);
-    else SLA_KV_LAUNCH(64, false);
+    if (Hb != nullptr) { if (pool) SLA_KV_LAUNCH(64, true, true); else SLA_KV_LAUNCH(64, true, false); }
+    else { if (pool) SLA_KV_LAUNCH(64, false, true); else SLA_KV_LAUNCH(64, false, false); }
   }
 #undef SLA_KV_LAUNCH
 }
@@ -262,7 +296,7 @@ static void launch_sum(const float* in, int parts, int64_t len, int bgs, float* 
 
 extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
                                            const float* k_shift, void* H, float* z, float* H_all, float* z_all,
-                                           void* workspace, size_t workspace_bytes, void* stream) {
+                                           float* k_pool, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace sla;
   sla_status st = check_tensor(k);
   if (st != SLA_OK) return st;
@@ -273,7 +307,7 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
   if ((H == nullptr) != (z == nullptr) || (H_all == nullptr) != (z_all == nullptr)) return SLA_ERR_NULL;
   if ((H != nullptr && (!aligned16(H) || !aligned16(z))) || (H_all != nullptr && (!aligned16(H_all) || !aligned16(z_all))))
     return SLA_ERR_ALIGN;
-  if (k_shift != nullptr && !aligned16(k_shift)) return SLA_ERR_ALIGN;
+  if ((k_shift != nullptr && !aligned16(k_shift)) || (k_pool != nullptr && !aligned16(k_pool))) return SLA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = k->N / kBlock;
   const int d = k->d;
@@ -287,8 +321,9 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     const int nch = (nb + cb - 1) / cb;
     float* Hp = static_cast<float*>(workspace);
     float* zp = Hp + int64_t(bgs) * nch * d * d;
-    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, s);
-    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, s);
+    float* kp = H == nullptr ? k_pool : nullptr;   // the key block means come from one of the two passes
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, kp, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, kp, s);
     launch_sum(Hp, nch, int64_t(d) * d, bgs, H_all, s);
     launch_sum(zp, nch, d, bgs, z_all, s);
   }
@@ -296,8 +331,8 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     // runs of a few blocks per workgroup (one block of prefetch), at least ~2048 workgroups
     const int cb = std::max(1, std::min(4, nb * bgs / 2048));
     const int nch = (nb + cb - 1) / cb;
-    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, s);
-    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, s);
+    if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, k_pool, s);
+    else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, static_cast<u16*>(H), nullptr, z, k_pool, s);
   }
   return launch_status();
 }

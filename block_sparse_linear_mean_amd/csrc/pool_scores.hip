@@ -17,7 +17,8 @@
 namespace sla {
 
 // One workgroup pools kPoolBlocks consecutive blocks of one (b, h) of Q or K (grid y runs over
-// the Q heads, then the K heads): 256 threads; each thread owns 8 consecutive features of one
+// the Q heads, then the nhk K heads; nhk = 0 when the key block means come from the key-state
+// pass): 256 threads; each thread owns 8 consecutive features of one
 // row group, issues all of its 16-byte loads before summing, and sums in fp64 (exact for bf16
 // inputs); partial sums are combined in a fixed order, so the result does not depend on
 // scheduling.
@@ -26,13 +27,13 @@ constexpr int kPoolBlocks = 4;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t qsB, int64_t qsH, int64_t qsN,
                                                    int Hq, const T* __restrict__ k, int64_t ksB, int64_t ksH,
-                                                   int64_t ksN, int Hkv, int nb, int n_valid,
+                                                   int64_t ksN, int Hkv, int nhk, int nb, int n_valid,
                                                    float* __restrict__ qout, float* __restrict__ kout) {
   constexpr int kTpr = D / 8;          // threads per row
   constexpr int kRpp = 256 / kTpr;     // rows per pass
   constexpr int kPasses = kBlock / kRpp;
   const int y = blockIdx.y;
-  const int B = gridDim.y / (Hq + Hkv);
+  const int B = gridDim.y / (Hq + nhk);
   const bool is_q = y < B * Hq;
   const int bh = is_q ? y : y - B * Hq;            // (b, h) index within its tensor
   const int H = is_q ? Hq : Hkv;
@@ -211,18 +212,19 @@ __global__ __launch_bounds__(64) void probs_kernel(const float* __restrict__ sco
 }
 
 template <typename T>
-static void launch_pool(const sla_tensor* q, const sla_tensor* k, int n_valid, float* qout, float* kout,
-                        hipStream_t st) {
+static void launch_pool(const sla_tensor* q, const sla_tensor* k, int n_valid, bool pool_k, float* qout,
+                        float* kout, hipStream_t st) {
   const int nb = q->N / kBlock;
-  dim3 grid((nb + kPoolBlocks - 1) / kPoolBlocks, q->B * (q->H + k->H));
+  const int nhk = pool_k ? k->H : 0;
+  dim3 grid((nb + kPoolBlocks - 1) / kPoolBlocks, q->B * (q->H + nhk));
   const T* qp = static_cast<const T*>(q->ptr);
   const T* kp = static_cast<const T*>(k->ptr);
   if (q->d == 128)
-    pool_kernel<T, 128><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nb,
-                                              n_valid, qout, kout);
+    pool_kernel<T, 128><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nhk,
+                                              nb, n_valid, qout, kout);
   else
-    pool_kernel<T, 64><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nb,
-                                             n_valid, qout, kout);
+    pool_kernel<T, 64><<<grid, 256, 0, st>>>(qp, q->sB, q->sH, q->sN, q->H, kp, k->sB, k->sH, k->sN, k->H, nhk,
+                                             nb, n_valid, qout, kout);
 }
 
 }  // namespace sla
@@ -234,7 +236,7 @@ extern "C" size_t sla_pool_scores_workspace_bytes(int32_t B, int32_t Hq, int32_t
 }
 
 extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
-                                      int32_t group_sum, int32_t causal, float scale, float* q_pool,
+                                      int32_t group_sum, int32_t causal, float scale, int32_t k_pooled, float* q_pool,
                                       float* k_pool, float* scores, float* probs, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   using namespace sla;
@@ -250,8 +252,8 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) return SLA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = q->N / kBlock;
-  if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, q_pool, k_pool, s);
-  else launch_pool<float>(q, k, n_valid, q_pool, k_pool, s);
+  if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, !k_pooled, q_pool, k_pool, s);
+  else launch_pool<float>(q, k, n_valid, !k_pooled, q_pool, k_pool, s);
   const int Hs = group_sum ? k->H : q->H;
   const double* qsum = nullptr;
   if (group_sum && q->H / k->H > 1) {             // the group sums once, instead of in every tile

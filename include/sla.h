@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SLA_ABI_VERSION 5
+#define SLA_ABI_VERSION 6
 #define SLA_BLOCK 64
 #define SLA_MAX_KEY_BLOCKS 4096 /* per row: N <= 262144 tokens */
 #define SLA_MAX_ROW_STRIDE (1 << 24) /* elements between consecutive tokens of one head */
@@ -118,11 +118,14 @@ sla_status sla_counts(int32_t nb, int32_t kh_bp, int32_t kl_bp, int32_t* n_crit,
  *     same shape as scores), for diagnostics; the classification ranks the scores.
  * q and k share dtype and d; n_valid as in the conventions; scale > 0 (normally 1/sqrt(d)).
  * q_pool and k_pool are 16-byte aligned (SLA_ERR_ALIGN otherwise).
+ * k_pooled != 0: k_pool already holds the key block means (written by sla_linear_kv_reduce's
+ *   k_pool output, which reads K once for both); only Q is pooled and K's data is not read
+ *   (its descriptor still gives the shapes).
  * workspace: sla_pool_scores_workspace_bytes(...) bytes (the fp64 group sums of the pooled
  * queries, non-zero only with group_sum and more than one query head per KV head).
  */
 sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
-                           int32_t group_sum, int32_t causal, float scale,
+                           int32_t group_sum, int32_t causal, float scale, int32_t k_pooled,
                            float* q_pool, float* k_pool, float* scores, float* probs,
                            void* workspace, size_t workspace_bytes, void* stream);
 
@@ -204,12 +207,17 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
  * sla_key_mean): when given, every phi(K[s,r]) above is phi(K[s,r] - k_shift[b,g,r]).
  * phi(K) is rounded to bf16 for the matrix-core contraction (fp32 accumulation); z sums
  * the same rounded values.  At least one of H, H_all must be non-NULL; outputs are 16-byte
- * aligned.  H_all needs a workspace of sla_kv_reduce_workspace_bytes(..., 1) bytes (fp32
+ * aligned.
+ * k_pool (nullable, fp32 [B, Hkv, nb, d], 16-byte aligned): also the key block means of the
+ * prediction step, k_pool[b,g,j,:] = mean of the valid rows of block j of K[b,g] (raw K, no
+ * shift), summed in fp64 and rounded once, the values sla_pool_scores writes (bit-identical
+ * for bf16 K, whose fp64 block sums are exact; for fp32 K whenever a block's values lie within
+ * 2^23 of each other in magnitude), so that sla_pool_scores with k_pooled skips reading K.  H_all needs a workspace of sla_kv_reduce_workspace_bytes(..., 1) bytes (fp32
  * partial sums over runs of 32 key blocks, then summed in a fixed order).
  */
 sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
                                 const float* k_shift, void* H, float* z, float* H_all, float* z_all,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                float* k_pool, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Marginal aggregation of one block map (marginal sets given as the bit masks sla_block_map

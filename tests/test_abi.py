@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert sla.sla_abi_version() == 5
+    assert sla.sla_abi_version() == 6
     for s in range(9):
         assert len(sla.sla_status_str(s)) > 0
     assert sla.sla_status_str(12345) == "unknown status"
@@ -85,7 +85,7 @@ P = ctypes.c_void_p(0x20000)   # a fake, 16-byte aligned device address: never d
 
 
 def pool_call(L, q, k, n_valid=256, scale=0.1, qp=P, kp=P, sc=P):
-    return L.sla_pool_scores(ctypes.byref(q), ctypes.byref(k), n_valid, 0, 0, scale, qp, kp, sc, None, None, 0, None)
+    return L.sla_pool_scores(ctypes.byref(q), ctypes.byref(k), n_valid, 0, 0, scale, 0, qp, kp, sc, None, None, 0, None)
 
 
 def test_pool_scores_validation(L):
@@ -108,7 +108,8 @@ def test_pool_scores_validation(L):
     assert pool_call(L, desc(N=64 * 4097), desc(N=64 * 4097)) == EUNSUP
     # group-summed scores of a GQA group need the workspace for the group sums
     q4, k1 = desc(H=4), desc(H=1)
-    assert L.sla_pool_scores(ctypes.byref(q4), ctypes.byref(k1), 256, 1, 1, 0.1, P, P, P, None, None, 0, None) == EWS
+    assert L.sla_pool_scores(ctypes.byref(q4), ctypes.byref(k1), 256, 1, 1, 0.1, 0, P, P, P, None, None, 0, None) == EWS
+    assert L.sla_pool_scores(ctypes.byref(q4), ctypes.byref(k1), 256, 1, 1, 0.1, 1, P, P, P, None, None, 0, None) == EWS
     assert L.sla_pool_scores_workspace_bytes(1, 4, 1, 256, 128, 1) == 4 * 128 * 8
     assert L.sla_pool_scores_workspace_bytes(1, 4, 1, 256, 128, 0) == 0
 
@@ -137,8 +138,8 @@ def test_block_map_validation(L):
 
 def test_kv_reduce_validation(L):
     k = desc()
-    def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0, shift=None):
-        return L.sla_linear_kv_reduce(ctypes.byref(kk), ctypes.byref(vv), nv, shift, H, z, Ha, za, ws, wsb, None)
+    def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0, shift=None, kp=None):
+        return L.sla_linear_kv_reduce(ctypes.byref(kk), ctypes.byref(vv), nv, shift, H, z, Ha, za, kp, ws, wsb, None)
     assert call(H=None, z=None) == ENULL
     assert call(z=None) == ENULL
     assert call(Ha=P, za=None) == ENULL
@@ -147,6 +148,8 @@ def test_kv_reduce_validation(L):
     assert call(nv=0) == ERANGE
     assert call(H=None, z=None, Ha=P, za=P) == EWS
     assert call(shift=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call(kp=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call(kp=P, H=None, z=None) == ENULL               # the key block means come with a state output
 
 
 def test_key_mean_validation(L):

@@ -163,6 +163,32 @@ def test_linear_states(name):
         assert rel < bound, what
 
 
+@pytest.mark.parametrize("name", ["tiny_sla", "med_sla", "med_sla_d64", "med_gqa_sla", "med_salad"])
+def test_fused_key_pooling(name):
+    """The key-state pass's key block means (per-block and all-key state passes) are the oracle's
+    pooled keys bit for bit, and the pooling pass with k_pooled leaves them untouched and pools Q."""
+    say(f"[fused key pooling] {name}")
+    w, (q, k, v, wg), f, layer = case(name)
+    import block_sparse_linear_mean_amd as sla
+    kp_ref = orc.pool(host(k), w.Nv)
+    for per_block, want_all in ((True, False), (False, True)):
+        kp = torch.full(layer.pool["k_pool"].shape, float("nan"), device=layer.k.device)
+        sla.sla_linear_kv_reduce(layer.k, layer.v, w.Nv, per_block=per_block, want_all=want_all, k_pool=kp)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(kp), kp_ref), (per_block, want_all)
+    out = dict(q_pool=torch.full_like(layer.pool["q_pool"], float("nan")), k_pool=kp,
+               scores=torch.empty_like(layer.pool["scores"]))
+    sla.sla_pool_scores(layer.q, layer.k, w.Nv, group_sum=f.group_sum, causal=f.causal, out=out, k_pooled=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["k_pool"]), kp_ref)
+    assert np.array_equal(host(out["q_pool"]), orc.pool(host(q), w.Nv))
+    ref = dict(scores=torch.empty_like(out["scores"]), q_pool=torch.empty_like(out["q_pool"]),
+               k_pool=torch.empty_like(kp))
+    sla.sla_pool_scores(layer.q, layer.k, w.Nv, group_sum=f.group_sum, causal=f.causal, out=ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out["scores"], ref["scores"])
+
+
 @pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla"])
 def test_marginal_states(name):
     say(f"[marginal states] {name}")
