@@ -5,8 +5,9 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input already
 resident in HBM: pooled scores, block map, linear key states, marginal sums and the
-attention kernel with its fused linear epilogue, in that order on one stream (--overlap runs the
-key states and marginal sums on a second HIP stream beside the scores and the block map).  Prints
+attention kernel with its fused linear epilogue, on one stream (the key states run first when
+they also write the key block means, so the pooling pass reads only Q; --overlap runs the key
+states and marginal sums on a second HIP stream beside the scores and the block map).  Prints
 one JSON line.
 
 value = effective TFLOP/s = dense-equivalent attention FLOPs (4 B Hq Nv^2 d, halved when
@@ -54,15 +55,19 @@ def pass_work(w, layer):
     heads_per_row = G if layer.group else 1
     pair_flops = 4.0 * 64 * 64 * d                 # QK^T and PV of one 64 x 64 block pair
     work = {}
-    work["pool_scores"] = ("hbm", B * (Hq + Hkv) * Nv * d * eb + B * (Hq + Hkv) * nb * d * 4 + rows * nb * 4)
+    # Q (and K, unless the key-state pass pools it) in, pooled vectors and scores out
+    pooled = Hq if getattr(layer, "fuse_key_pooling", False) else Hq + Hkv
+    work["pool_scores"] = ("hbm", B * pooled * Nv * d * eb + B * (Hq + Hkv) * nb * d * 4 + rows * nb * 4)
     work["block_map"] = ("hbm", rows * nb * 4 + (n_crit_entries + n_marg_entries) * 4 + rows * 20)
     if layer.lin == 1:
-        # K, V in; one bf16 state + fp32 z per key block out
-        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d * 2 + d * 4))
+        # K, V in; one bf16 state + fp32 z (+ the fp32 key block mean when fused) per key block out
+        kmean = d * 4 if getattr(layer, "fuse_key_pooling", False) else 0
+        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * nb * (d * d * 2 + d * 4 + kmean))
         # mask product S = M H: reads every bf16 state and z once, writes bf16 row sums + fp32 u
         work["marginal_states"] = ("hbm", B * Hkv * nb * (d * d * 2 + d * 4) + rows * (d * d * 2 + d * 4))
     elif layer.lin == 2:
-        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * (d * d + d) * 4)
+        kmean = B * Hkv * nb * d * 4 if getattr(layer, "fuse_key_pooling", False) else 0
+        work["kv_reduce"] = ("hbm", 2 * B * Hkv * Nv * d * eb + B * Hkv * (d * d + d) * 4 + kmean)
         work["marginal_states"] = ("hbm", 0)
     else:
         work["kv_reduce"] = ("hbm", 0)
