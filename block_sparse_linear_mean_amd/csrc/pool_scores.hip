@@ -22,7 +22,7 @@ namespace sla {
 // row group, issues all of its 16-byte loads before summing, and sums in fp64 (exact for bf16
 // inputs); partial sums are combined in a fixed order, so the result does not depend on
 // scheduling.
-constexpr int kPoolBlocks = 4;
+constexpr int kPoolBlocks = 1;   // one block per workgroup: the most loads in flight chip-wide
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, int64_t qsB, int64_t qsH, int64_t qsN,
