@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sla.h")
@@ -252,3 +253,19 @@ def test_nsa3_validation(L):
     assert call() == EWS
     assert L.sla_nsa3_workspace_bytes(1, 4, 1, 256, 128, 0, 256, 512, 32, 16) > 0
     assert L.sla_nsa3_workspace_bytes(1, 4, 3, 256, 128, 0, 256, 512, 32, 16) == 0
+
+
+def test_layer_fuses_key_pooling_only_when_exact(L):
+    """The layer takes the key block means from the key-state pass only when that pass runs without a
+    shift on bf16 K (exact fp64 block sums, so the same bits as the pooling pass); host logic only:
+    constructing the layer on CPU tensors launches nothing."""
+    def layer(dtype, mode="sla", smooth_k=False):
+        x = torch.zeros((1, 1, 256, 64), dtype=dtype)
+        wg = torch.zeros((1, 64)) if mode == "salad" else None
+        return sla.SlaForward(x, x, x, 256, mode, kh_bp=2500, kl_bp=5000, n_sel=2, window=64, smooth_k=smooth_k,
+                              w_gate=wg)
+    assert layer(torch.bfloat16).fuse_key_pooling
+    assert layer(torch.bfloat16, mode="salad").fuse_key_pooling
+    assert not layer(torch.float32).fuse_key_pooling
+    assert not layer(torch.bfloat16, smooth_k=True).fuse_key_pooling
+    assert not layer(torch.bfloat16, mode="nsa").fuse_key_pooling
