@@ -98,8 +98,8 @@ __global__ __launch_bounds__(256) void qsum_kernel(const float* __restrict__ qpo
 // features 16 c + 4 g .. 16 c + 4 g + 3 of its row and feeds them to four consecutive k-steps,
 // so one 16-byte load per row and chunk serves four instructions; A and B use the same feature
 // order, so every product pairs matching features.  The sum is taken in a different order from
-// the oracle's, so the fp64 values differ in their last bits; rounded to fp32 they agree except
-// on an fp32 rounding boundary.
+// the oracle's, so the fp64 values may differ in their last bits; rounded to fp32 they agree
+// except on an fp32 rounding boundary.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 constexpr int kScI = 64, kScJ = 64;
