@@ -12,9 +12,9 @@
 // One wavefront owns one row.  Scores are mapped to an order-preserving uint32 key
 // (larger key = more important; -0 -> +0; every NaN -> 0, the lowest key), so the
 // row's total order is (key descending, block index ascending).  The boundary of the
-// top-n set is found by an MSB-first 8-bit radix select over an LDS histogram (four
-// passes), and equal keys at the boundary are taken in ascending block order by a
-// ballot prefix count.  The lists are written with ballot compaction, which emits
+// top-n set is found by an MSB-first 8-bit radix select over LDS histograms (four
+// passes; the critical and the kept boundary of a row side by side in the same passes), and
+// equal keys at the boundary are taken in ascending block order by a ballot prefix count.  The lists are written with ballot compaction, which emits
 // ascending block indices.  Everything is integer work: results are bit-exact.
 #include "sla_device.h"
 #include "sla_host.h"
@@ -32,81 +32,100 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return (uint64_t(1) << threadIdx.x) - 1;          // one wavefront per workgroup
 }
 
-// Largest T such that at least n candidates (j < ncand) have key >= T, i.e. the key of
-// the n-th most important candidate, and `take` = how many candidates with key == T
-// belong to the top n (1 <= n <= ncand).
-template <int M>
-__device__ void radix_threshold(const uint32_t (&key)[M], int ncand, int n, uint32_t* hist,
-                                uint32_t& T, int& take) {
+// For each selection q: T[q] = the largest key such that at least n[q] candidates (j < ncand)
+// have key >= T[q], i.e. the key of the n[q]-th most important candidate, and take[q] = how many
+// candidates with key == T[q] belong to the top n[q] (n[q] clamped to 1 .. ncand; callers handle
+// the degenerate cases).  MSB-first 8-bit radix select over LDS histograms (hist: NS x 256
+// words), the NS selections side by side so that their dependent LDS round trips overlap; the
+// first digit's histogram has no prefix filter and serves every selection.
+template <int M, int NS>
+__device__ void radix_thresholds(const uint32_t (&key)[M], int ncand, const int (&n)[NS], uint32_t* hist,
+                                 uint32_t (&T)[NS], int (&take)[NS]) {
   const int lane = threadIdx.x;
-  uint32_t prefix = 0;
-  int rem = n;
+  uint32_t prefix[NS];
+  int rem[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    prefix[q] = 0;
+    rem[q] = min(max(n[q], 1), ncand);
+  }
 #pragma unroll 1
   for (int dgt = 3; dgt >= 0; --dgt) {
     const int shift = 8 * dgt;
-    for (int q = lane; q < 256; q += kWave) hist[q] = 0u;
+    const int nh = dgt == 3 ? 1 : NS;            // histograms built in this pass
+    for (int q = lane; q < 256 * nh; q += kWave) hist[q] = 0u;
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int j = lane + kWave * m;
       if (j < ncand) {
         const uint32_t k = key[m];
-        const bool match = dgt == 3 || (k >> (shift + 8)) == (prefix >> (shift + 8));
-        if (match) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        if (dgt == 3) {
+          atomicAdd(&hist[k >> 24], 1u);
+        } else {
+#pragma unroll
+          for (int q = 0; q < NS; ++q)
+            if ((k >> (shift + 8)) == (prefix[q] >> (shift + 8))) atomicAdd(&hist[256 * q + ((k >> shift) & 255u)], 1u);
+        }
       }
     }
     __syncthreads();
-    // lane l owns bins 255-4l .. 252-4l (descending), so lane order is key order
-    uint32_t c[4], lsum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = hist[255 - (4 * lane + q)];
-      lsum += c[q];
-    }
-    uint32_t incl = lsum;
+    for (int q = 0; q < NS; ++q) {
+      const uint32_t* hq = hist + (dgt == 3 ? 0 : 256 * q);
+      // lane l owns bins 255-4l .. 252-4l (descending), so lane order is key order
+      uint32_t c[4], lsum = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    const uint32_t excl = incl - lsum;
-    const bool hit = excl < uint32_t(rem) && uint32_t(rem) <= incl;
-    int bin = 0;
-    uint32_t above = excl;
-    if (hit) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (above + c[q] >= uint32_t(rem)) {
-          bin = 255 - (4 * lane + q);
-          break;
-        }
-        above += c[q];
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hq[255 - (4 * lane + e)];
+        lsum += c[e];
       }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const uint32_t excl = incl - lsum;
+      const bool hit = excl < uint32_t(rem[q]) && uint32_t(rem[q]) <= incl;
+      int bin = 0;
+      uint32_t above = excl;
+      if (hit) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (above + c[e] >= uint32_t(rem[q])) {
+            bin = 255 - (4 * lane + e);
+            break;
+          }
+          above += c[e];
+        }
+      }
+      const uint64_t hm = __ballot(hit);
+      const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
+      bin = __shfl(bin, src);
+      above = __shfl(above, src);
+      prefix[q] |= uint32_t(bin) << shift;
+      rem[q] -= int(above);
     }
-    const uint64_t hm = __ballot(hit);
-    const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-    bin = __shfl(bin, src);
-    above = __shfl(above, src);
-    prefix |= uint32_t(bin) << shift;
-    rem -= int(above);
     __syncthreads();
   }
-  T = prefix;
-  take = rem;
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    T[q] = prefix[q];
+    take[q] = rem[q];
+  }
 }
 
-// in[m] = candidate j = lane + 64 m is among the n most important of the first ncand.
+// in[m] = candidate j = lane + 64 m is among the n most important of the first ncand, given the
+// threshold (T, take) of n from radix_thresholds.
 template <int M>
-__device__ void top_set(const uint32_t (&key)[M], int ncand, int n, uint32_t* hist, bool (&in)[M]) {
+__device__ void top_set(const uint32_t (&key)[M], int ncand, int n, uint32_t T, int take, bool (&in)[M]) {
   const int lane = threadIdx.x;
   if (n <= 0 || n >= ncand) {
 #pragma unroll
     for (int m = 0; m < M; ++m) in[m] = n > 0 && lane + kWave * m < ncand;
     return;
   }
-  uint32_t T;
-  int take;
-  radix_threshold<M>(key, ncand, n, hist, T, take);
   int seen = 0;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
                                                       int* __restrict__ crit_idx, uint8_t* __restrict__ crit_flags,
                                                       int* __restrict__ marg_rowptr, int* __restrict__ marg_idx,
                                                       uint32_t* __restrict__ marg_bits, int* __restrict__ row_counts) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2 * 256];
   const int64_t r = blockIdx.x;
   const int lane = threadIdx.x;
   const float* s = scores + r * nkb;
@@ -157,8 +176,12 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
   const int n_keep = nkb - n_negl;       // critical + marginal
   const int n_marg = n_keep - n_crit;
   bool crit[M], keep[M];
-  top_set<M>(key, nkb, n_crit, hist, crit);
-  top_set<M>(key, nkb, n_keep, hist, keep);
+  const int nsel[2] = {n_crit, n_keep};
+  uint32_t T[2];
+  int take[2];
+  radix_thresholds<M, 2>(key, nkb, nsel, hist, T, take);   // both boundaries in the same passes
+  top_set<M>(key, nkb, n_crit, T[0], take[0], crit);
+  top_set<M>(key, nkb, n_keep, T[1], take[1], keep);
   uint8_t one[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) one[m] = 1;
@@ -212,7 +235,11 @@ __global__ __launch_bounds__(64) void select_causal_kernel(const float* __restri
     key[m] = j < ncand ? order_key(s[j]) : 0u;
   }
   bool sel[M];
-  top_set<M>(key, ncand, min(n_sel, ncand), hist, sel);
+  const int nsel[1] = {min(n_sel, ncand)};
+  uint32_t T[1];
+  int take[1];
+  radix_thresholds<M, 1>(key, ncand, nsel, hist, T, take);
+  top_set<M>(key, ncand, nsel[0], T[0], take[0], sel);
   bool mem[M];
   uint8_t flag[M];
 #pragma unroll
