@@ -128,16 +128,17 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   if (e < n) p[e] = v;
 }
 
-// One thread per map row (bh, i): set bit i of row (bh, j) of the transposed critical mask for
-// every listed block j (atomic OR: the result does not depend on the order).
-// Also counts, per key-block row, the query blocks that list it (the dK/dV workload of that row).
+// One wavefront per map row (bh, i), one lane per listed block j: set bit i of row (bh, j) of the
+// transposed critical mask (atomic OR: the result does not depend on the order), so every entry's
+// atomics are in flight at once.  Also counts, per key-block row, the query blocks that list it
+// (the dK/dV workload of that row).
 __global__ __launch_bounds__(256) void crit_transpose_kernel(const int* __restrict__ rowptr, const int* __restrict__ idx,
                                                              int rows, int nb, int wq, uint32_t* __restrict__ critT,
                                                              int* __restrict__ counts) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int r = blockIdx.x * 4 + int(threadIdx.x) / kWave;
   if (r >= rows) return;
   const int bh = r / nb, i = r % nb;
-  for (int e = rowptr[r]; e < rowptr[r + 1]; ++e) {
+  for (int e = rowptr[r] + int(threadIdx.x) % kWave; e < rowptr[r + 1]; e += kWave) {
     const int j = idx[e];
     if (unsigned(j) < unsigned(nb)) {
       const uint32_t bit = 1u << (i % 32);
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 // Dispatch order of the dK/dV workgroups: key-block rows sorted by how many query blocks list them
 // (counted by crit_transpose_kernel), most-used first, so the longest workgroups start first and
 // the round-robin dispatch spreads them over the XCDs.  One workgroup: a histogram of the counts in
-// LDS, a descending scan, a scatter (the order within one count is arbitrary; results do not depend
+// LDS, a descending scan (one wavefront: per-lane runs, then a wave scan of the run sums), a scatter (the order within one count is arbitrary; results do not depend
 // on the order).  Counts are at most nb <= 4096.
 __global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ counts, int rows, int max_count,
                                                         int* __restrict__ order) {
@@ -673,12 +674,29 @@ __global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ 
   __syncthreads();
   for (int r = t; r < rows; r += 1024) atomicAdd(&hist[counts[r]], 1);
   __syncthreads();
-  if (t == 0) {                                   // exclusive scan from the largest count down
-    int run = 0;
-    for (int c = max_count; c >= 0; --c) {
-      const int h = hist[c];
-      hist[c] = run;
-      run += h;
+  if (t < kWave) {                                // exclusive scan from the largest count down:
+    const int n = max_count + 1;                  // lane l takes descending positions l*per .. l*per+per-1
+    const int per = (n + kWave - 1) / kWave;      // (count = max_count - position)
+    int sum = 0;
+    for (int k = 0; k < per; ++k) {
+      const int pos = t * per + k;
+      if (pos < n) sum += hist[max_count - pos];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (t >= off) incl += y;
+    }
+    int run = incl - sum;
+    for (int k = 0; k < per; ++k) {
+      const int pos = t * per + k;
+      if (pos < n) {
+        const int c = max_count - pos;
+        const int h = hist[c];
+        hist[c] = run;
+        run += h;
+      }
     }
   }
   __syncthreads();
@@ -993,8 +1011,8 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
   fill_u32_kernel<<<dim3(uint32_t((nbits + 255) / 256)), 256, 0, s>>>(ws.margT, nbits, 0u);
   fill_u32_kernel<<<dim3(uint32_t((rows + 255) / 256)), 256, 0, s>>>(reinterpret_cast<uint32_t*>(ws.kv_counts),
                                                                      rows, 0u);
-  crit_transpose_kernel<<<dim3((rows + 255) / 256), 256, 0, s>>>(crit_rowptr, crit_idx, rows, nb, p.wq, ws.critT,
-                                                                 ws.kv_counts);
+  crit_transpose_kernel<<<dim3((rows + 3) / 4), 256, 0, s>>>(crit_rowptr, crit_idx, rows, nb, p.wq, ws.critT,
+                                                             ws.kv_counts);
   const int wk = (nb + 31) / 32;
   marg_transpose_kernel<<<dim3(uint32_t((int64_t(rows) * wk + 255) / 256)), 256, 0, s>>>(marg_bits, rows, nb, wk,
                                                                                         p.wq, ws.margT);
