@@ -88,6 +88,51 @@ def test_scores_closed_form_and_probs():
     assert np.array_equal(P.argmax(-1), S.argmax(-1))
 
 
+def test_default_scale_is_sdpa_default_on_exact_attention():
+    """The oracle's default scale against torch SDPA's own default (scale=None, 1/sqrt(d)): an
+    all-critical SLA forward with no scale given must be dense attention at SDPA's default."""
+    import torch
+    import torch.nn.functional as F
+    for d in (16, 64):
+        N = 192
+        Q, K, V = rand_qkv(1, 1, 1, N, d, seed=60 + d)
+        O = orc.forward(Q, K, V, n_valid=N, mode="sla", kh_bp=10000, kl_bp=0)
+        t = lambda x: torch.as_tensor(x[0, 0].astype(np.float64))
+        ref = F.scaled_dot_product_attention(t(Q), t(K), t(V)).numpy()      # SDPA picks its own scale
+        # the oracle rounds 1/sqrt(d) to float32 once: relative effect on the logits <= 2^-24
+        assert np.allclose(O[0, 0], ref, rtol=1e-6, atol=1e-7)
+        for wrong in (1.0 / d, math.sqrt(d), 1.0):
+            bad = F.scaled_dot_product_attention(t(Q), t(K), t(V), scale=wrong).numpy()
+            assert not np.allclose(O[0, 0], bad, rtol=1e-3, atol=1e-3)
+
+
+def test_score_probs_are_attention_weights_of_pooled_vectors():
+    """Row softmax of the pooled scores at the default scale against (a) torch SDPA's attention
+    weights over the pooled vectors (values = identity, SDPA's own default scale) and (b)
+    torch.softmax over rows with causal -inf entries."""
+    import torch
+    import torch.nn.functional as F
+    r = np.random.default_rng(61)
+    nb, d = 12, 32
+    qp = r.standard_normal((1, 1, nb, d)).astype(np.float32)
+    kp = r.standard_normal((1, 1, nb, d)).astype(np.float32)
+    S = orc.pooled_scores(qp, kp, orc.default_scale(d))
+    P = orc.score_probs(S)
+    eye = torch.eye(nb, dtype=torch.float64)
+    W = F.scaled_dot_product_attention(torch.as_tensor(qp[0, 0].astype(np.float64)),
+                                       torch.as_tensor(kp[0, 0].astype(np.float64)), eye).numpy()
+    assert np.allclose(P[0, 0], W, rtol=2e-6, atol=1e-7)
+    # softmax at another temperature is far from it
+    assert not np.allclose(orc.score_probs(2.0 * S)[0, 0], W, rtol=1e-2, atol=1e-3)
+    # causal rows: -inf entries get probability 0, the rest a softmax over the finite entries
+    Sc = orc.pooled_scores(qp, kp, orc.default_scale(d), causal=True)
+    Pc = orc.score_probs(Sc)
+    ref = torch.softmax(torch.as_tensor(Sc[0, 0].astype(np.float64)), dim=-1).numpy()
+    assert np.allclose(Pc[0, 0], ref, rtol=2e-6, atol=1e-7)
+    assert np.all(Pc[0, 0][np.triu_indices(nb, 1)] == 0.0)
+    assert np.allclose(Pc[0, 0, 0, 0], 1.0)
+
+
 def test_group_scores_are_sum_of_head_scores():
     B, Hq, Hkv, nb, d = 1, 4, 2, 6, 16
     qp = rng0.standard_normal((B, Hq, nb, d)).astype(np.float32)
