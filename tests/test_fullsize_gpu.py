@@ -1,9 +1,12 @@
 """Full-size parity, in the launch configuration bench.py times (SlaForward.run on the whole
-workload): sampled query blocks are recomputed one by one by the oracle, and properties that
-hold at any size are checked on every row.
+workload).
 
-Sampled blocks: first, second, middle, the last two (the last one holds the padding), and
-two seeded random ones, on the first, middle and last head.
+Every row of every workload: pooled scores within one fp32 ulp of the oracle's, and the block map
+(critical lists and flags, marginal lists and bit masks, row counts) bit for bit against the
+oracle's classification of the same scores, plus properties that hold at any size.  Outputs: every
+valid row of wan13b_sla and salad recomputed by the oracle; for nsa_prefill and wan14b_sla sampled
+query blocks (first, second, middle, the last two (the last one holds the padding), and two
+seeded random ones, on the first, middle and last head).
 """
 import numpy as np
 import pytest
@@ -61,8 +64,64 @@ def check_all_rows(w, f, layer):
         assert mark.max() == 1
 
 
+def marg_bits_from_csr(rowptr, idx, rows, nkb):
+    """Bit masks (bit j % 32 of word j / 32) of CSR marginal lists, as int32 words."""
+    bits = np.zeros((rows, (nkb + 31) // 32), dtype=np.uint32)
+    n = int(rowptr[-1])
+    row_of = np.repeat(np.arange(rows), np.diff(rowptr))
+    j = np.asarray(idx[:n], dtype=np.int64)
+    np.bitwise_or.at(bits, (row_of, j // 32), (np.uint32(1) << (j % 32).astype(np.uint32)))
+    return bits.view(np.int32)
+
+
+def check_maps_every_row(w, f, layer):
+    """Every row: the pooled scores against the oracle's (within one fp32 ulp), and the GPU's block
+    map bit for bit against the oracle's classification of the GPU's own scores (the scores the map
+    was built from).  Returns the oracle's per-row maps (used for the output comparison)."""
+    Hs = f.Hkv if f.group_sum else f.Hq
+    rows = w.B * Hs * f.nb
+    Sg = host(layer.pool["scores"])
+    say(f"  oracle pooling and scores of all {rows} rows")
+    S_own = orc.pooled_scores(orc.pool(f.Q, w.Nv), orc.pool(f.K, w.Nv), f.scale, group_sum=f.group_sum,
+                              causal=f.causal)
+    assert np.array_equal(np.isneginf(Sg), np.isneginf(S_own))
+    fin = np.isfinite(S_own)
+    ulp = ulp_distance(Sg[fin], S_own[fin])
+    say(f"  scores: {np.count_nonzero(ulp)} of {ulp.size} differ, max {ulp.max()} ulp")
+    assert ulp.max() <= 1
+    say(f"  oracle classification of every row of the GPU's scores")
+    maps = orc.block_map(Sg, n_h=f.n_sel if f.causal else f.n_h, n_l=f.n_l, causal=f.causal, n_sel=f.n_sel,
+                         window=f.window)
+    ref = orc.to_csr(maps, w.B, Hs, f.nb)
+    cr = layer.maps["crit_rowptr"].cpu().numpy()
+    n = int(cr[-1])
+    assert np.array_equal(cr, ref["crit_rowptr"])
+    assert np.array_equal(layer.maps["crit_idx"].cpu().numpy()[:n], ref["crit_idx"])
+    assert np.array_equal(layer.maps["crit_flags"].cpu().numpy()[:n], ref["crit_flags"])
+    assert np.array_equal(layer.maps["row_counts"].cpu().numpy(), ref["row_counts"])
+    if "marg_rowptr" in layer.maps:
+        mr = layer.maps["marg_rowptr"].cpu().numpy()
+        assert np.array_equal(mr, ref["marg_rowptr"])
+        assert np.array_equal(layer.maps["marg_idx"].cpu().numpy()[:int(mr[-1])], ref["marg_idx"])
+        assert np.array_equal(layer.maps["marg_bits"].cpu().numpy(),
+                              marg_bits_from_csr(ref["marg_rowptr"], ref["marg_idx"], rows, f.nb))
+    say(f"  block map: all {rows} rows bit-exact ({n} critical entries)")
+    # diagnostic: rows whose map would change if the oracle used its own scores
+    changed = 0
+    for r in np.flatnonzero((np.where(fin, Sg, 0) != np.where(fin, S_own, 0)).reshape(rows, -1).any(1)):
+        b, rem = divmod(int(r), Hs * f.nb)
+        h, i = divmod(rem, f.nb)
+        if f.map_row(b, h, i)["crit"] != maps[(b, h, i)]["crit"]:
+            changed += 1
+    say(f"  rows whose map differs under the oracle's own scores: {changed}")
+    return maps
+
+
+FULL_OUTPUT = {"wan13b_sla", "salad"}     # every valid row recomputed by the oracle
+
+
 @pytest.mark.parametrize("name", ["wan13b_sla", "salad", "nsa_prefill", "wan14b_sla"])
-def test_full_size_sampled(name):
+def test_full_size(name):
     w = WORKLOADS[name]
     say(f"[full size] {name}: generating inputs")
     q, k, v, wg = make_inputs(w)
@@ -74,38 +133,35 @@ def test_full_size_sampled(name):
     del q, k, v
     say(f"[full size] {name}: whole-map properties")
     check_all_rows(w, f, layer)
+    say(f"[full size] {name}: block maps of every row")
+    maps = check_maps_every_row(w, f, layer)
     Og = layer.out
     assert torch.isfinite(Og).all()
     assert not Og[:, :, w.Nv:].any()
-    Hs = f.Hkv if f.group_sum else f.Hq
-    scores = layer.pool["scores"]
-    heads = sorted(set([0, w.Hq // 2, w.Hq - 1]))
+    if name in FULL_OUTPUT:
+        heads = list(range(w.Hq))
+        blocks_of = lambda h: list(range(f.nb))
+    else:
+        heads = sorted(set([0, w.Hq // 2, w.Hq - 1]))
+        blocks_of = lambda h: sample_blocks(f.nb, 1000 * h + w.seed)
     diffs, refs_ = [], []
     n_rows = 0
     for h in heads:
         hs = f.map_head(h)
-        blocks = sample_blocks(f.nb, 1000 * h + w.seed)
-        got_rows = gpu_map_rows(layer.maps, [hs * f.nb + i for i in blocks])
-        for i in blocks:
-            m = f.map_row(0, hs, i)
-            srow = host(scores[0, hs, i])
-            fin = np.isfinite(m["scores"])
-            assert np.array_equal(np.isfinite(srow), fin)
-            assert ulp_distance(srow[fin], m["scores"][fin]).max() <= 1
-            crit, flags, marg, counts = got_rows[hs * f.nb + i]
-            assert crit == m["crit"] and flags == m["flags"], (h, i)
-            if marg is not None and not f.mode == "salad":
-                assert marg == m["marg"], (h, i)
-            ref = f.output_block(0, h, i, m)
-            got = host(Og[0, h, 64 * i:64 * i + 64]).astype(np.float64)
-            diffs.append(got - ref)
-            refs_.append(ref)
-            n_rows += 1
+        Oh = host(Og[0, h]).astype(np.float64)
+        for i in blocks_of(h):
+            ref = f.output_block(0, h, i, maps[(0, hs, i)])
+            hi = min(64, w.Nv - 64 * i)
+            diffs.append(Oh[64 * i:64 * i + hi] - ref[:hi])
+            refs_.append(ref[:hi])
+            n_rows += hi
+        if name in FULL_OUTPUT:
+            f._H.clear()          # the per-block states of this head are not needed again
     d = np.concatenate(diffs)
     r = np.concatenate(refs_)
     rel = np.linalg.norm(d) / np.linalg.norm(r)
     mx = np.abs(d).max()
-    say(f"  {name}: {n_rows} sampled blocks, rel-L2 {rel:.3e}, max-abs {mx:.3e}")
+    say(f"  {name}: {n_rows} valid rows compared, rel-L2 {rel:.3e}, max-abs {mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 

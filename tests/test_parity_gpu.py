@@ -29,6 +29,8 @@ MEDIUM = {
     "med_nsa_full": scaled(W["nsa_prefill"], "med_nsa_full", N=2048, Nv=2048, Hq=4),
     "med_gqa_sla": scaled(W["tiny_sla"], "med_gqa_sla", Hq=4, Hkv=2, N=1280, Nv=1250, d=128, dtype="bf16",
                           kh_bp=3000, kl_bp=4000),
+    # more than 512 key blocks (565): the marginal mask product reloads its mask words
+    "wide_sla": scaled(W["wan13b_sla"], "wide_sla", grid=(7, 40, 129), Hq=2, Hkv=2),
 }
 
 
@@ -189,7 +191,7 @@ def test_fused_key_pooling(name):
     assert torch.equal(out["scores"], ref["scores"])
 
 
-@pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla"])
+@pytest.mark.parametrize("name", ["med_sla", "med_gqa_sla", "wide_sla"])
 def test_marginal_states(name):
     say(f"[marginal states] {name}")
     w, _, f, layer = case(name)
@@ -297,3 +299,20 @@ def test_nothing_critical_is_linear_attention():
     for h in range(w.Hq):
         ref[0, h, :w.Nv] = refs.kernel_linear_attention(f.Q[0, h, :w.Nv], f.K[0, h, :w.Nv], f.V[0, h, :w.Nv])
     compare_outputs(O[:, :, :w.Nv], ref[:, :, :w.Nv], "linear closed form")
+
+
+@pytest.mark.parametrize("N,nv,d", [(9024, 9000, 128), (8448, 8400, 64)])
+def test_all_critical_long_lists(N, nv, d):
+    """Every key block critical with more than 128 of them per row: the attention kernel's critical
+    list window slides twice (at entries 64 and 128); every valid row against dense SDPA."""
+    say(f"[all critical, long lists] N={N} d={d}")
+    w = scaled(W["tiny_sla"], f"long_dense_{d}", N=N, Nv=nv, d=d, dtype="bf16", kh_bp=10000, kl_bp=0, seed=11)
+    q, k, v, wg = make_inputs(w)
+    layer = layer_for(w, q, k, v, wg)
+    O = host(layer.run())
+    torch.cuda.synchronize()
+    assert int(layer.maps["row_counts"][:, 0].min().item()) == N // 64 > 128
+    Q, K, V = (host(x)[0, 0, :nv].astype(np.float64) for x in (q, k, v))
+    ref = refs.sdpa(Q, K, V, orc.default_scale(d))
+    compare_outputs(O[0, 0, :nv], ref, f"long lists N={N} d={d} vs dense SDPA")
+    assert not O[:, :, nv:].any()
