@@ -6,6 +6,7 @@ Entry points keep the C names (see include/sla.h):
     sla_pool_scores      block mean pooling of Q, K and pooled scores
     sla_key_mean         smooth-K shift (mean key of each head) from the pooled key blocks
     sla_block_map        critical / marginal / negligible classification as CSR lists
+    sla_block_map_noalloc  the same without a workspace (static device scratch), for callers that cannot allocate
     sla_linear_kv_reduce per-key-block linear states H_j = phi(K_j)^T V_j, z_j
     sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
     sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
@@ -27,6 +28,7 @@ from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
     lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes,
     sla_hilbert_order, sla_nsa3_fwd, sla_nsa3_workspace_bytes, sla_permute_rows, sla_block_map, sla_block_map_capacity,
+    sla_block_map_noalloc,
     sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
     sla_marginal_states, sla_pool_scores, sla_status_str, tensor_desc,
 )

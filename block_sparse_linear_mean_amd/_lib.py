@@ -48,6 +48,8 @@ _SIGS = {
     "sla_block_map_workspace_bytes": (c_size_t, [c_int32] * 7),
     "sla_block_map": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                 _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, _P, c_size_t, _P]),
+    "sla_block_map_noalloc": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                        c_int32, _P, _P, _P, c_int64, _P, _P, c_int64, _P, _P, _P]),
     "sla_kv_reduce_workspace_bytes": (c_size_t, [c_int32] * 6),
     "sla_key_mean": (c_int32, [_P, c_int32, c_int32, c_int32, c_int32, c_int32, _P, _P]),
     "sla_linear_kv_reduce": (c_int32, [POINTER(SlaTensor), POINTER(SlaTensor), c_int32, _P, _P, _P, _P, _P, _P,
@@ -212,6 +214,21 @@ def sla_block_map(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=Tr
         _ptr(out["crit_rowptr"]), _ptr(out["crit_idx"]), _ptr(out["crit_flags"]), out["crit_cap"],
         _ptr(out.get("marg_rowptr")), _ptr(out.get("marg_idx")), out["marg_cap"], _ptr(out.get("marg_bits")),
         _ptr(out["row_counts"]), _ptr(out["workspace"]), out["workspace_bytes"], _stream(scores.device)))
+    return out
+
+
+def sla_block_map_noalloc(scores, n_crit, n_negl=0, causal=False, window=0, want_marg=True, out=None):
+    """sla_block_map without a workspace (the library's static device scratch serves the causal
+    path); out: the dict of alloc_block_map (its workspace entry is not used)."""
+    _require_gpu(scores)
+    B, Hs, nqb, nkb = scores.shape
+    if out is None:
+        out = alloc_block_map(B, Hs, nqb, nkb, n_crit, n_negl, causal, window, scores.device, want_marg)
+    _check("sla_block_map_noalloc", lib().sla_block_map_noalloc(
+        _ptr(scores), B, Hs, nqb, nkb, n_crit, n_negl, int(causal), window,
+        _ptr(out["crit_rowptr"]), _ptr(out["crit_idx"]), _ptr(out["crit_flags"]), out["crit_cap"],
+        _ptr(out.get("marg_rowptr")), _ptr(out.get("marg_idx")), out["marg_cap"], _ptr(out.get("marg_bits")),
+        _ptr(out["row_counts"]), _stream(scores.device)))
     return out
 
 

@@ -16,6 +16,8 @@
 // passes; the critical and the kept boundary of a row side by side in the same passes), and
 // equal keys at the boundary are taken in ascending block order by a ballot prefix count.  The lists are written with ballot compaction, which emits
 // ascending block indices.  Everything is integer work: results are bit-exact.
+#include <mutex>
+
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -311,23 +313,14 @@ __global__ __launch_bounds__(64) void compact_rows_kernel(const int* __restrict_
   }
 }
 
-}  // namespace sla
-
-extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
-                                    int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
-                                    int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags,
-                                    int64_t crit_cap, int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap,
-                                    uint32_t* marg_bits,
-                                    int32_t* row_counts, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
-  using namespace sla;
-  if (scores == nullptr || crit_rowptr == nullptr || crit_idx == nullptr || row_counts == nullptr)
-    return SLA_ERR_NULL;
-  if (B < 1 || Hs < 1 || nqb < 1 || nkb < 1) return SLA_ERR_SHAPE;
-  if (nkb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
-  if (n_crit < 0 || n_negl < 0 || window_tokens < 0) return SLA_ERR_RANGE;
+// Validation and launches of one block map; the causal path stages its padded per-row lists in
+// `workspace` (a caller buffer, or this file's device scratch array for the allocation-free entry).
+static sla_status block_map_impl(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                                 int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                                 int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags, int64_t crit_cap,
+                                 int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
+                                 int32_t* row_counts, void* workspace, size_t workspace_bytes, hipStream_t st) {
   const int64_t rows = int64_t(B) * Hs * nqb;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   int M = 1;
   while (M * kWave < nkb) M *= 2;
 #define SLA_DISPATCH_M(KERNEL, GRID, ...)                                    \
@@ -341,26 +334,16 @@ extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, 
     default: KERNEL<64><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
   }
   if (!causal) {
-    if (n_crit + n_negl > nkb) return SLA_ERR_RANGE;
-    const int64_t nm = nkb - n_crit - n_negl;
-    if ((marg_rowptr == nullptr) != (marg_idx == nullptr)) return SLA_ERR_NULL;
-    if (crit_cap < rows * n_crit || (marg_idx != nullptr && marg_cap < rows * nm)) return SLA_ERR_CAPACITY;
-    if (rows * n_crit > INT32_MAX || rows * nm > INT32_MAX) return SLA_ERR_CAPACITY;
     SLA_DISPATCH_M(classify_kernel, dim3(uint32_t(rows)), scores, nkb, n_crit, n_negl, rows, crit_rowptr,
                    crit_idx, crit_flags, marg_rowptr, marg_idx, marg_bits, row_counts);
     return launch_status();
   }
-  if (nqb != nkb) return SLA_ERR_SHAPE;
-  if (marg_bits != nullptr) return SLA_ERR_UNSUPPORTED;   // causal maps have no marginal class
-  const int64_t cap = sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, 1, window_tokens, 0);
-  if (crit_cap < cap || cap > INT32_MAX) return SLA_ERR_CAPACITY;
-  const size_t need = sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, 1, window_tokens);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
   const int reach = window_reach(window_tokens);
   const int row_cap = n_crit + reach + 1;
   int* pad_idx = static_cast<int*>(workspace);
   uint8_t* pad_flags =
       static_cast<uint8_t*>(workspace) + (rows * row_cap * 4 + 255) / 256 * 256;
+  (void)workspace_bytes;
   SLA_DISPATCH_M(select_causal_kernel, dim3(uint32_t(rows)), scores, nkb, n_crit, reach, row_cap, pad_idx,
                  pad_flags, row_counts);
 #undef SLA_DISPATCH_M
@@ -368,4 +351,108 @@ extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, 
   compact_rows_kernel<<<dim3(uint32_t(rows)), 64, 0, st>>>(crit_rowptr, pad_idx, pad_flags, row_cap, crit_idx,
                                                           crit_flags);
   return launch_status();
+}
+
+// Host-side checks shared by both entry points (no HIP call).  need_ws: workspace bytes the
+// causal path needs (0 for non-causal maps).
+static sla_status block_map_check(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                                  int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                                  const int32_t* crit_rowptr, const int32_t* crit_idx, int64_t crit_cap,
+                                  const int32_t* marg_rowptr, const int32_t* marg_idx, int64_t marg_cap,
+                                  const uint32_t* marg_bits, const int32_t* row_counts, size_t* need_ws) {
+  *need_ws = 0;
+  if (scores == nullptr || crit_rowptr == nullptr || crit_idx == nullptr || row_counts == nullptr)
+    return SLA_ERR_NULL;
+  if (B < 1 || Hs < 1 || nqb < 1 || nkb < 1) return SLA_ERR_SHAPE;
+  if (nkb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
+  if (n_crit < 0 || n_negl < 0 || window_tokens < 0) return SLA_ERR_RANGE;
+  const int64_t rows = int64_t(B) * Hs * nqb;
+  if (rows > INT32_MAX) return SLA_ERR_SHAPE;
+  if (!causal) {
+    if (n_crit + n_negl > nkb) return SLA_ERR_RANGE;
+    const int64_t nm = nkb - n_crit - n_negl;
+    if ((marg_rowptr == nullptr) != (marg_idx == nullptr)) return SLA_ERR_NULL;
+    if (crit_cap < rows * n_crit || (marg_idx != nullptr && marg_cap < rows * nm)) return SLA_ERR_CAPACITY;
+    if (rows * n_crit > INT32_MAX || rows * nm > INT32_MAX) return SLA_ERR_CAPACITY;
+    return SLA_OK;
+  }
+  if (nqb != nkb) return SLA_ERR_SHAPE;
+  if (marg_bits != nullptr) return SLA_ERR_UNSUPPORTED;   // causal maps have no marginal class
+  const int64_t cap = sla_block_map_capacity(B, Hs, nqb, nkb, n_crit, n_negl, 1, window_tokens, 0);
+  if (crit_cap < cap || cap > INT32_MAX) return SLA_ERR_CAPACITY;
+  *need_ws = sla_block_map_workspace_bytes(B, Hs, nqb, nkb, n_crit, 1, window_tokens);
+  return SLA_OK;
+}
+
+// ---- allocation-free variant: the causal path's scratch lives in a static device array
+
+// Largest causal workspace the allocation-free entry point serves (rows * row_cap * 5 bytes plus
+// alignment: e.g. 8 GQA groups x 16384 query blocks at 16 selected blocks and a 512-token window).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kScratchDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on each device, looked up once per device (with that device
+// current) on the entry point's first call there.  In host code the array's name is only a
+// host-side stand-in; kernels get this address.
+static void* g_scratch_dev[kScratchDevices] = {};
+static std::mutex g_scratch_mu;
+
+static sla_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SLA_ERR_HIP;
+  if (dev >= kScratchDevices) return SLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SLA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SLA_OK;
+}
+
+}  // namespace sla
+
+extern "C" sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                                    int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                                    int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags,
+                                    int64_t crit_cap, int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap,
+                                    uint32_t* marg_bits,
+                                    int32_t* row_counts, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  using namespace sla;
+  size_t need = 0;
+  const sla_status s = block_map_check(scores, B, Hs, nqb, nkb, n_crit, n_negl, causal, window_tokens,
+                                       crit_rowptr, crit_idx, crit_cap, marg_rowptr, marg_idx, marg_cap, marg_bits,
+                                       row_counts, &need);
+  if (s != SLA_OK) return s;
+  if (causal && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) return SLA_ERR_WORKSPACE;
+  return block_map_impl(scores, B, Hs, nqb, nkb, n_crit, n_negl, causal, window_tokens, crit_rowptr, crit_idx,
+                        crit_flags, crit_cap, marg_rowptr, marg_idx, marg_cap, marg_bits, row_counts, workspace,
+                        workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" sla_status sla_block_map_noalloc(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                                            int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                                            int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags,
+                                            int64_t crit_cap, int32_t* marg_rowptr, int32_t* marg_idx,
+                                            int64_t marg_cap, uint32_t* marg_bits, int32_t* row_counts,
+                                            void* stream) {
+  using namespace sla;
+  size_t need = 0;
+  const sla_status s = block_map_check(scores, B, Hs, nqb, nkb, n_crit, n_negl, causal, window_tokens,
+                                       crit_rowptr, crit_idx, crit_cap, marg_rowptr, marg_idx, marg_cap, marg_bits,
+                                       row_counts, &need);
+  if (s != SLA_OK) return s;
+  if (need > kScratchBytes) return SLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const sla_status a = scratch_address(&ws);
+  if (a != SLA_OK) return a;
+  // Nothing in the scratch needs clearing: each row's padded list is written in full up to its count
+  // by this call before the compaction reads it.
+  return block_map_impl(scores, B, Hs, nqb, nkb, n_crit, n_negl, causal, window_tokens, crit_rowptr, crit_idx,
+                        crit_flags, crit_cap, marg_rowptr, marg_idx, marg_cap, marg_bits, row_counts, ws, kScratchBytes,
+                        static_cast<hipStream_t>(stream));
 }

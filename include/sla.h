@@ -190,6 +190,26 @@ sla_status sla_block_map(const float* scores, int32_t B, int32_t Hs, int32_t nqb
                          int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
                          int32_t* row_counts, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Allocation-free sla_block_map, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, outputs, ownership and status codes as sla_block_map, minus the
+ * workspace: the causal path stages its padded per-row lists in a static device array of the
+ * library (16 MiB on every device the call runs on, held until the process ends; its address is
+ * looked up once per device on the first call there, with that device current).
+ * Limit: causal maps whose workspace (sla_block_map_workspace_bytes) exceeds 16 MiB return
+ * SLA_ERR_WORKSPACE before any launch.  Non-causal maps use no scratch.
+ * Concurrency: every call on one device shares that array, so calls that overlap on one device
+ * (other streams, other host threads) race; order them on one stream.  Nothing in the array
+ * needs clearing between calls (each call writes what it reads).  SLA_ERR_HIP if the device
+ * or the array's address cannot be obtained.
+ */
+sla_status sla_block_map_noalloc(const float* scores, int32_t B, int32_t Hs, int32_t nqb, int32_t nkb,
+                                 int32_t n_crit, int32_t n_negl, int32_t causal, int32_t window_tokens,
+                                 int32_t* crit_rowptr, int32_t* crit_idx, uint8_t* crit_flags, int64_t crit_cap,
+                                 int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
+                                 int32_t* row_counts, void* stream);
+
 /* Workspace bytes sla_linear_kv_reduce needs (non-zero only when the sums over all keys are wanted). */
 size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, int32_t want_blocks,
                                      int32_t want_all);

@@ -137,6 +137,29 @@ def test_block_map_validation(L):
     assert call(causal=1, nc=4, win=128, ccap=1000, ws=P, wsb=1 << 20, bits=P) == EUNSUP
 
 
+def test_block_map_noalloc_validation(L):
+    """The allocation-free block map checks its arguments like sla_block_map, and rejects causal maps
+    whose padded lists exceed its 16 MiB device scratch, all before any HIP call."""
+    def call(scores=P, B=1, Hs=1, nqb=16, nkb=16, nc=4, nn=8, causal=0, win=0, crp=P, ci=P, ccap=64,
+             mrp=P, mi=P, mcap=64, rc=P, bits=None):
+        return L.sla_block_map_noalloc(scores, B, Hs, nqb, nkb, nc, nn, causal, win, crp, ci, None, ccap, mrp, mi,
+                                       mcap, bits, rc, None)
+    assert call(scores=None) == ENULL
+    assert call(rc=None) == ENULL
+    assert call(mrp=None) == ENULL
+    assert call(nqb=0) == ESHAPE
+    assert call(nkb=5000) == EUNSUP
+    assert call(nc=10, nn=10) == ERANGE
+    assert call(ccap=63) == ECAP
+    assert call(causal=1, nqb=16, nkb=15) == ESHAPE
+    assert call(causal=1, nc=4, win=128, ccap=1000, bits=P) == EUNSUP
+    # 64 heads x 4096 query blocks x 25 entries x 5 bytes > 16 MiB of scratch
+    big = dict(causal=1, Hs=64, nqb=4096, nkb=4096, nc=16, win=512)
+    cap = L.sla_block_map_capacity(1, 64, 4096, 4096, 16, 0, 1, 512, 0)
+    assert L.sla_block_map_workspace_bytes(1, 64, 4096, 4096, 16, 1, 512) > 16 << 20
+    assert call(ccap=cap, **big) == EWS
+
+
 def test_kv_reduce_validation(L):
     k = desc()
     def call(kk=k, vv=k, nv=256, H=P, z=P, Ha=None, za=None, ws=None, wsb=0, shift=None, kp=None):
