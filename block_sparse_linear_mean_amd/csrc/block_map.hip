@@ -34,16 +34,113 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return (uint64_t(1) << threadIdx.x) - 1;          // one wavefront per workgroup
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront, in lane order, without LDS: a
+// Hillis-Steele scan inside each row of 16 lanes (DPP row shifts by 1, 2, 4, 8), then the row
+// totals carried forward by the row broadcasts of lanes 15 and 31 (gfx9 DPP).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // For each selection q: T[q] = the largest key such that at least n[q] candidates (j < ncand)
 // have key >= T[q], i.e. the key of the n[q]-th most important candidate, and take[q] = how many
 // candidates with key == T[q] belong to the top n[q] (n[q] clamped to 1 .. ncand; callers handle
-// the degenerate cases).  MSB-first 8-bit radix select over LDS histograms (hist: NS x 256
-// words), the NS selections side by side so that their dependent LDS round trips overlap; the
-// first digit's histogram has no prefix filter and serves every selection.
+// the degenerate cases).  MSB-first 8-bit radix select over LDS histograms (hist: at least
+// max(kSub1, NS) x 256 words), the NS selections side by side so that their dependent LDS round
+// trips overlap; the first digit's histogram has no prefix filter and serves every selection.
+// The first digit (sign and exponent bits) is shared by most keys of a row, so its histogram is
+// split into kSub1 copies (lane % kSub1), which cuts the serialisation of same-address atomics;
+// the bin counts are the sums over the copies.  Scans run on DPP, broadcasts by readlane.
+constexpr int kSub1 = 4;
+constexpr int kHistWords = kSub1 * 256;   // histogram words; 64 more follow, one per lane, that take
+                                          // the atomics of keys a pass does not count (branch-free)
+
+// One radix pass over digit DGT (bits 8 DGT .. 8 DGT + 7): histogram of the keys that match each
+// selection's prefix so far, then per selection the bin where its remaining count is reached.
+// Straight-line code per pass; the keys a pass does not count go to the lane's dummy word.
+template <int M, int NS, int DGT>
+__device__ __forceinline__ void radix_pass(const uint32_t (&key)[M], const bool (&valid)[M], uint32_t* hist,
+                                           uint32_t (&prefix)[NS], int (&rem)[NS]) {
+  constexpr int shift = 8 * DGT;
+  const int lane = threadIdx.x;
+  const uint32_t dummy = kHistWords + lane;
+  // selections whose prefixes agree so far share one histogram (always in the first pass)
+  bool shared = true;
+  if constexpr (DGT < 3) {
+#pragma unroll
+    for (int q = 1; q < NS; ++q) shared = shared && (prefix[q] >> (shift + 8)) == (prefix[0] >> (shift + 8));
+  }
+#pragma unroll
+  for (int c = 0; c < (DGT == 3 ? kSub1 : NS); ++c)
+    *reinterpret_cast<uint4*>(hist + 256 * c + 4 * lane) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  if constexpr (DGT == 3) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) atomicAdd(&hist[valid[m] ? 256 * (lane % kSub1) + (key[m] >> 24) : dummy], 1u);
+  } else if (shared) {
+    const uint32_t p0 = prefix[0] >> (shift + 8);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const bool match = valid[m] & ((key[m] >> (shift + 8)) == p0);
+      atomicAdd(&hist[match ? (key[m] >> shift) & 255u : dummy], 1u);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        const bool match = valid[m] & ((key[m] >> (shift + 8)) == (prefix[q] >> (shift + 8)));
+        atomicAdd(&hist[match ? 256 * q + ((key[m] >> shift) & 255u) : dummy], 1u);
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    // lane l owns bins 255-4l .. 252-4l (descending), so lane order is key order
+    const int lo = 252 - 4 * lane;               // bins lo .. lo + 3, c[e] = bin lo + 3 - e
+    uint4 w4;
+    if constexpr (DGT == 3) {
+      w4 = *reinterpret_cast<const uint4*>(hist + lo);
+#pragma unroll
+      for (int sub = 1; sub < kSub1; ++sub) {
+        const uint4 x = *reinterpret_cast<const uint4*>(hist + 256 * sub + lo);
+        w4.x += x.x; w4.y += x.y; w4.z += x.z; w4.w += x.w;
+      }
+    } else {
+      w4 = *reinterpret_cast<const uint4*>(hist + 256 * (shared ? 0 : q) + lo);
+    }
+    const uint32_t c[4] = {w4.w, w4.z, w4.y, w4.x};
+    const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(lsum);
+    const uint32_t excl = incl - lsum;
+    const uint32_t rq = uint32_t(rem[q]);
+    const bool hit = excl < rq && rq <= incl;
+    // in the hit lane: the first of its bins whose cumulative count reaches rq (branch-free)
+    const uint32_t a1 = excl + c[0], a2 = a1 + c[1], a3 = a2 + c[2];
+    const uint32_t s1 = a1 < rq ? ~0u : 0u, s2 = a2 < rq ? ~0u : 0u, s3 = a3 < rq ? ~0u : 0u;  // bins passed
+    const int bin = lo + 3 - int((s1 & 1u) + (s2 & 1u) + (s3 & 1u));
+    const uint32_t above = excl + (c[0] & s1) + (c[1] & s2) + (c[2] & s3);
+    const uint64_t hm = __ballot(hit);
+    const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(hm)) - 1);
+    prefix[q] |= uint32_t(__builtin_amdgcn_readlane(bin, src)) << shift;
+    rem[q] -= int(__builtin_amdgcn_readlane(above, src));
+  }
+  __syncthreads();
+}
+
 template <int M, int NS>
 __device__ void radix_thresholds(const uint32_t (&key)[M], int ncand, const int (&n)[NS], uint32_t* hist,
                                  uint32_t (&T)[NS], int (&take)[NS]) {
+  static_assert(NS <= kSub1, "one histogram per selection");
   const int lane = threadIdx.x;
+  bool valid[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) valid[m] = lane + kWave * m < ncand;
   uint32_t prefix[NS];
   int rem[NS];
 #pragma unroll
@@ -51,66 +148,10 @@ __device__ void radix_thresholds(const uint32_t (&key)[M], int ncand, const int 
     prefix[q] = 0;
     rem[q] = min(max(n[q], 1), ncand);
   }
-#pragma unroll 1
-  for (int dgt = 3; dgt >= 0; --dgt) {
-    const int shift = 8 * dgt;
-    const int nh = dgt == 3 ? 1 : NS;            // histograms built in this pass
-    for (int q = lane; q < 256 * nh; q += kWave) hist[q] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int j = lane + kWave * m;
-      if (j < ncand) {
-        const uint32_t k = key[m];
-        if (dgt == 3) {
-          atomicAdd(&hist[k >> 24], 1u);
-        } else {
-#pragma unroll
-          for (int q = 0; q < NS; ++q)
-            if ((k >> (shift + 8)) == (prefix[q] >> (shift + 8))) atomicAdd(&hist[256 * q + ((k >> shift) & 255u)], 1u);
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      const uint32_t* hq = hist + (dgt == 3 ? 0 : 256 * q);
-      // lane l owns bins 255-4l .. 252-4l (descending), so lane order is key order
-      uint32_t c[4], lsum = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = hq[255 - (4 * lane + e)];
-        lsum += c[e];
-      }
-      uint32_t incl = lsum;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const uint32_t excl = incl - lsum;
-      const bool hit = excl < uint32_t(rem[q]) && uint32_t(rem[q]) <= incl;
-      int bin = 0;
-      uint32_t above = excl;
-      if (hit) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (above + c[e] >= uint32_t(rem[q])) {
-            bin = 255 - (4 * lane + e);
-            break;
-          }
-          above += c[e];
-        }
-      }
-      const uint64_t hm = __ballot(hit);
-      const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-      bin = __shfl(bin, src);
-      above = __shfl(above, src);
-      prefix[q] |= uint32_t(bin) << shift;
-      rem[q] -= int(above);
-    }
-    __syncthreads();
-  }
+  radix_pass<M, NS, 3>(key, valid, hist, prefix, rem);
+  radix_pass<M, NS, 2>(key, valid, hist, prefix, rem);
+  radix_pass<M, NS, 1>(key, valid, hist, prefix, rem);
+  radix_pass<M, NS, 0>(key, valid, hist, prefix, rem);
 #pragma unroll
   for (int q = 0; q < NS; ++q) {
     T[q] = prefix[q];
@@ -131,11 +172,12 @@ __device__ void top_set(const uint32_t (&key)[M], int ncand, int n, uint32_t T, 
   int seen = 0;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
+    // bitwise & and | (no short-circuit branches)
     const bool valid = lane + kWave * m < ncand;
-    const bool eq = valid && key[m] == T;
+    const bool eq = valid & (key[m] == T);
     const uint64_t em = __ballot(eq);
     const int before = seen + __popcll(em & lanes_below());
-    in[m] = valid && (key[m] > T || (eq && before < take));
+    in[m] = valid & ((key[m] > T) | (eq & (before < take)));
     seen += __popcll(em);
   }
 }
@@ -150,7 +192,7 @@ __device__ int compact_write(const bool (&sel)[M], int* out, uint8_t* flags_out,
   for (int m = 0; m < M; ++m) {
     const uint64_t bm = __ballot(sel[m]);
     const int at = pos + __popcll(bm & lanes_below());
-    if (sel[m] && at < limit) {
+    if (sel[m] & (at < limit)) {
       out[at] = lane + kWave * m;
       if (flags_out) flags_out[at] = flag[m];
     }
@@ -165,15 +207,20 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
                                                       int* __restrict__ crit_idx, uint8_t* __restrict__ crit_flags,
                                                       int* __restrict__ marg_rowptr, int* __restrict__ marg_idx,
                                                       uint32_t* __restrict__ marg_bits, int* __restrict__ row_counts) {
-  __shared__ uint32_t hist[2 * 256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords + kWave];
   const int64_t r = blockIdx.x;
   const int lane = threadIdx.x;
   const float* s = scores + r * nkb;
   uint32_t key[M];
+  float x[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) x[m] = s[min(lane + kWave * m, nkb - 1)];   // in bounds for every slot
+  // the empty asm makes each value live here, after all loads are issued, so the compiler cannot
+  // move a load under the j < nkb condition (where each load would wait for the one before)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int j = lane + kWave * m;
-    key[m] = j < nkb ? order_key(s[j]) : 0u;
+    asm volatile("" : "+v"(x[m]));
+    key[m] = order_key(x[m]) & (lane + kWave * m < nkb ? ~0u : 0u);
   }
   const int n_keep = nkb - n_negl;       // critical + marginal
   const int n_marg = n_keep - n_crit;
@@ -191,7 +238,7 @@ __global__ __launch_bounds__(64) void classify_kernel(const float* __restrict__ 
   if (marg_idx != nullptr || marg_bits != nullptr) {
     bool marg[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) marg[m] = keep[m] && !crit[m];
+    for (int m = 0; m < M; ++m) marg[m] = keep[m] & !crit[m];
     if (marg_idx != nullptr) compact_write<M>(marg, marg_idx + r * n_marg, nullptr, one, n_marg);
     if (marg_bits != nullptr) {
       // block j = lane + 64 m is bit j % 32 of word j / 32: one ballot fills words 2m and 2m + 1
@@ -224,17 +271,20 @@ __global__ __launch_bounds__(64) void select_causal_kernel(const float* __restri
                                                            int reach, int row_cap, int* __restrict__ pad_idx,
                                                            uint8_t* __restrict__ pad_flags,
                                                            int* __restrict__ row_counts) {
-  __shared__ uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords + kWave];
   const int64_t r = blockIdx.x;
   const int i = int(r % nb);
   const int lane = threadIdx.x;
   const int ncand = i + 1;
   const float* s = scores + r * nb;
   uint32_t key[M];
+  float x[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) x[m] = s[min(lane + kWave * m, ncand - 1)];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int j = lane + kWave * m;
-    key[m] = j < ncand ? order_key(s[j]) : 0u;
+    asm volatile("" : "+v"(x[m]));
+    key[m] = order_key(x[m]) & (lane + kWave * m < ncand ? ~0u : 0u);
   }
   bool sel[M];
   const int nsel[1] = {min(n_sel, ncand)};
@@ -321,16 +371,24 @@ static sla_status block_map_impl(const float* scores, int32_t B, int32_t Hs, int
                                  int32_t* marg_rowptr, int32_t* marg_idx, int64_t marg_cap, uint32_t* marg_bits,
                                  int32_t* row_counts, void* workspace, size_t workspace_bytes, hipStream_t st) {
   const int64_t rows = int64_t(B) * Hs * nqb;
-  int M = 1;
-  while (M * kWave < nkb) M *= 2;
+  // key slots per lane: the smallest instantiated M with 64 M >= nkb
+  static constexpr int kSlots[] = {1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 64};
+  int M = 64;
+  for (int c : kSlots)
+    if (c * kWave >= nkb) { M = c; break; }
 #define SLA_DISPATCH_M(KERNEL, GRID, ...)                                    \
   switch (M) {                                                               \
     case 1: KERNEL<1><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;              \
     case 2: KERNEL<2><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;              \
     case 4: KERNEL<4><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;              \
     case 8: KERNEL<8><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;              \
+    case 12: KERNEL<12><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
     case 16: KERNEL<16><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
+    case 20: KERNEL<20><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
+    case 24: KERNEL<24><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
     case 32: KERNEL<32><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
+    case 40: KERNEL<40><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
+    case 48: KERNEL<48><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
     default: KERNEL<64><<<GRID, 64, 0, st>>>(__VA_ARGS__); break;            \
   }
   if (!causal) {

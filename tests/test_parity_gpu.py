@@ -113,7 +113,7 @@ def test_block_map_identical_scores(name):
     _check_map(maps, S, f.n_h, f.n_l, f.causal, f.window, f.n_sel)
 
 
-@pytest.mark.parametrize("nkb", [1, 7, 64, 65, 200, 700, 1300, 2100])
+@pytest.mark.parametrize("nkb", [1, 7, 64, 65, 200, 700, 1000, 1182, 1300, 2100, 2900, 4096])
 def test_block_map_ties_nan_signed_zero(nkb):
     say(f"[block_map ties] nkb={nkb}")
     r = np.random.default_rng(nkb)
