@@ -31,12 +31,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SLA fwd ms/layer + effective TFLOP/s, B1 H12 N32768 d128 bf16, 5% crit"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix cores)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-PASSES = ["pool_scores", "block_map", "kv_reduce", "marginal_states", "attention"]
+PEAKS = {"mfma": PEAK_BF16_TFLOPS, "fp64": PEAK_FP64_TFLOPS, "hbm": PEAK_HBM_GBS}
+PASSES = ["pool", "scores", "block_map", "kv_reduce", "marginal_states", "attention"]
 KERNEL_SOURCES = {
-    "pool_scores": "pool_scores.hip", "block_map": "block_map.hip", "kv_reduce": "kv_reduce.hip",
-    "marginal_states": "marginal.hip", "attention": "attn_fwd.hip",
+    "pool": "pool_scores.hip", "scores": "pool_scores.hip", "block_map": "block_map.hip",
+    "kv_reduce": "kv_reduce.hip", "marginal_states": "marginal.hip", "attention": "attn_fwd.hip",
 }
+# the kernel whose counters stand for each pass (a substring of its name in rocprofv3 output)
+PASS_KERNEL = {"attention": "attn_fwd_kernel", "marginal_states": "marginal_gemm_kernel",
+               "kv_reduce": "kv_state_kernel", "pool": "pool_kernel", "scores": "scores_kernel",
+               "block_map": "classify_kernel"}
 
 
 def log(*a):
@@ -55,9 +61,11 @@ def pass_work(w, layer):
     heads_per_row = G if layer.group else 1
     pair_flops = 4.0 * 64 * 64 * d                 # QK^T and PV of one 64 x 64 block pair
     work = {}
-    # Q (and K, unless the key-state pass pools it) in, pooled vectors and scores out
+    # Q (and K, unless the key-state pass pools it) in, fp32 block means out
     pooled = Hq if getattr(layer, "fuse_key_pooling", False) else Hq + Hkv
-    work["pool_scores"] = ("hbm", B * pooled * Nv * d * eb + B * (Hq + Hkv) * nb * d * 4 + rows * nb * 4)
+    work["pool"] = ("hbm", B * pooled * (Nv * d * eb + nb * d * 4))
+    # pooled scores on the fp64 matrix cores: 2 d FLOP per (row, candidate) pair
+    work["scores"] = ("fp64", 2.0 * rows * nb * d * (Hq // Hkv if layer.group else 1))
     work["block_map"] = ("hbm", rows * nb * 4 + (n_crit_entries + n_marg_entries) * 4 + rows * 20)
     if layer.lin == 1:
         # K, V in; one bf16 state + fp32 z (+ the fp32 key block mean when fused) per key block out
@@ -88,17 +96,32 @@ def kernel_source_digest(pass_name):
 def measured_traffic(pass_name, workload):
     """HBM bytes per launch from the committed counter summary, if it matches the current kernel source.
 
-    The summary file profiles/<kernel>_<workload>_counters.txt holds a line
-      TRAFFIC bytes_per_launch=<int> kernel_source_sha=<hex16>
+    The summary file profiles/hbm_counters_<workload>.txt holds one line per pass
+      TRAFFIC pass=<name> bytes_per_launch=<int> kernel_source_sha=<hex16>
     written from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), calibrated with a copy kernel.
     """
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_SOURCES[pass_name].split('.')[0]}_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.txt")
     if not os.path.exists(path):
         return None
-    m = re.search(r"TRAFFIC bytes_per_launch=(\d+) kernel_source_sha=([0-9a-f]+)", open(path).read())
+    m = re.search(rf"TRAFFIC pass={pass_name} bytes_per_launch=(\d+) kernel_source_sha=([0-9a-f]+)", open(path).read())
     if not m or m.group(2) != kernel_source_digest(pass_name):
         return None
     return int(m.group(1))
+
+
+def host_cpu():
+    """(cores this process may run on, CPU model name) of the host."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return int(cores), model
 
 
 def cpu_baseline(w, q, k, v, wg, heads):
@@ -123,14 +146,18 @@ def cpu_baseline(w, q, k, v, wg, heads):
     f.output()
     dt = time.perf_counter() - t0
     full = dt * (w.Hkv / heads)
+    cores, model = host_cpu()
     return {
         "value": round(w.dense_flops() / full / 1e12, 6),
         "unit": "TFLOP/s (effective, dense-equivalent)",
-        "cores": int(blas_threads),
+        "cores": cores,
         "kind": "oracle",
+        "cpu_model": model,
+        "blas_threads": int(blas_threads),
         "sample": (f"{heads} of {w.Hkv} KV heads ({heads * G} query heads), every query block, full forward "
                    f"in {dt:.1f} s, scaled x{w.Hkv / heads:g} to the whole layer ({full:.1f} s); "
-                   f"float64 numpy oracle, {blas_threads} BLAS thread(s)"),
+                   f"float64 numpy oracle on {cores} host cores ({model}), its matrix products on "
+                   f"{blas_threads} BLAS thread(s)"),
         "ms_per_layer": round(full * 1e3, 1),
     }
 
@@ -287,12 +314,11 @@ def summarize_trace(directory, command, note):
     return "\n".join(out) + "\n"
 
 
-def summarize_counters(fetch_dir, write_dir, kernel_pass, workload, copy_mib, commands):
-    """HBM traffic per launch of one pass's kernel from FETCH_SIZE and WRITE_SIZE runs (KiB per dispatch),
-    each scaled by the ratio of known to counted bytes of an elementwise copy of copy_mib MiB."""
+def summarize_counters(fetch_dir, write_dir, workload, copy_mib, commands, passes=None):
+    """HBM traffic per launch of each pass's kernel from FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each scaled by the ratio of known to counted bytes of an elementwise copy of copy_mib MiB.
+    One TRAFFIC line per pass whose kernel appears in both runs."""
     import statistics
-    key = {"attention": "attn_fwd_kernel", "marginal_states": "marginal_gemm_kernel",
-           "kv_reduce": "kv_state_kernel", "pool_scores": "scores_kernel", "block_map": "classify_kernel"}[kernel_pass]
 
     def per_kernel(directory, counter):
         vals = {}
@@ -304,27 +330,32 @@ def summarize_counters(fetch_dir, write_dir, kernel_pass, workload, copy_mib, co
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     copy_bytes = copy_mib * (1 << 20)
 
-    def pick(vals, match, counter):
+    def pick(vals, match):
         names = [n for n in vals if match(n)]
-        if not names:
-            raise SystemExit(f"no {counter} rows for the kernel matching the {kernel_pass} pass")
-        return names[0], statistics.median(vals[names[0]])
+        return (names[0], statistics.median(vals[names[0]])) if names else (None, None)
 
     is_copy = lambda n: "MulFunctor" in n or ("elementwise" in n and "mul" in n.lower())
-    ck_f, copy_f = pick(fetch, is_copy, "FETCH_SIZE")
-    ck_w, copy_w = pick(write, is_copy, "WRITE_SIZE")
+    ck_f, copy_f = pick(fetch, is_copy)
+    ck_w, copy_w = pick(write, is_copy)
+    if ck_f is None or ck_w is None:
+        raise SystemExit("no calibration copy kernel in the counter runs (run with --copy-calibration-mb)")
     fac_f, fac_w = copy_bytes / copy_f, copy_bytes / copy_w
-    kn, kf = pick(fetch, lambda n: key in n, "FETCH_SIZE")
-    _, kw = pick(write, lambda n: key in n, "WRITE_SIZE")
-    traffic = int(round(kf * fac_f + kw * fac_w))
-    out = [f"# HBM traffic per launch: {kernel_pass} pass ({_short(kn, 60)}), workload {workload}",
+    out = [f"# HBM traffic per launch of each pass's kernel, workload {workload}",
            f"# fetch run: {commands[0]}", f"# write run: {commands[1]}",
            f"# calibration kernel: {_short(ck_f, 60)}, {copy_mib} MiB read + {copy_mib} MiB written per launch",
            f"copy   FETCH_SIZE {copy_f:.0f} B counted / {copy_bytes} B known -> factor {fac_f:.4f}",
-           f"copy   WRITE_SIZE {copy_w:.0f} B counted / {copy_bytes} B known -> factor {fac_w:.4f}",
-           f"kernel FETCH_SIZE median {kf:.0f} B/launch (scaled {kf * fac_f:.0f})",
-           f"kernel WRITE_SIZE median {kw:.0f} B/launch (scaled {kw * fac_w:.0f})",
-           f"TRAFFIC bytes_per_launch={traffic} kernel_source_sha={kernel_source_digest(kernel_pass)}"]
+           f"copy   WRITE_SIZE {copy_w:.0f} B counted / {copy_bytes} B known -> factor {fac_w:.4f}"]
+    for pass_name in passes or PASSES:
+        key = PASS_KERNEL[pass_name]
+        kn, kf = pick(fetch, lambda n: key in n)
+        _, kw = pick(write, lambda n: key in n)
+        if kn is None or kw is None:
+            continue
+        traffic = int(round(kf * fac_f + kw * fac_w))
+        out += [f"{pass_name}: {_short(kn, 70)}",
+                f"  FETCH_SIZE median {kf:.0f} B/launch (scaled {kf * fac_f:.0f}); "
+                f"WRITE_SIZE median {kw:.0f} B/launch (scaled {kw * fac_w:.0f})",
+                f"TRAFFIC pass={pass_name} bytes_per_launch={traffic} kernel_source_sha={kernel_source_digest(pass_name)}"]
     return "\n".join(out) + "\n"
 
 
@@ -402,8 +433,7 @@ def main():
                     help="also run a plain device copy of this many MiB (calibrates HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a kernel-trace summary of a rocprofv3 run")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="print the HBM-traffic summary of the --pass kernel from two rocprofv3 --pmc runs")
-    ap.add_argument("--pass", dest="pass_name", default="attention", choices=PASSES)
+                    help="print the HBM-traffic summary of every pass's kernel from two rocprofv3 --pmc runs")
     ap.add_argument("--command", action="append", default=[], help="profiling command(s) to record")
     ap.add_argument("--note", default="")
     args = ap.parse_args()
@@ -413,8 +443,7 @@ def main():
         return
     if args.summarize_counters:
         cmds = (args.command + ["?", "?"])[:2]
-        print(summarize_counters(*args.summarize_counters, args.pass_name, args.workload,
-                                 args.copy_calibration_mb, cmds), end="")
+        print(summarize_counters(*args.summarize_counters, args.workload, args.copy_calibration_mb, cmds), end="")
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -478,12 +507,12 @@ def main():
     dom = max(PASSES, key=lambda n: pass_ms[n])
     bound, amount = work[dom]
     t_dom = pass_ms[dom] / 1e3
-    if bound == "mfma":
-        achieved = amount / t_dom / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
+    if bound == "hbm":
         achieved = amount / t_dom / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        achieved = amount / t_dom / 1e12
+        roof = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAKS[bound], "unit": "TFLOP/s"}
     roof["frac"] = round(achieved / roof["peak"], 4)
     roof["traffic"] = measured_traffic(dom, w.name)
     roof["kernel"] = dom
@@ -500,14 +529,26 @@ def main():
         b_, a_ = work[name]
         t_ = pass_ms[name] / 1e3
         if a_ and t_ > 0:
-            frac = (a_ / t_ / 1e12 / PEAK_BF16_TFLOPS) if b_ == "mfma" else (a_ / t_ / 1e9 / PEAK_HBM_GBS)
+            frac = (a_ / t_ / 1e9 / PEAK_HBM_GBS) if b_ == "hbm" else (a_ / t_ / 1e12 / PEAKS[b_])
         else:
             frac = None
         passes[name] = {"ms": round(pass_ms[name], 5), "bound": b_,
                         "roofline_frac": None if frac is None else round(frac, 4)}
-    if "pool_scores" in passes:
-        # the pass holds two kernels; its HBM fraction counts the pooling's bytes over both kernels' time
-        passes["pool_scores"]["note"] = "pooling (HBM bytes counted) and the fp64 pooled scores in one pass"
+        if name in PASS_KERNEL and a_:
+            passes[name]["algorithmic_per_launch"] = a_
+            passes[name]["traffic"] = measured_traffic(name, w.name)
+    if "marginal_states" in passes and layer.lin == 1 and pass_ms["marginal_states"] > 0:
+        # the 0/1-mask product: matrix-core FLOPs (2 nb^2 d^2 per head, the dense mask) and HBM bytes
+        t_ = pass_ms["marginal_states"] / 1e3
+        heads = w.B * (w.Hkv if layer.group else w.Hq)
+        mflops = 2.0 * heads * w.nb * w.nb * (w.d * w.d + w.d)
+        passes["marginal_states"]["mfma_frac"] = round(mflops / t_ / 1e12 / PEAK_BF16_TFLOPS, 4)
+        passes["marginal_states"]["hbm_frac"] = passes["marginal_states"]["roofline_frac"]
+        passes["marginal_states"]["mask_product_flops"] = mflops
+    if "scores" in passes and pass_ms["scores"] > 0:
+        # the pooled scores also write nb^2 fp32 per map row
+        rows = w.B * (w.Hkv if layer.group else w.Hq) * w.nb
+        passes["scores"]["hbm_frac"] = round(rows * w.nb * 4 / (pass_ms["scores"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
 
     value = w.dense_flops() / (ms_step / 1e3) / 1e12
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "n_valid": w.Nv, "d": w.d,

@@ -148,6 +148,16 @@ class SlaForward:
         return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
                                scale=self.scale, out=self.pool, k_pooled=k_pooled)
 
+    def pooling(self, k_pooled: bool = False):
+        """The pooling half of pool_scores: block means of Q (and of K unless k_pooled)."""
+        return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
+                               scale=self.scale, out=self.pool, k_pooled=k_pooled, want_scores=False)
+
+    def scoring(self):
+        """The scoring half of pool_scores, from the block means pooling() (and kv_reduce) wrote."""
+        return sla_pool_scores(self.q, self.k, self.n_valid, group_sum=self.group, causal=self.causal,
+                               scale=self.scale, out=self.pool, k_pooled=True, q_pooled=True)
+
     def block_map(self):
         return sla_block_map(self.pool["scores"], self.n_crit, self.n_negl, causal=self.causal,
                              window=self.window, out=self.maps)
@@ -208,7 +218,7 @@ class SlaForward:
         return tuple(grads) + tuple(g_r[3:])
 
     def run(self, overlap: bool = False, events=None) -> torch.Tensor:
-        """One full forward: (token order,) pool + scores, block map, linear states, marginal sums,
+        """One full forward: (token order,) pool, scores, block map, linear states, marginal sums,
         attention (, order undone).  With fuse_key_pooling the linear key states come first and also
         write the key block means, and the pooling pass reads only Q.
 
@@ -229,13 +239,16 @@ class SlaForward:
         timed("reorder", self.reorder)
         if self.fuse_key_pooling and not overlap:
             timed("kv_reduce", lambda: self.kv_reduce(k_pool=True))
-            timed("pool_scores", lambda: self.pool_scores(k_pooled=True))
+            timed("pool", lambda: self.pooling(k_pooled=True))
+            timed("scores", self.scoring)
             for name in ("block_map", "marginal_states", "attention"):
                 timed(name, getattr(self, name))
             timed("restore", self.restore)
             return self.out
         if not overlap or self.lin == SLA_LIN_NONE:
-            for name in ("pool_scores", "block_map", "kv_reduce", "marginal_states", "attention"):
+            timed("pool", self.pooling)
+            timed("scores", self.scoring)
+            for name in ("block_map", "kv_reduce", "marginal_states", "attention"):
                 timed(name, getattr(self, name))
             timed("restore", self.restore)
             return self.out
@@ -246,9 +259,10 @@ class SlaForward:
         e_in, e_map, e_marg = self._ev
         if not self.smooth_k:
             e_in.record(main)                  # inputs (and their reorder) are ready
-        timed("pool_scores", self.pool_scores)
+        timed("pool", self.pooling)
         if self.smooth_k:
             e_in.record(main)                  # the key shift needs the pooled keys
+        timed("scores", self.scoring)
         with torch.cuda.stream(side):
             side.wait_event(e_in)
             timed("kv_reduce", self.kv_reduce)

@@ -154,11 +154,11 @@ def sla_attn_workspace_bytes(B, Hs, nqb, d, lin_mode) -> int:
 # ----------------------------------------------------------------------------- GPU calls
 
 def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, want_probs=False, out=None,
-                    k_pooled=False):
+                    k_pooled=False, q_pooled=False, want_scores=True):
     """Returns dict(q_pool, k_pool, scores[, probs]); `out` may hold preallocated tensors.
 
     k_pooled: out["k_pool"] already holds the key block means (sla_linear_kv_reduce's k_pool output);
-    only Q is pooled.
+    q_pooled: out["q_pool"] already holds the query block means; want_scores=False: pooling only.
     """
     _require_gpu(q, k)
     B, Hq, N, d = q.shape
@@ -176,10 +176,11 @@ def sla_pool_scores(q, k, n_valid, group_sum=False, causal=False, scale=None, wa
     if ws and (out.get("workspace") is None or out["workspace"].numel() < ws):
         out["workspace"] = torch.empty(ws, device=q.device, dtype=torch.uint8)
     qd, kd = tensor_desc(q), tensor_desc(k)
+    pooled = (1 if k_pooled else 0) | (2 if q_pooled else 0)
     _check("sla_pool_scores", lib().sla_pool_scores(
-        ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale), int(bool(k_pooled)),
-        _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]), _ptr(out.get("probs")),
-        _ptr(out.get("workspace")), ws, _stream(q.device)))
+        ctypes.byref(qd), ctypes.byref(kd), n_valid, int(group_sum), int(causal), float(scale), pooled,
+        _ptr(out["q_pool"]), _ptr(out["k_pool"]), _ptr(out["scores"]) if want_scores else None,
+        _ptr(out.get("probs")) if want_scores else None, _ptr(out.get("workspace")), ws, _stream(q.device)))
     return out
 
 

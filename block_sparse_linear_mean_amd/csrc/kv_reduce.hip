@@ -317,7 +317,7 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     // fp32 sums over runs of key blocks into the workspace, then over the runs
     const size_t need = sla_kv_reduce_workspace_bytes(k->B, k->H, k->N, d, H != nullptr, 1);
     if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
-    const int cb = kKvSumRun;
+    const int cb = kv_sum_run(nb, bgs);
     const int nch = (nb + cb - 1) / cb;
     float* Hp = static_cast<float*>(workspace);
     float* zp = Hp + int64_t(bgs) * nch * d * d;

@@ -236,7 +236,7 @@ extern "C" size_t sla_pool_scores_workspace_bytes(int32_t B, int32_t Hq, int32_t
 }
 
 extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
-                                      int32_t group_sum, int32_t causal, float scale, int32_t k_pooled, float* q_pool,
+                                      int32_t group_sum, int32_t causal, float scale, int32_t pooled, float* q_pool,
                                       float* k_pool, float* scores, float* probs, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   using namespace sla;
@@ -244,16 +244,26 @@ extern "C" sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, 
   if (st != SLA_OK) return st;
   if ((st = check_tensor(k)) != SLA_OK) return st;
   if (!same_geometry(q, k) || q->H % k->H != 0) return SLA_ERR_SHAPE;
-  if (q_pool == nullptr || k_pool == nullptr || scores == nullptr) return SLA_ERR_NULL;
+  if (q_pool == nullptr || k_pool == nullptr) return SLA_ERR_NULL;
+  if (scores == nullptr && probs != nullptr) return SLA_ERR_NULL;
   if (!aligned16(q_pool) || !aligned16(k_pool)) return SLA_ERR_ALIGN;
   if ((st = check_valid_len(n_valid, q->N)) != SLA_OK) return st;
   if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
-  const size_t need = sla_pool_scores_workspace_bytes(q->B, q->H, k->H, q->N, q->d, group_sum);
+  if (pooled < 0 || pooled > 3) return SLA_ERR_RANGE;
+  const size_t need = scores ? sla_pool_scores_workspace_bytes(q->B, q->H, k->H, q->N, q->d, group_sum) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) return SLA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = q->N / kBlock;
-  if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, !k_pooled, q_pool, k_pool, s);
-  else launch_pool<float>(q, k, n_valid, !k_pooled, q_pool, k_pool, s);
+  const bool pool_q = !(pooled & SLA_POOLED_Q), pool_k = !(pooled & SLA_POOLED_K);
+  if (pool_q) {
+    if (q->dtype == SLA_BF16) launch_pool<bf16raw>(q, k, n_valid, pool_k, q_pool, k_pool, s);
+    else launch_pool<float>(q, k, n_valid, pool_k, q_pool, k_pool, s);
+  } else if (pool_k) {
+    // the key block means only: the same kernel with K in the place of Q
+    if (q->dtype == SLA_BF16) launch_pool<bf16raw>(k, k, n_valid, false, k_pool, k_pool, s);
+    else launch_pool<float>(k, k, n_valid, false, k_pool, k_pool, s);
+  }
+  if (scores == nullptr) return launch_status();   // pooling only
   const int Hs = group_sum ? k->H : q->H;
   const double* qsum = nullptr;
   if (group_sum && q->H / k->H > 1) {             // the group sums once, instead of in every tile

@@ -8,8 +8,14 @@
 
 namespace sla {
 
-// key blocks per fp32 partial state when summing the linear states over all keys
-constexpr int kKvSumRun = 32;
+// Key blocks per fp32 partial state when summing the linear states over all keys: runs short
+// enough that about two workgroups per compute unit (512 in all) share the pass, but at least 4
+// blocks (each run writes a d x d fp32 partial that the fixed-order final sum reads again) and at
+// most 32.  Depends on the shapes only, so the partial sums and their order are reproducible.
+inline int kv_sum_run(int64_t nb, int64_t heads) {
+  const int64_t r = (nb * heads + 511) / 512;
+  return int(r < 4 ? 4 : (r > 32 ? 32 : r));
+}
 
 inline int elem_bytes(int32_t dtype) { return dtype == SLA_BF16 ? 2 : 4; }
 

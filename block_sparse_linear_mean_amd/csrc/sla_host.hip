@@ -69,7 +69,8 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
   (void)want_blocks;   // per-block states need no workspace; the sum over all keys does
   if (!want_all || B < 1 || Hkv < 1 || N < SLA_BLOCK) return 0;
   const int64_t nb = N / SLA_BLOCK;
-  const int64_t chunks = (nb + sla::kKvSumRun - 1) / sla::kKvSumRun;   // fp32 partial state per run
+  const int run = sla::kv_sum_run(nb, int64_t(B) * Hkv);
+  const int64_t chunks = (nb + run - 1) / run;   // fp32 partial state per run
   return size_t(int64_t(B) * Hkv * chunks * (int64_t(d) * d + d) * 4);
 }
 

@@ -118,14 +118,22 @@ sla_status sla_counts(int32_t nb, int32_t kh_bp, int32_t kl_bp, int32_t* n_crit,
  *     same shape as scores), for diagnostics; the classification ranks the scores.
  * q and k share dtype and d; n_valid as in the conventions; scale > 0 (normally 1/sqrt(d)).
  * q_pool and k_pool are 16-byte aligned (SLA_ERR_ALIGN otherwise).
- * k_pooled != 0: k_pool already holds the key block means (written by sla_linear_kv_reduce's
- *   k_pool output, which reads K once for both); only Q is pooled and K's data is not read
- *   (its descriptor still gives the shapes).
+ * pooled (bit flags, 0 .. 3, SLA_ERR_RANGE otherwise):
+ *   SLA_POOLED_K: k_pool already holds the key block means (written by sla_linear_kv_reduce's
+ *     k_pool output, which reads K once for both); K's data is not read (its descriptor still
+ *     gives the shapes);
+ *   SLA_POOLED_Q: q_pool already holds the query block means (an earlier pooling-only call);
+ *     Q's data is not read.
+ * scores (nullable): NULL = pooling only (probs must be NULL too, no workspace needed), which
+ *   with a later call that passes both pooled flags splits the pass into its pooling and its
+ *   scoring kernels.
  * workspace: sla_pool_scores_workspace_bytes(...) bytes (the fp64 group sums of the pooled
  * queries, non-zero only with group_sum and more than one query head per KV head).
  */
+#define SLA_POOLED_K 1
+#define SLA_POOLED_Q 2
 sla_status sla_pool_scores(const sla_tensor* q, const sla_tensor* k, int32_t n_valid,
-                           int32_t group_sum, int32_t causal, float scale, int32_t k_pooled,
+                           int32_t group_sum, int32_t causal, float scale, int32_t pooled,
                            float* q_pool, float* k_pool, float* scores, float* probs,
                            void* workspace, size_t workspace_bytes, void* stream);
 
@@ -233,7 +241,8 @@ size_t sla_kv_reduce_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t 
  * shift), summed in fp64 and rounded once, the values sla_pool_scores writes (bit-identical
  * for bf16 K, whose fp64 block sums are exact; for fp32 K whenever a block's values lie within
  * 2^23 of each other in magnitude), so that sla_pool_scores with k_pooled skips reading K.  H_all needs a workspace of sla_kv_reduce_workspace_bytes(..., 1) bytes (fp32
- * partial sums over runs of 32 key blocks, then summed in a fixed order).
+ * partial sums over runs of consecutive key blocks, 4 to 32 of them by the shapes, then summed
+ * in a fixed order).
  */
 sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor* v, int32_t n_valid,
                                 const float* k_shift, void* H, float* z, float* H_all, float* z_all,

@@ -71,8 +71,12 @@ def test_capacities_and_workspaces(L):
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 * 2 + 128 * 4)
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_NONE) == 0
     assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 0) == 0
-    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 12 * 16 * (128 * 128 + 128) * 4
-    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 16 * (128 * 128 + 128) * 4
+    # runs of 12 key blocks at 12 heads x 512 blocks (about 512 workgroups): 43 fp32 partial states per head
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 12 * 43 * (128 * 128 + 128) * 4
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 43 * (128 * 128 + 128) * 4
+    # runs stay within 4 .. 32 blocks
+    assert sla.sla_kv_reduce_workspace_bytes(1, 1, 4096, 64, 1, 1) == 1 * 16 * (64 * 64 + 64) * 4
+    assert sla.sla_kv_reduce_workspace_bytes(1, 64, 262144, 64, 1, 1) == 64 * 128 * (64 * 64 + 64) * 4
 
 
 def desc(ptr=0x10000, dtype=0, B=1, H=2, N=256, d=128, sB=None, sH=None, sN=None):
