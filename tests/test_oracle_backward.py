@@ -145,3 +145,90 @@ def test_proj_weight_and_smooth_k_gradients_match_finite_differences(shared_w):
         fd = (loss(Kx=Kp) - loss(Kx=Km)) / (2 * eps)
         assert abs(fd - dK[kidx]) <= 1e-6 * (1 + abs(fd)), ("K", kidx, fd, dK[kidx])
     assert np.all(dK[:, :, nv:] == 0.0)
+
+
+# ----------------------------------------------------------------------------- SALAD and NSA (GQA)
+
+def _mode_loss(kw, maps, dO, Q, K, V, G=1, group_map=False):
+    """sum(dO * O) of the numpy oracle in any mode, with the block map held fixed."""
+    g = orc.Forward(Q, K, V, **kw)
+    Hq = Q.shape[1]
+    tot = 0.0
+    for b in range(Q.shape[0]):
+        for h in range(Hq):
+            mh = h // G if group_map else h
+            for i in range(Q.shape[2] // 64):
+                tot += float(np.sum(dO[b, h, 64 * i:64 * (i + 1)] * g.output_block(b, h, i, maps[(b, mh, i)])))
+    return tot
+
+
+def _fd_check(loss, arrays, grads, r, n=10, name_of=None):
+    eps = 1e-6
+    for name, X in arrays.items():
+        G = grads[name]
+        for _ in range(n):
+            idx = tuple(int(r.integers(s_)) for s_ in X.shape)
+            Xp, Xm = X.astype(np.float64).copy(), X.astype(np.float64).copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            fd = (loss(**{name: Xp}) - loss(**{name: Xm})) / (2 * eps)
+            assert abs(fd - G[idx]) <= 1e-6 * (1.0 + abs(fd)), (name, idx, fd, G[idx])
+
+
+@pytest.mark.parametrize("smooth_k", [False, True])
+def test_salad_gradients_match_finite_differences(smooth_k):
+    """SALAD: the sparse branch plus sigmoid(q . w_g) times linear attention over all valid keys;
+    dQ, dK, dV and the gate weights' gradient against central differences of the numpy oracle."""
+    N, nv, d, H = 256, 236, 8, 2
+    Q, K, V = rand_qkv(1, H, H, N, d, seed=51, n_valid=nv, garbage=True)
+    K = K + 0.2
+    r = np.random.default_rng(52)
+    wg = r.standard_normal((H, d)) / np.sqrt(d)
+    dO = r.standard_normal(Q.shape)
+    kw = dict(n_valid=nv, mode="salad", kh_bp=2500, w_gate=wg, smooth_k=smooth_k)
+    f = orc.Forward(Q, K, V, **kw)
+    maps = f.maps()
+    O, dQ, dK, dV, dwg = bwd.gradients(Q, K, V, dO, maps, nv, f.scale, smooth_k=smooth_k, mode="salad", w_gate=wg)
+    assert np.allclose(O, f.output(), rtol=1e-12, atol=1e-13)
+
+    def loss(Q=Q, K=K, V=V, wg=wg):
+        return _mode_loss(dict(kw, w_gate=wg), maps, dO, Q, K, V)
+    _fd_check(loss, {"Q": Q, "K": K, "V": V, "wg": wg}, {"Q": dQ, "K": dK, "V": dV, "wg": dwg}, r)
+    for G in (dQ, dK, dV):
+        assert np.all(G[:, :, nv:] == 0.0)
+
+
+def test_nsa_gqa_gradients_match_finite_differences():
+    """NSA-style causal selection shared by a GQA group (4 query heads on 2 KV heads), with a
+    window: dQ, and dK / dV summed over the group's heads, against central differences."""
+    N, nv, d, Hq, Hkv = 640, 630, 8, 4, 2
+    Q, K, V = rand_qkv(1, Hq, Hkv, N, d, seed=53, n_valid=nv, garbage=True)
+    r = np.random.default_rng(54)
+    dO = r.standard_normal(Q.shape)
+    kw = dict(n_valid=nv, mode="nsa", n_sel=3, window=100)
+    f = orc.Forward(Q, K, V, **kw)
+    maps = f.maps()
+    assert any(len(m["crit"]) > 3 for m in maps.values())          # window blocks beside the selection
+    O, dQ, dK, dV = bwd.gradients(Q, K, V, dO, maps, nv, f.scale, mode="nsa", window=100, group_map=True)
+    assert np.allclose(O, f.output(), rtol=1e-12, atol=1e-13)
+
+    def loss(Q=Q, K=K, V=V):
+        return _mode_loss(kw, maps, dO, Q, K, V, G=2, group_map=True)
+    _fd_check(loss, {"Q": Q, "K": K, "V": V}, {"Q": dQ, "K": dK, "V": dV}, r)
+    for G in (dQ, dK, dV):
+        assert np.all(G[:, :, nv:] == 0.0)
+
+
+def test_nsa_short_sequence_gradients_equal_causal_sdpa_autograd():
+    """Every causal block selected (8 blocks <= 16): causal GQA attention, whose gradients torch's
+    SDPA autograd gives (K and V repeated over the group, so their gradients sum over it)."""
+    N, d, Hq = 512, 16, 4
+    Q, K, V = rand_qkv(1, Hq, 1, N, d, seed=55)
+    dO = np.random.default_rng(56).standard_normal(Q.shape)
+    f = orc.Forward(Q, K, V, n_valid=N, mode="nsa", n_sel=16, window=128)
+    _, dQ, dK, dV = bwd.gradients(Q, K, V, dO, f.maps(), N, f.scale, mode="nsa", window=128, group_map=True)
+    q, k, v = (torch.tensor(np.asarray(X[0], np.float64), requires_grad=True) for X in (Q, K, V))
+    o = F.scaled_dot_product_attention(q, k.expand(Hq, -1, -1), v.expand(Hq, -1, -1), is_causal=True, scale=f.scale)
+    o.backward(torch.tensor(dO[0]))
+    for G, ref in [(dQ, q.grad), (dK, k.grad), (dV, v.grad)]:
+        assert np.allclose(G[0], ref.numpy(), rtol=1e-9, atol=1e-11)
