@@ -11,6 +11,7 @@ Entry points keep the C names (see include/sla.h):
     sla_marginal_states  per-row sums of the marginal states (also done inside sla_attn_fwd)
     sla_attn_fwd         block-sparse softmax attention + fused linear epilogue
     sla_attn_bwd         dQ, dK, dV of the SLA layer for a fixed block map
+    sla_attn_bwd_ext     the same for every forward mode (SALAD gate, NSA causal maps, GQA)
     sla_hilbert_order    token order of a video latent grid along a 3-D Hilbert curve (host)
     sla_nsa3_fwd         NSA with compressed, selected and window branches, gated
     sla_permute_rows     apply / undo a token order on [B, H, N, d] rows
@@ -26,7 +27,8 @@ import torch
 
 from ._lib import (  # noqa: F401
     BLOCK, SLA_BF16, SLA_F32, SLA_LIN_GLOBAL_GATED, SLA_LIN_MARGINAL, SLA_LIN_NONE, SLA_LIN_ROW_STATES, SlaError, alloc_block_map,
-    lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes,
+    lib, sla_abi_version, sla_attn_bwd, sla_attn_bwd_ext, sla_attn_bwd_ext_workspace_bytes,
+    sla_attn_bwd_workspace_bytes, sla_attn_fwd, sla_attn_workspace_bytes,
     sla_hilbert_order, sla_nsa3_fwd, sla_nsa3_workspace_bytes, sla_permute_rows, sla_block_map, sla_block_map_capacity,
     sla_block_map_noalloc,
     sla_block_map_workspace_bytes, sla_counts, sla_key_mean, sla_kv_reduce_workspace_bytes, sla_linear_kv_reduce,
@@ -117,8 +119,6 @@ class SlaForward:
         # means are the pooling pass's bit for bit, so the block map does not change.
         self.fuse_key_pooling = self.lin != SLA_LIN_NONE and not smooth_k and k.dtype == torch.bfloat16
         # training: the forward also writes each row's log-sum-exp, which backward() reads
-        if training and (mode != "sla" or Hq != Hkv):
-            raise ValueError("backward is provided for the sla mode with Hq == Hkv")
         self.lse = torch.empty((B, Hq, N), **f) if training else None
         self.bwd_ws = None
         self.row_states = None
@@ -189,28 +189,34 @@ class SlaForward:
                                 proj_w=self.proj_w, proj_b=self.proj_b, lse=self.lse)
         return sla_attn_fwd(self.q, self.k, self.v, self.n_valid, maps or self.maps, lin_mode=self.lin,
                             scale=self.scale, causal=self.causal, window=self.window, group_map=self.group,
-                            H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out_ordered)
+                            H_all=kv.get("H_all"), z_all=kv.get("z_all"), w_gate=self.w_gate, out=self.out_ordered,
+                            lse=self.lse)
 
     def backward(self, dout: torch.Tensor, maps=None, grads=None):
-        """(dq, dk, dv) fp32 of sum(dout * out) after run() (or attention()) with training=True;
-        with a Proj weight (dq, dk, dv, dW, db), db None without a bias."""
+        """Gradients of sum(dout * out) after run() (or attention()) with training=True, for the same
+        block map: (dq, dk, dv) fp32 (dk, dv per KV head); sla mode with a Proj weight adds (dW, db),
+        db None without a bias; salad mode adds dw_gate [Hq, d]."""
         if self.lse is None:
             raise ValueError("construct the layer with training=True to keep what the backward needs")
         proj_heads = 0 if self.proj_w is None else (1 if self.proj_w.dim() == 2 else self.proj_w.shape[0])
+        lin = SLA_LIN_ROW_STATES if self.lin == SLA_LIN_MARGINAL else self.lin
+        B, Hq, N, d = self.q.shape
+        Hkv = self.k.shape[1]
         if self.bwd_ws is None:
-            B, H, N, d = self.q.shape
-            self.bwd_ws = torch.empty(sla_attn_bwd_workspace_bytes(B, H, N, d, proj_heads), device=self.q.device,
-                                      dtype=torch.uint8)
-        S, u = self.row_states
-        extra = dict(scale=self.scale, workspace=self.bwd_ws, k_shift=self.k_mean, proj_w=self.proj_w,
-                     proj_b=self.proj_b)
+            ws = sla_attn_bwd_ext_workspace_bytes(B, Hq, Hkv, N, d, lin, self.causal, self.group, proj_heads)
+            self.bwd_ws = torch.empty(max(ws, 1), device=self.q.device, dtype=torch.uint8)
+        S, u = self.row_states if self.row_states is not None else (None, None)
+        extra = dict(scale=self.scale, causal=self.causal, window=self.window, group_map=self.group, S=S, u=u,
+                     H_all=self.kv.get("H_all"), z_all=self.kv.get("z_all"),
+                     w_gate=self.w_gate if lin == SLA_LIN_GLOBAL_GATED else None, k_shift=self.k_mean,
+                     proj_w=self.proj_w, proj_b=self.proj_b, workspace=self.bwd_ws)
         if self.order is None:
-            return sla_attn_bwd(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid, maps or self.maps,
-                                S, u, grads=grads, **extra)
+            return sla_attn_bwd_ext(self.q, self.k, self.v, self.out, dout, self.lse, self.n_valid,
+                                    maps or self.maps, lin, grads=grads, **extra)
         # in the token order, then scattered back (the order is a permutation: its gradient is the inverse)
         dout_r = sla_permute_rows(dout, self.order)
-        g_r = sla_attn_bwd(self.q, self.k, self.v, self.out_ordered, dout_r, self.lse, self.n_valid,
-                           maps or self.maps, S, u, **extra)
+        g_r = sla_attn_bwd_ext(self.q, self.k, self.v, self.out_ordered, dout_r, self.lse, self.n_valid,
+                               maps or self.maps, lin, **extra)
         if grads is None:
             grads = tuple(torch.empty_like(x) for x in g_r[:3])
         for src, dst in zip(g_r[:3], grads):

@@ -68,6 +68,11 @@ _SIGS = {
     "sla_attn_bwd_workspace_bytes": (c_size_t, [c_int32] * 5),
     "sla_attn_bwd": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, _P, _P, _P, _P, _P, _P, _P, _P,
                                                           c_int32, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "sla_attn_bwd_ext_workspace_bytes": (c_size_t, [c_int32] * 9),
+    "sla_attn_bwd_ext": (c_int32, [POINTER(SlaTensor)] * 5 + [_P, c_int32, c_float, c_int32, c_int32, c_int32,
+                                                              c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                              _P, c_int32, _P, _P, _P, _P, _P, _P, _P, c_size_t,
+                                                              _P]),
 }
 
 
@@ -383,6 +388,69 @@ def sla_attn_bwd(q, k, v, o, dout, lse, n_valid, maps, S, u, scale=None, grads=N
     if proj_w is not None:
         return dq, dk, dv, dW, db
     return dq, dk, dv
+
+
+def sla_attn_bwd_ext_workspace_bytes(B, Hq, Hkv, N, d, lin_mode, causal=False, group_map=False,
+                                     proj_heads=0) -> int:
+    return int(lib().sla_attn_bwd_ext_workspace_bytes(B, Hq, Hkv, N, d, lin_mode, int(causal), int(group_map),
+                                                      proj_heads))
+
+
+def sla_attn_bwd_ext(q, k, v, o, dout, lse, n_valid, maps, lin_mode, scale=None, causal=False, window=0,
+                     group_map=False, S=None, u=None, H_all=None, z_all=None, w_gate=None, k_shift=None,
+                     proj_w=None, proj_b=None, grads=None, proj_grads=None, dw_gate=None, workspace=None):
+    """Gradients of sum(dout * o) for every sla_attn_fwd mode, fixed map: (dq [B, Hq, N, d],
+    dk, dv [B, Hkv, N, d]) fp32, then (dW, db) with proj_w, then dw_gate [Hq, d] when gated.
+
+    lin_mode SLA_LIN_ROW_STATES: S, u the map's per-row marginal sums, maps["marg_bits"] its masks;
+    SLA_LIN_GLOBAL_GATED: H_all, z_all from sla_linear_kv_reduce and w_gate [Hq, d];
+    SLA_LIN_NONE: no linear branch (causal maps with window tokens, shared by a GQA group with
+    group_map).  k_shift [B, Hkv, d]: the smooth-K key mean given to the forward.
+    """
+    _require_gpu(q, k, v, o, dout, lse)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = (1.0 / d ** 0.5) if scale is None else scale
+    f32 = dict(device=q.device, dtype=torch.float32)
+    if grads is None:
+        grads = (torch.empty((B, Hq, N, d), **f32), torch.empty((B, Hkv, N, d), **f32),
+                 torch.empty((B, Hkv, N, d), **f32))
+    proj_heads = 0
+    dW = db = None
+    if proj_w is not None:
+        if proj_w.dtype != torch.float32 or not proj_w.is_contiguous() or proj_w.shape[-2:] != (d, d):
+            raise ValueError("proj_w must be a contiguous float32 [d, d] or [Hq, d, d] tensor")
+        proj_heads = 1 if proj_w.dim() == 2 else proj_w.shape[0]
+        if proj_grads is not None:
+            dW, db = proj_grads
+        else:
+            dW = torch.empty_like(proj_w)
+            db = None if proj_b is None else torch.empty(proj_w.shape[:-1], **f32)
+    elif proj_b is not None:
+        raise ValueError("proj_b without proj_w")
+    gated = lin_mode == SLA_LIN_GLOBAL_GATED
+    if gated and dw_gate is None:
+        dw_gate = torch.empty((Hq, d), **f32)
+    if k_shift is not None and (k_shift.dtype != torch.float32 or not k_shift.is_contiguous()
+                                or tuple(k_shift.shape) != (B, Hkv, d)):
+        raise ValueError("k_shift must be a contiguous float32 [B, Hkv, d] tensor")
+    ws_bytes = sla_attn_bwd_ext_workspace_bytes(B, Hq, Hkv, N, d, lin_mode, causal, group_map, proj_heads)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    descs = [tensor_desc(x) for x in (q, k, v, o, dout)]
+    dq, dk, dv = grads
+    _check("sla_attn_bwd_ext", lib().sla_attn_bwd_ext(
+        *[ctypes.byref(x) for x in descs], _ptr(lse), n_valid, float(scale), lin_mode, int(causal), int(window),
+        int(group_map), _ptr(maps["crit_rowptr"]), _ptr(maps["crit_idx"]), _ptr(maps.get("crit_flags")),
+        _ptr(maps.get("marg_bits")), _ptr(S), _ptr(u), _ptr(H_all), _ptr(z_all), _ptr(w_gate), _ptr(k_shift),
+        _ptr(proj_w), _ptr(proj_b), proj_heads, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(db), _ptr(dw_gate),
+        _ptr(workspace), workspace.numel(), _stream(q.device)))
+    out = (dq, dk, dv)
+    if proj_w is not None:
+        out = out + (dW, db)
+    if gated:
+        out = out + (dw_gate,)
+    return out
 
 
 def sla_hilbert_order(T, H, W) -> torch.Tensor:

@@ -24,6 +24,8 @@
 // row's lists; the key-stationary ones (linear dK/dV and sparse dK/dV) over the transposed
 // lists, kept as one bit per (key block, query block); no atomics on gradients, so results
 // are deterministic.
+#include <type_traits>
+
 #include "attn_tiles.h"
 #include "sla_device.h"
 #include "sla_host.h"
@@ -41,10 +43,19 @@ struct BwdParams {
   const void* dout;
   int64_t qsB, qsH, qsN, ksB, ksH, ksN, vsB, vsH, vsN, osB, osH, osN, dsB, dsH, dsN;
   int H, N, nb, n_valid, wq;      // wq: 32-bit words per transposed bit row, ceil(nb / 32)
+  int Hkv, G, Hs, group_map;      // KV heads, query heads per KV head, map heads, maps shared by a group
+  int window;                     // causal maps: key s of a window block is allowed iff t - s < window
+  int overwrite;                  // no linear branch: the sparse kernels write dQ, dK, dV (else add)
+  int gated;                      // SALAD: one linear state per head (all keys), gated by sigmoid(q . w_gate)
   float scale, scale_log2;
   const float* lse;               // [B, H, N] natural log-sum-exp of the forward's sparse branch
   const int* crit_rowptr;
   const int* crit_idx;
+  const uint8_t* crit_flags;      // causal maps: bit 0 = selected block (else a window block)
+  const uint32_t* critT_sel;      // causal maps: [map rows][wq], the selected bits of critT
+  const float* Sf;                // SALAD: H_all fp32 [B, H][c][r] (S, u then unused; u = z_all)
+  const float* w_gate;            // SALAD: [H][d]
+  float* gpart;                   // SALAD: [B, H, nb][d] partial gradients of w_gate per query block
   const u16* S;                   // per-row marginal sums, bf16 [rows][c][r]
   const float* u;                 // [rows][r]
   float* D;                       // [B, H, N]: dO . O_sparse
@@ -52,7 +63,7 @@ struct BwdParams {
   float* du;                      // [rows][r]
   const u16* dH;                  // [B, H, nb][c][r] bf16: gradient of H_j
   const float* dz;                // [B, H, nb][r]
-  const uint32_t* critT;          // [B, H, nb][wq]: bit i of row j = block j is critical for query block i
+  const uint32_t* critT;          // [map rows][wq]: bit i of row (b, m, j) = block j is critical for query block i
   const int* kv_order;            // [B * H * nb]: key-block rows, most-used first (dK/dV dispatch order)
   const float* k_shift;           // smooth-K: [B, H, d] key mean of the forward, or null
   const float* dk_mean;           // smooth-K: [B, H, d] mean over valid rows of the linear-branch dK
@@ -128,22 +139,30 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   if (e < n) p[e] = v;
 }
 
-// One wavefront per map row (bh, i), one lane per listed block j: set bit i of row (bh, j) of the
-// transposed critical mask (atomic OR: the result does not depend on the order), so every entry's
-// atomics are in flight at once.  Also counts, per key-block row, the query blocks that list it
-// (the dK/dV workload of that row).
+// One wavefront per map row (b, s, i), one lane per listed block j: set bit i of row (b, s, j) of
+// the transposed critical mask, and of its selected mask when the entry's flag has bit 0 (causal
+// maps; flags NULL: none), by atomic OR (the result does not depend on the order), so every
+// entry's atomics are in flight at once.  Also counts, per key-block row (b, g, j) of the KV head g
+// that map head s reads (s with shared maps, s / G otherwise), the listing entries (the dK/dV
+// workload of that row, up to a factor G with shared maps).
 __global__ __launch_bounds__(256) void crit_transpose_kernel(const int* __restrict__ rowptr, const int* __restrict__ idx,
-                                                             int rows, int nb, int wq, uint32_t* __restrict__ critT,
+                                                             const uint8_t* __restrict__ flags, int rows, int nb,
+                                                             int wq, int Hs, int Hkv, int kv_div,
+                                                             uint32_t* __restrict__ critT,
+                                                             uint32_t* __restrict__ critT_sel,
                                                              int* __restrict__ counts) {
   const int r = blockIdx.x * 4 + int(threadIdx.x) / kWave;
   if (r >= rows) return;
-  const int bh = r / nb, i = r % nb;
+  const int bs = r / nb, i = r % nb, b = bs / Hs, sh = bs % Hs;
+  const int64_t kvrow0 = (int64_t(b) * Hkv + sh / kv_div) * nb;
   for (int e = rowptr[r] + int(threadIdx.x) % kWave; e < rowptr[r + 1]; e += kWave) {
     const int j = idx[e];
     if (unsigned(j) < unsigned(nb)) {
       const uint32_t bit = 1u << (i % 32);
+      const int64_t word = (int64_t(bs) * nb + j) * wq + i / 32;
       // a repeated entry (a malformed list) is counted once
-      if ((atomicOr(critT + (int64_t(bh) * nb + j) * wq + i / 32, bit) & bit) == 0u) atomicAdd(counts + bh * nb + j, 1);
+      if ((atomicOr(critT + word, bit) & bit) == 0u) atomicAdd(counts + kvrow0 + j, 1);
+      if (flags != nullptr && (flags[e] & 1u) != 0u) atomicOr(critT_sel + word, bit);
     }
   }
 }
@@ -173,7 +192,11 @@ __device__ __forceinline__ bf16x4 lds_load8(const lds_u8* p) {
 // Writes dQ (linear part, all rows), D_t, and the per-row gradients dS_i ([c][r], bf16), du_i.
 // PROJ: O = O_s + O_l W^T + b, so O_s = O - O_l W^T - b, the gradient reaching O_l is dO W, and
 // O_l is written out (bf16) for the weight gradient.
-template <typename T, int D, bool PROJ>
+// GATED (SALAD): the state is the head's sum over all keys (H_all, z_all, fp32) and
+// O_l = sigmoid(q . w_g) phi(q)^T H_all / (phi(q) . z_all); the gate adds dlogit w_g to dq and
+// dlogit q to the gate weights' gradient (a partial per query block), dlogit = (dO . y) g (1 - g)
+// with y the ungated term.
+template <typename T, int D, bool PROJ, bool GATED>
 __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   constexpr int kKc = D / 32;     // 32-deep k-steps over features
   constexpr int kCt = D / 16;     // 16-wide feature tiles
@@ -184,6 +207,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char dn_sm[kBlock * RB]; // dN_i: [t][c]
   __shared__ float us[D];
   __shared__ float dden_s[kBlock];
+  __shared__ float dlog_s[GATED ? kBlock : 1];
   lds_u8* St = to_lds(st_sm);
   lds_u8* Pq = to_lds(pq_sm);
   lds_u8* Dn = to_lds(dn_sm);
@@ -191,12 +215,23 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
   const int64_t row = int64_t(bh) * p.nb + i;
-  const u16* Sg = p.S + row * D * D;
-  for (int e = t; e < D * D / 8; e += kBwThreads) {
-    const int c = e / (D / 8), r8 = e % (D / 8);
-    lds_store16(St + tpos<D>(c, r8), *reinterpret_cast<const bf16x8*>(Sg + int64_t(c) * D + 8 * r8));
+  // the state: the KV head's over all keys (gated), or the map row's marginal sum (the map row is
+  // the query row: a linear branch takes per-head maps)
+  const int64_t srow = GATED ? int64_t(b) * p.Hkv + h / p.G : row;
+  if constexpr (GATED) {
+    const float* Sg = p.Sf + srow * D * D;
+    for (int e = t; e < D * D / 8; e += kBwThreads) {
+      const int c = e / (D / 8), r8 = e % (D / 8);
+      lds_store16(St + tpos<D>(c, r8), In<float>::load8(Sg + int64_t(c) * D + 8 * r8));
+    }
+  } else {
+    const u16* Sg = p.S + row * D * D;
+    for (int e = t; e < D * D / 8; e += kBwThreads) {
+      const int c = e / (D / 8), r8 = e % (D / 8);
+      lds_store16(St + tpos<D>(c, r8), *reinterpret_cast<const bf16x8*>(Sg + int64_t(c) * D + 8 * r8));
+    }
   }
-  for (int e = t; e < D; e += kBwThreads) us[e] = p.u[row * D + e];
+  for (int e = t; e < D; e += kBwThreads) us[e] = p.u[srow * D + e];
   __syncthreads();
 
   const int tq = kBlock * i + 16 * w + l16;
@@ -207,7 +242,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 
   // phi(q) of this lane's row: B operands (features 32 kc + 8 g .. + 7) and the fp32 denominator
   bf16x8 pqf[kKc];
-  float den = 0.f;
+  float den = 0.f, glog = 0.f;
 #pragma unroll
   for (int kc = 0; kc < kKc; ++kc) {
     float x[8];
@@ -218,12 +253,15 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
     for (int m = 0; m < 8; ++m) {
       ph[m] = qv ? phi(x[m]) : 0.f;           // padded rows take no part
       den += ph[m] * us[32 * kc + 8 * g + m];
+      if constexpr (GATED) glog += x[m] * p.w_gate[int64_t(h) * D + 32 * kc + 8 * g + m];
     }
     pqf[kc] = cvt8(ph);
     lds_store16(Pq + tpos<D>(16 * w + l16, 4 * kc + g), pqf[kc]);
   }
   den = group4_sum(den);
   const float inv_den = (qv && den > 0.f) ? 1.f / den : 0.f;
+  float gate = 1.f;
+  if constexpr (GATED) gate = qv ? 1.f / (1.f + __expf(-group4_sum(glog))) : 0.f;
 
   // O_l^T = S_i^T phi(q)^T: lane holds O_l[t][c = 16 ct + 4 g + e]
   f32x4 xl[kCt];
@@ -279,13 +317,23 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
       *reinterpret_cast<bf16x4*>(p.xlin + (int64_t(bh) * p.N + tq) * D + 16 * ct + 4 * g) = cvt4(xl[ct]);
     }
   } else {
+    // ungated: O_l = y; gated: O_l = gate y, the gradient reaching y is gate dO
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
       const f32x4 oo = qv ? load4_f32(Or + 16 * ct + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsum += go[ct][e] * (oo[e] - xl[ct][e]);
-      ga[ct] = go[ct];
+      for (int e = 0; e < 4; ++e) dsum += go[ct][e] * (oo[e] - gate * xl[ct][e]);
+      ga[ct] = go[ct] * gate;
     }
+  }
+  float dlogit = 0.f;
+  if constexpr (GATED) {
+    float gy = 0.f;                  // dO . y
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gy += go[ct][e] * xl[ct][e];
+    dlogit = group4_sum(gy) * gate * (1.f - gate);
   }
   f32x4 dn[kCt];
 #pragma unroll
@@ -304,6 +352,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   if (g == 0) {
     p.D[int64_t(bh) * p.N + tq] = qv ? dsum : 0.f;
     dden_s[16 * w + l16] = dden;
+    if constexpr (GATED) dlog_s[16 * w + l16] = qv ? dlogit : 0.f;
   }
 
   // dphi(q)^T[r][t] = sum_c S[r][c] dn[t][c] (+ u[r] dden): A = S (transposing reads of the
@@ -324,10 +373,25 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
     const f32x4 qx = qv ? load4_f32(Qb + int64_t(tq) * p.qsN + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = qv ? (acc[e] + us[r0 + e] * dden) * dphi(qx[e]) : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      out[e] = qv ? (acc[e] + us[r0 + e] * dden) * dphi(qx[e]) : 0.f;
+      if constexpr (GATED) out[e] += qv ? dlogit * p.w_gate[int64_t(h) * D + r0 + e] : 0.f;
+    }
     *reinterpret_cast<f32x4*>(dqr + r0) = out;
   }
   __syncthreads();                // phi(Q_i), dN_i and dden complete in LDS
+  if constexpr (GATED) {
+    // the gate weights' partial gradient of this query block: sum over its rows of dlogit_t q_t
+    for (int r = t; r < D; r += kBwThreads) {
+      float s = 0.f;
+      for (int tt = 0; tt < kBlock && kBlock * i + tt < p.n_valid; ++tt) {
+        float x[8];
+        In<T>::load8_f32(Qb + int64_t(kBlock * i + tt) * p.qsN + 8 * (r / 8), x);
+        s += dlog_s[tt] * x[r % 8];
+      }
+      p.gpart[row * D + r] = s;
+    }
+  }
 
   // dS_i[r][c] = sum_t phi(q_t)[r] dn_t[c], stored [c][r]: wave w covers (rt, ct) tiles
   // n = w, w + 4, ... of the kCt x kCt grid; the k steps run over the 64 query rows
@@ -361,9 +425,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ linear branch, key side
 
-// One workgroup per (key block j, head); wavefront w owns keys 64 j + 16 w + l % 16.
+// One workgroup per (key block j, KV head g); wavefront w owns keys 64 j + 16 w + l % 16.
 // Writes dK and dV (linear part, all rows): dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k); with
-// smooth-K, phi and its derivative at the shifted key k - mean.
+// smooth-K, phi and its derivative at the shifted key k - mean.  dH_j and dz_j are summed over
+// the query heads that read KV head g (one per head: each head has its own map and queries).
 template <typename T, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
   constexpr int kKc = D / 32;
@@ -373,21 +438,41 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
   __shared__ float dzs[D];
   lds_u8* Ht = to_lds(dh_sm);
 
-  const int j = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int j = blockIdx.x, bh = blockIdx.y, b = bh / p.Hkv, gk = bh % p.Hkv;
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
-  const int64_t row = int64_t(bh) * p.nb + j;
-  const u16* Hg = p.dH + row * D * D;
+  // the state gradient of query head h for this key block: its own, or (SALAD) the head's one
+  // state over all keys
+  auto srow = [&](int h) -> int64_t {
+    const int64_t hrow = int64_t(b) * p.H + h;
+    return p.gated ? hrow : hrow * p.nb + j;
+  };
+  const int h0 = gk * p.G;
   for (int e = t; e < D * D / 8; e += kBwThreads) {
     const int c = e / (D / 8), r8 = e % (D / 8);
-    lds_store16(Ht + tpos<D>(c, r8), *reinterpret_cast<const bf16x8*>(Hg + int64_t(c) * D + 8 * r8));
+    float acc[8];
+    In<bf16raw>::load8_f32(reinterpret_cast<const bf16raw*>(p.dH + srow(h0) * D * D + int64_t(c) * D + 8 * r8), acc);
+    for (int hh = 1; hh < p.G; ++hh) {
+      float x[8];
+      In<bf16raw>::load8_f32(reinterpret_cast<const bf16raw*>(p.dH + srow(h0 + hh) * D * D + int64_t(c) * D + 8 * r8), x);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] += x[m];
+    }
+    f32x8 a8;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) a8[m] = acc[m];
+    lds_store16(Ht + tpos<D>(c, r8), cvt8(a8));
   }
-  for (int e = t; e < D; e += kBwThreads) dzs[e] = p.dz[row * D + e];
+  for (int e = t; e < D; e += kBwThreads) {
+    float z = 0.f;
+    for (int hh = 0; hh < p.G; ++hh) z += p.dz[srow(h0 + hh) * D + e];
+    dzs[e] = z;
+  }
   __syncthreads();
 
   const int s = kBlock * j + 16 * w + l16;
   const bool kv = s < p.n_valid;
-  const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(h) * p.ksH + int64_t(s) * p.ksN;
-  const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(h) * p.vsH + int64_t(s) * p.vsN;
+  const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(gk) * p.ksH + int64_t(s) * p.ksN;
+  const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(gk) * p.vsH + int64_t(s) * p.vsN;
   bf16x8 vf[kKc], pkf[kKc];
 #pragma unroll
   for (int kc = 0; kc < kKc; ++kc) {
@@ -543,10 +628,13 @@ __device__ __forceinline__ void zero_rows(lds_u8* tile, int r0) {
     lds_store16(tile + tpos<D>(r0 + e / kChunks, e % kChunks), zero8());
 }
 
-// One workgroup per (query block i, head); wavefront w owns query rows 64 i + 16 w + l % 16.
-// Over the row's critical blocks: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
-// K and V tiles are double-buffered: the next block's direct-to-LDS copies run during this one.
-template <typename T, int D>
+// One workgroup per (query block i, query head h); wavefront w owns query rows 64 i + 16 w + l % 16.
+// Over the blocks of the row's map (the head's own, or its GQA group's): S^T = K Q^T,
+// dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T, with K and V of the group's KV head.
+// CAUSAL (NSA-style maps): key s of block j is allowed iff s <= t and (j is a selected block or
+// t - s < window).  K and V tiles are double-buffered: the next block's direct-to-LDS copies run
+// during this one.
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
@@ -555,29 +643,33 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v_sm[2][Tl::kTileB];
 
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int gk = h / p.G;                          // KV head
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
-  const int64_t row = int64_t(bh) * p.nb + i;
+  const int64_t row = (int64_t(b) * p.Hs + (p.group_map ? gk : h)) * p.nb + i;   // map row
   const int tq = kBlock * i + 16 * w + l16;
   const bool qv = tq < p.n_valid;
   const T* Qr = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH + int64_t(tq) * p.qsN;
   const T* Gr = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH + int64_t(tq) * p.dsN;
-  const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(h) * p.ksH;
-  const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(h) * p.vsH;
+  const T* K = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(gk) * p.ksH;
+  const T* V = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(gk) * p.vsH;
   const StageOff<D, kBwWaves> koff = stage_offsets<D, false, kBwWaves>(p.ksN);
   const StageOff<D, kBwWaves> voff = stage_offsets<D, false, kBwWaves>(p.vsN);
 
   const int cbeg = p.crit_rowptr[row], cend = p.crit_rowptr[row + 1];
-  // the row's next valid block index at or after list position e (or -1), wave-uniform
-  auto next_block = [&](int& e) -> int {
+  // the row's next valid block index at or after list position e (or -1), wave-uniform; sel: its
+  // selected flag (causal maps)
+  auto next_block = [&](int& e, bool& sel) -> int {
     while (e < cend) {
       const int jraw = __builtin_amdgcn_readfirstlane(p.crit_idx[e]);
+      if constexpr (CAUSAL) sel = (__builtin_amdgcn_readfirstlane(int(p.crit_flags[e])) & 1) != 0;
       ++e;
       if (unsigned(jraw) < unsigned(p.nb)) return jraw;   // malformed entries are skipped
     }
     return -1;
   };
   int epos = cbeg;
-  int cur = next_block(epos);
+  bool sel_cur = true, sel_nxt = true;
+  int cur = next_block(epos, sel_cur);
   if (cur >= 0) {
     stage_tile<T, D, false, kBwWaves>(K, p.ksN, cur, to_lds(k_sm[0]), koff);
     stage_tile<T, D, false, kBwWaves>(V, p.vsN, cur, to_lds(v_sm[0]), voff);
@@ -600,7 +692,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 
   int buf = 0;
   while (cur >= 0) {
-    const int nxt = next_block(epos);
+    const int nxt = next_block(epos, sel_nxt);
     lds_u8* Kt = to_lds(k_sm[buf]);
     lds_u8* Vt = to_lds(v_sm[buf]);
     SLA_WAIT_VMCNT(0);               // this block's copies have landed ...
@@ -630,7 +722,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
       f32x4 ds;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const bool ok = has && 16 * st + 4 * g + e4 < rv;
+        bool ok = has && 16 * st + 4 * g + e4 < rv;
+        if constexpr (CAUSAL) {
+          const int sk = kBlock * cur + 16 * st + 4 * g + e4;
+          ok = ok && sk <= tq && (sel_cur || tq - sk < p.window);
+        }
         const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -lse2)) : 0.f;
         ds[e4] = ok ? pr * (pacc[e4] - Dt) : 0.f;
       }
@@ -646,11 +742,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
         acc[rt] = mfma16(a, join(dsb[2 * pr], dsb[2 * pr + 1]), acc[rt]);
       }
     cur = nxt;
+    sel_cur = sel_nxt;
     buf ^= 1;
   }
-  // lane holds dQ^T[r = 16 rt + 4 g + e][t]: add to the linear part
-  if (qv) {
-    float* dqr = p.dq + (int64_t(bh) * p.N + tq) * D;
+  // lane holds dQ^T[r = 16 rt + 4 g + e][t]: added to the linear part, or written (no linear branch;
+  // padded rows then get their zeros here)
+  float* dqr = p.dq + (int64_t(bh) * p.N + tq) * D;
+  if (p.overwrite) {
+#pragma unroll
+    for (int rt = 0; rt < kCt; ++rt)
+      *reinterpret_cast<f32x4*>(dqr + 16 * rt + 4 * g) = qv ? acc[rt] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (qv) {
 #pragma unroll
     for (int rt = 0; rt < kCt; ++rt) {
       f32x4* q4 = reinterpret_cast<f32x4*>(dqr + 16 * rt + 4 * g);
@@ -665,14 +767,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
 // (counted by crit_transpose_kernel), most-used first, so the longest workgroups start first and
 // the round-robin dispatch spreads them over the XCDs.  One workgroup: a histogram of the counts in
 // LDS, a descending scan (one wavefront: per-lane runs, then a wave scan of the run sums), a scatter (the order within one count is arbitrary; results do not depend
-// on the order).  Counts are at most nb <= 4096.
+// on the order).  Counts above max_count <= 4096 rank as max_count.
 __global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ counts, int rows, int max_count,
                                                         int* __restrict__ order) {
   __shared__ int hist[kMaxKeyBlocksBwd + 2];
   const int t = threadIdx.x;
   for (int c = t; c <= max_count + 1; c += 1024) hist[c] = 0;
   __syncthreads();
-  for (int r = t; r < rows; r += 1024) atomicAdd(&hist[counts[r]], 1);
+  for (int r = t; r < rows; r += 1024) atomicAdd(&hist[min(counts[r], max_count)], 1);
   __syncthreads();
   if (t < kWave) {                                // exclusive scan from the largest count down:
     const int n = max_count + 1;                  // lane l takes descending positions l*per .. l*per+per-1
@@ -700,14 +802,15 @@ __global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ 
     }
   }
   __syncthreads();
-  for (int r = t; r < rows; r += 1024) order[atomicAdd(&hist[counts[r]], 1)] = r;
+  for (int r = t; r < rows; r += 1024) order[atomicAdd(&hist[min(counts[r], max_count)], 1)] = r;
 }
 
-// One workgroup per (key block j, head); wavefront w owns keys 64 j + 16 w + l % 16.  Over the
-// query blocks i that list j as critical: S = Q K^T, dP = dO V^T, dS = P (dP - D),
-// dV^T += dO^T P, dK^T += Q^T dS.  Q, dO tiles and the rows' log-sum-exp and D are
-// double-buffered: the next query block's direct-to-LDS copies run during this one.
-template <typename T, int D>
+// One workgroup per (key block j, KV head g); wavefront w owns keys 64 j + 16 w + l % 16.  Over
+// the query heads h of the group and, for each, the query blocks i whose map row lists j:
+// S = Q K^T, dP = dO V^T, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Q, dO tiles and the
+// rows' log-sum-exp and D are double-buffered: the next (head, query block)'s direct-to-LDS copies
+// run during this one.  CAUSAL: the masks of the dQ kernel (s <= t and (selected or t - s < window)).
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
@@ -717,47 +820,58 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lse_s[2][kBlock];
   __shared__ __attribute__((aligned(256))) float d_s[2][kBlock];
 
-  const int krow = p.kv_order[blockIdx.x];        // (bh, j), most-used key blocks first
-  const int j = krow % p.nb, bh = krow / p.nb, b = bh / p.H, h = bh % p.H;
+  const int krow = p.kv_order[blockIdx.x];        // (b, g, j), most-used key blocks first
+  const int j = krow % p.nb, bk = krow / p.nb, b = bk / p.Hkv, gk = bk % p.Hkv;
   const int t = threadIdx.x, lane = t % kWave, l16 = lane % 16, g = lane / 16;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
   const int s = kBlock * j + 16 * w + l16;
   const bool kv = s < p.n_valid;
-  const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(h) * p.ksH + int64_t(s) * p.ksN;
-  const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(h) * p.vsH + int64_t(s) * p.vsN;
-  const T* Q = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
-  const T* G = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH;
-  const float* lse_h = p.lse + int64_t(bh) * p.N;
-  const float* D_h = p.D + int64_t(bh) * p.N;
+  const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(gk) * p.ksH + int64_t(s) * p.ksN;
+  const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(gk) * p.vsH + int64_t(s) * p.vsN;
   const StageOff<D, kBwWaves> qoff = stage_offsets<D, false, kBwWaves>(p.qsN);
   const StageOff<D, kBwWaves> goff = stage_offsets<D, false, kBwWaves>(p.dsN);
+  const int h0 = gk * p.G;
 
-  // the query blocks that list j, ascending: a wave-uniform scan of the transposed bit row
-  const uint32_t* bits = p.critT + (int64_t(bh) * p.nb + j) * p.wq;
-  int word = 0;
-  uint32_t m = 0u;
-  auto next_block = [&]() -> int {
+  // the (head, query block) pairs that list j, heads ascending, then query blocks ascending: a
+  // wave-uniform scan of the transposed bit rows (the group's one row G times with shared maps)
+  int hh = 0, word = 0;
+  uint32_t m = 0u, msel = 0u;
+  auto next_block = [&](int& head, bool& sel) -> int {
     while (m == 0u) {
-      if (word >= p.wq) return -1;
-      m = __builtin_amdgcn_readfirstlane(bits[word]);
+      if (word >= p.wq) {
+        if (hh + 1 >= p.G) return -1;
+        ++hh;
+        word = 0;
+        continue;
+      }
+      const int64_t brow = (int64_t(b) * p.Hs + (p.group_map ? gk : h0 + hh)) * p.nb + j;
+      m = __builtin_amdgcn_readfirstlane(p.critT[brow * p.wq + word]);
+      if constexpr (CAUSAL) msel = __builtin_amdgcn_readfirstlane(p.critT_sel[brow * p.wq + word]);
       ++word;
     }
-    const int i = 32 * (word - 1) + __builtin_ctz(m);
+    const int bit = __builtin_ctz(m);
     m &= m - 1u;
-    return i;
+    head = h0 + hh;
+    if constexpr (CAUSAL) sel = ((msel >> bit) & 1u) != 0u;
+    return 32 * (word - 1) + bit;
   };
-  // copies of query block i into buffer bf: Q and dO tiles by every wavefront, the 64 rows'
-  // log-sum-exp and D (256 bytes each) by wavefront 0
-  auto stage = [&](int i, int bf) {
+  // copies of query block i of head h into buffer bf: Q and dO tiles by every wavefront, the 64
+  // rows' log-sum-exp and D (256 bytes each) by wavefront 0
+  auto stage = [&](int i, int h, int bf) {
+    const T* Q = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
+    const T* G = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH;
     stage_tile<T, D, false, kBwWaves>(Q, p.qsN, i, to_lds(q_sm[bf]), qoff);
     stage_tile<T, D, false, kBwWaves>(G, p.dsN, i, to_lds(g_sm[bf]), goff);
     if (w == 0) {
-      load_lds4_sbase(lse_h + kBlock * i, uint32_t(4 * lane), to_lds(lse_s[bf]));
-      load_lds4_sbase(D_h + kBlock * i, uint32_t(4 * lane), to_lds(d_s[bf]));
+      const int64_t r0 = (int64_t(b) * p.H + h) * p.N + kBlock * i;
+      load_lds4_sbase(p.lse + r0, uint32_t(4 * lane), to_lds(lse_s[bf]));
+      load_lds4_sbase(p.D + r0, uint32_t(4 * lane), to_lds(d_s[bf]));
     }
   };
-  int cur = next_block();
-  if (cur >= 0) stage(cur, 0);
+  int h_cur = h0, h_nxt = h0;
+  bool sel_cur = true, sel_nxt = true;
+  int cur = next_block(h_cur, sel_cur);
+  if (cur >= 0) stage(cur, h_cur, 0);
 
   bf16x8 kf[kKc], vf[kKc];
 #pragma unroll
@@ -775,7 +889,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
 
   int buf = 0;
   while (cur >= 0) {
-    const int nxt = next_block();
+    const int nxt = next_block(h_nxt, sel_nxt);
     lds_u8* Qt = to_lds(q_sm[buf]);
     lds_u8* Gt = to_lds(g_sm[buf]);
     SLA_WAIT_VMCNT(0);               // this block's copies have landed ...
@@ -788,7 +902,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
     }
-    if (nxt >= 0) stage(nxt, buf ^ 1);
+    if (nxt >= 0) stage(nxt, h_nxt, buf ^ 1);
     bf16x4 pb[4], db[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -804,7 +918,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
       f32x4 pr, ds;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const bool ok = kv && 16 * tt + 4 * g + e4 < rq && l4[e4] > -__builtin_inff();
+        bool ok = kv && 16 * tt + 4 * g + e4 < rq && l4[e4] > -__builtin_inff();
+        if constexpr (CAUSAL) {
+          const int tq = kBlock * cur + 16 * tt + 4 * g + e4;
+          ok = ok && s <= tq && (sel_cur || tq - s < p.window);
+        }
         pr[e4] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e4], c2, -l4[e4] * kLog2e)) : 0.f;
         ds[e4] = ok ? pr[e4] * (pacc[e4] - d4[e4]) : 0.f;
       }
@@ -824,22 +942,74 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
         dk[ct] = mfma16(aq, join(db[2 * pr], db[2 * pr + 1]), dk[ct]);
       }
     cur = nxt;
+    h_cur = h_nxt;
+    sel_cur = sel_nxt;
     buf ^= 1;
   }
-  if (kv) {
-    float* dkr = p.dk + (int64_t(bh) * p.N + s) * D;
-    float* dvr = p.dv + (int64_t(bh) * p.N + s) * D;
+  float* dkr = p.dk + (int64_t(bk) * p.N + s) * D;
+  float* dvr = p.dv + (int64_t(bk) * p.N + s) * D;
+  if (p.overwrite) {                 // no linear branch: this kernel writes every row (padded: 0)
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      *reinterpret_cast<f32x4*>(dkr + 16 * ct + 4 * g) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else if (kv) {
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
       f32x4* k4 = reinterpret_cast<f32x4*>(dkr + 16 * ct + 4 * g);
       f32x4* v4 = reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g);
       f32x4 add = dk[ct] * p.scale;
       // smooth-K: the linear branch saw k - mean(k), so its dK loses its own mean over the valid rows
-      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bh) * D + 16 * ct + 4 * g);
+      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + 16 * ct + 4 * g);
       *k4 = *k4 + add;
       *v4 = *v4 + dv[ct];
     }
   }
+}
+
+// D_t = dO_t . O_t for every row (no linear branch: O_sparse = O): 16 lanes per row, fp32 sums.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p, int rows) {
+  const int r = blockIdx.x * 16 + int(threadIdx.x) / 16, l = int(threadIdx.x) % 16;
+  if (r >= rows) return;
+  const int tq = r % p.N, bh = r / p.N, b = bh / p.H, h = bh % p.H;
+  float acc = 0.f;
+  if (tq < p.n_valid) {
+    const T* Or = static_cast<const T*>(p.o) + int64_t(b) * p.osB + int64_t(h) * p.osH + int64_t(tq) * p.osN;
+    const T* Gr = static_cast<const T*>(p.dout) + int64_t(b) * p.dsB + int64_t(h) * p.dsH + int64_t(tq) * p.dsN;
+#pragma unroll
+    for (int c = 8 * l; c < D; c += 128) {
+      float x[8], y[8];
+      In<T>::load8_f32(Or + c, x);
+      In<T>::load8_f32(Gr + c, y);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc += x[m] * y[m];
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+  if (l == 0) p.D[r] = acc;
+}
+
+// SALAD: dw_gate[h][r] = sum over b and the query blocks i of gpart[(b, h, i)][r], in order.
+__global__ __launch_bounds__(256) void gate_reduce_kernel(const float* __restrict__ gpart, int B, int H, int nb, int d,
+                                                          float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= H * d) return;
+  const int h = e / d, r = e % d;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < nb; ++i) s += gpart[((int64_t(b) * H + h) * nb + i) * d + r];
+  out[e] = s;
+}
+
+// One bit per query block of every row: word w of a row holds blocks 32 w .. 32 w + 31 below nb.
+__global__ __launch_bounds__(256) void ones_bits_kernel(uint32_t* __restrict__ bits, int rows, int nb, int wq) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= int64_t(rows) * wq) return;
+  const int word = int(e % wq), n = min(32, nb - 32 * word);
+  bits[e] = n >= 32 ? ~0u : (1u << n) - 1u;
 }
 
 struct BwdWs {
@@ -849,6 +1019,7 @@ struct BwdWs {
   u16* dH;
   float* dz;
   uint32_t* critT;
+  uint32_t* critT_sel;
   uint32_t* margT;
   int* kv_counts;
   int* kv_order;
@@ -856,34 +1027,50 @@ struct BwdWs {
   u16* xlin;
   float* partW;
   float* partB;
+  float* gpart;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 constexpr int kProjChunk = 16;   // query blocks per partial of the Proj weight gradient
 
-static size_t bwd_ws_layout(int B, int H, int N, int d, bool proj, BwdWs* ws, void* base) {
-  const int64_t nb = N / kBlock, rows = int64_t(B) * H * nb, wq = (nb + 31) / 32;
-  const int64_t parts = proj ? int64_t(B) * H * ((nb + kProjChunk - 1) / kProjChunk) : 0;
+// The shapes a backward call works on: B, Hq query heads, Hkv KV heads, Hs map heads, N, d.
+struct BwdShape {
+  int B, Hq, Hkv, Hs, N, d, lin, causal, proj;
+};
+
+static size_t bwd_ws_layout(const BwdShape& sh, BwdWs* ws, void* base) {
+  const int64_t nb = sh.N / kBlock, wq = (nb + 31) / 32;
+  const int64_t qrows = int64_t(sh.B) * sh.Hq * nb;          // query-head rows (b, h, i)
+  const int64_t mrows = int64_t(sh.B) * sh.Hs * nb;          // map rows
+  const int64_t krows = int64_t(sh.B) * sh.Hkv * nb;         // key-block rows (b, g, j)
+  const bool lin = sh.lin != SLA_LIN_NONE, gated = sh.lin == SLA_LIN_GLOBAL_GATED;
+  const int64_t hrows = gated ? int64_t(sh.B) * sh.Hq : qrows;   // rows of dH, dz
+  const int64_t parts = sh.proj ? int64_t(sh.B) * sh.Hq * ((nb + kProjChunk - 1) / kProjChunk) : 0;
+  const size_t d = size_t(sh.d);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += align256(bytes);
     return o;
   };
-  const size_t oD = take(size_t(B) * H * N * 4);
-  const size_t odS = take(size_t(rows) * d * d * 2);
-  const size_t odu = take(size_t(rows) * d * 4);
-  const size_t odH = take(size_t(rows) * d * d * 2);
-  const size_t odz = take(size_t(rows) * d * 4);
-  const size_t oc = take(size_t(rows) * wq * 4);
-  const size_t om = take(size_t(rows) * wq * 4);
-  const size_t okc = take(size_t(rows) * 4);
-  const size_t oko = take(size_t(rows) * 4);
-  const size_t okm = take(size_t(B) * H * d * 4);
-  const size_t ox = take(proj ? size_t(B) * H * N * d * 2 : 0);
+  const size_t oD = take(size_t(sh.B) * sh.Hq * sh.N * 4);
+  const size_t odS = take(lin ? size_t(qrows) * d * d * 2 : 0);
+  const size_t odu = take(lin ? size_t(qrows) * d * 4 : 0);
+  const size_t odH = take(lin ? size_t(hrows) * d * d * 2 : 0);
+  const size_t odz = take(lin ? size_t(hrows) * d * 4 : 0);
+  const size_t oc = take(size_t(mrows) * wq * 4);
+  const size_t ocs = take(sh.causal ? size_t(mrows) * wq * 4 : 0);
+  // transposed marginal masks, or (gated) the all-ones masks of the per-head state sums
+  const size_t om = take(sh.lin == SLA_LIN_ROW_STATES ? size_t(qrows) * wq * 4
+                                                      : gated ? size_t(sh.B) * sh.Hq * wq * 4 : 0);
+  const size_t okc = take(size_t(krows) * 4);
+  const size_t oko = take(size_t(krows) * 4);
+  const size_t okm = take(lin ? size_t(sh.B) * sh.Hkv * d * 4 : 0);
+  const size_t ox = take(sh.proj ? size_t(sh.B) * sh.Hq * sh.N * d * 2 : 0);
   const size_t opw = take(size_t(parts) * d * d * 4);
   const size_t opb = take(size_t(parts) * d * 4);
+  const size_t og = take(gated ? size_t(qrows) * d * 4 : 0);
   if (ws != nullptr) {
     unsigned char* p = static_cast<unsigned char*>(base);
     ws->D = reinterpret_cast<float*>(p + oD);
@@ -892,6 +1079,7 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, bool proj, BwdWs* ws, vo
     ws->dH = reinterpret_cast<u16*>(p + odH);
     ws->dz = reinterpret_cast<float*>(p + odz);
     ws->critT = reinterpret_cast<uint32_t*>(p + oc);
+    ws->critT_sel = reinterpret_cast<uint32_t*>(p + ocs);
     ws->margT = reinterpret_cast<uint32_t*>(p + om);
     ws->kv_counts = reinterpret_cast<int*>(p + okc);
     ws->kv_order = reinterpret_cast<int*>(p + oko);
@@ -899,25 +1087,40 @@ static size_t bwd_ws_layout(int B, int H, int N, int d, bool proj, BwdWs* ws, vo
     ws->xlin = reinterpret_cast<u16*>(p + ox);
     ws->partW = reinterpret_cast<float*>(p + opw);
     ws->partB = reinterpret_cast<float*>(p + opb);
+    ws->gpart = reinterpret_cast<float*>(p + og);
   }
   return off;
 }
 
 template <typename T, int D>
-static void launch_bwd_kernels(const BwdParams& p, int BH, hipStream_t st) {
-  const dim3 grid(p.nb, BH);
-  if (p.proj_w != nullptr) bwd_lin_q_kernel<T, D, true><<<grid, kBwThreads, 0, st>>>(p);
-  else bwd_lin_q_kernel<T, D, false><<<grid, kBwThreads, 0, st>>>(p);
+static void launch_bwd_q_side(const BwdParams& p, int B, hipStream_t st) {
+  const dim3 grid(p.nb, B * p.H);
+  if (p.gated) bwd_lin_q_kernel<T, D, false, true><<<grid, kBwThreads, 0, st>>>(p);
+  else if (p.proj_w != nullptr) bwd_lin_q_kernel<T, D, true, false><<<grid, kBwThreads, 0, st>>>(p);
+  else if (p.S != nullptr) bwd_lin_q_kernel<T, D, false, false><<<grid, kBwThreads, 0, st>>>(p);
+  else {
+    const int rows = B * p.H * p.N;
+    bwd_dot_kernel<T, D><<<dim3((rows + 15) / 16), 256, 0, st>>>(p, rows);
+  }
 }
 
 template <typename T, int D>
-static void launch_bwd_k_side(const BwdParams& p, int BH, hipStream_t st) {
-  const dim3 grid(p.nb, BH);
-  bwd_lin_k_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
-  if (p.dk_mean != nullptr)
-    dk_mean_kernel<<<dim3(D / 8, BH), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
-  bwd_dq_kernel<T, D><<<grid, kBwThreads, 0, st>>>(p);
-  bwd_dkdv_kernel<T, D><<<dim3(p.nb * BH), kBwThreads, 0, st>>>(p);
+static void launch_bwd_k_side(const BwdParams& p, int B, bool lin, hipStream_t st) {
+  const int BK = B * p.Hkv;
+  if (lin) {
+    bwd_lin_k_kernel<T, D><<<dim3(p.nb, BK), kBwThreads, 0, st>>>(p);
+    if (p.dk_mean != nullptr)
+      dk_mean_kernel<<<dim3(D / 8, BK), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
+  }
+  const dim3 qgrid(p.nb, B * p.H);
+  const dim3 kgrid(p.nb * BK);
+  if (p.critT_sel != nullptr) {
+    bwd_dq_kernel<T, D, true><<<qgrid, kBwThreads, 0, st>>>(p);
+    bwd_dkdv_kernel<T, D, true><<<kgrid, kBwThreads, 0, st>>>(p);
+  } else {
+    bwd_dq_kernel<T, D, false><<<qgrid, kBwThreads, 0, st>>>(p);
+    bwd_dkdv_kernel<T, D, false><<<kgrid, kBwThreads, 0, st>>>(p);
+  }
 }
 
 // dW (and db) of the Proj layer: partials over chunks of query blocks, then their ordered sums.
@@ -932,12 +1135,193 @@ static void launch_proj_grad(const BwdParams& p, int B, int per_head, const BwdW
   if (db != nullptr) proj_reduce_kernel<<<dim3(1, weights), 256, 0, st>>>(ws.partB, parts, D, db);
 }
 
+template <typename F>
+static void by_type(int dtype, int d, F&& f) {
+  // f is a generic lambda called with (T{}, integral_constant<D>)
+  if (d == 128) {
+    if (dtype == SLA_BF16) f(bf16raw{}, std::integral_constant<int, 128>{});
+    else f(float{}, std::integral_constant<int, 128>{});
+  } else {
+    if (dtype == SLA_BF16) f(bf16raw{}, std::integral_constant<int, 64>{});
+    else f(float{}, std::integral_constant<int, 64>{});
+  }
+}
+
+static bool bwd_shape_of(int B, int Hq, int Hkv, int N, int d, int lin, int causal, int group_map, int proj_heads,
+                         BwdShape* sh) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < kBlock || N % kBlock != 0 || (d != 64 && d != 128))
+    return false;
+  if (N / kBlock > SLA_MAX_KEY_BLOCKS) return false;
+  if (lin != SLA_LIN_NONE && lin != SLA_LIN_ROW_STATES && lin != SLA_LIN_GLOBAL_GATED) return false;
+  if (lin != SLA_LIN_NONE && (causal || group_map)) return false;
+  if (proj_heads != 0 && (lin != SLA_LIN_ROW_STATES || (proj_heads != 1 && proj_heads != Hq))) return false;
+  *sh = BwdShape{B, Hq, Hkv, group_map ? Hkv : Hq, N, d, lin, causal ? 1 : 0, proj_heads != 0 ? 1 : 0};
+  return true;
+}
+
 }  // namespace sla
 
+extern "C" size_t sla_attn_bwd_ext_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                                                   int32_t lin_mode, int32_t causal, int32_t group_map,
+                                                   int32_t proj_heads) {
+  sla::BwdShape sh{};
+  if (!sla::bwd_shape_of(B, Hq, Hkv, N, d, lin_mode, causal, group_map, proj_heads, &sh)) return 0;
+  return sla::bwd_ws_layout(sh, nullptr, nullptr);
+}
+
 extern "C" size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, int32_t proj_heads) {
-  if (B < 1 || H < 1 || N < sla::kBlock || N % sla::kBlock != 0 || (d != 64 && d != 128)) return 0;
   if (proj_heads != 0 && proj_heads != 1 && proj_heads != H) return 0;
-  return sla::bwd_ws_layout(B, H, N, d, proj_heads != 0, nullptr, nullptr);
+  return sla_attn_bwd_ext_workspace_bytes(B, H, H, N, d, SLA_LIN_ROW_STATES, 0, 0, proj_heads);
+}
+
+extern "C" sla_status sla_attn_bwd_ext(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
+                                       const sla_tensor* o, const sla_tensor* dout, const float* lse,
+                                       int32_t n_valid, float scale, int32_t lin_mode, int32_t causal,
+                                       int32_t window_tokens, int32_t group_map, const int32_t* crit_rowptr,
+                                       const int32_t* crit_idx, const uint8_t* crit_flags,
+                                       const uint32_t* marg_bits, const void* S, const float* u,
+                                       const float* H_all, const float* z_all, const float* w_gate,
+                                       const float* k_shift, const float* proj_w, const float* proj_b,
+                                       int32_t proj_heads, float* dq, float* dk, float* dv, float* dproj_w,
+                                       float* dproj_b, float* dw_gate, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  using namespace sla;
+  sla_status st = check_tensor(q);
+  if (st != SLA_OK) return st;
+  if ((st = check_tensor(k)) != SLA_OK) return st;
+  if ((st = check_tensor(v)) != SLA_OK) return st;
+  if ((st = check_tensor(o)) != SLA_OK) return st;
+  if ((st = check_tensor(dout)) != SLA_OK) return st;
+  if (!same_geometry(q, k) || !same_geometry(k, v) || !same_geometry(q, o) || !same_geometry(q, dout))
+    return SLA_ERR_SHAPE;
+  if (v->H != k->H || o->H != q->H || dout->H != q->H || q->H % k->H != 0) return SLA_ERR_SHAPE;
+  if ((st = check_valid_len(n_valid, q->N)) != SLA_OK) return st;
+  if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
+  if (lin_mode != SLA_LIN_NONE && lin_mode != SLA_LIN_ROW_STATES && lin_mode != SLA_LIN_GLOBAL_GATED)
+    return SLA_ERR_UNSUPPORTED;
+  if (lin_mode != SLA_LIN_NONE && (causal != 0 || group_map != 0)) return SLA_ERR_UNSUPPORTED;
+  if (causal != 0 && crit_flags == nullptr) return SLA_ERR_NULL;
+  if (causal != 0 && window_tokens < 0) return SLA_ERR_RANGE;
+  if (lse == nullptr || crit_rowptr == nullptr || crit_idx == nullptr || dq == nullptr || dk == nullptr ||
+      dv == nullptr)
+    return SLA_ERR_NULL;
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return SLA_ERR_ALIGN;
+  const bool rowst = lin_mode == SLA_LIN_ROW_STATES, gated = lin_mode == SLA_LIN_GLOBAL_GATED;
+  if (rowst && (marg_bits == nullptr || S == nullptr || u == nullptr)) return SLA_ERR_NULL;
+  if (rowst && (!aligned16(S) || !aligned16(u))) return SLA_ERR_ALIGN;
+  if (gated && (H_all == nullptr || z_all == nullptr || w_gate == nullptr || dw_gate == nullptr)) return SLA_ERR_NULL;
+  if (gated && (!aligned16(H_all) || !aligned16(z_all) || !aligned16(w_gate) || !aligned16(dw_gate)))
+    return SLA_ERR_ALIGN;
+  if (!gated && dw_gate != nullptr) return SLA_ERR_NULL;
+  const bool proj = proj_w != nullptr;
+  if (!proj && (proj_b != nullptr || dproj_w != nullptr || dproj_b != nullptr)) return SLA_ERR_NULL;
+  if (proj) {
+    if (!rowst) return SLA_ERR_UNSUPPORTED;
+    if (dproj_w == nullptr) return SLA_ERR_NULL;
+    if (proj_heads != 1 && proj_heads != q->H) return SLA_ERR_SHAPE;
+    if (!aligned16(proj_w) || !aligned16(dproj_w) || (proj_b != nullptr && !aligned16(proj_b)) ||
+        (dproj_b != nullptr && !aligned16(dproj_b)))
+      return SLA_ERR_ALIGN;
+  }
+  if (k_shift != nullptr && (lin_mode == SLA_LIN_NONE)) return SLA_ERR_UNSUPPORTED;
+  if (k_shift != nullptr && !aligned16(k_shift)) return SLA_ERR_ALIGN;
+  const int d = q->d, B = q->B, Hq = q->H, Hkv = k->H, N = q->N, nb = N / kBlock;
+  if (nb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
+  BwdShape sh{};
+  if (!bwd_shape_of(B, Hq, Hkv, N, d, lin_mode, causal, group_map, proj ? proj_heads : 0, &sh))
+    return SLA_ERR_UNSUPPORTED;
+  const size_t need = bwd_ws_layout(sh, nullptr, nullptr);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
+  BwdWs ws{};
+  bwd_ws_layout(sh, &ws, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  BwdParams p{};
+  p.q = q->ptr; p.k = k->ptr; p.v = v->ptr; p.o = o->ptr; p.dout = dout->ptr;
+  p.qsB = q->sB; p.qsH = q->sH; p.qsN = q->sN;
+  p.ksB = k->sB; p.ksH = k->sH; p.ksN = k->sN;
+  p.vsB = v->sB; p.vsH = v->sH; p.vsN = v->sN;
+  p.osB = o->sB; p.osH = o->sH; p.osN = o->sN;
+  p.dsB = dout->sB; p.dsH = dout->sH; p.dsN = dout->sN;
+  p.H = Hq; p.N = N; p.nb = nb; p.n_valid = n_valid; p.wq = (nb + 31) / 32;
+  p.Hkv = Hkv; p.G = Hq / Hkv; p.Hs = sh.Hs; p.group_map = group_map ? 1 : 0;
+  p.window = causal ? window_tokens : 0;
+  p.overwrite = lin_mode == SLA_LIN_NONE ? 1 : 0;
+  p.gated = gated ? 1 : 0;
+  p.scale = scale; p.scale_log2 = scale * kLog2e;
+  p.lse = lse; p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx;
+  p.crit_flags = causal ? crit_flags : nullptr;
+  p.critT_sel = causal ? ws.critT_sel : nullptr;
+  if (rowst) {
+    p.S = static_cast<const u16*>(S);
+    p.u = u;
+  }
+  if (gated) {
+    p.Sf = H_all;
+    p.u = z_all;
+    p.w_gate = w_gate;
+    p.gpart = ws.gpart;
+  }
+  p.D = ws.D; p.dS = ws.dS; p.du = ws.du; p.dH = ws.dH; p.dz = ws.dz; p.critT = ws.critT;
+  p.kv_order = ws.kv_order;
+  p.k_shift = k_shift;
+  p.dk_mean = k_shift != nullptr ? ws.dk_mean : nullptr;
+  if (proj) {
+    p.proj_w = proj_w; p.proj_b = proj_b;
+    p.proj_sH = proj_heads != 1 ? int64_t(d) * d : 0;
+    p.xlin = ws.xlin;
+  }
+  p.dq = dq; p.dk = dk; p.dv = dv;
+
+  // transposed masks (cleared by a fill kernel, then set by atomic OR) and the dK/dV order
+  const int mrows = B * sh.Hs * nb, qrows = B * Hq * nb, krows = B * Hkv * nb;
+  const int64_t nbits = int64_t(mrows) * p.wq;
+  auto fill = [&](uint32_t* ptr, int64_t n, uint32_t val) {
+    fill_u32_kernel<<<dim3(uint32_t((n + 255) / 256)), 256, 0, s>>>(ptr, n, val);
+  };
+  fill(ws.critT, nbits, 0u);
+  if (causal) fill(ws.critT_sel, nbits, 0u);
+  fill(reinterpret_cast<uint32_t*>(ws.kv_counts), krows, 0u);
+  crit_transpose_kernel<<<dim3((mrows + 3) / 4), 256, 0, s>>>(crit_rowptr, crit_idx, p.crit_flags, mrows, nb, p.wq,
+                                                              sh.Hs, Hkv, group_map ? 1 : p.G, ws.critT,
+                                                              ws.critT_sel, ws.kv_counts);
+  if (rowst) {
+    fill(ws.margT, int64_t(qrows) * p.wq, 0u);
+    const int wk = (nb + 31) / 32;
+    marg_transpose_kernel<<<dim3(uint32_t((int64_t(qrows) * wk + 255) / 256)), 256, 0, s>>>(marg_bits, qrows, nb, wk,
+                                                                                           p.wq, ws.margT);
+  } else if (gated) {
+    ones_bits_kernel<<<dim3(uint32_t((int64_t(B) * Hq * p.wq + 255) / 256)), 256, 0, s>>>(ws.margT, B * Hq, nb, p.wq);
+  }
+  const int max_count = min(nb * (group_map ? 1 : p.G), kMaxKeyBlocksBwd);
+  kv_order_kernel<<<1, 1024, 0, s>>>(ws.kv_counts, krows, max_count, ws.kv_order);
+
+  // 1. query side: linear dQ, D, dS_i, du_i (and O_l with Proj; the gate weights' partials when
+  //    gated), or D alone without a linear branch
+  by_type(q->dtype, d, [&](auto tv, auto dv_) { launch_bwd_q_side<decltype(tv), decltype(dv_)::value>(p, B, s); });
+  if (proj) {
+    const int per_head = proj_heads != 1;
+    by_type(q->dtype, d, [&](auto tv, auto dv_) {
+      launch_proj_grad<decltype(tv), decltype(dv_)::value>(p, B, per_head, ws, dproj_w, dproj_b, s);
+    });
+  }
+  if (gated) gate_reduce_kernel<<<dim3((Hq * d + 255) / 256), 256, 0, s>>>(ws.gpart, B, Hq, nb, d, dw_gate);
+  // 2. dH_j = sum of dS_i, dz_j = sum of du_i over the query blocks i with j marginal: the
+  //    marginal aggregation with the mask transposed (rows = key blocks, summed items = query
+  //    blocks); gated: one row per head whose mask holds every query block
+  if (rowst) {
+    if ((st = launch_marginal_states(ws.dS, ws.du, B, Hq, Hq, nb, nb, d, 0, ws.margT, ws.dH, ws.dz, s)) != SLA_OK)
+      return st;
+  } else if (gated) {
+    if ((st = launch_marginal_states(ws.dS, ws.du, B, Hq, Hq, 1, nb, d, 0, ws.margT, ws.dH, ws.dz, s)) != SLA_OK)
+      return st;
+  }
+  // 3. linear branch, key side (dK, dV written; with smooth-K the mean of that dK), then the sparse
+  //    branch (dQ, dK, dV accumulated, or written without a linear branch)
+  by_type(q->dtype, d, [&](auto tv, auto dv_) {
+    launch_bwd_k_side<decltype(tv), decltype(dv_)::value>(p, B, lin_mode != SLA_LIN_NONE, s);
+  });
+  return launch_status();
 }
 
 extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
@@ -951,103 +1335,8 @@ extern "C" sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, con
   sla_status st = check_tensor(q);
   if (st != SLA_OK) return st;
   if ((st = check_tensor(k)) != SLA_OK) return st;
-  if ((st = check_tensor(v)) != SLA_OK) return st;
-  if ((st = check_tensor(o)) != SLA_OK) return st;
-  if ((st = check_tensor(dout)) != SLA_OK) return st;
-  if (!same_geometry(q, k) || !same_geometry(k, v) || !same_geometry(q, o) || !same_geometry(q, dout))
-    return SLA_ERR_SHAPE;
-  if (k->H != q->H || v->H != q->H || o->H != q->H || dout->H != q->H) return SLA_ERR_UNSUPPORTED;  // MHA only
-  if (o->dtype != q->dtype || dout->dtype != q->dtype) return SLA_ERR_SHAPE;
-  if ((st = check_valid_len(n_valid, q->N)) != SLA_OK) return st;
-  if (!(scale > 0.f) || !__builtin_isfinite(scale)) return SLA_ERR_RANGE;
-  if (lse == nullptr || crit_rowptr == nullptr || crit_idx == nullptr || marg_bits == nullptr || S == nullptr ||
-      u == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
-    return SLA_ERR_NULL;
-  if (!aligned16(S) || !aligned16(u) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return SLA_ERR_ALIGN;
-  const bool proj = proj_w != nullptr;
-  if (!proj && (proj_b != nullptr || dproj_w != nullptr || dproj_b != nullptr)) return SLA_ERR_NULL;
-  if (proj) {
-    if (dproj_w == nullptr) return SLA_ERR_NULL;
-    if (proj_heads != 1 && proj_heads != q->H) return SLA_ERR_SHAPE;
-    if (!aligned16(proj_w) || !aligned16(dproj_w) || (proj_b != nullptr && !aligned16(proj_b)) ||
-        (dproj_b != nullptr && !aligned16(dproj_b)))
-      return SLA_ERR_ALIGN;
-  }
-  if (k_shift != nullptr && !aligned16(k_shift)) return SLA_ERR_ALIGN;
-  const int d = q->d, B = q->B, H = q->H, N = q->N, nb = N / kBlock;
-  if (nb > SLA_MAX_KEY_BLOCKS) return SLA_ERR_UNSUPPORTED;
-  const size_t need = bwd_ws_layout(B, H, N, d, proj, nullptr, nullptr);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return SLA_ERR_WORKSPACE;
-  BwdWs ws{};
-  bwd_ws_layout(B, H, N, d, proj, &ws, workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  BwdParams p{};
-  p.q = q->ptr; p.k = k->ptr; p.v = v->ptr; p.o = o->ptr; p.dout = dout->ptr;
-  p.qsB = q->sB; p.qsH = q->sH; p.qsN = q->sN;
-  p.ksB = k->sB; p.ksH = k->sH; p.ksN = k->sN;
-  p.vsB = v->sB; p.vsH = v->sH; p.vsN = v->sN;
-  p.osB = o->sB; p.osH = o->sH; p.osN = o->sN;
-  p.dsB = dout->sB; p.dsH = dout->sH; p.dsN = dout->sN;
-  p.H = H; p.N = N; p.nb = nb; p.n_valid = n_valid; p.wq = (nb + 31) / 32;
-  p.scale = scale; p.scale_log2 = scale * kLog2e;
-  p.lse = lse; p.crit_rowptr = crit_rowptr; p.crit_idx = crit_idx;
-  p.S = static_cast<const u16*>(S); p.u = u;
-  p.D = ws.D; p.dS = ws.dS; p.du = ws.du; p.dH = ws.dH; p.dz = ws.dz; p.critT = ws.critT;
-  p.kv_order = ws.kv_order;
-  p.k_shift = k_shift;
-  p.dk_mean = k_shift != nullptr ? ws.dk_mean : nullptr;
-  if (proj) {
-    p.proj_w = proj_w; p.proj_b = proj_b;
-    p.proj_sH = proj_heads != 1 ? int64_t(d) * d : 0;
-    p.xlin = ws.xlin;
-  }
-  p.dq = dq; p.dk = dk; p.dv = dv;
-
-  // transposed masks (cleared by a fill kernel, then set by atomic OR)
-  const int rows = B * H * nb;
-  const int64_t nbits = int64_t(rows) * p.wq;
-  fill_u32_kernel<<<dim3(uint32_t((nbits + 255) / 256)), 256, 0, s>>>(ws.critT, nbits, 0u);
-  fill_u32_kernel<<<dim3(uint32_t((nbits + 255) / 256)), 256, 0, s>>>(ws.margT, nbits, 0u);
-  fill_u32_kernel<<<dim3(uint32_t((rows + 255) / 256)), 256, 0, s>>>(reinterpret_cast<uint32_t*>(ws.kv_counts),
-                                                                     rows, 0u);
-  crit_transpose_kernel<<<dim3((rows + 3) / 4), 256, 0, s>>>(crit_rowptr, crit_idx, rows, nb, p.wq, ws.critT,
-                                                             ws.kv_counts);
-  const int wk = (nb + 31) / 32;
-  marg_transpose_kernel<<<dim3(uint32_t((int64_t(rows) * wk + 255) / 256)), 256, 0, s>>>(marg_bits, rows, nb, wk,
-                                                                                        p.wq, ws.margT);
-  kv_order_kernel<<<1, 1024, 0, s>>>(ws.kv_counts, rows, nb, ws.kv_order);
-  const bool bf = q->dtype == SLA_BF16;
-  // 1. linear branch, query side: dQ (linear part), D, dS_i, du_i (and O_l with Proj)
-  if (d == 128) {
-    if (bf) launch_bwd_kernels<bf16raw, 128>(p, B * H, s);
-    else launch_bwd_kernels<float, 128>(p, B * H, s);
-  } else {
-    if (bf) launch_bwd_kernels<bf16raw, 64>(p, B * H, s);
-    else launch_bwd_kernels<float, 64>(p, B * H, s);
-  }
-  if (proj) {
-    const int per_head = proj_heads != 1;
-    if (d == 128) {
-      if (bf) launch_proj_grad<bf16raw, 128>(p, B, per_head, ws, dproj_w, dproj_b, s);
-      else launch_proj_grad<float, 128>(p, B, per_head, ws, dproj_w, dproj_b, s);
-    } else {
-      if (bf) launch_proj_grad<bf16raw, 64>(p, B, per_head, ws, dproj_w, dproj_b, s);
-      else launch_proj_grad<float, 64>(p, B, per_head, ws, dproj_w, dproj_b, s);
-    }
-  }
-  // 2. dH_j = sum of dS_i, dz_j = sum of du_i over the query blocks i with j marginal: the
-  //    marginal aggregation with the mask transposed (rows = key blocks, summed items = query blocks)
-  if ((st = launch_marginal_states(ws.dS, ws.du, B, H, H, nb, nb, d, 0, ws.margT, ws.dH, ws.dz, s)) != SLA_OK)
-    return st;
-  // 3. linear branch, key side (dK, dV written; with smooth-K the mean of that dK), then the sparse
-  //    branch (dQ, dK, dV accumulated)
-  if (d == 128) {
-    if (bf) launch_bwd_k_side<bf16raw, 128>(p, B * H, s);
-    else launch_bwd_k_side<float, 128>(p, B * H, s);
-  } else {
-    if (bf) launch_bwd_k_side<bf16raw, 64>(p, B * H, s);
-    else launch_bwd_k_side<float, 64>(p, B * H, s);
-  }
-  return launch_status();
+  if (k->H != q->H) return SLA_ERR_UNSUPPORTED;  // one KV head per query head
+  return sla_attn_bwd_ext(q, k, v, o, dout, lse, n_valid, scale, SLA_LIN_ROW_STATES, 0, 0, 0, crit_rowptr, crit_idx,
+                          nullptr, marg_bits, S, u, nullptr, nullptr, nullptr, k_shift, proj_w, proj_b, proj_heads,
+                          dq, dk, dv, dproj_w, dproj_b, nullptr, workspace, workspace_bytes, stream);
 }

@@ -408,6 +408,52 @@ sla_status sla_attn_bwd(const sla_tensor* q, const sla_tensor* k, const sla_tens
                         float* dq, float* dk, float* dv, float* dproj_w, float* dproj_b,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes sla_attn_bwd_ext needs for these shapes and options (0 for unsupported ones);
+ * proj_heads 0 without Proj. */
+size_t sla_attn_bwd_ext_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                                        int32_t lin_mode, int32_t causal, int32_t group_map,
+                                        int32_t proj_heads);
+
+/*
+ * Backward of every sla_attn_fwd mode for a fixed block map: gradients of sum(dout * O) with
+ * respect to Q, K, V and the learned parameters of the mode.  The pages fine-tune both hybrids
+ * (SLA analysis page for arXiv 2509.24006: Proj and the linear path; SALAD page, method
+ * framework: the gated linear branch) and NSA trains its selection end to end ("Sparse
+ * Attention 方法综述", section 2 NSA), so each forward has its backward.  With P, dP, D and dS as
+ * in sla_attn_bwd over each row's ALLOWED keys (the forward's masks), per lin_mode:
+ *   SLA_LIN_ROW_STATES (MARGINAL maps; S, u and marg_bits as for sla_attn_bwd): the marginal
+ *     branch, Proj (proj_w, proj_b, proj_heads, dproj_w, dproj_b) and smooth-K as sla_attn_bwd;
+ *   SLA_LIN_GLOBAL_GATED (H_all, z_all fp32 from sla_linear_kv_reduce, w_gate [Hq, d] fp32):
+ *     O_linear = g y with g = sigmoid(q . w_gate[h]) and y = phi(q)^T H_all / (phi(q) . z_all):
+ *     the gradient reaching y is g dO; dlogit = g (1 - g) (dO . y) adds dlogit w_gate[h] to dq
+ *     and dw_gate[h] = sum over b and valid rows of dlogit q (dw_gate fp32 [Hq, d], required);
+ *     dH_all, dz_all are the sums over every query block of the per-block state gradients;
+ *     smooth-K as above;
+ *   SLA_LIN_NONE: the sparse branch alone (D = dout . o); with causal != 0 the forward's causal
+ *     masks (s <= t, and flag bit 0 of the entry or t - s < window_tokens; crit_flags required).
+ * GQA: q, o, dout [B, Hq, N, d]; k, v [B, Hkv, N, d], Hq a multiple of Hkv, query head h reads
+ * KV head h / (Hq / Hkv); dk, dv sum over the query heads of each KV head.  group_map != 0: the
+ * map rows are per KV head (Hs = Hkv, as sla_block_map wrote them from group-summed scores), else
+ * per query head.  A linear branch needs causal == 0 and group_map == 0 (SLA_ERR_UNSUPPORTED);
+ * Proj needs SLA_LIN_ROW_STATES; k_shift (fp32 [B, Hkv, d]) needs a linear branch.
+ * lse: fp32 [B, Hq, N] written by the forward.  Outputs dq [B, Hq, N, d], dk, dv [B, Hkv, N, d]
+ * contiguous fp32, 16-byte aligned, fully overwritten (rows >= n_valid zero); pointers a mode
+ * does not use must be NULL for the outputs (dw_gate, dproj_w, dproj_b) and are ignored for the
+ * inputs.  Arithmetic, determinism and error codes as sla_attn_bwd.
+ * workspace: sla_attn_bwd_ext_workspace_bytes(B, Hq, Hkv, N, d, lin_mode, causal, group_map,
+ * proj_w ? proj_heads : 0) bytes.
+ */
+sla_status sla_attn_bwd_ext(const sla_tensor* q, const sla_tensor* k, const sla_tensor* v,
+                            const sla_tensor* o, const sla_tensor* dout, const float* lse, int32_t n_valid,
+                            float scale, int32_t lin_mode, int32_t causal, int32_t window_tokens,
+                            int32_t group_map, const int32_t* crit_rowptr, const int32_t* crit_idx,
+                            const uint8_t* crit_flags, const uint32_t* marg_bits, const void* S,
+                            const float* u, const float* H_all, const float* z_all, const float* w_gate,
+                            const float* k_shift, const float* proj_w, const float* proj_b,
+                            int32_t proj_heads, float* dq, float* dk, float* dv, float* dproj_w,
+                            float* dproj_b, float* dw_gate, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

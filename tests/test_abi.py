@@ -262,6 +262,43 @@ def test_attn_bwd_validation(L):
     assert L.sla_attn_bwd_workspace_bytes(1, 2, 100, 128, 0) == 0
 
 
+def test_attn_bwd_ext_validation(L):
+    q = desc(H=4)
+    kv = desc(H=2)
+    ROW, NONE, GATED = 3, 0, 2
+    def call(qq=q, kk=kv, vv=kv, oo=q, gg=q, lse=P, nv=256, scale=0.1, lin=NONE, causal=0, win=0, gm=0, crp=P,
+             ci=P, cf=None, mb=None, S=None, u=None, Ha=None, za=None, wg=None, ks=None, pw=None, pb=None, ph=0,
+             dq=P, dk=P, dv=P, dw=None, db=None, dwg=None, ws=None, wsb=0):
+        return L.sla_attn_bwd_ext(ctypes.byref(qq), ctypes.byref(kk), ctypes.byref(vv), ctypes.byref(oo),
+                                  ctypes.byref(gg), lse, nv, scale, lin, causal, win, gm, crp, ci, cf, mb, S, u, Ha,
+                                  za, wg, ks, pw, pb, ph, dq, dk, dv, dw, db, dwg, ws, wsb, None)
+    assert call(kk=desc(H=3), vv=desc(H=3)) == ESHAPE           # Hq not a multiple of Hkv
+    assert call(vv=desc(H=4)) == ESHAPE                         # K and V disagree
+    assert call(lin=1 + 8) == EUNSUP                            # unknown linear mode
+    assert call(lin=ROW, causal=1, cf=P) == EUNSUP              # a linear branch is non-causal
+    assert call(lin=GATED, gm=1) == EUNSUP                      # ... and takes per-head maps
+    assert call(causal=1) == ENULL                              # causal maps need their flags
+    assert call(causal=1, cf=P, win=-1) == ERANGE
+    assert call(lin=ROW) == ENULL                               # row states and masks
+    assert call(lin=ROW, mb=P, S=P, u=ctypes.c_void_p(0x20004)) == EALIGN
+    assert call(lin=GATED, Ha=P, za=P, wg=P) == ENULL           # the gate gradient is required
+    assert call(dwg=P) == ENULL                                 # ... and only with the gate
+    assert call(pw=P, ph=1, dw=P) == EUNSUP                     # Proj belongs to the row-states mode
+    assert call(ks=P) == EUNSUP                                 # smooth-K needs a linear branch
+    assert call() == EWS
+    need = L.sla_attn_bwd_ext_workspace_bytes(1, 4, 2, 256, 128, NONE, 1, 1, 0)
+    assert call(causal=1, cf=P, gm=1, ws=P, wsb=need - 1) == EWS
+    assert need > 0
+    assert L.sla_attn_bwd_ext_workspace_bytes(1, 4, 2, 256, 128, ROW, 0, 0, 0) > need
+    assert L.sla_attn_bwd_ext_workspace_bytes(1, 4, 2, 256, 128, GATED, 0, 0, 0) > need
+    assert L.sla_attn_bwd_ext_workspace_bytes(1, 4, 3, 256, 128, NONE, 0, 0, 0) == 0
+    assert L.sla_attn_bwd_ext_workspace_bytes(1, 4, 2, 256, 128, ROW, 1, 0, 0) == 0
+    assert L.sla_attn_bwd_ext_workspace_bytes(1, 4, 2, 256, 128, GATED, 0, 0, 1) == 0
+    # the MHA entry point is the row-states mode of the extended one
+    assert (L.sla_attn_bwd_workspace_bytes(1, 2, 256, 128, 1)
+            == L.sla_attn_bwd_ext_workspace_bytes(1, 2, 2, 256, 128, ROW, 0, 0, 1))
+
+
 def test_nsa3_validation(L):
     q = desc(H=4)
     kv = desc(H=1)
