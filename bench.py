@@ -231,24 +231,28 @@ def bench_nsa3(args, w, qd, kd, vd):
 
 
 def bench_backward(args, w, qd, kd, vd):
-    """Time the backward (dQ, dK, dV of one SLA layer for its block map) and print one JSON line.
+    """Time the backward (dQ, dK, dV, and dw_gate for SALAD, of one layer for its block map) and
+    print one JSON line.
 
     The forward runs once in training mode (it also keeps each row's log-sum-exp); each timed step
-    is one sla_attn_bwd call on a fixed seeded dO.  Executed FLOPs: per critical pair the five
-    64 x 64 x d products of the sparse backward recomputation and gradients (S and dP in both the
-    dQ and the dK/dV kernels, dQ, dK, dV: 7 x 2 * 64^2 * d), per query block the three 64 x d x d
-    products of the linear query side, per key block the two of the key side, and the transposed
-    mask product over the state gradients (2 nb^2 d^2 per head).
+    is one backward call on a fixed seeded dO.  Executed FLOPs: per critical (query head, key block)
+    pair the seven 64 x 64 x d products of the sparse backward (S and dP in both the dQ and the
+    dK/dV kernels, dQ, dK, dV); with a linear branch, per query block the three 64 x d x d products
+    of the query side and per key block the two of the key side, plus the transposed mask product
+    over the state gradients (2 nb^2 d^2 per head; gated: 2 nb d^2, one row per head).
     """
     import torch
     import block_sparse_linear_mean_amd as sla
-    if w.mode != "sla" or w.Hq != w.Hkv:
-        raise SystemExit("--backward is provided for the sla workloads with one KV head per query head")
-    layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, training=True)
+    from workloads import make_inputs
+    wg = make_inputs(w)[3] if w.mode == "salad" else None
+    layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
+                           window=w.window, w_gate=wg, training=True)
     layer.run()
     g = torch.Generator(device="cpu").manual_seed(7)
     dout = torch.randn(qd.shape, generator=g).to(device=qd.device, dtype=qd.dtype)
-    grads = tuple(torch.empty(qd.shape, device=qd.device, dtype=torch.float32) for _ in range(3))
+    grads = (torch.empty(qd.shape, device=qd.device, dtype=torch.float32),
+             torch.empty(kd.shape, device=qd.device, dtype=torch.float32),
+             torch.empty(kd.shape, device=qd.device, dtype=torch.float32))
     for _ in range(args.warmup):
         layer.backward(dout, grads=grads)
     torch.cuda.synchronize()
@@ -261,22 +265,28 @@ def bench_backward(args, w, qd, kd, vd):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_gpu = ev[0].elapsed_time(ev[-1]) / args.steps
-    pairs = int(layer.maps["crit_rowptr"][-1].item())
-    d, nb, BH = w.d, w.nb, w.B * w.Hq
-    flops = pairs * 7 * 2.0 * 64 * 64 * d + BH * nb * (3 + 2) * 2.0 * 64 * d * d + BH * 2.0 * nb * nb * d * d
+    entries = int(layer.maps["crit_rowptr"][-1].item())
+    pairs = entries * (w.Hq // w.Hkv if layer.group else 1)
+    d, nb, BH, BK = w.d, w.nb, w.B * w.Hq, w.B * w.Hkv
+    flops = pairs * 7 * 2.0 * 64 * 64 * d
+    if layer.lin != sla.SLA_LIN_NONE:
+        flops += BH * nb * 3 * 2.0 * 64 * d * d + BK * nb * 2 * 2.0 * 64 * d * d
+        flops += BH * 2.0 * (nb if layer.lin == sla.SLA_LIN_MARGINAL else 1) * nb * d * d
     achieved = flops / (ms_gpu / 1e3) / 1e12
     dense = 2.5 * w.dense_flops()          # dense-equivalent backward: 2.5x the forward's products
     log(f"bench: backward {ms_gpu:.4f} ms/layer (HIP events), wall {ms_step:.4f}; executed {flops / 1e9:.1f} GFLOP")
+    name = {"sla": "SLA", "salad": "SALAD", "nsa": "NSA-style selected + window"}[w.mode]
     print(json.dumps({
-        "metric": "SLA bwd ms/layer + effective TFLOP/s (dQ, dK, dV), " + METRIC.split(", ", 1)[1],
+        "metric": f"{name} bwd ms/layer + effective TFLOP/s (dQ, dK, dV), " + METRIC.split(", ", 1)[1],
         "value": round(dense / (ms_step / 1e3) / 1e12, 3),
         "unit": "TFLOP/s (effective, dense-equivalent backward = 2.5x forward)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded)", "config": {"workload": w.name, "pass": "backward", "critical_pairs": pairs},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "sla_attn_bwd (all kernels)",
-                     "algorithmic_per_launch": flops, "avg_launch_ms": round(ms_gpu, 5)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "sla_attn_bwd_ext (all kernels)", "algorithmic_per_launch": flops,
+                     "avg_launch_ms": round(ms_gpu, 5)},
     }))
 
 
@@ -420,7 +430,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the cold-cache steps and the copy / GEMM reference measurements")
-    ap.add_argument("--backward", action="store_true", help="time the layer backward instead (sla workloads)")
+    ap.add_argument("--backward", action="store_true", help="time the layer backward instead")
     ap.add_argument("--overlap", action="store_true",
                     help="run the key states and marginal sums on a second stream, overlapping scores and map")
     ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",

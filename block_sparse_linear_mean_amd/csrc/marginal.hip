@@ -35,14 +35,16 @@ constexpr int kMgStages = 4;    // H tiles in flight
 constexpr int kMgWords = 16;    // mask words per row held in LDS (512 key blocks)
 constexpr int kMgTileB = kMgK * kMgCols * 2;
 
-// 8 mask bits -> 8 bf16 values 1.0 / 0.0 (bit m -> element m).
+// 8 mask bits -> 8 bf16 values 1.0 / 0.0 (bit m -> element m).  z = byte * 0x8001 holds the byte
+// twice, at bits 0..7 and 15..22, so bit 16 + 2k of z is bit 2k + 1 of the byte: word k keeps bits
+// 2k and 16 + 2k of z and scales them to bf16(1.0) = 0x3F80 in its low and high half with one
+// 24-bit multiply by 0x3F80 >> 2k (exact: 0x3F80 is a multiple of 2^7).  Ten VALU operations with
+// the byte extraction.
 __device__ __forceinline__ bf16x8 expand_bits(uint32_t byte) {
+  const uint32_t z = byte * 0x8001u;
   u32x4 w;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t two = (byte >> (2 * k)) & 3u;
-    w[k] = ((two & 1u) | ((two & 2u) << 15)) * 0x3F80u;   // bf16(1.0) in the low / high half
-  }
+  for (int k = 0; k < 4; ++k) w[k] = (z & (0x00010001u << (2 * k))) * (0x3F80u >> (2 * k));
   return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -174,20 +176,26 @@ __global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restric
     const uint32_t w0 = mask[64 * w + lane % 32][wq];
     const uint32_t w1 = mask[64 * w + 32 + lane % 32][wq];
     if (__ballot((w0 | w1) != 0u) == 0) continue;  // no marginal block of this wavefront's rows here
+    // every A operand of the step (key blocks 16 h .. 16 h + 15, column tiles ct) is requested
+    // first, the mask operands are expanded while they are in flight, then the 16 products
+    bf16x8 a[2][4], bm[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {                  // 16 key blocks 16 h .. 16 h + 15
-      bf16x8 a[4];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) a[ct] = tr_operand(tile + 16 * h * 256, aoff[ct], 4 * 256);
+      for (int ct = 0; ct < 4; ++ct) a[h][ct] = tr_operand(tile + 16 * h * 256, aoff[ct], 4 * 256);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
       const int sh = 8 * (2 * h + lane / 32);
-      const bf16x8 b0 = expand_bits((w0 >> sh) & 0xffu);
-      const bf16x8 b1 = expand_bits((w1 >> sh) & 0xffu);
+      bm[h][0] = expand_bits((w0 >> sh) & 0xffu);
+      bm[h][1] = expand_bits((w1 >> sh) & 0xffu);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        acc[0][ct] = mfma32(a[ct], b0, acc[0][ct]);
-        acc[1][ct] = mfma32(a[ct], b1, acc[1][ct]);
+        acc[0][ct] = mfma32(a[h][ct], bm[h][0], acc[0][ct]);
+        acc[1][ct] = mfma32(a[h][ct], bm[h][1], acc[1][ct]);
       }
-    }
   }
 
   // lane holds S[row0 + 64 w + 32 rr + lane % 32][c0 + 32 ct + 8 q + 4 (lane / 32) + 0..3] in acc[rr][ct][4 q ..]
