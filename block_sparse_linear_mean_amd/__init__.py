@@ -225,8 +225,8 @@ class SlaForward:
 
     def run(self, overlap: bool = False, events=None) -> torch.Tensor:
         """One full forward: (token order,) pool, scores, block map, linear states, marginal sums,
-        attention (, order undone).  With fuse_key_pooling the linear key states come first and also
-        write the key block means, and the pooling pass reads only Q.
+        attention (, order undone).  With fuse_key_pooling the pooling pass reads only Q, and the linear
+        key states, which follow it, also write the key block means that the scores use.
 
         overlap: the linear key states depend only on K and V (and, with smooth-K, on the pooled
         keys), so they can run on a second stream while the scores and the block map run; the
@@ -244,8 +244,10 @@ class SlaForward:
                 fn()
         timed("reorder", self.reorder)
         if self.fuse_key_pooling and not overlap:
-            timed("kv_reduce", lambda: self.kv_reduce(k_pool=True))
+            # Q's block means first: the pass reads Q only, and the key-state pass's writes of
+            # the per-block states are still draining from the caches when the next pass runs
             timed("pool", lambda: self.pooling(k_pooled=True))
+            timed("kv_reduce", lambda: self.kv_reduce(k_pool=True))
             timed("scores", self.scoring)
             for name in ("block_map", "marginal_states", "attention"):
                 timed(name, getattr(self, name))

@@ -8,12 +8,14 @@
 
 namespace sla {
 
-// Key blocks per fp32 partial state when summing the linear states over all keys: runs short
-// enough that about two workgroups per compute unit (512 in all) share the pass, but at least 4
-// blocks (each run writes a d x d fp32 partial that the fixed-order final sum reads again) and at
-// most 32.  Depends on the shapes only, so the partial sums and their order are reproducible.
+// Key blocks per fp32 partial state when summing the linear states over all keys: the shortest
+// run for which all the runs fit in one wave of workgroups, two per compute unit (512 in all: the
+// kernel's occupancy), since a second, nearly empty wave would double the pass; at least 4 blocks
+// (each run writes a d x d fp32 partial that the fixed-order final sum reads again) and at most 32.
+// Depends on the shapes only, so the partial sums and their order are reproducible.
 inline int kv_sum_run(int64_t nb, int64_t heads) {
-  const int64_t r = (nb * heads + 511) / 512;
+  int64_t r = (nb * heads + 511) / 512;
+  while (r < 32 && heads * ((nb + r - 1) / r) > 512) ++r;
   return int(r < 4 ? 4 : (r > 32 ? 32 : r));
 }
 

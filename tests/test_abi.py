@@ -71,9 +71,10 @@ def test_capacities_and_workspaces(L):
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_MARGINAL) == 12 * 512 * (128 * 128 * 2 + 128 * 4)
     assert sla.sla_attn_workspace_bytes(1, 12, 512, 128, _lib.SLA_LIN_NONE) == 0
     assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 0) == 0
-    # runs of 12 key blocks at 12 heads x 512 blocks (about 512 workgroups): 43 fp32 partial states per head
-    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 12 * 43 * (128 * 128 + 128) * 4
-    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 43 * (128 * 128 + 128) * 4
+    # 12 heads x 512 blocks: runs of 12 blocks would make 43 x 12 = 516 workgroups, one more wave than
+    # the 512 that run at once, so runs of 13 blocks: 40 fp32 partial states per head
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 1, 1) == 12 * 40 * (128 * 128 + 128) * 4
+    assert sla.sla_kv_reduce_workspace_bytes(1, 12, 32768, 128, 0, 1) == 12 * 40 * (128 * 128 + 128) * 4
     # runs stay within 4 .. 32 blocks
     assert sla.sla_kv_reduce_workspace_bytes(1, 1, 4096, 64, 1, 1) == 1 * 16 * (64 * 64 + 64) * 4
     assert sla.sla_kv_reduce_workspace_bytes(1, 64, 262144, 64, 1, 1) == 64 * 128 * (64 * 64 + 64) * 4
