@@ -255,14 +255,25 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   }
 }
 
-// out[bg] = sum over p of in[bg * parts + p] (fixed order), for states of `len` floats.
+// out[bg] = sum over p of in[bg * parts + p] (fixed order), for states of `len` floats.  The
+// partials are read 8 at a time, all 8 loads in flight before the adds (one load at a time would
+// expose a memory latency per partial).
 __global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict__ in, int parts, int64_t len,
                                                          float* __restrict__ out) {
+  constexpr int kU = 8;
   const int64_t bg = blockIdx.y;
   const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (e >= len) return;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < parts; ++p) s += *reinterpret_cast<const f32x4*>(in + (bg * parts + p) * len + e);
+  for (int p0 = 0; p0 < parts; p0 += kU) {
+    f32x4 x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      x[u] = *reinterpret_cast<const f32x4*>(in + (bg * parts + min(p0 + u, parts - 1)) * len + e);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u < parts) s += x[u];
+  }
   *reinterpret_cast<f32x4*>(out + bg * len + e) = s;
 }
 
