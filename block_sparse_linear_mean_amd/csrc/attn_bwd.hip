@@ -42,11 +42,14 @@ struct BwdParams {
   const void* o;
   const void* dout;
   int64_t qsB, qsH, qsN, ksB, ksH, ksN, vsB, vsH, vsN, osB, osH, osN, dsB, dsH, dsN;
-  int H, N, nb, n_valid, wq;      // wq: 32-bit words per transposed bit row, ceil(nb / 32)
+  int B, H, N, nb, n_valid, wq;   // wq: 32-bit words per transposed bit row, ceil(nb / 32)
   int Hkv, G, Hs, group_map;      // KV heads, query heads per KV head, map heads, maps shared by a group
   int window;                     // causal maps: key s of a window block is allowed iff t - s < window
   int overwrite;                  // no linear branch: the sparse kernels write dQ, dK, dV (else add)
   int gated;                      // SALAD: one linear state per head (all keys), gated by sigmoid(q . w_gate)
+  int hsplit;                     // dK/dV workgroups per key block: each takes G / hsplit of the group's heads
+  float* part_k;                  // hsplit > 1: [hsplit][B, Hkv, N, d] partial dK (scaled) and dV per subset
+  float* part_v;
   float scale, scale_log2;
   const float* lse;               // [B, H, N] natural log-sum-exp of the forward's sparse branch
   const int* crit_rowptr;
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   __shared__ float us[D];
   __shared__ float dden_s[kBlock];
   __shared__ float dlog_s[GATED ? kBlock : 1];
+  __shared__ float gred[GATED ? kBwThreads / (D / 8) : 1][GATED ? D : 1];   // gate-gradient row-group sums
   lds_u8* St = to_lds(st_sm);
   lds_u8* Pq = to_lds(pq_sm);
   lds_u8* Dn = to_lds(dn_sm);
@@ -381,14 +385,31 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   }
   __syncthreads();                // phi(Q_i), dN_i and dden complete in LDS
   if constexpr (GATED) {
-    // the gate weights' partial gradient of this query block: sum over its rows of dlogit_t q_t
+    // the gate weights' partial gradient of this query block: sum over its rows of dlogit_t q_t.
+    // Thread t takes the 8-feature chunk t % kCh of rows t / kCh + kRg u (all its loads in flight
+    // at once), then the kRg row groups are summed through LDS in a fixed order.
+    constexpr int kCh = D / 8, kRg = kBwThreads / kCh, kPer = kBlock / kRg;
+    const int ch = t % kCh, rg = t / kCh;
+    float x[kPer][8];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      In<T>::load8_f32(Qb + int64_t(min(kBlock * i + rg + kRg * u, p.n_valid - 1)) * p.qsN + 8 * ch, x[u]);
+    float s8[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s8[m] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (kBlock * i + rg + kRg * u < p.n_valid) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) s8[m] += dlog_s[rg + kRg * u] * x[u][m];
+      }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) gred[rg][8 * ch + m] = s8[m];
+    __syncthreads();
     for (int r = t; r < D; r += kBwThreads) {
       float s = 0.f;
-      for (int tt = 0; tt < kBlock && kBlock * i + tt < p.n_valid; ++tt) {
-        float x[8];
-        In<T>::load8_f32(Qb + int64_t(kBlock * i + tt) * p.qsN + 8 * (r / 8), x);
-        s += dlog_s[tt] * x[r % 8];
-      }
+#pragma unroll
+      for (int g2 = 0; g2 < kRg; ++g2) s += gred[g2][r];
       p.gpart[row * D + r] = s;
     }
   }
@@ -575,14 +596,27 @@ __global__ __launch_bounds__(kBwThreads) void proj_grad_kernel(BwdParams p, int 
   if (t < D) partB[part * D + t] = bsum;
 }
 
+// s += x[0] + ... + x[n - 1] in this order, x[q] = p[q * stride]: loads issued 8 at a time, all in
+// flight before their adds (one at a time would expose a memory latency per term).
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int n, int64_t stride, float s) {
+  constexpr int kU = 8;
+  for (int q0 = 0; q0 < n; q0 += kU) {
+    float x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) x[u] = p[int64_t(min(q0 + u, n - 1)) * stride];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (q0 + u < n) s += x[u];
+  }
+  return s;
+}
+
 // out[y][e] = sum over the parts of weight y, in order.
 __global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int parts, int len,
                                                           float* __restrict__ out) {
   const int e = blockIdx.x * 256 + threadIdx.x, y = blockIdx.y;
   if (e >= len) return;
-  float s = 0.f;
-  for (int q = 0; q < parts; ++q) s += part[(int64_t(y) * parts + q) * len + e];
-  out[int64_t(y) * len + e] = s;
+  out[int64_t(y) * len + e] = ordered_sum(part + int64_t(y) * parts * len + e, parts, len, 0.f);
 }
 
 // Smooth-K: the mean over the valid rows of the linear-branch dK of each head (the gradient that
@@ -594,14 +628,24 @@ __global__ __launch_bounds__(256) void dk_mean_kernel(const float* __restrict__ 
   float s[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) s[m] = 0.f;
-  for (int row = t; row < n_valid; row += 256) {
-    const float* src = dk + (int64_t(bh) * N + row) * d + r0;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src), b4 = *reinterpret_cast<const f32x4*>(src + 4);
+  // rows t, t + 256, ...: 4 rows' loads in flight at a time, added in row order
+  for (int row0 = t; row0 < n_valid; row0 += 4 * 256) {
+    f32x4 a[4], b4[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      s[m] += a[m];
-      s[4 + m] += b4[m];
+    for (int u = 0; u < 4; ++u) {
+      const float* src = dk + (int64_t(bh) * N + min(row0 + 256 * u, n_valid - 1)) * d + r0;
+      a[u] = *reinterpret_cast<const f32x4*>(src);
+      b4[u] = *reinterpret_cast<const f32x4*>(src + 4);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (row0 + 256 * u < n_valid) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s[m] += a[u][m];
+          s[4 + m] += b4[u][m];
+        }
+      }
   }
   __shared__ float red[256][9];
 #pragma unroll
@@ -820,7 +864,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(256))) float lse_s[2][kBlock];
   __shared__ __attribute__((aligned(256))) float d_s[2][kBlock];
 
-  const int krow = p.kv_order[blockIdx.x];        // (b, g, j), most-used key blocks first
+  const int krow = p.kv_order[blockIdx.x / p.hsplit];   // (b, g, j), most-used key blocks first
+  const int hs = blockIdx.x % p.hsplit;                  // this workgroup's subset of the group's heads
   const int j = krow % p.nb, bk = krow / p.nb, b = bk / p.Hkv, gk = bk % p.Hkv;
   const int t = threadIdx.x, lane = t % kWave, l16 = lane % 16, g = lane / 16;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -830,16 +875,18 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(gk) * p.vsH + int64_t(s) * p.vsN;
   const StageOff<D, kBwWaves> qoff = stage_offsets<D, false, kBwWaves>(p.qsN);
   const StageOff<D, kBwWaves> goff = stage_offsets<D, false, kBwWaves>(p.dsN);
-  const int h0 = gk * p.G;
+  const int Gs = p.G / p.hsplit;                         // heads per subset
+  const int h0 = gk * p.G + hs * Gs;
 
-  // the (head, query block) pairs that list j, heads ascending, then query blocks ascending: a
-  // wave-uniform scan of the transposed bit rows (the group's one row G times with shared maps)
+  // the (head, query block) pairs that list j, heads ascending (the subset's), then query blocks
+  // ascending: a wave-uniform scan of the transposed bit rows (the group's one row per head with
+  // shared maps)
   int hh = 0, word = 0;
   uint32_t m = 0u, msel = 0u;
   auto next_block = [&](int& head, bool& sel) -> int {
     while (m == 0u) {
       if (word >= p.wq) {
-        if (hh + 1 >= p.G) return -1;
+        if (hh + 1 >= Gs) return -1;
         ++hh;
         word = 0;
         continue;
@@ -946,6 +993,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     sel_cur = sel_nxt;
     buf ^= 1;
   }
+  if (p.hsplit > 1) {                // a subset's partial sums, added up by dkdv_combine_kernel
+    const int64_t off = ((int64_t(hs) * p.B * p.Hkv + bk) * p.N + s) * D;
+    float* pk = p.part_k + off;
+    float* pv = p.part_v + off;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      *reinterpret_cast<f32x4*>(pk + 16 * ct + 4 * g) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(pv + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   float* dkr = p.dk + (int64_t(bk) * p.N + s) * D;
   float* dvr = p.dv + (int64_t(bk) * p.N + s) * D;
   if (p.overwrite) {                 // no linear branch: this kernel writes every row (padded: 0)
@@ -992,16 +1050,73 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p, int rows) {
   if (l == 0) p.D[r] = acc;
 }
 
-// SALAD: dw_gate[h][r] = sum over b and the query blocks i of gpart[(b, h, i)][r], in order.
+// SALAD: dw_gate[h][r] = sum over b and the query blocks i of gpart[(b, h, i)][r].  One workgroup
+// per (head, 8 features): thread t sums the rows (b, i) with b nb + i = t, t + 256, ... (4 rows'
+// loads in flight at a time), then a fixed-order LDS tree over the threads (deterministic).
 __global__ __launch_bounds__(256) void gate_reduce_kernel(const float* __restrict__ gpart, int B, int H, int nb, int d,
                                                           float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= H * d) return;
-  const int h = e / d, r = e % d;
-  float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int i = 0; i < nb; ++i) s += gpart[((int64_t(b) * H + h) * nb + i) * d + r];
-  out[e] = s;
+  const int h = blockIdx.y, r0 = 8 * blockIdx.x, t = threadIdx.x;
+  const int rows = B * nb;
+  float s[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) s[m] = 0.f;
+  for (int q0 = t; q0 < rows; q0 += 4 * 256) {
+    f32x4 a[4], c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = min(q0 + 256 * u, rows - 1), b = q / nb, i = q % nb;
+      const float* src = gpart + ((int64_t(b) * H + h) * nb + i) * d + r0;
+      a[u] = *reinterpret_cast<const f32x4*>(src);
+      c[u] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q0 + 256 * u < rows) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s[m] += a[u][m];
+          s[4 + m] += c[u][m];
+        }
+      }
+  }
+  __shared__ float red[256][9];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) red[t][m] = s[m];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) red[t][m] += red[t + w][m];
+    }
+    __syncthreads();
+  }
+  if (t < 8) out[int64_t(h) * d + r0 + t] = red[0][t];
+}
+
+// dK and dV from the head subsets' partials (hsplit > 1): summed in subset order, then written (no
+// linear branch) or added to the linear part (valid rows; with smooth-K minus the mean of that
+// part), as the dK/dV kernel does without a split.  One thread per 4 features of a row.
+__global__ __launch_bounds__(256) void dkdv_combine_kernel(BwdParams p, int D) {
+  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t total = int64_t(p.B) * p.Hkv * p.N * D;
+  if (e >= total) return;
+  const int64_t rowi = e / D;
+  const int bk = int(rowi / p.N), s = int(rowi % p.N), c = int(e % D);
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int hs = 0; hs < p.hsplit; ++hs) {
+    sk += *reinterpret_cast<const f32x4*>(p.part_k + hs * total + e);
+    sv += *reinterpret_cast<const f32x4*>(p.part_v + hs * total + e);
+  }
+  f32x4* k4 = reinterpret_cast<f32x4*>(p.dk + e);
+  f32x4* v4 = reinterpret_cast<f32x4*>(p.dv + e);
+  if (p.overwrite) {
+    *k4 = sk;                        // padded rows: the partials are 0
+    *v4 = sv;
+  } else if (s < p.n_valid) {
+    if (p.dk_mean != nullptr) sk -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + c);
+    *k4 = *k4 + sk;
+    *v4 = *v4 + sv;
+  }
 }
 
 // One bit per query block of every row: word w of a row holds blocks 32 w .. 32 w + 31 below nb.
@@ -1028,9 +1143,22 @@ struct BwdWs {
   float* partW;
   float* partB;
   float* gpart;
+  float* part_k;
+  float* part_v;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// dK/dV workgroups per key block.  A key block's work is every (head, query block) pair that lists
+// it, G heads per KV head: with few key-block rows (one wave of workgroups or less) the most-listed
+// block alone sets the kernel's time (at the NSA prefill: 114 listing query blocks x 16 heads against
+// 24 x 16 on average), so the group's heads are split over 2 or 4 workgroups whose partial sums a
+// second kernel adds up in a fixed order.
+static int bwd_hsplit(int B, int Hq, int Hkv, int nb) {
+  const int G = Hq / Hkv;
+  if (G < 2 || int64_t(B) * Hkv * nb >= 2048) return 1;
+  return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+}
 
 constexpr int kProjChunk = 16;   // query blocks per partial of the Proj weight gradient
 
@@ -1071,6 +1199,10 @@ static size_t bwd_ws_layout(const BwdShape& sh, BwdWs* ws, void* base) {
   const size_t opw = take(size_t(parts) * d * d * 4);
   const size_t opb = take(size_t(parts) * d * 4);
   const size_t og = take(gated ? size_t(qrows) * d * 4 : 0);
+  const int hsplit = bwd_hsplit(sh.B, sh.Hq, sh.Hkv, int(nb));
+  const size_t npart = hsplit > 1 ? size_t(hsplit) * sh.B * sh.Hkv * sh.N * d : 0;
+  const size_t opk = take(npart * 4);
+  const size_t opv = take(npart * 4);
   if (ws != nullptr) {
     unsigned char* p = static_cast<unsigned char*>(base);
     ws->D = reinterpret_cast<float*>(p + oD);
@@ -1088,6 +1220,8 @@ static size_t bwd_ws_layout(const BwdShape& sh, BwdWs* ws, void* base) {
     ws->partW = reinterpret_cast<float*>(p + opw);
     ws->partB = reinterpret_cast<float*>(p + opb);
     ws->gpart = reinterpret_cast<float*>(p + og);
+    ws->part_k = reinterpret_cast<float*>(p + opk);
+    ws->part_v = reinterpret_cast<float*>(p + opv);
   }
   return off;
 }
@@ -1113,13 +1247,17 @@ static void launch_bwd_k_side(const BwdParams& p, int B, bool lin, hipStream_t s
       dk_mean_kernel<<<dim3(D / 8, BK), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
   }
   const dim3 qgrid(p.nb, B * p.H);
-  const dim3 kgrid(p.nb * BK);
+  const dim3 kgrid(p.nb * BK * p.hsplit);
   if (p.critT_sel != nullptr) {
     bwd_dq_kernel<T, D, true><<<qgrid, kBwThreads, 0, st>>>(p);
     bwd_dkdv_kernel<T, D, true><<<kgrid, kBwThreads, 0, st>>>(p);
   } else {
     bwd_dq_kernel<T, D, false><<<qgrid, kBwThreads, 0, st>>>(p);
     bwd_dkdv_kernel<T, D, false><<<kgrid, kBwThreads, 0, st>>>(p);
+  }
+  if (p.hsplit > 1) {
+    const int64_t quads = int64_t(B) * p.Hkv * p.N * D / 4;
+    dkdv_combine_kernel<<<dim3(uint32_t((quads + 255) / 256)), 256, 0, st>>>(p, D);
   }
 }
 
@@ -1243,7 +1381,10 @@ extern "C" sla_status sla_attn_bwd_ext(const sla_tensor* q, const sla_tensor* k,
   p.vsB = v->sB; p.vsH = v->sH; p.vsN = v->sN;
   p.osB = o->sB; p.osH = o->sH; p.osN = o->sN;
   p.dsB = dout->sB; p.dsH = dout->sH; p.dsN = dout->sN;
-  p.H = Hq; p.N = N; p.nb = nb; p.n_valid = n_valid; p.wq = (nb + 31) / 32;
+  p.B = B; p.H = Hq; p.N = N; p.nb = nb; p.n_valid = n_valid; p.wq = (nb + 31) / 32;
+  p.hsplit = bwd_hsplit(B, Hq, Hkv, nb);
+  p.part_k = ws.part_k;
+  p.part_v = ws.part_v;
   p.Hkv = Hkv; p.G = Hq / Hkv; p.Hs = sh.Hs; p.group_map = group_map ? 1 : 0;
   p.window = causal ? window_tokens : 0;
   p.overwrite = lin_mode == SLA_LIN_NONE ? 1 : 0;
@@ -1305,7 +1446,7 @@ extern "C" sla_status sla_attn_bwd_ext(const sla_tensor* q, const sla_tensor* k,
       launch_proj_grad<decltype(tv), decltype(dv_)::value>(p, B, per_head, ws, dproj_w, dproj_b, s);
     });
   }
-  if (gated) gate_reduce_kernel<<<dim3((Hq * d + 255) / 256), 256, 0, s>>>(ws.gpart, B, Hq, nb, d, dw_gate);
+  if (gated) gate_reduce_kernel<<<dim3(d / 8, Hq), 256, 0, s>>>(ws.gpart, B, Hq, nb, d, dw_gate);
   // 2. dH_j = sum of dS_i, dz_j = sum of du_i over the query blocks i with j marginal: the
   //    marginal aggregation with the mask transposed (rows = key blocks, summed items = query
   //    blocks); gated: one row per head whose mask holds every query block
