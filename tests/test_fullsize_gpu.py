@@ -6,7 +6,8 @@ Every row of every workload: pooled scores within one fp32 ulp of the oracle's, 
 oracle's classification of the same scores, plus properties that hold at any size.  Outputs: every
 valid row of wan13b_sla and salad recomputed by the oracle; for nsa_prefill and wan14b_sla sampled
 query blocks (first, second, middle, the last two (the last one holds the padding), and two
-seeded random ones, on the first, middle and last head).
+seeded random ones, on the first, middle and last head).  Backward: wan13b_sla and nsa_prefill on
+sampled blocks, salad on every valid row of two heads.
 """
 import numpy as np
 import pytest
@@ -214,3 +215,96 @@ def test_full_size_backward_sampled():
             say(f"  head {h} {name}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
             assert rel <= REL_L2 and mx <= 3e-2, (h, name)
     assert not dq[:, :, nv:].any() and not dk[:, :, nv:].any() and not dv[:, :, nv:].any()
+
+
+def _rel(d_, r_):
+    return np.linalg.norm(d_) / np.linalg.norm(r_), np.abs(d_).max() / np.abs(r_).max()
+
+
+def test_full_size_backward_salad():
+    """The SALAD backward at full size (sla_attn_bwd_ext, gated all-key branch): every valid row of
+    dQ, dK, dV and the head's dw_g against the gradient oracle, on the first and last head (each key
+    block's gradient depends on every query block through the all-key state, so the whole head is
+    recomputed)."""
+    w = WORKLOADS["salad"]
+    say("[full size backward, salad] generating inputs")
+    q, k, v, wg = make_inputs(w)
+    layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, "salad", kh_bp=w.kh_bp, w_gate=wg, training=True)
+    layer.run()
+    r = np.random.default_rng(w.seed + 19)
+    dO = torch.from_numpy(r.standard_normal(q.shape, dtype=np.float32)).to(torch.bfloat16)
+    dq, dk, dv, dwg = layer.backward(dO.cuda())
+    torch.cuda.synchronize()
+    f = oracle_for(w, q, k, v, wg)
+    nb, nv = f.nb, w.Nv
+    for h in [0, w.Hq - 1]:
+        maps_h = {(0, 0, i): f.map_row(0, h, i) for i in range(nb)}
+        got_rows = gpu_map_rows(layer.maps, [h * nb + i for i in range(nb)])
+        for i in range(nb):
+            assert got_rows[h * nb + i][0] == maps_h[(0, 0, i)]["crit"], (h, i)
+        say(f"[full size backward, salad] head {h}: gradient oracle over the whole head")
+        Qh, Kh, Vh = (X[:, h:h + 1] for X in (f.Q, f.K, f.V))
+        dOh = host(dO[:, h:h + 1]).astype(np.float64)
+        _, dQr, dKr, dVr, dWr = obwd.gradients(Qh, Kh, Vh, dOh, maps_h, nv, f.scale, mode="salad",
+                                               w_gate=wg.numpy()[h:h + 1])
+        for name, g_, r_ in (("dQ", dq, dQr), ("dK", dk, dKr), ("dV", dv, dVr)):
+            rel, mx = _rel(host(g_[0, h, :nv]).astype(np.float64) - r_[0, 0, :nv], r_[0, 0, :nv])
+            say(f"  head {h} {name}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
+            assert rel <= REL_L2 and mx <= 3e-2, (h, name)
+        rel, mx = _rel(host(dwg[h]).astype(np.float64) - dWr[0], dWr[0])
+        say(f"  head {h} dw_g: rel-L2 {rel:.3e}, max-abs {mx:.3e}")
+        assert rel <= REL_L2 and mx <= 3e-2
+    assert not dq[:, :, nv:].any() and not dk[:, :, nv:].any() and not dv[:, :, nv:].any()
+
+
+def test_full_size_backward_nsa():
+    """The NSA-style backward at the full prefill (16 query heads on one KV head, causal selected +
+    window maps shared by the group; sla_attn_bwd_ext with the key blocks' heads split over
+    workgroups): dQ rows of sampled query blocks on two query heads, and dK / dV rows of sampled key
+    blocks recomputed from every (query head, query block) that lists them."""
+    w = WORKLOADS["nsa_prefill"]
+    say("[full size backward, nsa] generating inputs")
+    q, k, v, wg = make_inputs(w)
+    layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, "nsa", n_sel=w.n_sel, window=w.window, training=True)
+    layer.run()
+    r = np.random.default_rng(w.seed + 23)
+    dO = torch.from_numpy(r.standard_normal(q.shape, dtype=np.float32)).to(torch.bfloat16)
+    dq, dk, dv = layer.backward(dO.cuda())
+    torch.cuda.synchronize()
+    f = oracle_for(w, q, k, v, wg)
+    nb, nv = f.nb, w.Nv
+    maps = {(0, 0, i): f.map_row(0, 0, i) for i in range(nb)}
+    got_rows = gpu_map_rows(layer.maps, list(range(nb)))
+    for i in range(nb):
+        assert got_rows[i][0] == maps[(0, 0, i)]["crit"] and got_rows[i][1] == maps[(0, 0, i)]["flags"], i
+    dOn = host(dO).astype(np.float64)
+    heads = [0, w.Hq - 1]
+    qblocks = sample_blocks(nb, 31)
+    say(f"[full size backward, nsa] dQ of query blocks {qblocks} on heads {heads}")
+    _, dQr, _, _ = obwd.gradients(f.Q, f.K, f.V, dOn, maps, nv, f.scale, mode="nsa", window=w.window,
+                                  group_map=True, blocks={(0, h, i) for h in heads for i in qblocks})
+    users_of = {j: [i for i in range(nb) if j in maps[(0, 0, i)]["crit"]] for j in range(nb)}
+    # the last block (listed only by itself) and the two least-listed of 12 seeded candidates
+    cand = sorted(set(np.random.default_rng(37).integers(0, nb - 1, 12).tolist()))
+    kblocks = [nb - 1] + sorted(cand, key=lambda j: (len(users_of[j]), j))[:2]
+    diffs = {"dQ": [], "dK": [], "dV": []}
+    refs_ = {"dQ": [], "dK": [], "dV": []}
+    gq, gk, gv = host(dq), host(dk), host(dv)
+    for h in heads:
+        for i in qblocks:
+            rows = slice(64 * i, min(64 * i + 64, nv))
+            diffs["dQ"].append(gq[0, h, rows] - dQr[0, h, rows])
+            refs_["dQ"].append(dQr[0, h, rows])
+    for j in kblocks:
+        users = {(0, h, i) for h in range(w.Hq) for i in users_of[j]}
+        say(f"  key block {j}: {len(users_of[j])} query blocks x {w.Hq} heads list it")
+        _, _, dKr, dVr = obwd.gradients(f.Q, f.K, f.V, dOn, maps, nv, f.scale, mode="nsa", window=w.window,
+                                        group_map=True, blocks=users)
+        rows = slice(64 * j, min(64 * j + 64, nv))
+        for name, g_, r_ in (("dK", gk, dKr), ("dV", gv, dVr)):
+            diffs[name].append(g_[0, 0, rows] - r_[0, 0, rows])
+            refs_[name].append(r_[0, 0, rows])
+    for name in diffs:
+        rel, mx = _rel(np.concatenate(diffs[name]), np.concatenate(refs_[name]))
+        say(f"  {name}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
+        assert rel <= REL_L2 and mx <= 3e-2, name
