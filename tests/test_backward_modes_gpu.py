@@ -38,6 +38,11 @@ CASES = {
     # a window that ends inside a block, two KV heads
     "nsa_gqa_win200": (scaled(W["nsa_prefill"], "nsa_gqa_win200", N=2048, Nv=2000, Hq=4, Hkv=2, n_sel=4,
                               window=200), False),
+    # two sequences: the split dK/dV partials and the gate gradient sum over the batch
+    "nsa_gqa_b2": (scaled(W["nsa_prefill"], "nsa_gqa_b2", B=2, N=1024, Nv=1000, Hq=4, Hkv=1, n_sel=3,
+                          window=150), False),
+    "gqa_salad_b2": (scaled(W["tiny_sla"], "gqa_salad_b2", mode="salad", B=2, Hq=4, Hkv=2, N=640, Nv=600,
+                            d=64, dtype="bf16", kh_bp=2000, kl_bp=0, gate_seed=11), False),
     # selection only (no window), fp32 inputs, d = 64
     "nsa_sel_only_f32_d64": (scaled(W["nsa_prefill"], "nsa_sel_only_f32_d64", N=1024, Nv=1000, Hq=2, Hkv=1,
                                     d=64, dtype="f32", n_sel=3, window=0), False),
