@@ -98,6 +98,19 @@ __device__ __forceinline__ int tr_addr(int row_g, int col0, int lane) {
   return tpos<D>(row_g + i / 4, col0 / 8 + (i % 4) / 2) + 8 * (i % 2);
 }
 
+// dK tiles use a permuted feature order: tile ct holds, in lane group g, the 4 consecutive features
+// kcol(ct, g) .. + 3 = 32 (ct / 2) + 8 g + 4 (ct % 2) + 0..3 — the features that the 8-feature
+// operand chunk 32 kc + 8 g of a lane holds (kc = ct / 2), so the key values the linear branch's dK
+// needs at its output positions are already in the lane's K operand.  tr_addr_kperm is the
+// transposing read of tile ct's features in that order (its 16 lanes point at 4 rows x 4 pieces of
+// 4 features; output lane i gets piece i / 4, element i % 4 of each row).
+__device__ __forceinline__ int kcol(int ct, int g) { return 32 * (ct / 2) + 8 * g + 4 * (ct % 2); }
+template <int D>
+__device__ __forceinline__ int tr_addr_kperm(int row_g, int ct, int lane) {
+  const int i = lane % 16;
+  return tpos<D>(row_g + i / 4, 4 * (ct / 2) + i % 4) + 8 * (ct % 2);
+}
+
 __device__ __forceinline__ bf16x8 join(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -450,6 +463,126 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 // Writes dK and dV (linear part, all rows): dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k); with
 // smooth-K, phi and its derivative at the shifted key k - mean.  dH_j and dz_j are summed over
 // the query heads that read KV head g (one per head: each head has its own map and queries).
+// Linear branch, key side, for key rows s = 64 j + 16 w + l16 (16 rows per wavefront).  The state
+// gradients dH_j, dz_j are those of the KV head's query heads, summed (SALAD: every key block reads
+// its heads' one all-key state gradient).
+__device__ __forceinline__ int64_t lin_k_srow(const BwdParams& p, int b, int h, int j) {
+  const int64_t hrow = int64_t(b) * p.H + h;
+  return p.gated ? hrow : hrow * p.nb + j;
+}
+
+// dH_j as the [c][r] tile of D rows (2 D bytes each) in two 64-row halves: rows c < 64 at lo, the
+// others at hi (D = 64: lo only).  One query head per KV head: straight from global memory to LDS
+// (the caller waits on vmcnt before its barrier); several: summed in fp32 through registers, every
+// load of one head in flight together.
+template <int D>
+__device__ __forceinline__ void lin_k_stage_dh(const BwdParams& p, int b, int gk, int j, lds_u8* lo, lds_u8* hi) {
+  const int h0 = gk * p.G;
+  if (p.G == 1) {
+    const bf16raw* src = reinterpret_cast<const bf16raw*>(p.dH + lin_k_srow(p, b, h0, j) * D * D);
+    const StageOff<D, kBwWaves> off = stage_offsets<D, false, kBwWaves>(D);
+    stage_tile<bf16raw, D, false, kBwWaves>(src, D, 0, lo, off);
+    if constexpr (D > kBlock) stage_tile<bf16raw, D, false, kBwWaves>(src, D, 1, hi, off);
+    return;
+  }
+  constexpr int kPer = D * D / 8 / kBwThreads;    // 16-byte chunks per thread
+  const int t = threadIdx.x;
+  float acc[kPer][8];
+  for (int hh = 0; hh < p.G; ++hh) {
+    const bf16raw* src = reinterpret_cast<const bf16raw*>(p.dH + lin_k_srow(p, b, h0 + hh, j) * D * D);
+    float x[kPer][8];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) In<bf16raw>::load8_f32(src + 8 * (t + kBwThreads * u), x[u]);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[u][m] = hh == 0 ? x[u][m] : acc[u][m] + x[u][m];
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = t + kBwThreads * u, c = e / (D / 8), r8 = e % (D / 8);
+    f32x8 a8;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) a8[m] = acc[u][m];
+    lds_store16((c < kBlock ? lo : hi) + tpos<D>(c % kBlock, r8), cvt8(a8));
+  }
+}
+
+// dz_j[r] for thread r < D (0 for the others)
+__device__ __forceinline__ float lin_k_dz(const BwdParams& p, int b, int gk, int j, int D) {
+  const int r = threadIdx.x;
+  float z = 0.f;
+  if (r < D)
+    for (int hh = 0; hh < p.G; ++hh) z += p.dz[lin_k_srow(p, b, gk * p.G + hh, j) * D + r];
+  return z;
+}
+
+// The linear branch's dK (with respect to the shifted key when smooth-K) and dV of this lane's key
+// row s (Kr its row of K; kf, vf its K and V rows as the B operands; kv: s < n_valid), from the
+// staged dH tile (lo, hi) and dzs: lk[rt][e] is column kcol(rt, g) + e of dK, lv[ct][e] column
+// 16 ct + 4 g + e of dV; rows past n_valid get 0.
+template <typename T, int D>
+__device__ __forceinline__ void lin_k_grads(const BwdParams& p, int bh, const T* Kr, bool kv,
+                                            const bf16x8 (&kf)[D / 32], const bf16x8 (&vf)[D / 32], lds_u8* lo,
+                                            lds_u8* hi, const float* dzs, f32x4 (&lk)[D / 16],
+                                            f32x4 (&lv)[D / 16]) {
+  constexpr int kKc = D / 32;
+  constexpr int kCt = D / 16;
+  const int lane = threadIdx.x % kWave, l16 = lane % 16, g = lane / 16;
+  auto half = [&](int r) { return r < kBlock ? lo : hi; };   // the half that holds tile row r
+  bf16x8 pkf[kKc];
+#pragma unroll
+  for (int kc = 0; kc < kKc; ++kc) {
+    float x[8];
+    if constexpr (sizeof(T) == 2) {  // bf16 keys: the lane's K operand holds them exactly
+#pragma unroll
+      for (int m = 0; m < 8; ++m) x[m] = static_cast<float>(kf[kc][m]);
+    } else if (kv) {
+      In<T>::load8_f32(Kr + 32 * kc + 8 * g, x);
+    }
+    f32x8 ph;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) ph[m] = kv ? phi(x[m] - (p.k_shift ? p.k_shift[int64_t(bh) * D + 32 * kc + 8 * g + m] : 0.f)) : 0.f;
+    pkf[kc] = cvt8(ph);
+  }
+#pragma unroll
+  for (int rt = 0; rt < kCt; ++rt) {
+    // dphi(k)^T[r][s] = sum_c dH[r][c] v[s][c]: A = dH rows r (transposing reads of [c][r]), the
+    // features r of tile rt in the kcol order
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < kKc; ++kc) {
+      const int c0 = 32 * kc + 8 * g;                 // rows c0 .. c0 + 7 lie in one half
+      lds_u8* Hh = half(c0);
+      const bf16x8 a = join(lds_read_tr4(Hh + tr_addr_kperm<D>(c0 % kBlock, rt, lane)),
+                            lds_read_tr4(Hh + tr_addr_kperm<D>(c0 % kBlock + 4, rt, lane)));
+      acc = mfma16(a, vf[kc], acc);
+    }
+    const int r0 = kcol(rt, g);       // lane holds features r0 .. r0 + 3 = elements 4 (rt % 2) .. of kf[rt / 2]
+    f32x4 kx;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kx[e] = static_cast<float>(kf[rt / 2][4 * (rt % 2) + e]);
+    } else {
+      kx = kv ? load4_f32(Kr + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (p.k_shift != nullptr) kx -= *reinterpret_cast<const f32x4*>(p.k_shift + int64_t(bh) * D + r0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lk[rt][e] = kv ? (acc[e] + dzs[r0 + e]) * dphi(kx[e]) : 0.f;
+  }
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    // dv^T[c][s] = sum_r dH[r][c] phi(k)[s][r]: A = rows c of the [c][r] tile
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int c = 16 * ct + l16;
+#pragma unroll
+    for (int kc = 0; kc < kKc; ++kc) acc = mfma16(lds_load16(half(c) + tpos<D>(c % kBlock, 4 * kc + g)), pkf[kc], acc);
+    lv[ct] = kv ? acc : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// The linear key side as a pass of its own (used with smooth-K, whose dK mean needs every row's
+// linear dK before the sparse branch adds its part): one WG per (key block, KV head) writes dK, dV.
 template <typename T, int D>
 __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
   constexpr int kKc = D / 32;
@@ -457,82 +590,36 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
   constexpr int RB = 2 * D;
   __shared__ __attribute__((aligned(1024))) unsigned char dh_sm[D * RB];   // dH_j: [c][r]
   __shared__ float dzs[D];
-  lds_u8* Ht = to_lds(dh_sm);
+  lds_u8* lo = to_lds(dh_sm);
+  lds_u8* hi = lo + AttnTile<D>::kTileB;
 
   const int j = blockIdx.x, bh = blockIdx.y, b = bh / p.Hkv, gk = bh % p.Hkv;
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
-  // the state gradient of query head h for this key block: its own, or (SALAD) the head's one
-  // state over all keys
-  auto srow = [&](int h) -> int64_t {
-    const int64_t hrow = int64_t(b) * p.H + h;
-    return p.gated ? hrow : hrow * p.nb + j;
-  };
-  const int h0 = gk * p.G;
-  for (int e = t; e < D * D / 8; e += kBwThreads) {
-    const int c = e / (D / 8), r8 = e % (D / 8);
-    float acc[8];
-    In<bf16raw>::load8_f32(reinterpret_cast<const bf16raw*>(p.dH + srow(h0) * D * D + int64_t(c) * D + 8 * r8), acc);
-    for (int hh = 1; hh < p.G; ++hh) {
-      float x[8];
-      In<bf16raw>::load8_f32(reinterpret_cast<const bf16raw*>(p.dH + srow(h0 + hh) * D * D + int64_t(c) * D + 8 * r8), x);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] += x[m];
-    }
-    f32x8 a8;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) a8[m] = acc[m];
-    lds_store16(Ht + tpos<D>(c, r8), cvt8(a8));
-  }
-  for (int e = t; e < D; e += kBwThreads) {
-    float z = 0.f;
-    for (int hh = 0; hh < p.G; ++hh) z += p.dz[srow(h0 + hh) * D + e];
-    dzs[e] = z;
-  }
-  __syncthreads();
+  lin_k_stage_dh<D>(p, b, gk, j, lo, hi);
+  const float z = lin_k_dz(p, b, gk, j, D);
+  if (t < D) dzs[t] = z;
+  SLA_WAIT_VMCNT(0);
+  SLA_WAIT_LGKM0();
+  SLA_BARRIER();
 
   const int s = kBlock * j + 16 * w + l16;
   const bool kv = s < p.n_valid;
   const T* Kr = static_cast<const T*>(p.k) + int64_t(b) * p.ksB + int64_t(gk) * p.ksH + int64_t(s) * p.ksN;
   const T* Vr = static_cast<const T*>(p.v) + int64_t(b) * p.vsB + int64_t(gk) * p.vsH + int64_t(s) * p.vsN;
-  bf16x8 vf[kKc], pkf[kKc];
+  bf16x8 kf[kKc], vf[kKc];
 #pragma unroll
   for (int kc = 0; kc < kKc; ++kc) {
+    kf[kc] = kv ? In<T>::load8(Kr + 32 * kc + 8 * g) : zero8();
     vf[kc] = kv ? In<T>::load8(Vr + 32 * kc + 8 * g) : zero8();
-    float x[8];
-    if (kv) In<T>::load8_f32(Kr + 32 * kc + 8 * g, x);
-    f32x8 ph;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) ph[m] = kv ? phi(x[m] - (p.k_shift ? p.k_shift[int64_t(bh) * D + 32 * kc + 8 * g + m] : 0.f)) : 0.f;
-    pkf[kc] = cvt8(ph);
   }
+  f32x4 lk[kCt], lv[kCt];
+  lin_k_grads<T, D>(p, bh, Kr, kv, kf, vf, lo, hi, dzs, lk, lv);
   float* dkr = p.dk + (int64_t(bh) * p.N + s) * D;
   float* dvr = p.dv + (int64_t(bh) * p.N + s) * D;
 #pragma unroll
-  for (int rt = 0; rt < kCt; ++rt) {
-    // dphi(k)^T[r][s] = sum_c dH[r][c] v[s][c]: A = dH rows r (transposing reads of [c][r])
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < kKc; ++kc) {
-      const bf16x8 a = join(lds_read_tr4(Ht + tr_addr<D>(32 * kc + 8 * g, 16 * rt, lane)),
-                            lds_read_tr4(Ht + tr_addr<D>(32 * kc + 8 * g + 4, 16 * rt, lane)));
-      acc = mfma16(a, vf[kc], acc);
-    }
-    const int r0 = 16 * rt + 4 * g;
-    f32x4 kx = kv ? load4_f32(Kr + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (p.k_shift != nullptr) kx -= *reinterpret_cast<const f32x4*>(p.k_shift + int64_t(bh) * D + r0);
-    f32x4 out;                       // the gradient with respect to the (shifted) key of the linear branch
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = kv ? (acc[e] + dzs[r0 + e]) * dphi(kx[e]) : 0.f;
-    *reinterpret_cast<f32x4*>(dkr + r0) = out;
-  }
-#pragma unroll
   for (int ct = 0; ct < kCt; ++ct) {
-    // dv^T[c][s] = sum_r dH[r][c] phi(k)[s][r]: A = rows c of the [c][r] tile
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < kKc; ++kc) acc = mfma16(lds_load16(Ht + tpos<D>(16 * ct + l16, 4 * kc + g)), pkf[kc], acc);
-    const int c0 = 16 * ct + 4 * g;
-    *reinterpret_cast<f32x4*>(dvr + c0) = kv ? acc : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(dkr + kcol(ct, g)) = lk[ct];
+    *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = lv[ct];
   }
 }
 
@@ -854,7 +941,10 @@ __global__ __launch_bounds__(1024) void kv_order_kernel(const int* __restrict__ 
 // S = Q K^T, dP = dO V^T, dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Q, dO tiles and the
 // rows' log-sum-exp and D are double-buffered: the next (head, query block)'s direct-to-LDS copies
 // run during this one.  CAUSAL: the masks of the dQ kernel (s <= t and (selected or t - s < window)).
-template <typename T, int D, bool CAUSAL>
+// LIN: the linear branch's key side (lin_k_stage_dh / lin_k_grads; not with smooth-K) is added in
+// this kernel's epilogue, so dK and dV are written once; dH_j and dz_j are requested during the
+// last listed block.
+template <typename T, int D, bool CAUSAL, bool LIN>
 __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
@@ -935,6 +1025,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   int buf = 0;
+  int dh_buf = -1;                   // LIN: the buffer pair that received dH_j during the last block
+  float dzv = 0.f;                   // LIN: dz_j[t], requested before the loop
+  if constexpr (LIN) {
+    if (hs == 0) dzv = lin_k_dz(p, b, gk, j, D);
+  }
   while (cur >= 0) {
     const int nxt = next_block(h_nxt, sel_nxt);
     lds_u8* Qt = to_lds(q_sm[buf]);
@@ -949,7 +1044,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
     }
-    if (nxt >= 0) stage(nxt, h_nxt, buf ^ 1);
+    if (nxt >= 0) {
+      stage(nxt, h_nxt, buf ^ 1);
+    } else if constexpr (LIN) {      // last block: the linear part's dH_j and dz_j into the free buffers
+      if (hs == 0 && p.G == 1) {
+        lin_k_stage_dh<D>(p, b, gk, j, to_lds(q_sm[buf ^ 1]), to_lds(g_sm[buf ^ 1]));
+        dh_buf = buf ^ 1;
+      }
+    }
     bf16x4 pb[4], db[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -976,7 +1078,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
       pb[tt] = cvt4(pr);
       db[tt] = cvt4(ds);
     }
-    // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s]
+    // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s] (r in the kcol order)
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
@@ -984,8 +1086,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 ag = join(lds_read_tr4(Gt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
                                lds_read_tr4(Gt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
         dv[ct] = mfma16(ag, join(pb[2 * pr], pb[2 * pr + 1]), dv[ct]);
-        const bf16x8 aq = join(lds_read_tr4(Qt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
-                               lds_read_tr4(Qt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
+        const bf16x8 aq = join(lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 4 * g, ct, lane)),
+                               lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 16 + 4 * g, ct, lane)));
         dk[ct] = mfma16(aq, join(db[2 * pr], db[2 * pr + 1]), dk[ct]);
       }
     cur = nxt;
@@ -993,33 +1095,64 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     sel_cur = sel_nxt;
     buf ^= 1;
   }
+  float* dkr = p.dk + (int64_t(bk) * p.N + s) * D;
+  float* dvr = p.dv + (int64_t(bk) * p.N + s) * D;
+  f32x4 lk[kCt], lv[kCt];
+  if constexpr (LIN) {
+    if (hs == 0) {                   // once per key row: the first head subset's workgroup
+      lds_u8* lo = to_lds(dh_buf >= 0 ? q_sm[dh_buf] : q_sm[0]);
+      lds_u8* hi = to_lds(dh_buf >= 0 ? g_sm[dh_buf] : q_sm[1]);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();                 // every wavefront is done with the last block's tiles and lse_s
+      if (dh_buf < 0) lin_k_stage_dh<D>(p, b, gk, j, lo, hi);   // several query heads, or no listing block
+      float* dzs = &lse_s[0][0];     // D floats
+      if (t < D) dzs[t] = dzv;
+      SLA_WAIT_VMCNT(0);
+      SLA_WAIT_LGKM0();
+      SLA_BARRIER();
+      lin_k_grads<T, D>(p, bk, Kr, kv, kf, vf, lo, hi, dzs, lk, lv);
+    }
+  }
   if (p.hsplit > 1) {                // a subset's partial sums, added up by dkdv_combine_kernel
+    if constexpr (LIN) {
+      if (hs == 0) {                 // the linear part is written first; the combine adds the partials
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
+          *reinterpret_cast<f32x4*>(dkr + kcol(ct, g)) = lk[ct];
+          *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = lv[ct];
+        }
+      }
+    }
     const int64_t off = ((int64_t(hs) * p.B * p.Hkv + bk) * p.N + s) * D;
     float* pk = p.part_k + off;
     float* pv = p.part_v + off;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      *reinterpret_cast<f32x4*>(pk + 16 * ct + 4 * g) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(pk + kcol(ct, g)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(pv + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     return;
   }
-  float* dkr = p.dk + (int64_t(bk) * p.N + s) * D;
-  float* dvr = p.dv + (int64_t(bk) * p.N + s) * D;
-  if (p.overwrite) {                 // no linear branch: this kernel writes every row (padded: 0)
+  if constexpr (LIN) {               // linear part + sparse part, every row written (padded: 0)
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      *reinterpret_cast<f32x4*>(dkr + 16 * ct + 4 * g) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dkr + kcol(ct, g)) = kv ? lk[ct] + dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = kv ? lv[ct] + dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else if (p.overwrite) {          // no linear branch: this kernel writes every row (padded: 0)
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      *reinterpret_cast<f32x4*>(dkr + kcol(ct, g)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   } else if (kv) {
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      f32x4* k4 = reinterpret_cast<f32x4*>(dkr + 16 * ct + 4 * g);
+      f32x4* k4 = reinterpret_cast<f32x4*>(dkr + kcol(ct, g));
       f32x4* v4 = reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g);
       f32x4 add = dk[ct] * p.scale;
       // smooth-K: the linear branch saw k - mean(k), so its dK loses its own mean over the valid rows
-      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + 16 * ct + 4 * g);
+      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + kcol(ct, g));
       *k4 = *k4 + add;
       *v4 = *v4 + dv[ct];
     }
@@ -1241,19 +1374,22 @@ static void launch_bwd_q_side(const BwdParams& p, int B, hipStream_t st) {
 template <typename T, int D>
 static void launch_bwd_k_side(const BwdParams& p, int B, bool lin, hipStream_t st) {
   const int BK = B * p.Hkv;
-  if (lin) {
+  // with smooth-K the linear dK's mean over all rows is needed before the sparse part is added, so
+  // the linear key side runs first as a pass of its own; otherwise the dK/dV kernel adds it
+  const bool fused = lin && p.dk_mean == nullptr;
+  if (lin && !fused) {
     bwd_lin_k_kernel<T, D><<<dim3(p.nb, BK), kBwThreads, 0, st>>>(p);
-    if (p.dk_mean != nullptr)
-      dk_mean_kernel<<<dim3(D / 8, BK), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
+    dk_mean_kernel<<<dim3(D / 8, BK), 256, 0, st>>>(p.dk, p.N, D, p.n_valid, const_cast<float*>(p.dk_mean));
   }
   const dim3 qgrid(p.nb, B * p.H);
   const dim3 kgrid(p.nb * BK * p.hsplit);
   if (p.critT_sel != nullptr) {
     bwd_dq_kernel<T, D, true><<<qgrid, kBwThreads, 0, st>>>(p);
-    bwd_dkdv_kernel<T, D, true><<<kgrid, kBwThreads, 0, st>>>(p);
+    bwd_dkdv_kernel<T, D, true, false><<<kgrid, kBwThreads, 0, st>>>(p);
   } else {
     bwd_dq_kernel<T, D, false><<<qgrid, kBwThreads, 0, st>>>(p);
-    bwd_dkdv_kernel<T, D, false><<<kgrid, kBwThreads, 0, st>>>(p);
+    if (fused) bwd_dkdv_kernel<T, D, false, true><<<kgrid, kBwThreads, 0, st>>>(p);
+    else bwd_dkdv_kernel<T, D, false, false><<<kgrid, kBwThreads, 0, st>>>(p);
   }
   if (p.hsplit > 1) {
     const int64_t quads = int64_t(B) * p.Hkv * p.N * D / 4;
