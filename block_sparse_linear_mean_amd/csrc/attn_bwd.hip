@@ -459,13 +459,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ linear branch, key side
 
-// One workgroup per (key block j, KV head g); wavefront w owns keys 64 j + 16 w + l % 16.
-// Writes dK and dV (linear part, all rows): dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k); with
-// smooth-K, phi and its derivative at the shifted key k - mean.  dH_j and dz_j are summed over
-// the query heads that read KV head g (one per head: each head has its own map and queries).
-// Linear branch, key side, for key rows s = 64 j + 16 w + l16 (16 rows per wavefront).  The state
-// gradients dH_j, dz_j are those of the KV head's query heads, summed (SALAD: every key block reads
-// its heads' one all-key state gradient).
+// The linear part of dK and dV for key block j of KV head g, wavefront w owning keys
+// 64 j + 16 w + l % 16: dphi(k) = dH_j v + dz_j, dv = dH_j^T phi(k); with smooth-K, phi and its
+// derivative at the shifted key k - mean.  dH_j and dz_j are summed over the query heads that read
+// KV head g (one per head: each head has its own map and queries; SALAD: every key block reads its
+// heads' one all-key state gradient).  The dK/dV kernel adds this in its epilogue; with smooth-K it
+// runs as a pass of its own (bwd_lin_k_kernel).
 __device__ __forceinline__ int64_t lin_k_srow(const BwdParams& p, int b, int h, int j) {
   const int64_t hrow = int64_t(b) * p.H + h;
   return p.gated ? hrow : hrow * p.nb + j;
