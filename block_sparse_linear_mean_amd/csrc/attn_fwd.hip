@@ -560,7 +560,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int rr = e / Tl::kChunks, c = e % Tl::kChunks;
         bf16x8 x = lds_load16(Kb + rr * Tl::kRowB + 16 * (c ^ (rr % Tl::kChunks)));
         if (kBlock * i + rr >= p.n_valid) x = zero8();
-        *reinterpret_cast<bf16x8*>(ob + rr * D + 8 * c) = x;
+        // streaming store: the output is not read again by this layer, and the next pass's reads
+        // then find fewer dirty lines to evict
+        __builtin_nontemporal_store(x, reinterpret_cast<bf16x8*>(ob + rr * D + 8 * c));
       }
       return;
     }
