@@ -98,7 +98,8 @@ __device__ __forceinline__ int tr_addr(int row_g, int col0, int lane) {
   return tpos<D>(row_g + i / 4, col0 / 8 + (i % 4) / 2) + 8 * (i % 2);
 }
 
-// dK tiles use a permuted feature order: tile ct holds, in lane group g, the 4 consecutive features
+// With the linear key side in the dK/dV epilogue, dK tiles use a permuted feature order: tile ct
+// holds, in lane group g, the 4 consecutive features
 // kcol(ct, g) .. + 3 = 32 (ct / 2) + 8 g + 4 (ct % 2) + 0..3 — the features that the 8-feature
 // operand chunk 32 kc + 8 g of a lane holds (kc = ct / 2), so the key values the linear branch's dK
 // needs at its output positions are already in the lane's K operand.  tr_addr_kperm is the
@@ -1023,6 +1024,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // the first of the 4 dK features a lane holds in tile ct: the kcol order with the linear epilogue
+  // (faster there, and the epilogue needs it), the plain order otherwise (2% faster for NSA-style maps)
+  auto dcol = [&](int ct) { return LIN ? kcol(ct, g) : 16 * ct + 4 * g; };
   int buf = 0;
   int dh_buf = -1;                   // LIN: the buffer pair that received dH_j during the last block
   float dzv = 0.f;                   // LIN: dz_j[t], requested before the loop
@@ -1077,7 +1081,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
       pb[tt] = cvt4(pr);
       db[tt] = cvt4(ds);
     }
-    // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s] (r in the kcol order)
+    // dV^T[c][s] += sum_t dO[t][c] P[t][s]; dK^T[r][s] += sum_t Q[t][r] dS[t][s] (LIN: r in the kcol order)
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
@@ -1085,8 +1089,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 ag = join(lds_read_tr4(Gt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
                                lds_read_tr4(Gt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
         dv[ct] = mfma16(ag, join(pb[2 * pr], pb[2 * pr + 1]), dv[ct]);
-        const bf16x8 aq = join(lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 4 * g, ct, lane)),
-                               lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 16 + 4 * g, ct, lane)));
+        bf16x8 aq;
+        if constexpr (LIN)
+          aq = join(lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 4 * g, ct, lane)),
+                    lds_read_tr4(Qt + tr_addr_kperm<D>(32 * pr + 16 + 4 * g, ct, lane)));
+        else
+          aq = join(lds_read_tr4(Qt + tr_addr<D>(32 * pr + 4 * g, 16 * ct, lane)),
+                    lds_read_tr4(Qt + tr_addr<D>(32 * pr + 16 + 4 * g, 16 * ct, lane)));
         dk[ct] = mfma16(aq, join(db[2 * pr], db[2 * pr + 1]), dk[ct]);
       }
     cur = nxt;
@@ -1127,7 +1136,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
     float* pv = p.part_v + off;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      *reinterpret_cast<f32x4*>(pk + kcol(ct, g)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(pk + dcol(ct)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(pv + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     return;
@@ -1141,17 +1150,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dkdv_kernel(BwdParams p) {
   } else if (p.overwrite) {          // no linear branch: this kernel writes every row (padded: 0)
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      *reinterpret_cast<f32x4*>(dkr + kcol(ct, g)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dkr + dcol(ct)) = kv ? dk[ct] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g) = kv ? dv[ct] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   } else if (kv) {
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      f32x4* k4 = reinterpret_cast<f32x4*>(dkr + kcol(ct, g));
+      f32x4* k4 = reinterpret_cast<f32x4*>(dkr + dcol(ct));
       f32x4* v4 = reinterpret_cast<f32x4*>(dvr + 16 * ct + 4 * g);
       f32x4 add = dk[ct] * p.scale;
       // smooth-K: the linear branch saw k - mean(k), so its dK loses its own mean over the valid rows
-      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + kcol(ct, g));
+      if (p.dk_mean != nullptr) add -= *reinterpret_cast<const f32x4*>(p.dk_mean + int64_t(bk) * D + dcol(ct));
       *k4 = *k4 + add;
       *v4 = *v4 + dv[ct];
     }
