@@ -141,11 +141,17 @@ __device__ __forceinline__ float group4_sum(float x) {
 // n_rows are written as zeros (and never read from X).
 template <typename T, int D>
 __device__ __forceinline__ void stage64(const T* __restrict__ X, int64_t sN, int row0, int n_rows, lds_u8* tile) {
-  constexpr int kChunks = D / 8;
-  for (int e = threadIdx.x; e < kBlock * kChunks; e += kBwThreads) {
-    const int r = e / kChunks, c = e % kChunks;
-    const bf16x8 x = row0 + r < n_rows ? In<T>::load8(X + int64_t(row0 + r) * sN + 8 * c) : zero8();
-    lds_store16(tile + tpos<D>(r, c), x);
+  constexpr int kChunks = D / 8, kPer = kBlock * kChunks / kBwThreads;
+  bf16x8 x[kPer];                    // every load of the thread in flight together
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = threadIdx.x + kBwThreads * u, r = e / kChunks, c = e % kChunks;
+    x[u] = row0 + r < n_rows ? In<T>::load8(X + int64_t(row0 + r) * sN + 8 * c) : zero8();
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = threadIdx.x + kBwThreads * u;
+    lds_store16(tile + tpos<D>(e / kChunks, e % kChunks), x[u]);
   }
 }
 
@@ -236,20 +242,28 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   // the state: the KV head's over all keys (gated), or the map row's marginal sum (the map row is
   // the query row: a linear branch takes per-head maps)
   const int64_t srow = GATED ? int64_t(b) * p.Hkv + h / p.G : row;
+  constexpr int kPer = D * D / 8 / kBwThreads;   // 16-byte chunks of a d x d tile per thread
   if constexpr (GATED) {
+    // the KV head's fp32 state, converted to bf16 through registers, the thread's loads in flight
+    // together
     const float* Sg = p.Sf + srow * D * D;
-    for (int e = t; e < D * D / 8; e += kBwThreads) {
-      const int c = e / (D / 8), r8 = e % (D / 8);
-      lds_store16(St + tpos<D>(c, r8), In<float>::load8(Sg + int64_t(c) * D + 8 * r8));
+    bf16x8 x[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) x[u] = In<float>::load8(Sg + 8 * (t + kBwThreads * u));
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = t + kBwThreads * u;
+      lds_store16(St + tpos<D>(e / (D / 8), e % (D / 8)), x[u]);
     }
   } else {
-    const u16* Sg = p.S + row * D * D;
-    for (int e = t; e < D * D / 8; e += kBwThreads) {
-      const int c = e / (D / 8), r8 = e % (D / 8);
-      lds_store16(St + tpos<D>(c, r8), *reinterpret_cast<const bf16x8*>(Sg + int64_t(c) * D + 8 * r8));
-    }
+    // the row's bf16 sums straight from global memory to LDS (64-row tile copies)
+    const bf16raw* Sg = reinterpret_cast<const bf16raw*>(p.S + row * D * D);
+    const StageOff<D, kBwWaves> off = stage_offsets<D, false, kBwWaves>(D);
+    stage_tile<bf16raw, D, false, kBwWaves>(Sg, D, 0, St, off);
+    if constexpr (D > kBlock) stage_tile<bf16raw, D, false, kBwWaves>(Sg, D, 1, St + AttnTile<D>::kTileB, off);
   }
   for (int e = t; e < D; e += kBwThreads) us[e] = p.u[srow * D + e];
+  SLA_WAIT_VMCNT(0);
   __syncthreads();
 
   const int tq = kBlock * i + 16 * w + l16;
@@ -298,9 +312,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   if constexpr (PROJ) {
     lds_u8* Wt = to_lds(w_sm);
     const float* Wg = p.proj_w + int64_t(h) * p.proj_sH;
-    for (int e = t; e < D * D / 8; e += kBwThreads) {
-      const int o = e / (D / 8), c8 = e % (D / 8);
-      lds_store16(Wt + tpos<D>(o, c8), In<float>::load8(Wg + int64_t(o) * D + 8 * c8));
+    bf16x8 wx[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) wx[u] = In<float>::load8(Wg + 8 * (t + kBwThreads * u));
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = t + kBwThreads * u;
+      lds_store16(Wt + tpos<D>(e / (D / 8), e % (D / 8)), wx[u]);
     }
     __syncthreads();
     const float* bias = p.proj_b != nullptr ? p.proj_b + int64_t(h) * (p.proj_sH != 0 ? D : 0) : nullptr;
