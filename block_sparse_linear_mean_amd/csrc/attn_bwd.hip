@@ -211,8 +211,24 @@ __device__ __forceinline__ bf16x4 lds_load8(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x4*>(p);
 }
 
-// One workgroup per (query block i, head); wavefront w owns query rows 64 i + 16 w + l % 16.
-// Writes dQ (linear part, all rows), D_t, and the per-row gradients dS_i ([c][r], bf16), du_i.
+// LDS the linear query side works in: St the row's state as the [c][r] tile (D rows of 2 D bytes),
+// Pq and Dn 64-row tiles (phi(Q_i) [t][r], dN_i [t][c]), Wt the Proj weight [o][c] (PROJ), us D
+// floats, dden_s and dlog_s 64 floats, gred the gate-gradient row-group sums (GATED, kRg x D).
+struct LinQLds {
+  lds_u8* St;
+  lds_u8* Pq;
+  lds_u8* Dn;
+  lds_u8* Wt;
+  float* us;
+  float* dden_s;
+  float* dlog_s;
+  float* gred;
+};
+
+// Linear branch, query side, of query block i of head h (wavefront w owns query rows
+// 64 i + 16 w + l % 16): writes D_t and the per-row gradients dS_i ([c][r], bf16) and du_i, and
+// returns the lane's linear dQ (dql[rt][e]: feature 16 rt + 4 g + e of its row; 0 on padded rows)
+// and its row's D_t.
 // PROJ: O = O_s + O_l W^T + b, so O_s = O - O_l W^T - b, the gradient reaching O_l is dO W, and
 // O_l is written out (bf16) for the weight gradient.
 // GATED (SALAD): the state is the head's sum over all keys (H_all, z_all, fp32) and
@@ -220,23 +236,18 @@ __device__ __forceinline__ bf16x4 lds_load8(const lds_u8* p) {
 // dlogit q to the gate weights' gradient (a partial per query block), dlogit = (dO . y) g (1 - g)
 // with y the ungated term.
 template <typename T, int D, bool PROJ, bool GATED>
-__global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
+__device__ __forceinline__ void lin_q_side(const BwdParams& p, int b, int h, int i, const LinQLds& L,
+                                           f32x4 (&dql)[D / 16], float& Dt) {
   constexpr int kKc = D / 32;     // 32-deep k-steps over features
   constexpr int kCt = D / 16;     // 16-wide feature tiles
-  constexpr int RB = 2 * D;
-  __shared__ __attribute__((aligned(1024))) unsigned char w_sm[PROJ ? D * RB : 16];  // W: [o][c]
-  __shared__ __attribute__((aligned(1024))) unsigned char st_sm[D * RB];      // S_i^T: [c][r]
-  __shared__ __attribute__((aligned(1024))) unsigned char pq_sm[kBlock * RB]; // phi(Q_i): [t][r]
-  __shared__ __attribute__((aligned(1024))) unsigned char dn_sm[kBlock * RB]; // dN_i: [t][c]
-  __shared__ float us[D];
-  __shared__ float dden_s[kBlock];
-  __shared__ float dlog_s[GATED ? kBlock : 1];
-  __shared__ float gred[GATED ? kBwThreads / (D / 8) : 1][GATED ? D : 1];   // gate-gradient row-group sums
-  lds_u8* St = to_lds(st_sm);
-  lds_u8* Pq = to_lds(pq_sm);
-  lds_u8* Dn = to_lds(dn_sm);
+  lds_u8* St = L.St;
+  lds_u8* Pq = L.Pq;
+  lds_u8* Dn = L.Dn;
+  float* us = L.us;
+  float* dden_s = L.dden_s;
+  float* dlog_s = L.dlog_s;
 
-  const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int bh = b * p.H + h;
   const int t = threadIdx.x, lane = t % kWave, w = t / kWave, l16 = lane % 16, g = lane / 16;
   const int64_t row = int64_t(bh) * p.nb + i;
   // the state: the KV head's over all keys (gated), or the map row's marginal sum (the map row is
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) go[ct] = qv ? load4_f32(Gr + 16 * ct + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (PROJ) {
-    lds_u8* Wt = to_lds(w_sm);
+    lds_u8* Wt = L.Wt;
     const float* Wg = p.proj_w + int64_t(h) * p.proj_sH;
     bf16x8 wx[kPer];
 #pragma unroll
@@ -385,8 +396,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   dsum = group4_sum(dsum);
   ax = group4_sum(ax);
   const float dden = -ax * inv_den;
+  Dt = qv ? dsum : 0.f;
   if (g == 0) {
-    p.D[int64_t(bh) * p.N + tq] = qv ? dsum : 0.f;
+    p.D[int64_t(bh) * p.N + tq] = Dt;
     dden_s[16 * w + l16] = dden;
     if constexpr (GATED) dlog_s[16 * w + l16] = qv ? dlogit : 0.f;
   }
@@ -394,7 +406,6 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
   // dphi(q)^T[r][t] = sum_c S[r][c] dn[t][c] (+ u[r] dden): A = S (transposing reads of the
   // [c][r] tile, rows c paired as 16 (2 kc) + 4 g .. and 16 (2 kc + 1) + 4 g ..), B = dn
   const T* Qb = static_cast<const T*>(p.q) + int64_t(b) * p.qsB + int64_t(h) * p.qsH;
-  float* dqr = p.dq + (int64_t(bh) * p.N + tq) * D;
 #pragma unroll
   for (int rt = 0; rt < kCt; ++rt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -413,7 +424,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
       out[e] = qv ? (acc[e] + us[r0 + e] * dden) * dphi(qx[e]) : 0.f;
       if constexpr (GATED) out[e] += qv ? dlogit * p.w_gate[int64_t(h) * D + r0 + e] : 0.f;
     }
-    *reinterpret_cast<f32x4*>(dqr + r0) = out;
+    dql[rt] = out;
   }
   __syncthreads();                // phi(Q_i), dN_i and dden complete in LDS
   if constexpr (GATED) {
@@ -436,12 +447,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
         for (int m = 0; m < 8; ++m) s8[m] += dlog_s[rg + kRg * u] * x[u][m];
       }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) gred[rg][8 * ch + m] = s8[m];
+    for (int m = 0; m < 8; ++m) L.gred[rg * D + 8 * ch + m] = s8[m];
     __syncthreads();
     for (int r = t; r < D; r += kBwThreads) {
       float s = 0.f;
 #pragma unroll
-      for (int g2 = 0; g2 < kRg; ++g2) s += gred[g2][r];
+      for (int g2 = 0; g2 < kRg; ++g2) s += L.gred[g2 * D + r];
       p.gpart[row * D + r] = s;
     }
   }
@@ -474,6 +485,32 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
     }
     p.du[row * D + r] = s;
   }
+}
+
+// One workgroup per (query block i, head): the linear query side as a pass of its own (with Proj,
+// whose weight needs the LDS the dQ kernel uses for its tiles), writing the linear dQ of every row.
+template <typename T, int D, bool PROJ, bool GATED>
+__global__ __launch_bounds__(kBwThreads) void bwd_lin_q_kernel(BwdParams p) {
+  constexpr int RB = 2 * D;
+  constexpr int kCt = D / 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char w_sm[PROJ ? D * RB : 16];  // W: [o][c]
+  __shared__ __attribute__((aligned(1024))) unsigned char st_sm[D * RB];      // S_i^T: [c][r]
+  __shared__ __attribute__((aligned(1024))) unsigned char pq_sm[kBlock * RB]; // phi(Q_i): [t][r]
+  __shared__ __attribute__((aligned(1024))) unsigned char dn_sm[kBlock * RB]; // dN_i: [t][c]
+  __shared__ float us[D];
+  __shared__ float dden_s[kBlock];
+  __shared__ float dlog_s[GATED ? kBlock : 1];
+  __shared__ float gred[GATED ? kBwThreads / (D / 8) * D : 1];   // gate-gradient row-group sums
+  const LinQLds L{to_lds(st_sm), to_lds(pq_sm), to_lds(dn_sm), to_lds(w_sm), us, dden_s, dlog_s, gred};
+  const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  f32x4 dql[kCt];
+  float Dt;
+  lin_q_side<T, D, PROJ, GATED>(p, b, h, i, L, dql, Dt);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int tq = kBlock * i + 16 * w + lane % 16;
+  float* dqr = p.dq + (int64_t(bh) * p.N + tq) * D;
+#pragma unroll
+  for (int rt = 0; rt < kCt; ++rt) *reinterpret_cast<f32x4*>(dqr + 16 * rt + 4 * (lane / 16)) = dql[rt];
 }
 
 // ------------------------------------------------------------------ linear branch, key side
@@ -783,13 +820,19 @@ __device__ __forceinline__ void zero_rows(lds_u8* tile, int r0) {
 // CAUSAL (NSA-style maps): key s of block j is allowed iff s <= t and (j is a selected block or
 // t - s < window).  K and V tiles are double-buffered: the next block's direct-to-LDS copies run
 // during this one.
-template <typename T, int D, bool CAUSAL>
+// LINQ (1: row states, 2: gated): the linear query side (lin_q_side) runs first in the same
+// workgroup, in the tile buffers, and gives the rows' D and linear dQ; dQ is then written once.
+template <typename T, int D, bool CAUSAL, int LINQ>
 __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   using Tl = AttnTile<D>;
   constexpr int kKc = D / 32;
   constexpr int kCt = D / 16;
   __shared__ __attribute__((aligned(1024))) unsigned char k_sm[2][Tl::kTileB];
   __shared__ __attribute__((aligned(1024))) unsigned char v_sm[2][Tl::kTileB];
+  __shared__ float lq_us[LINQ ? D : 1];
+  __shared__ float lq_dden[LINQ ? kBlock : 1];
+  __shared__ float lq_dlog[LINQ == 2 ? kBlock : 1];
+  __shared__ float lq_gred[LINQ == 2 ? kBwThreads / (D / 8) * D : 1];
 
   const int i = blockIdx.x, bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
   const int gk = h / p.G;                          // KV head
@@ -816,6 +859,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
     }
     return -1;
   };
+  f32x4 dql[kCt];
+  float Dt_lin = 0.f;
+  if constexpr (LINQ != 0) {         // St in the K buffers (D rows of 2 D bytes), Pq and Dn in the V buffers
+    const LinQLds L{to_lds(k_sm[0]), to_lds(v_sm[0]), to_lds(v_sm[1]), nullptr, lq_us, lq_dden, lq_dlog, lq_gred};
+    lin_q_side<T, D, false, LINQ == 2>(p, b, h, i, L, dql, Dt_lin);
+    SLA_WAIT_LGKM0();
+    SLA_BARRIER();                   // the tile buffers are free again
+  }
   int epos = cbeg;
   bool sel_cur = true, sel_nxt = true;
   int cur = next_block(epos, sel_cur);
@@ -832,7 +883,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   const float lse_raw = qv ? p.lse[int64_t(bh) * p.N + tq] : -__builtin_inff();
   const bool has = qv && lse_raw > -__builtin_inff();
   const float lse2 = has ? lse_raw * kLog2e : 0.f;
-  const float Dt = qv ? p.D[int64_t(bh) * p.N + tq] : 0.f;
+  const float Dt = LINQ != 0 ? Dt_lin : (qv ? p.D[int64_t(bh) * p.N + tq] : 0.f);
   const float c2 = p.scale_log2;
 
   f32x4 acc[kCt];
@@ -897,7 +948,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_kernel(BwdParams p) {
   // lane holds dQ^T[r = 16 rt + 4 g + e][t]: added to the linear part, or written (no linear branch;
   // padded rows then get their zeros here)
   float* dqr = p.dq + (int64_t(bh) * p.N + tq) * D;
-  if (p.overwrite) {
+  if constexpr (LINQ != 0) {         // linear part + sparse part, every row written (padded: 0)
+#pragma unroll
+    for (int rt = 0; rt < kCt; ++rt)
+      *reinterpret_cast<f32x4*>(dqr + 16 * rt + 4 * g) = qv ? dql[rt] + acc[rt] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (p.overwrite) {
 #pragma unroll
     for (int rt = 0; rt < kCt; ++rt)
       *reinterpret_cast<f32x4*>(dqr + 16 * rt + 4 * g) = qv ? acc[rt] * p.scale : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1385,12 +1440,15 @@ static size_t bwd_ws_layout(const BwdShape& sh, BwdWs* ws, void* base) {
   return off;
 }
 
+// The query side: with a linear branch and no Proj, the dQ kernel that also does the linear query
+// side (dQ complete after it); with Proj, the linear query side as a pass of its own (the dQ kernel
+// follows with the key side); without a linear branch, D = dO . O.
 template <typename T, int D>
 static void launch_bwd_q_side(const BwdParams& p, int B, hipStream_t st) {
   const dim3 grid(p.nb, B * p.H);
-  if (p.gated) bwd_lin_q_kernel<T, D, false, true><<<grid, kBwThreads, 0, st>>>(p);
+  if (p.gated) bwd_dq_kernel<T, D, false, 2><<<grid, kBwThreads, 0, st>>>(p);
   else if (p.proj_w != nullptr) bwd_lin_q_kernel<T, D, true, false><<<grid, kBwThreads, 0, st>>>(p);
-  else if (p.S != nullptr) bwd_lin_q_kernel<T, D, false, false><<<grid, kBwThreads, 0, st>>>(p);
+  else if (p.S != nullptr) bwd_dq_kernel<T, D, false, 1><<<grid, kBwThreads, 0, st>>>(p);
   else {
     const int rows = B * p.H * p.N;
     bwd_dot_kernel<T, D><<<dim3((rows + 15) / 16), 256, 0, st>>>(p, rows);
@@ -1410,10 +1468,11 @@ static void launch_bwd_k_side(const BwdParams& p, int B, bool lin, hipStream_t s
   const dim3 qgrid(p.nb, B * p.H);
   const dim3 kgrid(p.nb * BK * p.hsplit);
   if (p.critT_sel != nullptr) {
-    bwd_dq_kernel<T, D, true><<<qgrid, kBwThreads, 0, st>>>(p);
+    bwd_dq_kernel<T, D, true, 0><<<qgrid, kBwThreads, 0, st>>>(p);
     bwd_dkdv_kernel<T, D, true, false><<<kgrid, kBwThreads, 0, st>>>(p);
   } else {
-    bwd_dq_kernel<T, D, false><<<qgrid, kBwThreads, 0, st>>>(p);
+    // with a linear branch and no Proj the query side's kernel has written dQ already
+    if (!lin || p.proj_w != nullptr) bwd_dq_kernel<T, D, false, 0><<<qgrid, kBwThreads, 0, st>>>(p);
     if (fused) bwd_dkdv_kernel<T, D, false, true><<<kgrid, kBwThreads, 0, st>>>(p);
     else bwd_dkdv_kernel<T, D, false, false><<<kgrid, kBwThreads, 0, st>>>(p);
   }
@@ -1600,7 +1659,8 @@ extern "C" sla_status sla_attn_bwd_ext(const sla_tensor* q, const sla_tensor* k,
   kv_order_kernel<<<1, 1024, 0, s>>>(ws.kv_counts, krows, max_count, ws.kv_order);
 
   // 1. query side: linear dQ, D, dS_i, du_i (and O_l with Proj; the gate weights' partials when
-  //    gated), or D alone without a linear branch
+  //    gated) — without Proj inside the dQ kernel, which then writes the whole dQ — or D alone
+  //    without a linear branch
   by_type(q->dtype, d, [&](auto tv, auto dv_) { launch_bwd_q_side<decltype(tv), decltype(dv_)::value>(p, B, s); });
   if (proj) {
     const int per_head = proj_heads != 1;
