@@ -461,8 +461,8 @@ __device__ __forceinline__ void lin_q_side(const BwdParams& p, int b, int h, int
   // n = w, w + 4, ... of the kCt x kCt grid; the k steps run over the 64 query rows
   u16* dSg = p.dS + row * D * D;
 #pragma unroll
-  for (int n = w; n < kCt * kCt; n += kBwWaves) {
-    const int rt = n / kCt, ct = n % kCt;
+  for (int m = 0; m < kCt * kCt / kBwWaves; ++m) {
+    const int n = w + kBwWaves * m, rt = n / kCt, ct = n % kCt;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_lin_k_kernel(BwdParams p) {
 // query blocks of one (batch, head): grid x = chunk (of the rows that share weight y), y = weight.
 // Rows past n_valid take no part.  Partials are summed by proj_reduce_kernel in a fixed order.
 template <typename T, int D>
-__global__ __launch_bounds__(kBwThreads) void proj_grad_kernel(BwdParams p, int B, int per_head, int chunks_per_bh,
+__global__ __launch_bounds__(kBwThreads) void proj_grad_kernel(BwdParams p, int per_head, int chunks_per_bh,
                                                                float* __restrict__ partW, float* __restrict__ partB) {
   constexpr int kCt = D / 16;
   constexpr int kTiles = kCt * kCt / kBwWaves;   // 16 x 16 output tiles per wavefront
@@ -1489,7 +1489,7 @@ static void launch_proj_grad(const BwdParams& p, int B, int per_head, const BwdW
   const int chunks = (p.nb + kProjChunk - 1) / kProjChunk;
   const int weights = per_head ? p.H : 1;
   const int parts = (per_head ? B : B * p.H) * chunks;
-  proj_grad_kernel<T, D><<<dim3(parts, weights), kBwThreads, 0, st>>>(p, B, per_head, chunks, ws.partW, ws.partB);
+  proj_grad_kernel<T, D><<<dim3(parts, weights), kBwThreads, 0, st>>>(p, per_head, chunks, ws.partW, ws.partB);
   proj_reduce_kernel<<<dim3((D * D + 255) / 256, weights), 256, 0, st>>>(ws.partW, parts, D * D, dw);
   if (db != nullptr) proj_reduce_kernel<<<dim3(1, weights), 256, 0, st>>>(ws.partB, parts, D, db);
 }

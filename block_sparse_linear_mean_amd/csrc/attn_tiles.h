@@ -131,7 +131,6 @@ template <typename T, int D, bool KLAYOUT, int NW>
 __device__ __forceinline__ void stage_half(const T* __restrict__ X, int64_t sN, int j, int h, lds_u8* tile,
                                            const StageOff<D, NW>& off, const HalfSteps<D, NW>& hs) {
   using Tl = AttnTile<D>;
-  using SO = StageOff<D, NW>;
   constexpr int kHS = HalfSteps<D, NW>::kSteps;
   // the K layout's per-lane offset depends on the step only at d = 128, through step % 4: the
   // half's step q = h kInst/2 + kHS w + n has the remainder of this wavefront's full-tile step
