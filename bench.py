@@ -467,7 +467,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("bench.py measures one GPU only: this build has no multi-GPU path "
+        msg = ("bench.py measures one GPU only: the library has no multi-GPU path "
                f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).")
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         log(msg)
