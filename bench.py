@@ -400,8 +400,8 @@ def cold_steps(layer, args, dev):
 
 def achievable_peaks(dev, attention_ms, attention_flops):
     """Context for the roofline fractions, measured in the same process: a device copy of 1 GiB
-    (read + write) and a large bf16 GEMM (8192^3, the vendor library), with the attention pass's
-    rate as a fraction of the GEMM's."""
+    (read + write), a large bf16 GEMM (8192^3, the vendor library) and the vendor's dense
+    FlashAttention at B1 H12 N8192 d128, with the attention pass's rate as a fraction of each."""
     import torch
     def timed(fn, reps):
         fn()
@@ -425,8 +425,23 @@ def achievable_peaks(dev, attention_ms, attention_flops):
     del a, b
     gemm_tf = 2 * m ** 3 / (gemm_ms / 1e3) / 1e12
     att_tf = attention_flops / (attention_ms / 1e3) / 1e12
-    return {"copy_GBps": round(2 * n * 4 / (copy_ms / 1e3) / 1e9, 1), "gemm_bf16_TFLOPs": round(gemm_tf, 1),
-            "gemm_shape": [m, m, m], "attention_frac_of_gemm": round(att_tf / gemm_tf, 4)}
+    res = {"copy_GBps": round(2 * n * 4 / (copy_ms / 1e3) / 1e9, 1), "gemm_bf16_TFLOPs": round(gemm_tf, 1),
+           "gemm_shape": [m, m, m], "attention_frac_of_gemm": round(att_tf / gemm_tf, 4)}
+    # the vendor's dense FlashAttention (torch SDPA, flash backend only) at B1 H12 N8192 d128 bf16
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        g = torch.Generator(device=dev).manual_seed(0)
+        q, k, v = (torch.randn(1, 12, 8192, 128, device=dev, dtype=torch.bfloat16, generator=g) for _ in range(3))
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            sdpa_ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), 10)
+        sdpa_tf = 4.0 * 12 * 8192 ** 2 * 128 / (sdpa_ms / 1e3) / 1e12
+        res.update({"sdpa_flash_dense_TFLOPs": round(sdpa_tf, 1), "sdpa_shape": [1, 12, 8192, 128],
+                    "attention_frac_of_sdpa": round(att_tf / sdpa_tf, 4)})
+        del q, k, v
+    except (RuntimeError, ImportError) as e:
+        res["sdpa_flash_dense_TFLOPs"] = None
+        log(f"bench: no flash SDPA for the context line ({e})")
+    return res
 
 
 def main():
