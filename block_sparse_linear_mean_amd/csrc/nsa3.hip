@@ -8,8 +8,9 @@
 // O = sum_b sigmoid(q . w_b) O_b with caller weights w_b per head (zero weights: every gate 1/2).
 //
 // Design: the three branches are three passes of the selected-block attention kernel over
-// explicit block lists (so every pass keeps its copy pipeline and shares each staged tile across
-// the four query heads of a GQA group): the selection map from sla_block_map (no window), a
+// explicit block lists (so every pass keeps its copy pipeline; one workgroup per query block and
+// query head, the heads of a GQA group back to back on one XCD): the selection map from
+// sla_block_map (no window), a
 // generated window list (blocks i - 8 .. i, token-level band mask in the kernel) and a generated
 // list of compressed-token blocks (a causal limit on the window end).  Compression is one HBM
 // pass over K and V; the gated merge one pass over the three fp32 branch outputs.
