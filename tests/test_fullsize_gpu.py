@@ -118,7 +118,9 @@ def check_maps_every_row(w, f, layer):
     return maps
 
 
-FULL_OUTPUT = {"wan13b_sla", "salad"}     # every valid row recomputed by the oracle
+FULL_OUTPUT = {"wan13b_sla", "salad", "nsa_prefill"}     # every valid row recomputed by the oracle
+# wan14b: every valid row of these heads, sampled query blocks of the middle head
+FULL_HEADS = {"wan14b_sla": [0, 13, 26, 39]}
 
 
 @pytest.mark.parametrize("name", ["wan13b_sla", "salad", "nsa_prefill", "wan14b_sla"])
@@ -143,8 +145,9 @@ def test_full_size(name):
         heads = list(range(w.Hq))
         blocks_of = lambda h: list(range(f.nb))
     else:
-        heads = sorted(set([0, w.Hq // 2, w.Hq - 1]))
-        blocks_of = lambda h: sample_blocks(f.nb, 1000 * h + w.seed)
+        heads = sorted(set([0, w.Hq // 2, w.Hq - 1] + FULL_HEADS[name]))
+        blocks_of = lambda h: (list(range(f.nb)) if h in FULL_HEADS[name]
+                               else sample_blocks(f.nb, 1000 * h + w.seed))
     diffs, refs_ = [], []
     n_rows = 0
     for h in heads:
@@ -156,7 +159,7 @@ def test_full_size(name):
             diffs.append(Oh[64 * i:64 * i + hi] - ref[:hi])
             refs_.append(ref[:hi])
             n_rows += hi
-        if name in FULL_OUTPUT:
+        if name in FULL_OUTPUT or h in FULL_HEADS.get(name, []):
             f._H.clear()          # the per-block states of this head are not needed again
     d = np.concatenate(diffs)
     r = np.concatenate(refs_)
