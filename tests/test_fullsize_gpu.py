@@ -4,10 +4,10 @@ workload).
 Every row of every workload: pooled scores within one fp32 ulp of the oracle's, and the block map
 (critical lists and flags, marginal lists and bit masks, row counts) bit for bit against the
 oracle's classification of the same scores, plus properties that hold at any size.  Outputs: every
-valid row of wan13b_sla and salad recomputed by the oracle; for nsa_prefill and wan14b_sla sampled
-query blocks (first, second, middle, the last two (the last one holds the padding), and two
-seeded random ones, on the first, middle and last head).  Backward: wan13b_sla and nsa_prefill on
-sampled blocks, salad on every valid row of two heads.
+valid row of wan13b_sla, salad and nsa_prefill recomputed by the oracle; for wan14b_sla every valid
+row of four of its 40 heads and sampled query blocks of the middle head (first, second, middle, the
+last two (the last one holds the padding), and two seeded random ones).  Backward: wan13b_sla and
+salad on every valid row of two heads, nsa_prefill on sampled blocks.
 """
 import numpy as np
 import pytest
