@@ -130,6 +130,15 @@ __device__ __forceinline__ f32x4 load4_f32(const T* p) {
 
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
 
+// dO as the matrix-core products see it: fp32 inputs are rounded to bf16 for dP = dO V^T, so
+// D = dO . O is formed from the same rounded values and dP - D cancels exactly where it must
+// (a row whose softmax has a single key); bf16 inputs are unchanged.
+template <typename T>
+__device__ __forceinline__ float as_operand(float x) {
+  if constexpr (sizeof(T) == 2) return x;
+  else return static_cast<float>(static_cast<__bf16>(x));
+}
+
 // sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
 __device__ __forceinline__ float group4_sum(float x) {
   x += __shfl_xor(x, 16);
@@ -348,7 +357,7 @@ __device__ __forceinline__ void lin_q_side(const BwdParams& p, int b, int h, int
       const f32x4 oo = qv ? load4_f32(Or + o0) : f32x4{0.f, 0.f, 0.f, 0.f};
       const f32x4 bb = bias != nullptr ? *reinterpret_cast<const f32x4*>(bias + o0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsum += go[ot][e] * (oo[e] - y[e] - bb[e]);
+      for (int e = 0; e < 4; ++e) dsum += as_operand<T>(go[ot][e]) * (oo[e] - y[e] - bb[e]);
     }
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
@@ -369,7 +378,7 @@ __device__ __forceinline__ void lin_q_side(const BwdParams& p, int b, int h, int
     for (int ct = 0; ct < kCt; ++ct) {
       const f32x4 oo = qv ? load4_f32(Or + 16 * ct + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsum += go[ct][e] * (oo[e] - gate * xl[ct][e]);
+      for (int e = 0; e < 4; ++e) dsum += as_operand<T>(go[ct][e]) * (oo[e] - gate * xl[ct][e]);
       ga[ct] = go[ct] * gate;
     }
   }
@@ -1256,7 +1265,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdParams p, int rows) {
       In<T>::load8_f32(Or + c, x);
       In<T>::load8_f32(Gr + c, y);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) acc += x[m] * y[m];
+      for (int m = 0; m < 8; ++m) acc += x[m] * as_operand<T>(y[m]);
     }
   }
 #pragma unroll
