@@ -1,6 +1,7 @@
 """GPU parity at the degenerate sizes: one 64-token block, a single valid token, a last block with
 one valid row, a map with empty marginal lists, and the SALAD / NSA-style modes at one and two
-blocks — the whole layer (end to end) and its backward against the oracles, every valid row.
+blocks — the whole layer (end to end) and its backward against the oracles, every valid row — and
+at the maximum length (4096 key blocks).
 
 The layer's own block map is checked against the oracle's map row for row first; the backward runs
 on the oracle's map (as the other backward tests do).  Bars: the output tolerance of the forward
@@ -126,3 +127,44 @@ def test_backward(name):
             assert mx <= 1e-2, (what, mx)
         if what != "dw_gate":
             assert not g_[:, :, nv:].any(), f"padded rows of {what} must be zero"
+
+
+def test_maximum_length():
+    """The longest sequence the library takes (4096 key blocks: N = 262144) on one head, bf16 d 128,
+    5% critical / 85% negligible: every map row against the oracle's classification of the GPU's
+    scores, sampled output blocks (first, second, middle, last two) against the oracle, and the
+    backward's dQ on two of those blocks (every key block's gradient is covered at smaller sizes)."""
+    from tests.test_fullsize_gpu import check_maps_every_row
+    w = scaled(T, "max_len", N=262144, Nv=262144 - 37, d=128, dtype="bf16", kh_bp=500, kl_bp=8500, seed=13)
+    say(f"[edge maximum] N {w.N} n_valid {w.Nv}: inputs and the layer")
+    q, k, v, wg, f, layer = make_case(w, training=True)
+    O = layer.run()
+    torch.cuda.synchronize()
+    assert f.nb == 4096
+    maps = check_maps_every_row(w, f, layer)
+    Oh = host(O[0, 0]).astype(np.float64)
+    assert np.all(np.isfinite(Oh)) and not Oh[w.Nv:].any()
+    blocks = [0, 1, f.nb // 2, f.nb - 2, f.nb - 1]
+    got, refs_ = [], []
+    for i in blocks:
+        ref = f.output_block(0, 0, i, maps[(0, 0, i)])
+        hi = min(64, w.Nv - 64 * i)
+        got.append(Oh[64 * i:64 * i + hi])
+        refs_.append(ref[:hi])
+    compare_outputs(np.concatenate(got), np.concatenate(refs_), "max_len sampled blocks")
+    say("[edge maximum] backward")
+    dO = torch.from_numpy(np.random.default_rng(3).standard_normal(q.shape).astype(np.float32)).to(torch.bfloat16)
+    dq, dk, dv = (host(x) for x in layer.backward(dO.cuda()))
+    torch.cuda.synchronize()
+    for g_ in (dq, dk, dv):
+        assert np.all(np.isfinite(g_)) and not g_[:, :, w.Nv:].any()
+    qblocks = [1, f.nb - 1]
+    _, dQr, _, _ = obwd.gradients(f.Q, f.K, f.V, host(dO).astype(np.float64), maps, w.Nv, f.scale,
+                                  blocks={(0, 0, i) for i in qblocks})
+    for i in qblocks:
+        rows = slice(64 * i, min(64 * i + 64, w.Nv))
+        diff = dq[0, 0, rows].astype(np.float64) - dQr[0, 0, rows]
+        rel = np.linalg.norm(diff) / np.linalg.norm(dQr[0, 0, rows])
+        mx = np.abs(diff).max() / np.abs(dQr[0, 0, rows]).max()
+        say(f"  dQ of query block {i}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
+        assert rel <= REL_L2_G and mx <= MAX_ABS_G
