@@ -394,8 +394,11 @@ size_t sla_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, 
  * Outputs dq, dk, dv: contiguous fp32 [B, H, N, d], 16-byte aligned, fully overwritten; rows
  * t >= n_valid are zero.  dproj_w (required with Proj, else NULL): fp32 [proj_heads, d, d],
  * fully overwritten; dproj_b (nullable; NULL without Proj): fp32 [proj_heads, d].
- * O_sparse is taken as o - Proj(O_linear).  Arithmetic: bf16 matrix-core operands (the Proj
- * weight rounded to bf16), fp32 accumulation; deterministic (no atomics on gradients).
+ * O_sparse is taken as o - Proj(O_linear), and D is formed from dO as the matrix-core products
+ * see it (rounded to bf16 for fp32 inputs), so dP - D cancels exactly where a row's softmax is
+ * constant; with a bf16 o the rounding of the stored sum O_sparse + O_linear stays in D.
+ * Arithmetic: bf16 matrix-core operands (the Proj weight rounded to bf16), fp32 accumulation;
+ * deterministic (no atomics on gradients).
  * Errors: SLA_ERR_NULL for a missing required pointer or a Proj output without proj_w,
  * SLA_ERR_SHAPE for proj_heads not 1 or H, SLA_ERR_ALIGN, SLA_ERR_WORKSPACE.
  * workspace: sla_attn_bwd_workspace_bytes(B, H, N, d, proj_w ? proj_heads : 0) bytes.
