@@ -168,3 +168,65 @@ def test_maximum_length():
         mx = np.abs(diff).max() / np.abs(dQr[0, 0, rows]).max()
         say(f"  dQ of query block {i}: rel-L2 {rel:.3e}, max-abs {mx:.3e} of max |ref|")
         assert rel <= REL_L2_G and mx <= MAX_ABS_G
+
+
+def _random_cases(n, seed):
+    """Seeded random configurations: batch, heads and grouping, length and its ragged tail, head
+    size, dtype, mode and shares (each a valid call of the library)."""
+    r = np.random.default_rng(seed)
+    out = {}
+    for c in range(n):
+        mode = ["sla", "salad", "nsa"][c % 3]
+        Hkv = int(r.integers(1, 3))
+        Hq = Hkv * int(r.choice([1, 2])) if mode != "sla" else Hkv
+        nb = int(r.integers(1, 13))
+        N = 64 * nb
+        Nv = N - int(r.integers(0, 64))
+        d = int(r.choice([64, 128]))
+        dtype = str(r.choice(["bf16", "f32"]))
+        B = int(r.choice([1, 2]))
+        name = f"rand{c}_{mode}"
+        if mode == "nsa":
+            w = scaled(W["nsa_prefill"], name, B=B, Hq=Hq, Hkv=Hkv, N=N, Nv=Nv, d=d, dtype=dtype,
+                       n_sel=int(r.integers(1, 5)), window=int(r.choice([0, 37, 200])), seed=100 + c)
+        else:
+            kh = int(r.integers(0, 10001))
+            kl = int(r.integers(0, 10001 - kh)) if mode == "sla" else 0
+            w = scaled(T, name, mode=mode, B=B, Hq=Hq, Hkv=Hkv, N=N, Nv=Nv, d=d, dtype=dtype, kh_bp=kh, kl_bp=kl,
+                       seed=100 + c, gate_seed=200 + c if mode == "salad" else None)
+        out[name] = w
+    return out
+
+
+RANDOM = _random_cases(12, 2024)
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_shapes(name):
+    """Forward end to end and backward of a seeded random configuration against the oracles."""
+    w = RANDOM[name]
+    say(f"[edge random] {name}: B {w.B} Hq {w.Hq} Hkv {w.Hkv} N {w.N} n_valid {w.Nv} d {w.d} {w.dtype} "
+        f"kh {w.kh_bp} kl {w.kl_bp} n_sel {w.n_sel} window {w.window}")
+    q, k, v, wg, f, layer = make_case(w, training=True)
+    O = host(layer.run())
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(O)) and not O[:, :, w.Nv:].any()
+    compare_outputs(O[:, :, :w.Nv], f.output()[:, :, :w.Nv], name)
+    Hs = f.Hkv if f.group_sum else f.Hq
+    maps = {(b, h, i): f.map_row(b, h, i) for b in range(w.B) for h in range(Hs) for i in range(f.nb)}
+    dO = torch.from_numpy(np.random.default_rng(9).standard_normal(q.shape).astype(np.float32)).to(q.dtype)
+    got = tuple(host(x) for x in layer.backward(dO.cuda()))
+    torch.cuda.synchronize()
+    ref = obwd.gradients(f.Q, f.K, f.V, host(dO).astype(np.float64), maps, w.Nv, f.scale, mode=w.mode,
+                         w_gate=None if wg is None else wg.numpy(), window=w.window, group_map=w.mode == "nsa")
+    rows = (slice(None), slice(None), slice(0, w.Nv))
+    gscale = max(np.abs(r_[rows]).max() for r_ in ref[1:4])
+    for g_, r_, what in zip(got[:3], ref[1:4], ("dQ", "dK", "dV")):
+        diff = g_[rows].astype(np.float64) - r_[rows]
+        # max-abs against the case's largest gradient (a single-key row can leave the bf16 term of
+        # R28 in a small gradient), rel-L2 at the ordinary bar (none of these cases has such a row)
+        mx = np.abs(diff).max() / gscale
+        rel = np.linalg.norm(diff) / max(np.linalg.norm(r_[rows]), 1e-30)
+        say(f"  {what}: max-abs {mx:.3e} of the largest gradient, rel-L2 {rel:.3e}")
+        assert mx <= 1e-2 and rel <= REL_L2_G, (what, mx, rel)
+        assert not g_[:, :, w.Nv:].any()
