@@ -93,8 +93,21 @@ def pass_work(w, layer):
     attn = n_crit_entries * heads_per_row * pair_flops
     if layer.lin != 0:
         attn += B * Hq * nb * 64 * 2.0 * d * d    # linear epilogue phi(Q) S per query block
+    if getattr(layer, "proj_w", None) is not None:
+        attn += B * Hq * nb * 64 * 2.0 * d * d    # Proj: O_l W^T per query block
     work["attention"] = ("mfma", attn)
     return work, n_crit_entries * heads_per_row
+
+
+def proj_weights(w, kind):
+    """Seeded Proj weight (one [d, d] for all heads, or one per head) and bias, fp32 CPU tensors."""
+    import numpy as np
+    import torch
+    r = np.random.default_rng(w.seed + 77)
+    shape = (w.d, w.d) if kind == "shared" else (w.Hq, w.d, w.d)
+    W = r.standard_normal(shape).astype(np.float32) / np.float32(np.sqrt(w.d))
+    b = (0.1 * r.standard_normal(shape[:-1])).astype(np.float32)
+    return torch.from_numpy(W), torch.from_numpy(b)
 
 
 def kernel_source_digest(pass_name):
@@ -134,8 +147,9 @@ def host_cpu():
     return int(cores), model
 
 
-def cpu_baseline(w, q, k, v, wg, heads):
-    """The CPU oracle as it stands, on whole heads of the same workload, extrapolated to all heads."""
+def cpu_baseline(w, q, k, v, wg, heads, proj_w=None, proj_b=None, smooth_k=False):
+    """The CPU oracle as it stands, on whole heads of the same workload (and options), extrapolated
+    to all heads."""
     import numpy as np
     from oracle import sla_oracle as orc
     try:
@@ -151,8 +165,12 @@ def cpu_baseline(w, q, k, v, wg, heads):
     V = v[:, :heads].float().numpy()
     wgn = None if wg is None else wg[:heads * G].numpy()
     t0 = time.perf_counter()
+    pw = pb = None
+    if proj_w is not None:
+        pw = proj_w.numpy() if proj_w.dim() == 2 else proj_w[:heads * G].numpy()
+        pb = proj_b.numpy() if proj_b.dim() == 1 else proj_b[:heads * G].numpy()
     f = orc.Forward(Q, K, V, n_valid=w.Nv, mode=w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
-                    window=w.window, w_gate=wgn)
+                    window=w.window, w_gate=wgn, proj_w=pw, proj_b=pb, smooth_k=smooth_k)
     f.output()
     dt = time.perf_counter() - t0
     full = dt * (w.Hkv / heads)
@@ -459,6 +477,9 @@ def main():
                     help="run the key states and marginal sums on a second stream, overlapping scores and map")
     ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",
                     help="run the layer on Q, K, V gathered along a 3-D Hilbert curve of the latent grid")
+    ap.add_argument("--proj", choices=["none", "shared", "per-head"], default="none",
+                    help="SLA only: the learned projection of the linear branch (seeded random weights and bias)")
+    ap.add_argument("--smooth-k", action="store_true", help="SLA/SALAD: keys of the linear branch centred by their mean")
     ap.add_argument("--nsa-branches", type=int, choices=[2, 3], default=2,
                     help="3: time NSA with its compressed branch and gated merge (nsa workloads)")
     ap.add_argument("--captured-mass", action="store_true",
@@ -508,8 +529,17 @@ def main():
         if getattr(w, "grid", None) is None:
             raise SystemExit("--token-order hilbert needs a workload with a latent grid")
         order = sla.sla_hilbert_order(*w.grid)
+    proj_w = proj_b = None
+    if args.proj != "none":
+        if w.mode != "sla":
+            raise SystemExit("--proj applies to the SLA workloads")
+        proj_w, proj_b = proj_weights(w, args.proj)
+    if args.smooth_k and w.mode == "nsa":
+        raise SystemExit("--smooth-k applies to a linear branch (SLA, SALAD)")
     layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
-                           window=w.window, w_gate=wg, token_order=order)
+                           window=w.window, w_gate=wg, token_order=order,
+                           proj_w=None if proj_w is None else proj_w.to(dev),
+                           proj_b=None if proj_b is None else proj_b.to(dev), smooth_k=args.smooth_k)
     passes_run = (["reorder"] if order is not None else []) + PASSES + (["restore"] if order is not None else [])
     log(f"bench: {args.warmup} warm-up steps")
     for _ in range(args.warmup):
@@ -612,8 +642,15 @@ def main():
     cfg["critical_pairs"] = pairs
     if order is not None:
         cfg["token_order"] = "hilbert"
+    metric = metric_for(w)
+    if args.proj != "none":
+        cfg["proj"] = args.proj
+        metric += f", + Proj ({args.proj})"
+    if args.smooth_k:
+        cfg["smooth_k"] = True
+        metric += ", smooth-K"
     result = {
-        "metric": metric_for(w),
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s (effective, dense-equivalent)",
         "n_gpus": 1,
@@ -653,7 +690,7 @@ def main():
         log(f"bench: copy calibration, 3 elementwise copies of {args.copy_calibration_mb} MiB")
     if not args.no_cpu_baseline:
         log(f"bench: cpu baseline (oracle) on {args.cpu_sample_heads} head(s)")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, wg, args.cpu_sample_heads)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, wg, args.cpu_sample_heads, proj_w, proj_b, args.smooth_k)
     print(json.dumps(result), flush=True)
 
 

@@ -137,3 +137,13 @@ def test_algorithmic_work_of_the_headline_layer():
     # without fusing the key means, pooling reads K as well
     layer2, _ = _fake_layer(w, n_crit, n_marg, lin=1, fuse=False)
     assert bench.pass_work(w, layer2)[0]["pool"][1] == B * 2 * H * (Nv * d * 2 + nb * d * 4)
+
+
+def test_algorithmic_work_with_proj():
+    """The Proj epilogue adds one 64 x d x d product per query block of every head."""
+    w = WORKLOADS["wan13b_sla"]
+    n_crit = 26 * w.B * w.Hq * w.nb
+    layer, _ = _fake_layer(w, n_crit, 51 * w.B * w.Hq * w.nb, lin=1, fuse=True)
+    plain = bench.pass_work(w, layer)[0]["attention"][1]
+    layer.proj_w = object()
+    assert bench.pass_work(w, layer)[0]["attention"][1] - plain == w.B * w.Hq * w.nb * 2.0 * 64 * w.d * w.d
