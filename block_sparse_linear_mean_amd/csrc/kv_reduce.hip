@@ -255,26 +255,32 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   }
 }
 
-// out[bg] = sum over p of in[bg * parts + p] (fixed order), for states of `len` floats.  The
-// partials are read 8 at a time, all 8 loads in flight before the adds (one load at a time would
+// out[bg] = sum over p of in[bg * parts + p] (fixed order), for states of `len` floats, and the
+// same for the z partials (zlen floats) in the workgroups from xh on: one launch for both.  The
+// partials are read 16 at a time, all 16 loads in flight before the adds (one load at a time would
 // expose a memory latency per partial).
-__global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict__ in, int parts, int64_t len,
-                                                         float* __restrict__ out) {
-  constexpr int kU = 8;
+__global__ __launch_bounds__(256) void sum_states_kernel(const float* __restrict__ in, const float* __restrict__ zin,
+                                                         int parts, int64_t len, int64_t zlen, int xh,
+                                                         float* __restrict__ out, float* __restrict__ zout) {
+  constexpr int kU = 16;
+  const bool is_z = int(blockIdx.x) >= xh;
+  const float* src = is_z ? zin : in;
+  float* dst = is_z ? zout : out;
+  const int64_t n = is_z ? zlen : len;
   const int64_t bg = blockIdx.y;
-  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (e >= len) return;
+  const int64_t e = (int64_t(is_z ? blockIdx.x - xh : blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < parts; p0 += kU) {
     f32x4 x[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      x[u] = *reinterpret_cast<const f32x4*>(in + (bg * parts + min(p0 + u, parts - 1)) * len + e);
+      x[u] = *reinterpret_cast<const f32x4*>(src + (bg * parts + min(p0 + u, parts - 1)) * n + e);
 #pragma unroll
     for (int u = 0; u < kU; ++u)
       if (p0 + u < parts) s += x[u];
   }
-  *reinterpret_cast<f32x4*>(out + bg * len + e) = s;
+  *reinterpret_cast<f32x4*>(dst + bg * n + e) = s;
 }
 
 template <typename T>
@@ -298,9 +304,11 @@ static void launch_kv(const sla_tensor* k, const sla_tensor* v, int n_valid, int
 #undef SLA_KV_LAUNCH
 }
 
-static void launch_sum(const float* in, int parts, int64_t len, int bgs, float* out, hipStream_t st) {
-  dim3 grid(uint32_t((len / 4 + 255) / 256), bgs);
-  sum_states_kernel<<<grid, 256, 0, st>>>(in, parts, len, out);
+static void launch_sum(const float* in, const float* zin, int parts, int d, int bgs, float* out, float* zout,
+                       hipStream_t st) {
+  const int64_t len = int64_t(d) * d;
+  const int xh = int((len / 4 + 255) / 256), xz = (d / 4 + 255) / 256;
+  sum_states_kernel<<<dim3(uint32_t(xh + xz), bgs), 256, 0, st>>>(in, zin, parts, len, d, xh, out, zout);
 }
 
 }  // namespace sla
@@ -335,8 +343,7 @@ extern "C" sla_status sla_linear_kv_reduce(const sla_tensor* k, const sla_tensor
     float* kp = H == nullptr ? k_pool : nullptr;   // the key block means come from one of the two passes
     if (bf) launch_kv<bf16raw>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, kp, s);
     else launch_kv<float>(k, v, n_valid, cb, nch, k_shift, nullptr, Hp, zp, kp, s);
-    launch_sum(Hp, nch, int64_t(d) * d, bgs, H_all, s);
-    launch_sum(zp, nch, d, bgs, z_all, s);
+    launch_sum(Hp, zp, nch, d, bgs, H_all, z_all, s);
   }
   if (H != nullptr) {
     // runs of a few blocks per workgroup (one block of prefetch), at least ~2048 workgroups
