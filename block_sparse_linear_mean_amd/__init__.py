@@ -17,7 +17,8 @@ Entry points keep the C names (see include/sla.h):
     sla_permute_rows     apply / undo a token order on [B, H, N, d] rows
 
 `SlaForward` strings the four calls into one layer forward with every buffer
-allocated up front, so a step launches kernels only.
+allocated up front, so a step launches kernels only.  `sla_attention` is the same forward as a
+differentiable function (torch autograd, gradients through sla_attn_bwd_ext).
 """
 from __future__ import annotations
 
@@ -284,3 +285,50 @@ class SlaForward:
         timed("attention", self.attention)
         timed("restore", self.restore)
         return self.out
+
+
+class _SlaAttention(torch.autograd.Function):
+    """Autograd glue: forward = SlaForward(training=True).run(), backward = its backward() for the
+    forward's own block map (the map is a discrete function of the inputs; like every top-k
+    selection it passes no gradient)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, w_gate, proj_w, proj_b, cfg):
+        layer = SlaForward(q.detach(), k.detach(), v.detach(), training=True,
+                           w_gate=None if w_gate is None else w_gate.detach(),
+                           proj_w=None if proj_w is None else proj_w.detach(),
+                           proj_b=None if proj_b is None else proj_b.detach(), **cfg)
+        out = layer.run()
+        ctx.layer = layer
+        ctx.dtypes = tuple(None if x is None else x.dtype for x in (q, k, v, w_gate, proj_w, proj_b))
+        ctx.save_for_backward(out)      # an in-place change of the output is caught before backward
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        ctx.saved_tensors               # version check of the output
+        layer = ctx.layer
+        g = layer.backward(dout.to(layer.q.dtype).contiguous())
+        dq, dk, dv = g[:3]
+        dW = db = dwg = None
+        if layer.proj_w is not None:
+            dW, db = g[3], g[4]
+        if layer.lin == SLA_LIN_GLOBAL_GATED:
+            dwg = g[-1]
+        grads = (dq, dk, dv, dwg, dW, db)
+        return tuple(None if x is None or t is None else x.to(t) for x, t in zip(grads, ctx.dtypes)) + (None,)
+
+
+def sla_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_valid: int, mode: str = "sla", *,
+                  kh_bp: int = 0, kl_bp: int = 0, n_sel: int = 0, window: int = 0,
+                  w_gate: Optional[torch.Tensor] = None, proj_w: Optional[torch.Tensor] = None,
+                  proj_b: Optional[torch.Tensor] = None, smooth_k: bool = False, scale: Optional[float] = None,
+                  token_order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Differentiable layer forward: the output of SlaForward(...).run() for these arguments, with
+    gradients for q, k, v and, where given, w_gate (salad), proj_w and proj_b (sla) through libsla's
+    backward.  Shapes and modes as in SlaForward: q [B, Hq, N, d], k and v [B, Hkv, N, d] on the GPU,
+    N a multiple of 64, N - 64 < n_valid <= N; rows past n_valid get zero output and zero gradient.
+    Each call builds the layer's buffers; for repeated steps of one shape keep a SlaForward instead."""
+    cfg = dict(n_valid=n_valid, mode=mode, kh_bp=kh_bp, kl_bp=kl_bp, n_sel=n_sel, window=window,
+               smooth_k=smooth_k, scale=scale, token_order=token_order)
+    return _SlaAttention.apply(q, k, v, w_gate, proj_w, proj_b, cfg)

@@ -334,3 +334,10 @@ def test_layer_fuses_key_pooling_only_when_exact(L):
     assert not layer(torch.float32).fuse_key_pooling
     assert not layer(torch.bfloat16, smooth_k=True).fuse_key_pooling
     assert not layer(torch.bfloat16, mode="nsa").fuse_key_pooling
+
+
+def test_differentiable_layer_fails_loudly_without_the_gpu(L):
+    """sla_attention has no CPU fallback: on CPU tensors the first library call refuses them."""
+    x = torch.zeros((1, 1, 256, 64), dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        sla.sla_attention(x, x, x, 256, "sla", kh_bp=2500, kl_bp=5000)
