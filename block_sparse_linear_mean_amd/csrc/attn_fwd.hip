@@ -11,8 +11,9 @@
 // heads of a GQA group share the selection ("Sparse Attention 方法综述", section 2 NSA).
 //
 // Design (gfx950, wave64, 32x32x16 bf16 matrix cores):
-//  * one workgroup = one 64-row query block of one head (2 wavefronts x 32 query rows); the
-//    heads of a GQA group that share the block map run on one XCD back to back (shared L2);
+//  * one workgroup = one 64-row query block of one head (2 wavefronts x 32 query rows), or of
+//    two heads of a GQA group that share a causal block map (4 wavefronts, each staged K/V tile
+//    serving both); the heads of a group run on one XCD back to back (shared L2);
 //  * the query fragment stays in registers for the whole block list;
 //  * per critical key block, K and V tiles are copied global -> LDS by the direct-to-LDS
 //    loads; scores are computed transposed (S^T = K Q^T), so each lane owns one query
@@ -69,11 +70,12 @@ struct WgCoord {
 };
 // Causal rows do work that grows with i: there (heavy_first) each XCD's range takes every 8th
 // query block, largest i first, so the XCDs stay balanced and the longest blocks start first.
-__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, bool heavy_first = false) {
+// hp: query heads per workgroup (consecutive heads of one GQA group; hp divides the group size).
+__device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, bool heavy_first = false, int hp = 1) {
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int G = Hq / Hkv;
-  const int hh = logical % G;
-  const int rest = logical / G;
+  const int hh = (logical % (G / hp)) * hp;
+  const int rest = logical / (G / hp);
   int i = rest % nqb;
   if (heavy_first) {
     const int per = nqb / 8;
@@ -85,11 +87,13 @@ __device__ __forceinline__ WgCoord wg_coord(int nqb, int Hq, int Hkv, bool heavy
 }
 
 // One workgroup = one 64-row query block of one head: 2 wavefronts x 32 query rows, 32x32x16
-// bf16 matrix cores.  Per critical key block: S^T = K Q^T (lane = one query column, 32 keys),
+// bf16 matrix cores; for causal maps shared by a GQA group, of two heads of the group (NW = 4:
+// wavefronts 2 and 3 take the second head), which then share every staged K/V tile.  Per critical key block: S^T = K Q^T (lane = one query column, 32 keys),
 // online softmax in registers, O^T += V^T P^T with P^T fed from registers and V^T from the
-// transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU).  (Four heads
-// of a GQA group sharing each staged tile in one 8-wavefront workgroup measured slower at the
-// NSA prefill: 1.31 ms against 1.08 ms, one workgroup per CU against four.)
+// transposing LDS read.  One 32 KB K+V stage per workgroup (four workgroups per CU; two of the
+// 4-wavefront head pairs).  At the NSA prefill head pairs take the pass from 1.08 to 1.05 ms; four
+// heads sharing each staged tile in one 8-wavefront workgroup measured slower, 1.31 ms (one
+// workgroup per CU).
 // Step k of NSTEP of the softmax of a 32-key half (scores sc, 16 per lane): elements
 // E k .. E k + E - 1 (E = 16 / NSTEP) of P = exp2(c2 s - off); each time eight are done they are
 // packed into a bf16 B operand (p0, then p1) and added to the row sum (of those bf16 values, two
@@ -122,8 +126,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int t = threadIdx.x, lane = t % kWave, l32 = lane % 32, lg = lane / 32;
   const int w = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform: head and K/V bases in SGPRs
-  static_assert(NW == 2, "one head per workgroup: two wavefronts of 32 query rows");
-  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, CAUSAL);
+  static_assert(NW == 2 || (NW == 4 && LIN == SLA_LIN_NONE),
+                "one head per workgroup (two wavefronts of 32 query rows), or two heads without a linear branch");
+  const WgCoord wc = wg_coord(p.nqb, p.Hq, p.Hkv, CAUSAL, NW / 2);
   const int i = wc.i, h = wc.h + w / 2, b = wc.b;  // this wavefront's head
   const int G = p.Hq / p.Hkv;
   const int g = h / G;
@@ -537,10 +542,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ---- store: lane holds O[tq][32 dt + 8 (e / 4) + 4 lg + e % 4]; padded query rows are zero
   {
     if (!p.out_f32) {
-      // bf16 output of one head: re-staged through the K buffer (64 rows of 2 D bytes, 16-byte
-      // chunk c of row r at c ^ (r % chunks)) so that every store writes whole rows, 16 bytes a lane
+      // bf16 output of a head: re-staged through the K buffer (the second head of a pair: the V
+      // buffer; 64 rows of 2 D bytes, 16-byte chunk c of row r at c ^ (r % chunks)) so that every
+      // store writes whole rows, 16 bytes a lane
       SLA_WAIT_LGKM0();
       SLA_BARRIER();                                 // every wavefront is done with the buffers
+      lds_u8* ost = w / 2 ? Vb : Kb;
       const int r = 32 * (w % 2) + l32;
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt)
@@ -549,16 +556,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           const f32x4 o = {oacc[dt][4 * e4], oacc[dt][4 * e4 + 1], oacc[dt][4 * e4 + 2], oacc[dt][4 * e4 + 3]};
           const int c = 4 * dt + e4;
           *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
-              Kb + r * Tl::kRowB + 16 * (c ^ (r % Tl::kChunks)) + 8 * lg) = __builtin_convertvector(o, bf16x4);
+              ost + r * Tl::kRowB + 16 * (c ^ (r % Tl::kChunks)) + 8 * lg) = __builtin_convertvector(o, bf16x4);
         }
       SLA_WAIT_LGKM0();
       SLA_BARRIER();
+      // each half of the workgroup (NW / 2 wavefronts) stores one head's tile
+      constexpr int kHalfT = kThreads / (NW / 2);
+      const int th = t % kHalfT;
       u16* ob = static_cast<u16*>(p.out) + ((int64_t(b) * p.Hq + h) * p.N + kBlock * i) * D;
 #pragma unroll
-      for (int n = 0; n < kBlock * Tl::kChunks / kThreads; ++n) {
-        const int e = t + kThreads * n;
+      for (int n = 0; n < kBlock * Tl::kChunks / kHalfT; ++n) {
+        const int e = th + kHalfT * n;
         const int rr = e / Tl::kChunks, c = e % Tl::kChunks;
-        bf16x8 x = lds_load16(Kb + rr * Tl::kRowB + 16 * (c ^ (rr % Tl::kChunks)));
+        bf16x8 x = lds_load16(ost + rr * Tl::kRowB + 16 * (c ^ (rr % Tl::kChunks)));
         if (kBlock * i + rr >= p.n_valid) x = zero8();
         // streaming store: the output is not read again by this layer, and the next pass's reads
         // then find fewer dirty lines to evict
@@ -586,7 +596,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <typename T, int D>
 static void launch_attn(const AttnParams& p, int causal, int lin, dim3 grid, hipStream_t st) {
   if (causal) {
-    attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
+    // maps shared by a GQA group of an even number of heads: two heads per workgroup share each
+    // staged K/V tile (half the workgroups)
+    if (p.group_map && (p.Hq / p.Hkv) % 2 == 0)
+      attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 4><<<dim3(grid.x / 2), 256, 0, st>>>(p);
+    else
+      attn_fwd_kernel<T, D, true, SLA_LIN_NONE, 2><<<grid, 128, 0, st>>>(p);
   } else if (lin == SLA_LIN_MARGINAL || lin == SLA_LIN_ROW_STATES) {
     if (p.proj_w != nullptr) attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2, true><<<grid, 128, 0, st>>>(p);
     else attn_fwd_kernel<T, D, false, SLA_LIN_MARGINAL, 2><<<grid, 128, 0, st>>>(p);

@@ -112,16 +112,26 @@ template <int D, int NW>
 struct HalfSteps {
   static constexpr int kSteps = AttnTile<D>::kInst / 2 / NW;
   uint32_t step[kSteps];
+  uint32_t klane[kSteps];   // the K layout's per-lane part of step n (used at d = 128 with 2 steps)
 };
 
 template <int D, int NW>
 __device__ __forceinline__ HalfSteps<D, NW> half_steps(int64_t sN) {
-  constexpr int R = 1024 / AttnTile<D>::kRowB;
+  using Tl = AttnTile<D>;
+  constexpr int R = 1024 / Tl::kRowB;
+  constexpr int kS = HalfSteps<D, NW>::kSteps;
+  const int lane = threadIdx.x % kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int r = (16 * lane) / Tl::kRowB, pc = lane % Tl::kChunks;
   HalfSteps<D, NW> o;
 #pragma unroll
-  for (int n = 0; n < HalfSteps<D, NW>::kSteps; ++n)
-    o.step[n] = uint32_t(int64_t(HalfSteps<D, NW>::kSteps * w + n) * R * sN * 2);
+  for (int n = 0; n < kS; ++n) {
+    o.step[n] = uint32_t(int64_t(kS * w + n) * R * sN * 2);
+    // a half's step q = h kInst / 2 + kS w + n leaves the remainder (kS w + n) % 4 (kInst / 2 is
+    // a multiple of 4 at d = 128), which is all the K layout's chunk order depends on
+    const int c = pc ^ (((kS * w + n) * R + r) % Tl::kChunks);
+    o.klane[n] = uint32_t(2 * (r * sN + 8 * c));
+  }
   return o;
 }
 
@@ -146,7 +156,8 @@ __device__ __forceinline__ void stage_half(const T* __restrict__ X, int64_t sN, 
       uint32_t lo = off.lane[0];
       if constexpr (KLAYOUT && D == 128) {
         if constexpr (kHS == 4) lo = off.lane[n];
-        else lo = (w & 1) ? off.lane[(n + 2) & 3] : off.lane[n & 3];
+        else lo = hs.klane[n];   // computed per step: a select between two entries of off.lane
+                                 // becomes an indexed read that the compiler moves to LDS
       }
       const uint32_t vo = lo + hs.step[n];
       load_lds16_sbase(tb, vo, tile + q * 1024);
