@@ -51,6 +51,9 @@ CASES = {
     "nsa_one_block": scaled(W["nsa_prefill"], "nsa_one_block", N=64, Nv=50, Hq=2, Hkv=1, n_sel=16, window=512),
     "nsa_two_blocks_win": scaled(W["nsa_prefill"], "nsa_two_blocks_win", N=128, Nv=128, Hq=4, Hkv=2, n_sel=1,
                                  window=20),
+    # head pairs (an even group shares each staged tile) at d 64 in bf16, a ragged tail
+    "nsa_pairs_bf16_d64": scaled(W["nsa_prefill"], "nsa_pairs_bf16_d64", N=320, Nv=300, Hq=4, Hkv=2, d=64,
+                                 n_sel=2, window=100),
 }
 REL_L2_G, MAX_ABS_G = 1e-2, 3e-2
 # bf16 cases whose dQ / dK carry the single-key rounding term described above
