@@ -331,4 +331,8 @@ def sla_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_valid: in
     Each call builds the layer's buffers; for repeated steps of one shape keep a SlaForward instead."""
     cfg = dict(n_valid=n_valid, mode=mode, kh_bp=kh_bp, kl_bp=kl_bp, n_sel=n_sel, window=window,
                smooth_k=smooth_k, scale=scale, token_order=token_order)
-    return _SlaAttention.apply(q, k, v, w_gate, proj_w, proj_b, cfg)
+    tensors = (q, k, v, w_gate, proj_w, proj_b)
+    if not (torch.is_grad_enabled() and any(x is not None and x.requires_grad for x in tensors)):
+        # nothing to differentiate: the plain forward, without keeping what the backward needs
+        return SlaForward(q, k, v, w_gate=w_gate, proj_w=proj_w, proj_b=proj_b, **cfg).run()
+    return _SlaAttention.apply(*tensors, cfg)

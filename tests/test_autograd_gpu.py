@@ -118,3 +118,19 @@ def test_autograd_catches_an_inplace_change_of_the_output():
     out.add_(1.0)
     with pytest.raises(RuntimeError):
         out.backward(torch.ones_like(out))
+
+
+def test_no_grad_gives_the_same_output():
+    """Without anything to differentiate the plain forward runs: the same bits, no graph."""
+    w = CASES["salad_gqa"]
+    say("[sla_attention autograd] no_grad")
+    q, k, v, wg = make_inputs(w)
+    args = (q.cuda(), k.cuda(), v.cuda(), w.Nv, "salad")
+    kw = dict(kh_bp=w.kh_bp, w_gate=wg.cuda())
+    with torch.no_grad():
+        plain = sla.sla_attention(*args, **kw)
+    qa = args[0].clone().requires_grad_(True)
+    tracked = sla.sla_attention(qa, *args[1:], **kw)
+    torch.cuda.synchronize()
+    assert not plain.requires_grad and tracked.requires_grad
+    assert torch.equal(plain, tracked.detach())
