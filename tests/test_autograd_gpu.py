@@ -134,3 +134,25 @@ def test_no_grad_gives_the_same_output():
     torch.cuda.synchronize()
     assert not plain.requires_grad and tracked.requires_grad
     assert torch.equal(plain, tracked.detach())
+
+
+def test_autograd_with_smooth_k_and_token_order_matches_direct():
+    """The options pass through: smooth-K and a Hilbert token order (the library's own order of the
+    latent grid), gradients bit for bit those of SlaForward.backward."""
+    w = scaled(W["wan13b_sla"], "ag_sla_order", grid=(3, 10, 30), Hq=2, Hkv=2, kh_bp=2500, kl_bp=5000)
+    say("[sla_attention autograd] smooth-K + token order")
+    q, k, v, _ = make_inputs(w)
+    order = sla.sla_hilbert_order(*w.grid)
+    kw = dict(kh_bp=w.kh_bp, kl_bp=w.kl_bp, smooth_k=True, token_order=order)
+    dO = torch.from_numpy(np.random.default_rng(5).standard_normal(q.shape).astype(np.float32)).to(q.dtype).cuda()
+    layer = sla.SlaForward(q.cuda(), k.cuda(), v.cuda(), w.Nv, "sla", training=True, **kw)
+    out_d = layer.run()
+    g_d = layer.backward(dO)
+    leaf = lambda x: x.detach().clone().cuda().requires_grad_(True)
+    qa, ka, va = leaf(q), leaf(k), leaf(v)
+    out_a = sla.sla_attention(qa, ka, va, w.Nv, "sla", **kw)
+    out_a.backward(dO)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.detach(), out_d)
+    for got, ref in zip((qa.grad, ka.grad, va.grad), g_d[:3]):
+        assert torch.equal(got, ref.to(got.dtype))
