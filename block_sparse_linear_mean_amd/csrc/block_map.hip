@@ -30,8 +30,10 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t lanes_below() {
-  return (uint64_t(1) << threadIdx.x) - 1;          // one wavefront per workgroup
+// Number of set bits of the wave-wide mask m in the lanes below this one (v_mbcnt_lo / _hi: two
+// instructions, no per-lane mask arithmetic).
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront, in lane order, without LDS: a
@@ -88,6 +90,15 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&key)[M], const bool 
     for (int m = 0; m < M; ++m) {
       const bool match = valid[m] & ((key[m] >> (shift + 8)) == p0);
       atomicAdd(&hist[match ? (key[m] >> shift) & 255u : dummy], 1u);
+    }
+  } else if constexpr (NS == 2) {
+    // two different prefixes: a key matches at most one of them, so one atomic per key
+    const uint32_t p0 = prefix[0] >> (shift + 8), p1 = prefix[1] >> (shift + 8);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t hi = key[m] >> (shift + 8), dig = (key[m] >> shift) & 255u;
+      const uint32_t at = hi == p0 ? dig : (hi == p1 ? 256u + dig : dummy);
+      atomicAdd(&hist[valid[m] ? at : dummy], 1u);
     }
   } else {
 #pragma unroll
@@ -176,7 +187,7 @@ __device__ void top_set(const uint32_t (&key)[M], int ncand, int n, uint32_t T, 
     const bool valid = lane + kWave * m < ncand;
     const bool eq = valid & (key[m] == T);
     const uint64_t em = __ballot(eq);
-    const int before = seen + __popcll(em & lanes_below());
+    const int before = seen + bits_below(em);
     in[m] = valid & ((key[m] > T) | (eq & (before < take)));
     seen += __popcll(em);
   }
@@ -191,7 +202,7 @@ __device__ int compact_write(const bool (&sel)[M], int* out, uint8_t* flags_out,
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint64_t bm = __ballot(sel[m]);
-    const int at = pos + __popcll(bm & lanes_below());
+    const int at = pos + bits_below(bm);
     if (sel[m] & (at < limit)) {
       out[at] = lane + kWave * m;
       if (flags_out) flags_out[at] = flag[m];
