@@ -30,6 +30,10 @@ CASES = {
                                     dtype="f32", kh_bp=1500, kl_bp=6000), True, True, True),
     "b2_shared_bias_smoothk": (scaled(W["wan13b_sla"], "b2_sla", B=2, grid=(3, 10, 30), Hq=2, Hkv=2, kh_bp=2500,
                                       kl_bp=5000), False, True, True),
+    # GQA (two query heads per KV head, maps per query head): dW per query head, the key side's state
+    # gradients summed over the group's heads
+    "gqa_per_head_bias_smoothk": (scaled(W["tiny_sla"], "gqa_bp", Hq=4, Hkv=2, N=1280, Nv=1250, d=128,
+                                         dtype="bf16", kh_bp=2500, kl_bp=5000), True, True, True),
     "all_linear_proj": (scaled(W["wan13b_sla"], "med_all_linear", grid=(3, 10, 30), Hq=1, Hkv=1, kh_bp=0, kl_bp=0),
                         True, True, True),
     "all_crit_proj": (scaled(W["wan13b_sla"], "med_all_crit", grid=(3, 10, 30), Hq=1, Hkv=1, kh_bp=10000, kl_bp=0),
