@@ -473,6 +473,8 @@ def main():
     ap.add_argument("--no-context", action="store_true",
                     help="skip the cold-cache steps and the copy / GEMM reference measurements")
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one HIP graph of the layer (one host launch per step)")
     ap.add_argument("--overlap", action="store_true",
                     help="run the key states and marginal sums on a second stream, overlapping scores and map")
     ap.add_argument("--token-order", choices=["row-major", "hilbert"], default="row-major",
@@ -569,15 +571,20 @@ def main():
     # timed region: the plain layer, with one event pair around the dominant pass only (its launch
     # duration for the roofline, measured live; a pair around every pass costs ~0.04 ms per layer)
     ev_dom = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    log(f"bench: {args.steps} timed steps")
+    graph = layer.capture() if args.graph else None
+    log(f"bench: {args.steps} timed steps" + (" (replays of one HIP graph of the layer)" if graph else ""))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        layer.run(overlap=args.overlap, events={dom: ev_dom[s]})
+        if graph is not None:
+            graph.replay()
+        else:
+            layer.run(overlap=args.overlap, events={dom: ev_dom[s]})
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in ev_dom) / args.steps
+    # with a graph the dominant pass's launch time comes from the instrumented run before it
+    dom_ms = pre_ms[dom] if graph is not None else sum(a.elapsed_time(b) for a, b in ev_dom) / args.steps
     # per-pass breakdown: a separate instrumented run of as many steps, after the timed region
     pass_ms, step_gpu_ms, per_step = instrumented(args.steps)
     gpu_ms = step_gpu_ms
@@ -649,6 +656,8 @@ def main():
     if args.smooth_k:
         cfg["smooth_k"] = True
         metric += ", smooth-K"
+    if args.graph:
+        cfg["hip_graph"] = True
     result = {
         "metric": metric,
         "value": round(value, 3),

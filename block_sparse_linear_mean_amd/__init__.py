@@ -224,6 +224,24 @@ class SlaForward:
             sla_permute_rows(src, self.order, inverse=True, out=dst)
         return tuple(grads) + tuple(g_r[3:])
 
+    def capture(self) -> "torch.cuda.CUDAGraph":
+        """Record one run() into a HIP graph and return it; graph.replay() then launches the whole
+        forward from the host at once (launch-bound sizes, serving loops).  The graph reads the
+        layer's input tensors and writes self.out: copy new inputs into q, k, v (as given to the
+        constructor) before a replay.  Every buffer is allocated by the constructor and no pass
+        clears memory with a memset, so replays recompute everything from the inputs."""
+        dev = self.q.device
+        main = torch.cuda.current_stream(dev)
+        warm = torch.cuda.Stream(device=dev)
+        warm.wait_stream(main)
+        with torch.cuda.stream(warm):          # first calls (library load, workspaces) off the capture
+            self.run()
+        main.wait_stream(warm)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run()
+        return graph
+
     def run(self, overlap: bool = False, events=None) -> torch.Tensor:
         """One full forward: (token order,) pool, scores, block map, linear states, marginal sums,
         attention (, order undone).  With fuse_key_pooling the pooling pass reads only Q, and the linear
