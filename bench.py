@@ -258,17 +258,10 @@ def bench_nsa3(args, w, qd, kd, vd):
     }))
 
 
-def bench_backward(args, w, qd, kd, vd):
-    """Time the backward (dQ, dK, dV, and dw_gate for SALAD, of one layer for its block map) and
-    print one JSON line.
-
-    The forward runs once in training mode (it also keeps each row's log-sum-exp); each timed step
-    is one backward call on a fixed seeded dO.  Executed FLOPs: per critical (query head, key block)
-    pair the seven 64 x 64 x d products of the sparse backward (S and dP in both the dQ and the
-    dK/dV kernels, dQ, dK, dV); with a linear branch, per query block the three 64 x d x d products
-    of the query side and per key block the two of the key side, plus the transposed mask product
-    over the state gradients (2 nb^2 d^2 per head; gated: 2 nb d^2, one row per head).
-    """
+def backward_numbers(w, qd, kd, vd, steps, warmup):
+    """One training forward, then `warmup` untimed and `steps` timed backward calls on a fixed seeded
+    dO: wall and HIP-event ms per backward, executed FLOPs (as bench_backward states them), the
+    critical pairs and the achieved TFLOP/s."""
     import torch
     import block_sparse_linear_mean_amd as sla
     from workloads import make_inputs
@@ -281,18 +274,18 @@ def bench_backward(args, w, qd, kd, vd):
     grads = (torch.empty(qd.shape, device=qd.device, dtype=torch.float32),
              torch.empty(kd.shape, device=qd.device, dtype=torch.float32),
              torch.empty(kd.shape, device=qd.device, dtype=torch.float32))
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.backward(dout, grads=grads)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     ev[0].record()
-    for s_ in range(args.steps):
+    for s_ in range(steps):
         layer.backward(dout, grads=grads)
         ev[s_ + 1].record()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms_gpu = ev[0].elapsed_time(ev[-1]) / args.steps
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ms_gpu = ev[0].elapsed_time(ev[-1]) / steps
     entries = int(layer.maps["crit_rowptr"][-1].item())
     pairs = entries * (w.Hq // w.Hkv if layer.group else 1)
     d, nb, BH, BK = w.d, w.nb, w.B * w.Hq, w.B * w.Hkv
@@ -301,6 +294,66 @@ def bench_backward(args, w, qd, kd, vd):
         flops += BH * nb * 3 * 2.0 * 64 * d * d + BK * nb * 2 * 2.0 * 64 * d * d
         flops += BH * 2.0 * (nb if layer.lin == sla.SLA_LIN_MARGINAL else 1) * nb * d * d
     achieved = flops / (ms_gpu / 1e3) / 1e12
+    return dict(ms_per_step=ms_step, gpu_ms=ms_gpu, flops=flops, pairs=pairs, achieved=achieved)
+
+
+def other_workloads(dev, steps, warmup):
+    """The layer forward of the salad and nsa_prefill workloads and the backward of wan13b_sla, each
+    on its own seeded inputs in this process (wall ms per step over `steps` after `warmup`), so that
+    the default run times them beside the headline."""
+    import torch
+    import block_sparse_linear_mean_amd as sla
+    from workloads import WORKLOADS, make_inputs
+    out = {}
+    for name in ("salad", "nsa_prefill"):
+        w = WORKLOADS[name]
+        log(f"bench: other workload {name}: inputs")
+        q, k, v, wg = make_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        layer = sla.SlaForward(qd, kd, vd, w.Nv, w.mode, kh_bp=w.kh_bp, kl_bp=w.kl_bp, n_sel=w.n_sel,
+                               window=w.window, w_gate=None if wg is None else wg.to(dev))
+        for _ in range(warmup):
+            layer.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.run()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out[name] = {"pass": "forward", "ms_per_step": round(ms, 5),
+                     "value": round(w.dense_flops() / (ms / 1e3) / 1e12, 3),
+                     "unit": "TFLOP/s (effective, dense-equivalent)", "metric": metric_for(w)}
+        log(f"bench: {name} forward {ms:.4f} ms/layer")
+        del layer, qd, kd, vd
+        torch.cuda.empty_cache()
+    w = WORKLOADS["wan13b_sla"]
+    log("bench: other workload wan13b_sla backward: inputs")
+    q, k, v, _ = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    r = backward_numbers(w, qd, kd, vd, steps, warmup)
+    out["wan13b_sla_backward"] = {"pass": "backward (dQ, dK, dV)", "ms_per_step": round(r["ms_per_step"], 5),
+                                  "gpu_ms": round(r["gpu_ms"], 5), "executed_flops": r["flops"],
+                                  "mfma_frac": round(r["achieved"] / PEAK_BF16_TFLOPS, 4)}
+    log(f"bench: wan13b_sla backward {r['ms_per_step']:.4f} ms/layer")
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    out["note"] = f"{warmup} warm-up and {steps} timed steps each, wall clock, after the headline's timed region"
+    return out
+
+
+def bench_backward(args, w, qd, kd, vd):
+    """Time the backward (dQ, dK, dV, and dw_gate for SALAD, of one layer for its block map) and
+    print one JSON line.
+
+    The forward runs once in training mode (it also keeps each row's log-sum-exp); each timed step
+    is one backward call on a fixed seeded dO.  Executed FLOPs: per critical (query head, key block)
+    pair the seven 64 x 64 x d products of the sparse backward (S and dP in both the dQ and the
+    dK/dV kernels, dQ, dK, dV); with a linear branch, per query block the three 64 x d x d products
+    of the query side and per key block the two of the key side, plus the transposed mask product
+    over the state gradients (2 nb^2 d^2 per head; gated: 2 nb d^2, one row per head).
+    """
+    r = backward_numbers(w, qd, kd, vd, args.steps, args.warmup)
+    ms_step, ms_gpu, flops, pairs, achieved = r["ms_per_step"], r["gpu_ms"], r["flops"], r["pairs"], r["achieved"]
     dense = 2.5 * w.dense_flops()          # dense-equivalent backward: 2.5x the forward's products
     log(f"bench: backward {ms_gpu:.4f} ms/layer (HIP events), wall {ms_step:.4f}; executed {flops / 1e9:.1f} GFLOP")
     print(json.dumps({
@@ -470,6 +523,8 @@ def main():
     ap.add_argument("--workload", default="wan13b_sla")
     ap.add_argument("--cpu-sample-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip timing the salad and nsa_prefill forwards and the wan13b_sla backward")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the cold-cache steps and the copy / GEMM reference measurements")
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead")
@@ -685,6 +740,9 @@ def main():
     if not args.no_context:
         result["cold"] = cold_steps(layer, args, dev)
         result["achievable"] = achievable_peaks(dev, pass_ms["attention"], work["attention"][1])
+    if (not args.no_others and w.name == "wan13b_sla" and order is None and args.proj == "none"
+            and not args.smooth_k and not args.graph and not args.overlap):
+        result["other_workloads"] = other_workloads(dev, 10, 3)
     if args.captured_mass:
         result["captured_mass"] = captured_mass(w, qd, kd, vd)
     if args.copy_calibration_mb:
