@@ -14,13 +14,14 @@
 // A workgroup owns 256 map rows x 128 state columns; each of its 4 wavefronts takes 64 rows and
 // all 128 columns, so each expanded mask operand feeds 4 products.  H tiles (32 key
 // blocks x 128 columns, 8 KB) go straight from global memory to LDS in a 4-stage ring, in the
-// layout of the transposing LDS read that feeds the A operand; the mask comes in as one bit per
+// bank-conflict-free layout of the transposing LDS read that feeds the A operand; the mask comes in as one bit per
 // (row, key block), staged in LDS 512 key blocks at a time, and each lane expands 8 bits into
 // its B operand.  A wavefront skips a step whose 64 x 32 mask block is all zero.  Sums
 // accumulate in fp32 in a fixed order (deterministic); S is written once in bf16, the
 // precision the epilogue consumes, re-staged through LDS for 1 KB-contiguous stores.  The z columns (u) take the same
 // path from fp32 z converted to bf16 operands, in workgroups dispatched first.  State workgroups
 // are numbered so that the row tiles of one column slice run on one XCD and share its L2.
+#include "attn_tiles.h"
 #include "sla_device.h"
 #include "sla_host.h"
 
@@ -91,7 +92,10 @@ __global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restric
   // ---- H tile staging: step ks holds key blocks 32 ks .. 32 ks + 31 (rows past nkb repeat row
   // nkb - 1; their mask bits are zero), columns c0 .. c0 + 127
   const u16* hsrc = H + head * nkb * D * D + c0;
-  const int lrow = lane / 16, lchunk = (lane % 16) ^ (2 * lrow);   // trs layout: row % 4 == lrow
+  // H tiles have 256-byte rows, the rows of a d = 128 V tile: they take its layout (v_pos), whose
+  // chunk order keeps a 32-lane transposing-read pass on 64 distinct banks (the plain transposing
+  // layout puts two lanes on each bank at this row size).  Row 4 qi + lrow leaves lrow mod 4.
+  const int lrow = lane / 16, lchunk = v_chunk_at<128>(lrow, lane % 16);
   auto issue = [&](int ks) {
     lds_u8* dst = to_lds(bsm[ks % kMgStages]);
 #pragma unroll
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restric
 #pragma unroll
         for (int m = 0; m < 8; ++m) x[m] = 0.f;
       }
-      lds_store16(dst + trs_pos<256>(r, c), cvt8(x));
+      lds_store16(dst + v_pos<128>(r, c), cvt8(x));
     }
   };
 
@@ -134,7 +138,11 @@ __global__ __launch_bounds__(256) void marginal_gemm_kernel(const u16* __restric
       for (int e = 0; e < 16; ++e) acc[rr][ct][e] = 0.f;
   int aoff[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) aoff[ct] = tr_operand_off<256>(32 * ct, lane);
+  for (int ct = 0; ct < 4; ++ct) {
+    // the operand lane l reads with the two transposing reads (as tr_operand_off, in the v_pos layout)
+    const int sg = (lane / 16) % 2, kk = lane % 16, lg = lane / 32;
+    aoff[ct] = v_pos<128>(8 * lg + kk / 4, 4 * ct + 2 * sg + (kk % 4) / 2) + 8 * (kk % 2);
+  }
   const bool my_row = row0 + t < nqb;
   const uint32_t* my_bits = bits + (int64_t(bs) * nqb + min(row0 + t, nqb - 1)) * nw;
 
