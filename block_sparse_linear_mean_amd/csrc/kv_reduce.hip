@@ -24,12 +24,21 @@
 // 1 KB-contiguous wavefront stores, fp32 run sums with 16-byte stores.  The pass is HBM-bound:
 // K and V in, one state per block out.  Optionally it also writes the key block means of the
 // prediction step from the same registers, so the pooling pass need not read K again.
+#include "attn_tiles.h"
 #include "sla_device.h"
 #include "sla_host.h"
 
 #include <algorithm>
 
 namespace sla {
+
+// Per-lane offset of a 32x32x16 operand read with two transposing reads (tr_operand) from a tile in
+// the v_pos layout: the element each lane addresses is that of tr_operand_off in the plain layout.
+template <int D>
+__device__ __forceinline__ int kv_operand_off(int m0, int lane) {
+  const int sg = (lane / 16) % 2, kk = lane % 16, lg = lane / 32;
+  return v_pos<D>(8 * lg + kk / 4, m0 / 8 + 2 * sg + (kk % 4) / 2) + 8 * (kk % 2);
+}
 
 // The 16-byte pieces one thread moves per tile: element chunk e = t + 256 n of the 64 x D tile.
 // load() only issues the global loads (raw input elements stay in registers, so the loads of
@@ -76,7 +85,9 @@ struct KvPiece {
       for (int i = 0; i < 4; ++i) { out[i] = x[0][i]; out[4 + i] = x[1][i]; }
     }
   }
-  // phi(K - shift) rounded to bf16 and V (zero for padded rows), into trs-layout tiles.  A
+  // phi(K - shift) rounded to bf16 and V (zero for padded rows), into tiles in the V-tile layout of
+  // the attention (v_pos: at d = 128 the chunk order that keeps a 32-lane transposing-read pass on
+  // 64 distinct banks; at d = 64 the plain transposing layout, already conflict-free there).  A
   // thread's pieces all cover features 8 (t % kChunks) .. + 7, the 8 entries of `shift`.
   // POOL: ps = this thread's fp64 sums of its valid rows of raw K (before the shift), the
   // partial sums of the key block mean.
@@ -110,8 +121,8 @@ struct KvPiece {
         vb = cvt8(vf);
       }
       const bool ok = (valid >> n) & 1u;
-      lds_store16(kt + trs_pos<2 * D>(r, c), ok ? cvt8(f) : zero8());
-      lds_store16(vt + trs_pos<2 * D>(r, c), ok ? vb : zero8());
+      lds_store16(kt + v_pos<D>(r, c), ok ? cvt8(f) : zero8());
+      lds_store16(vt + v_pos<D>(r, c), ok ? vb : zero8());
     }
   }
 };
@@ -152,9 +163,9 @@ __global__ __launch_bounds__(256) void kv_state_kernel(const T* __restrict__ k, 
   const bool z_owner = D == 128 || w < 2;
 
   int aoff, boff[kCt];
-  aoff = tr_operand_off<RB>(32 * rt, lane);
+  aoff = kv_operand_off<D>(32 * rt, lane);
 #pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) boff[ct] = tr_operand_off<RB>(32 * (ct0 + ct), lane);
+  for (int ct = 0; ct < kCt; ++ct) boff[ct] = kv_operand_off<D>(32 * (ct0 + ct), lane);
   bf16x8 ones;
 #pragma unroll
   for (int m = 0; m < 8; ++m) ones[m] = (__bf16)1.0f;
